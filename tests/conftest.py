@@ -1,0 +1,22 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (runs the HIP library on the device)")
+    config.addinivalue_line("markers", "slow: long-running CPU check")
+
+
+def pytest_report_header(config):
+    return f"repo root: {ROOT}"
+
+
+@pytest.fixture(scope="session")
+def repo_root():
+    return ROOT
