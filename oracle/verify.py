@@ -57,8 +57,8 @@ SAMPLE, GREEDY, ONEHOT = 0, 1, 2
 ST_BAD_LAYOUT = 1         # num_draft negative or not summing to total_draft
 ST_K_TOO_LARGE = 2        # K_s > max_k
 ST_BAD_MODE = 4           # mode not in {SAMPLE, GREEDY, ONEHOT}
-ST_BAD_TEMPERATURE = 8    # SAMPLE/ONEHOT with T not finite or T <= 0
-ST_NO_DRAFT_LOGITS = 16   # SAMPLE sequence but no draft logits given
+ST_BAD_TEMPERATURE = 8    # SAMPLE/ONEHOT with T not finite or below MIN_TEMPERATURE
+ST_NO_DRAFT_LOGITS = 16   # SAMPLE sequence with K > 0 but no draft logits given
 ST_BAD_TOKEN = 32         # a proposed token outside [0, V)
 ST_NONFINITE = 64         # NaN, +inf, or an all -inf row among the used rows
 ST_ZERO_RESIDUAL = 128    # residual had no mass; drew from p instead (valid)
@@ -69,6 +69,7 @@ BAND = 1e-5               # a uniform this close to a ratio or CDF boundary is a
 CDF_ABS_BAND = 4e-7       # float32 conditioning of a residual CDF (absolute, in units of mass)
 Q_UNDERFLOW = 1e-30       # q(x) below this is in float32's underflow zone
 Z_DEGENERATE = 1e-6       # a residual with less mass than this is numerically empty in float32
+MIN_TEMPERATURE = float(np.float32(1e-6))   # smallest valid SAMPLE/ONEHOT temperature (float32 value)
 
 
 def widen(rows: np.ndarray, dtype: str) -> np.ndarray:
@@ -211,9 +212,9 @@ def verify_sequence(xt: np.ndarray, xd: Optional[np.ndarray], tokens: np.ndarray
         status |= ST_K_TOO_LARGE
     if mode not in (SAMPLE, GREEDY, ONEHOT):
         status |= ST_BAD_MODE
-    if mode in (SAMPLE, ONEHOT) and not (np.isfinite(T) and T > 0):
+    if mode in (SAMPLE, ONEHOT) and not (np.isfinite(T) and T >= MIN_TEMPERATURE):
         status |= ST_BAD_TEMPERATURE
-    if mode == SAMPLE and not draft_present:
+    if mode == SAMPLE and K > 0 and not draft_present:
         status |= ST_NO_DRAFT_LOGITS
     if K and ((tokens < 0).any() or (tokens >= vocab).any()):
         status |= ST_BAD_TOKEN

@@ -30,8 +30,11 @@ def test_status_bits():
     assert _one(t, d, [0, 1], T=0.0).status[0] == ov.ST_BAD_TEMPERATURE
     assert _one(t, d, [0, 1], T=np.inf, mode=ov.ONEHOT).status[0] == ov.ST_BAD_TEMPERATURE
     assert _one(t, d, [0, 1], T=0.0, mode=ov.GREEDY).status[0] == 0          # greedy ignores T
+    assert _one(t, d, [0, 1], T=np.float32(1e-6)).status[0] == 0
+    assert _one(t, d, [0, 1], T=np.float32(9.9e-7)).status[0] == ov.ST_BAD_TEMPERATURE
     assert _one(t, None, [0, 1]).status[0] == ov.ST_NO_DRAFT_LOGITS
     assert _one(t, None, [0, 1], mode=ov.ONEHOT).status[0] == 0
+    assert _one(t[:1], None, []).status[0] == 0                  # K = 0 reads no draft row
     assert _one(t, d, [0, 4]).status[0] == ov.ST_BAD_TOKEN
     assert _one(t, d, [-1, 0]).status[0] == ov.ST_BAD_TOKEN
     assert _one(t, None, [9, 0], T=-1.0).status[0] == ov.ST_BAD_TEMPERATURE | ov.ST_NO_DRAFT_LOGITS | ov.ST_BAD_TOKEN
