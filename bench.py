@@ -1,0 +1,242 @@
+"""Throughput of the batched speculative-decoding verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3]
+
+A step is one call of the library's verify step (prep, row statistics,
+final draw) over one batch of a synthetic workload whose inputs are already
+resident in HBM.  R distinct input sets rotate so that the 256 MB
+last-level cache cannot serve repeated reads.  Prints one JSON line:
+
+  value       verified positions per second, sum_s (K_s + 1) per step
+  roofline    the row-statistics kernel (the dominant one): algorithmic
+              bytes per launch (every streamed logit row read once) over its
+              mean duration from HIP events recorded around it on the
+              library's stream, against 8 TB/s; ``traffic`` is the HBM bytes
+              per launch measured by rocprofv3 FETCH_SIZE + WRITE_SIZE when a
+              counter summary for the current kernel source is committed
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same
+              workload, single process
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified positions/sec (B·(K+1) over V) + achieved HBM GB/s vs peak"
+PEAK_HBM_GBPS = 8000.0
+WORKLOADS = {"C0": 0, "C1": 1, "C2": 2, "C3": 3, "C4": 4}
+ROTATE = {0: 64, 1: 64, 2: 6, 3: 2, 4: 6}
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "row_stats_counters.json")
+KERNEL_SOURCE = os.path.join(ROOT, "rejection_sampling_verify_06_amd", "csrc", "sv_kernels.hip")
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def row_bytes(batch) -> dict:
+    """Algorithmic bytes of one step: every target row, and every draft row of
+    a SAMPLE sequence, read once by the row-statistics kernel; plus the final
+    draw's re-read (computed from the outputs)."""
+    bt = 2 if batch.dtype == "bf16" else 4
+    V = batch.vocab
+    K = batch.num_draft.astype(np.int64)
+    sample = batch.mode == 0
+    stats = int(V * bt * ((K + 1).sum() + (K[sample]).sum() * (batch.draft is not None)))
+    return {"row_stats": stats}
+
+
+def final_bytes(batch, accepted_len) -> int:
+    bt = 2 if batch.dtype == "bf16" else 4
+    V = batch.vocab
+    total = 0
+    for s in range(batch.batch):
+        m = int(batch.mode[s])
+        if m == 1:
+            continue
+        A, K = int(accepted_len[s]), int(batch.num_draft[s])
+        if A < 0:
+            continue
+        total += V * bt * (2 if (m == 0 and A < K) else 1)
+    return total
+
+
+def to_device(batch, torch):
+    dev = torch.device("cuda", 0)
+
+    def logits(a):
+        if a is None:
+            return None
+        if batch.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+    return dict(
+        target=logits(batch.target), draft=logits(batch.draft),
+        draft_tokens=torch.from_numpy(batch.draft_tokens).to(dev),
+        num_draft=torch.from_numpy(batch.num_draft).to(dev),
+        temperature=torch.from_numpy(batch.temperature).to(dev),
+        mode=torch.from_numpy(batch.mode).to(dev),
+        seq_ids=torch.from_numpy(batch.seq_ids.view(np.int32)).to(dev),
+    )
+
+
+def cpu_baseline(cfg: int, budget_s: float) -> dict:
+    """The CPU oracle as it stands, single process, on sequences of step 0
+    of the same workload until about ``budget_s`` seconds have been spent."""
+    import oracle
+    from workloads import make_config_batch
+    b = make_config_batch(cfg, 0)
+    off_d = np.concatenate(([0], np.cumsum(b.num_draft)[:-1])).astype(np.int64)
+    off_t = off_d + np.arange(b.batch)
+    done_pos = 0
+    nseq = 0
+    t0 = time.perf_counter()
+    for s in range(b.batch):
+        K = int(b.num_draft[s])
+        sl_t = slice(int(off_t[s]), int(off_t[s]) + K + 1)
+        sl_d = slice(int(off_d[s]), int(off_d[s]) + K)
+        oracle.verify_batch(target=b.target[sl_t], draft=None if b.draft is None else b.draft[sl_d],
+                            dtype=b.dtype, vocab=b.vocab, num_draft=b.num_draft[s:s + 1],
+                            draft_tokens=b.draft_tokens[sl_d], temperature=b.temperature[s:s + 1],
+                            mode=b.mode[s:s + 1], seq_ids=b.seq_ids[s:s + 1], seed=b.seed)
+        done_pos += K + 1
+        nseq += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_pos / dt, 3), "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nseq} of {b.batch} sequences of step 0 ({done_pos} positions), "
+                      f"{dt:.1f} s, numpy float64, one process"}
+
+
+def load_traffic(launch_bytes: float):
+    if not os.path.exists(COUNTERS_FILE):
+        return None, None
+    with open(COUNTERS_FILE) as f:
+        c = json.load(f)
+    if c.get("kernel_source_sha") != kernel_source_sha():
+        return None, c
+    return c.get("hbm_bytes_per_launch"), c
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="C3", choices=sorted(WORKLOADS))
+    ap.add_argument("--rotate", type=int, default=None, help="input sets kept resident and cycled")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true", help="time without per-kernel HIP events")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world} requested): the verify "
+              f"step of a sequence-sharded batch needs no communication, so a multi-GPU run would just repeat "
+              f"this line per device.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rejection_sampling_verify_06_amd as sv
+    from workloads import make_config_batch, config_description, CONFIG_NAMES
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sv.library_loaded_path()
+    cfg = WORKLOADS[args.workload]
+    R = args.rotate or ROTATE[cfg]
+
+    t_gen = time.perf_counter()
+    batches = [make_config_batch(cfg, i) for i in range(R)]
+    dev_in = [to_device(b, torch) for b in batches]
+    gen_s = time.perf_counter() - t_gen
+    desc = config_description(cfg)
+    maxk = max(8, int(max(b.num_draft.max() for b in batches)))
+    v = sv.Verifier(max_batch=desc["batch"], max_k=maxk, max_vocab=desc["vocab"], device=0)
+    outs = [v.make_outputs(b.batch, b.total_draft, want_pq=True, want_status=True) for b in batches]
+    packed = [v.build_args(d["target"], d["draft"], d["draft_tokens"], d["num_draft"], d["temperature"],
+                           d["mode"], d["seq_ids"], seed=b.seed, out=o, vocab=b.vocab)
+              for b, d, o in zip(batches, dev_in, outs)]
+
+    def step(i):
+        packed[i % R].seed = i
+        v.run_args(packed[i % R])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # final-draw bytes depend on the outcome; measure them on the rotating sets
+    fin_b = []
+    for r in range(R):
+        fin_b.append(final_bytes(batches[r], outs[r]["accepted_len"].cpu().numpy()))
+        st = outs[r]["status"].cpu().numpy()
+        if (st & 127).any():
+            raise RuntimeError(f"input set {r}: unexpected status bits {np.unique(st)}")
+
+    events = not args.no_kernel_events
+    if events:
+        v.timing_enable(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = {}
+    if events:
+        n, ms = v.timing_read()
+        kern = {k: ms[k] / max(n, 1) for k in ms}
+        v.timing_enable(0)
+
+    sets_used = [(args.warmup + i) % R for i in range(args.steps)]
+    pos = np.mean([batches[r].positions for r in sets_used])
+    stats_bytes = np.mean([row_bytes(batches[r])["row_stats"] for r in sets_used])
+    fin_bytes = np.mean([fin_b[r] for r in sets_used])
+    ms_step = elapsed * 1e3 / args.steps
+    value = pos * args.steps / elapsed
+
+    roofline = None
+    if events and kern.get("row_stats", 0) > 0:
+        ach = stats_bytes / (kern["row_stats"] * 1e-3) / 1e9
+        traffic, _ = load_traffic(stats_bytes)
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                    "kernel": "k_row_stats", "algorithmic_bytes_per_launch": int(stats_bytes),
+                    "mean_launch_ms": round(kern["row_stats"], 5)}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_budget)
+    line = {
+        "metric": METRIC, "value": round(float(value), 1), "unit": "positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": CONFIG_NAMES[cfg], "batch": desc["batch"], "k": desc["k"],
+                   "vocab": desc["vocab"], "logits": desc["dtype"], "rotating_input_sets": R,
+                   "positions_per_step": round(float(pos), 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "step_bytes": {"row_stats": int(stats_bytes), "final_draw": int(fin_bytes),
+                       "step_GBps": round((stats_bytes + fin_bytes) / (ms_step * 1e-3) / 1e9, 1)},
+        "kernel_ms": {k: round(x, 5) for k, x in kern.items()},
+        "input_generation_s": round(gen_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+    v.close()
+
+
+if __name__ == "__main__":
+    main()

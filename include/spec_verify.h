@@ -1,0 +1,169 @@
+/*
+ * spec_verify.h -- C interface of the batched speculative-decoding verify step
+ * (accept/reject of draft tokens plus the corrected or bonus draw) on an
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What one call computes, for every sequence s of a batch (K = K_s proposed
+ * tokens x_0..x_{K-1}, target logits at K+1 positions, draft logits at K):
+ *
+ *   p_i = softmax(target_i / T),  q_i = softmax(draft_i / T)
+ *       Both logit rows are divided by the temperature before the softmax
+ *       (gitcode.csdn.net tutorial, section 4.3).
+ *   scan i = 0..K-1: accept x_i iff u_i < min(1, p_i(x_i) / q_i(x_i)),
+ *       stop at the first rejection
+ *       ("Draft Model（草稿模型）", compassingai.com, section 2
+ *       接受-拒绝准则 and the one-step algorithm box under 技术原理).
+ *   on a rejection at A: draw from norm(max(0, p_A - q_A))
+ *       (same page, section 2; tutorial section 3.2);
+ *   if all K are accepted: draw one bonus token from p_K
+ *       (same page, the one-step algorithm box).
+ *   One round therefore emits between 1 and K+1 tokens.
+ *
+ * Modes per sequence:
+ *   SV_SAMPLE  the rule above.
+ *   SV_ONEHOT  deterministic proposal (N-gram / prompt lookup): q is the
+ *              one-hot distribution on the proposed token, so x_i is accepted
+ *              iff u_i < p_i(x_i), and a rejection draws from p_A with x_A
+ *              removed ("5.2 Draft 模型与无模型方案", AIInfraGuide, section 4.3).
+ *              No draft logits are read.
+ *   SV_GREEDY  strict greedy: accept iff x_i is the argmax of the raw target
+ *              logits (lowest index on ties); emit that argmax on a mismatch
+ *              and as the bonus.  The temperature is ignored.
+ *
+ * Randomness: u_i and the final draw's uniform come from Philox4x32-10
+ * (Salmon et al., SC'11) with key = seed and counter = (position, purpose,
+ * seq_id, 0); purpose 0 for u_i at positions 0..K-1, purpose 1 for the final
+ * draw at position A; u = (word0 >> 8) * 2^-24.  Results are a pure function
+ * of (inputs, seed, seq_ids): any call can be replayed exactly, and a batch
+ * split across calls (with global seq_ids) gives the same outputs.
+ *
+ * Final draw: inverse CDF over the unnormalised weights w (residual, one-hot
+ * residual or p_K): t = u * sum(w), emit the first token k whose inclusive
+ * prefix sum exceeds t; tokens with w = 0 are never emitted.
+ *
+ * Packed ragged layout (no padding between sequences):
+ *   off_d[s] = sum_{j<s} K_j            draft rows / draft_tokens / p,q at proposal
+ *   off_t[s] = off_d[s] + s             target rows / emitted_tokens
+ *   target row off_t[s]+i judges draft token i; row off_t[s]+K_s is the bonus row.
+ *   Logit rows are ld elements apart (ld >= vocab); columns >= vocab are never read.
+ *
+ * Arithmetic: float32 (logits are read as float32 or bfloat16 and widened
+ * exactly); exp2-based online max/sum; fixed-order reductions, no float
+ * atomics, so repeated calls are bitwise identical.
+ *
+ * Threading: a context owns device scratch memory; calls that share a context
+ * must be ordered on one stream.  Use one context per concurrent stream.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct spec_verify_ctx spec_verify_ctx;
+
+/* logits element type */
+enum { SV_F32 = 0, SV_BF16 = 1 };
+
+/* per-sequence verify mode (values of args->mode[s]) */
+enum { SV_SAMPLE = 0, SV_GREEDY = 1, SV_ONEHOT = 2 };
+
+/* return codes */
+enum {
+  SV_OK = 0,
+  SV_ERR_INVALID = -1,   /* bad argument; nothing was enqueued */
+  SV_ERR_NOMEM = -2,     /* device allocation failed (create / timing_enable only) */
+  SV_ERR_HIP = -3,       /* a HIP call failed; see spec_verify_last_error() */
+  SV_ERR_CAPACITY = -4   /* the call exceeds the sizes given to spec_verify_create */
+};
+
+/* per-sequence status bits (args->status[s]).  Any bit in 1..64 means the
+ * sequence was not verified: accepted_len = -1, its emitted slots are -1 and
+ * its p/q at proposal are NaN.  Bit 128 is informational. */
+enum {
+  SV_ST_BAD_LAYOUT = 1,        /* num_draft has a negative entry or does not sum to total_draft (set for every sequence; every output slot is cleared) */
+  SV_ST_K_TOO_LARGE = 2,       /* K_s > max_k of the context */
+  SV_ST_BAD_MODE = 4,          /* mode[s] not one of SV_SAMPLE, SV_GREEDY, SV_ONEHOT */
+  SV_ST_BAD_TEMPERATURE = 8,   /* SAMPLE/ONEHOT with temperature not finite or below SV_MIN_TEMPERATURE */
+  SV_ST_NO_DRAFT_LOGITS = 16,  /* SAMPLE sequence with K_s > 0 but draft_logits == NULL */
+  SV_ST_BAD_TOKEN = 32,        /* a proposed token outside [0, vocab) */
+  SV_ST_NONFINITE = 64,        /* a used logit row holds NaN or +inf, or is entirely -inf */
+  SV_ST_ZERO_RESIDUAL = 128    /* the residual had no mass (rounding only); the token was drawn from p_A instead */
+};
+
+/* smallest accepted temperature for SAMPLE/ONEHOT (float32 1e-6) */
+#define SV_MIN_TEMPERATURE 1e-6f
+
+typedef struct spec_verify_args {
+  int32_t batch;               /* B >= 0 (host value); 0 is a no-op */
+  int64_t vocab;               /* V >= 1 (host value) */
+  int64_t total_draft;         /* sum_s K_s (host value): sizes the grids, must match num_draft */
+  int32_t target_dtype;        /* SV_F32 or SV_BF16 */
+  int32_t draft_dtype;         /* SV_F32 or SV_BF16 (ignored when draft_logits == NULL) */
+  const void* target_logits;   /* device, [total_draft + B][ld_target] */
+  int64_t ld_target;           /* elements between target rows, >= vocab */
+  const void* draft_logits;    /* device, [total_draft][ld_draft], or NULL if no SV_SAMPLE sequence has K_s > 0 */
+  int64_t ld_draft;            /* elements between draft rows, >= vocab */
+  const int32_t* draft_tokens; /* device, [total_draft]; may be NULL iff total_draft == 0 */
+  const int32_t* num_draft;    /* device, [B], K_s */
+  const float* temperature;    /* device, [B], or NULL (= 1.0 for every sequence) */
+  const uint8_t* mode;         /* device, [B], or NULL (= SV_SAMPLE for every sequence) */
+  const uint32_t* seq_ids;     /* device, [B], or NULL (= s): Philox counter word 2 */
+  uint64_t seed;               /* Philox key */
+  int32_t* accepted_len;       /* device out, [B]: accepted draft tokens A_s (0..K_s), -1 if not verified */
+  int32_t* emitted_tokens;     /* device out, [total_draft + B]: seq s at off_t[s]: x_0..x_{A-1}, y, then -1 */
+  float* p_at_proposal;        /* device out, [total_draft] or NULL: p_i(x_i) for every i < K_s (T = 1 for GREEDY) */
+  float* q_at_proposal;        /* device out, [total_draft] or NULL: q_i(x_i); 1.0 for ONEHOT and GREEDY */
+  int32_t* status;             /* device out, [B] or NULL: SV_ST_* bits */
+} spec_verify_args;
+
+/* Create a context on HIP device `device` for batches of at most max_batch
+ * sequences, K_s <= max_k (1..128) and vocab <= max_vocab.  Allocates the
+ * context's device scratch (per-row partial statistics, per-sequence
+ * records, tile sums); the caller owns every input and output
+ * buffer.  Returns SV_OK and sets *out, or an error code (then *out = NULL). */
+int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int32_t max_k, int64_t max_vocab);
+
+/* Enqueue one verify step on `hip_stream` (a hipStream_t; NULL = the null
+ * stream).  Validates the host-side arguments first (SV_ERR_INVALID /
+ * SV_ERR_CAPACITY: nothing is enqueued); problems that only the device can
+ * see are reported per sequence through `status`.  Does not allocate, does
+ * not synchronise; outputs are valid once the stream has reached this point.
+ * Launches four kernels: row statistics (one block per 32 KB of every logit
+ * row), scan (one block per sequence: acceptance test), tile sums and select
+ * (the final draw at the stop position). */
+int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* args, void* hip_stream);
+
+/* Free the context and its device memory.  NULL is accepted. */
+void spec_verify_destroy(spec_verify_ctx* ctx);
+
+/* Message of the last failing call on this thread (static storage). */
+const char* spec_verify_last_error(void);
+
+/* ---- measurement hooks ---------------------------------------------------
+ * spec_verify_timing_enable(ctx, n) makes the next n calls of
+ * spec_verify_run record a HIP event before and after each of its four
+ * kernels on the call's stream (n = 0 turns it off; events are created here,
+ * never inside run).  spec_verify_timing_read waits for those events and
+ * returns the number of recorded calls and, per kernel, the summed elapsed
+ * milliseconds (ms_per_kernel has SV_NUM_KERNELS entries: row statistics,
+ * scan, tile sums, select), then resets the record. */
+#define SV_NUM_KERNELS 4
+int spec_verify_timing_enable(spec_verify_ctx* ctx, int32_t max_calls);
+int spec_verify_timing_read(spec_verify_ctx* ctx, int32_t* calls, double* ms_per_kernel);
+
+/* Library version string. */
+const char* spec_verify_version(void);
+
+/* sizeof(spec_verify_args) as compiled into the library, so that a binding
+ * can check its own copy of the struct layout. */
+int64_t spec_verify_args_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,211 @@
+"""Batched speculative-decoding verify step on AMD MI355X (gfx950).
+
+A thin Python face of the C library ``libspec_verify.so`` (include/spec_verify.h).
+Everything the verify step computes runs in the library's HIP kernels; this
+module only checks tensor shapes and passes device pointers and torch's
+current stream.  PyTorch supplies device memory and streams.
+
+    v = Verifier(max_batch=256, max_k=8, max_vocab=152064)
+    out = v.run(target, draft, draft_tokens, num_draft, temperature, mode, seed=step)
+    out["accepted_len"], out["emitted"], out["p_at"], out["q_at"], out["status"]
+
+If the library has not been built, every entry point raises ``LibraryMissing``:
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    SV_F32, SV_BF16, SV_SAMPLE, SV_GREEDY, SV_ONEHOT,
+    SV_ST_BAD_LAYOUT, SV_ST_K_TOO_LARGE, SV_ST_BAD_MODE, SV_ST_BAD_TEMPERATURE,
+    SV_ST_NO_DRAFT_LOGITS, SV_ST_BAD_TOKEN, SV_ST_NONFINITE, SV_ST_ZERO_RESIDUAL,
+    KERNEL_NAMES, LibraryMissing,
+)
+
+__all__ = ["Verifier", "VerifyError", "verify", "LibraryMissing", "KERNEL_NAMES"]
+
+
+class VerifyError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"spec_verify error {code}: {msg}")
+        self.code = code
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise VerifyError(rc, _lib.last_error())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _logits_dtype(t, torch):
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _need(t, name, dtypes, torch, numel=None, device=None):
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+
+
+class Verifier:
+    """One library context (device scratch sized for the given maxima)."""
+
+    def __init__(self, max_batch: int, max_k: int, max_vocab: int, device: Optional[int] = None):
+        import torch
+        self._torch = torch
+        self._lib = _lib.load()
+        self.device = torch.cuda.current_device() if device is None else int(device)
+        self.max_batch, self.max_k, self.max_vocab = int(max_batch), int(max_k), int(max_vocab)
+        h = ctypes.c_void_p()
+        _check(self._lib.spec_verify_create(ctypes.byref(h), self.device, self.max_batch, self.max_k,
+                                            self.max_vocab))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.spec_verify_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- outputs ------------------------------------------------------------
+    def make_outputs(self, batch: int, total_draft: int, want_pq: bool = True, want_status: bool = True) -> dict:
+        torch = self._torch
+        dev = torch.device("cuda", self.device)
+        return {
+            "accepted_len": torch.empty(batch, dtype=torch.int32, device=dev),
+            "emitted": torch.empty(total_draft + batch, dtype=torch.int32, device=dev),
+            "p_at": torch.empty(total_draft, dtype=torch.float32, device=dev) if want_pq else None,
+            "q_at": torch.empty(total_draft, dtype=torch.float32, device=dev) if want_pq else None,
+            "status": torch.empty(batch, dtype=torch.int32, device=dev) if want_status else None,
+        }
+
+    # -- the step -------------------------------------------------------------
+    def build_args(self, target, draft, draft_tokens, num_draft, temperature=None, mode=None, seq_ids=None,
+                   seed: int = 0, out: Optional[dict] = None, vocab: Optional[int] = None,
+                   total_draft: Optional[int] = None) -> "_lib.SpecVerifyArgs":
+        """Check shapes and pack the argument struct (no device work)."""
+        torch = self._torch
+        dev = torch.device("cuda", self.device)
+        if target.dim() != 2 or target.stride(1) != 1:
+            raise ValueError("target must be 2-D with unit column stride")
+        B = int(num_draft.numel())
+        T = int(draft_tokens.numel()) if total_draft is None else int(total_draft)
+        V = int(target.shape[1]) if vocab is None else int(vocab)
+        if target.shape[0] != T + B:
+            raise ValueError(f"target has {target.shape[0]} rows, expected total_draft + B = {T + B}")
+        if not target.is_cuda or target.device != dev:
+            raise ValueError("target must be on the context's device")
+        if draft is not None and draft.numel() == 0:
+            draft = None
+        if draft is not None:
+            if draft.dim() != 2 or draft.stride(1) != 1 or draft.shape[0] != T or not draft.is_cuda:
+                raise ValueError("draft must be a 2-D device tensor [total_draft, >= vocab] with unit column stride")
+        _need(draft_tokens, "draft_tokens", (torch.int32,), torch, T, dev)
+        _need(num_draft, "num_draft", (torch.int32,), torch, B, dev)
+        _need(temperature, "temperature", (torch.float32,), torch, B, dev)
+        _need(mode, "mode", (torch.uint8,), torch, B, dev)
+        _need(seq_ids, "seq_ids", (torch.int32, getattr(torch, "uint32", torch.int32)), torch, B, dev)
+        if out is None:
+            raise ValueError("out is required (see make_outputs)")
+        _need(out["accepted_len"], "accepted_len", (torch.int32,), torch, B, dev)
+        _need(out["emitted"], "emitted", (torch.int32,), torch, T + B, dev)
+        _need(out.get("p_at"), "p_at", (torch.float32,), torch, T, dev)
+        _need(out.get("q_at"), "q_at", (torch.float32,), torch, T, dev)
+        _need(out.get("status"), "status", (torch.int32,), torch, B, dev)
+        a = _lib.SpecVerifyArgs()
+        a.batch = B
+        a.vocab = V
+        a.total_draft = T
+        a.target_dtype = _logits_dtype(target, torch)
+        a.draft_dtype = _logits_dtype(draft, torch) if draft is not None else SV_F32
+        a.target_logits = target.data_ptr()
+        a.ld_target = target.stride(0)
+        a.draft_logits = _ptr(draft)
+        a.ld_draft = draft.stride(0) if draft is not None else 0
+        a.draft_tokens = _ptr(draft_tokens) if T > 0 else None
+        a.num_draft = num_draft.data_ptr()
+        a.temperature = _ptr(temperature)
+        a.mode = _ptr(mode)
+        a.seq_ids = _ptr(seq_ids)
+        a.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+        a.accepted_len = out["accepted_len"].data_ptr()
+        a.emitted_tokens = out["emitted"].data_ptr()
+        a.p_at_proposal = _ptr(out.get("p_at"))
+        a.q_at_proposal = _ptr(out.get("q_at"))
+        a.status = _ptr(out.get("status"))
+        return a
+
+    def run_args(self, args: "_lib.SpecVerifyArgs", stream=None):
+        """Enqueue one step from a packed argument struct on ``stream``
+        (default: torch's current stream on the context's device)."""
+        s = self._torch.cuda.current_stream(self.device) if stream is None else stream
+        _check(self._lib.spec_verify_run(self._h, ctypes.byref(args), ctypes.c_void_p(s.cuda_stream)))
+
+    def run(self, target, draft, draft_tokens, num_draft, temperature=None, mode=None, seq_ids=None,
+            seed: int = 0, out: Optional[dict] = None, want_pq: bool = True, want_status: bool = True,
+            vocab: Optional[int] = None, total_draft: Optional[int] = None, stream=None) -> dict:
+        if out is None:
+            T = int(draft_tokens.numel()) if total_draft is None else int(total_draft)
+            out = self.make_outputs(int(num_draft.numel()), T, want_pq, want_status)
+        args = self.build_args(target, draft, draft_tokens, num_draft, temperature, mode, seq_ids, seed, out,
+                               vocab, total_draft)
+        self.run_args(args, stream)
+        return out
+
+    # -- measurement hooks ------------------------------------------------------
+    def timing_enable(self, max_calls: int):
+        _check(self._lib.spec_verify_timing_enable(self._h, int(max_calls)))
+
+    def timing_read(self):
+        calls = ctypes.c_int32()
+        ms = (ctypes.c_double * _lib.SV_NUM_KERNELS)()
+        _check(self._lib.spec_verify_timing_read(self._h, ctypes.byref(calls), ms))
+        return int(calls.value), dict(zip(KERNEL_NAMES, list(ms)))
+
+
+_CACHE: dict = {}
+
+
+def verify(target, draft, draft_tokens, num_draft, temperature=None, mode=None, seed: int = 0,
+           want_pq: bool = False, seq_ids=None) -> dict:
+    """One-shot verify step with a cached context sized for the call."""
+    import torch
+    dev = target.device.index if target.device.index is not None else torch.cuda.current_device()
+    B = int(num_draft.numel())
+    T = int(draft_tokens.numel())
+    kmax = 128 if B == 0 else max(1, min(128, T))
+    key = (dev, B, kmax, int(target.shape[1]))
+    v = _CACHE.get(key)
+    if v is None:
+        v = _CACHE[key] = Verifier(max(B, 1), kmax, int(target.shape[1]), dev)
+    return v.run(target, draft, draft_tokens, num_draft, temperature, mode, seq_ids, seed, want_pq=want_pq)
+
+
+def library_loaded_path() -> str:
+    """Path of the loaded library (raises LibraryMissing if not built)."""
+    _lib.load()
+    return _lib.library_path()

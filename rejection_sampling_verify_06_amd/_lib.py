@@ -1,0 +1,99 @@
+"""ctypes view of the C interface in include/spec_verify.h (marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import library_path
+
+# values from include/spec_verify.h
+SV_F32, SV_BF16 = 0, 1
+SV_SAMPLE, SV_GREEDY, SV_ONEHOT = 0, 1, 2
+SV_OK, SV_ERR_INVALID, SV_ERR_NOMEM, SV_ERR_HIP, SV_ERR_CAPACITY = 0, -1, -2, -3, -4
+SV_ST_BAD_LAYOUT = 1
+SV_ST_K_TOO_LARGE = 2
+SV_ST_BAD_MODE = 4
+SV_ST_BAD_TEMPERATURE = 8
+SV_ST_NO_DRAFT_LOGITS = 16
+SV_ST_BAD_TOKEN = 32
+SV_ST_NONFINITE = 64
+SV_ST_ZERO_RESIDUAL = 128
+SV_NUM_KERNELS = 4
+KERNEL_NAMES = ("row_stats", "scan", "tile_sums", "select")
+
+EXPORTED = (
+    "spec_verify_create", "spec_verify_run", "spec_verify_destroy", "spec_verify_last_error",
+    "spec_verify_timing_enable", "spec_verify_timing_read", "spec_verify_version",
+    "spec_verify_args_size",
+)
+
+
+class SpecVerifyArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("vocab", ctypes.c_int64),
+        ("total_draft", ctypes.c_int64),
+        ("target_dtype", ctypes.c_int32),
+        ("draft_dtype", ctypes.c_int32),
+        ("target_logits", ctypes.c_void_p),
+        ("ld_target", ctypes.c_int64),
+        ("draft_logits", ctypes.c_void_p),
+        ("ld_draft", ctypes.c_int64),
+        ("draft_tokens", ctypes.c_void_p),
+        ("num_draft", ctypes.c_void_p),
+        ("temperature", ctypes.c_void_p),
+        ("mode", ctypes.c_void_p),
+        ("seq_ids", ctypes.c_void_p),
+        ("seed", ctypes.c_uint64),
+        ("accepted_len", ctypes.c_void_p),
+        ("emitted_tokens", ctypes.c_void_p),
+        ("p_at_proposal", ctypes.c_void_p),
+        ("q_at_proposal", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+    ]
+
+
+_LIB = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def load() -> ctypes.CDLL:
+    """Load libspec_verify.so.  torch is imported first so that the library
+    binds to the HIP runtime torch already loaded (one runtime per process,
+    so torch's stream handles are valid in the library)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    import torch  # noqa: F401  (loads torch's HIP runtime first)
+    path = library_path()
+    if not os.path.exists(path):
+        raise LibraryMissing(f"{path} is not built; run __graft_entry__.build() (hipcc for gfx950)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.spec_verify_create.argtypes = [ctypes.POINTER(P), ctypes.c_int, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
+    lib.spec_verify_create.restype = ctypes.c_int
+    lib.spec_verify_run.argtypes = [P, ctypes.POINTER(SpecVerifyArgs), P]
+    lib.spec_verify_run.restype = ctypes.c_int
+    lib.spec_verify_destroy.argtypes = [P]
+    lib.spec_verify_destroy.restype = None
+    lib.spec_verify_last_error.argtypes = []
+    lib.spec_verify_last_error.restype = ctypes.c_char_p
+    lib.spec_verify_timing_enable.argtypes = [P, ctypes.c_int32]
+    lib.spec_verify_timing_enable.restype = ctypes.c_int
+    lib.spec_verify_timing_read.argtypes = [P, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]
+    lib.spec_verify_timing_read.restype = ctypes.c_int
+    lib.spec_verify_version.argtypes = []
+    lib.spec_verify_version.restype = ctypes.c_char_p
+    lib.spec_verify_args_size.argtypes = []
+    lib.spec_verify_args_size.restype = ctypes.c_int64
+    if lib.spec_verify_args_size() != ctypes.sizeof(SpecVerifyArgs):
+        raise RuntimeError("spec_verify_args layout differs between the library and the binding")
+    _LIB = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().spec_verify_last_error().decode(errors="replace")

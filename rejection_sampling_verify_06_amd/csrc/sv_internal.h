@@ -1,0 +1,95 @@
+// Internal layout shared by the host library (sv_api.cpp) and the kernels
+// (sv_kernels.hip).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kThreads = 256;           // every kernel: 4 waves of 64
+constexpr int kChunkBytes = 32768;      // bytes of one logit row streamed by one row-stats block
+constexpr int kTileElems = 8192;        // elements of a row per final-draw block
+constexpr int kTileVec = kTileElems / kThreads;   // elements per thread in a tile (32)
+constexpr int kMaxK = 128;
+constexpr int kMaxTiles = 256;          // => vocab <= 2,097,152
+
+// Row statistics of one chunk of one row: max of the raw logits m, the sum
+// s = sum exp2(x*c - round(m*c)), and the lowest index attaining m.
+struct Partial {
+  float m;
+  float s;
+  int32_t idx;
+  int32_t pad;
+};
+
+enum FinalKind : int32_t {
+  kFinalDone = 0,         // nothing left for the final-draw kernel
+  kFinalResidual = 1,     // w = max(0, p_A - q_A)
+  kFinalOnehot = 2,       // w = p_A with the proposed token removed
+  kFinalBonus = 3         // w = p_K
+};
+
+// What the final draw needs, written by the scan kernel for every sequence.
+struct SeqFinal {
+  int32_t kind;
+  int32_t A;
+  int32_t trow;       // target row of position A
+  int32_t drow;       // draft row of position A (kFinalResidual)
+  float mct;          // round(M_t * c) of target row A
+  float inv_st;       // 1 / S_t
+  float mcd;          // round(M_d * c) of draft row A
+  float inv_sd;       // 1 / S_d
+  float c;
+  float u;            // uniform of the final draw
+  int32_t xhat;       // proposed token at A (kFinalOnehot)
+  int32_t emit_pos;   // slot of the final token in emitted_tokens
+  int32_t s;
+  int32_t pad[3];
+};
+
+struct Params {
+  int32_t B;
+  int32_t V;
+  int32_t total_draft;
+  int32_t max_k;
+  int32_t n_t;        // target rows = total_draft + B
+  int32_t n_d;        // draft rows streamed = total_draft, or 0 without draft logits
+  const void* tgt;
+  int64_t ld_t;
+  int32_t t_bf16;
+  int32_t t_vec;      // rows 16-byte aligned: vector loads allowed
+  const void* dft;
+  int64_t ld_d;
+  int32_t d_bf16;
+  int32_t d_vec;
+  const int32_t* tokens;
+  const int32_t* num_draft;
+  const float* temperature;   // never NULL on the device: the host substitutes
+  const uint8_t* mode;        // the context's default arrays (1.0, SAMPLE, s)
+  const uint32_t* seq_ids;
+  uint32_t seed_lo;
+  uint32_t seed_hi;
+  int32_t* accepted_len;
+  int32_t* emitted;
+  float* p_at;
+  float* q_at;
+  int32_t* status;
+  // scratch owned by the context
+  Partial* partials;  // target row r chunk k at r*nch_t + k; draft row r at n_t*nch_t + r*nch_d + k
+  SeqFinal* fin;      // [B]
+  float* tilesum;     // [B * ntiles]
+  int32_t nch_t;      // chunks per target row
+  int32_t nch_d;      // chunks per draft row
+  int32_t ce_t;       // elements per target chunk (32 KB)
+  int32_t ce_d;       // elements per draft chunk (32 KB)
+  int32_t ntiles;     // tiles per row for the final draw
+};
+
+// The four kernels of one verify step, in stream order.
+hipError_t launch_row_stats(const Params& p, hipStream_t st);
+hipError_t launch_scan(const Params& p, hipStream_t st);
+hipError_t launch_tile_sums(const Params& p, hipStream_t st);
+hipError_t launch_select(const Params& p, hipStream_t st);
+
+}  // namespace sv

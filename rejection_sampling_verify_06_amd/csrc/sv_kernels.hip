@@ -1,0 +1,926 @@
+// Kernels of the batched speculative-decoding verify step for gfx950.
+//
+// row_stats   one block per (logit row, 32 KB chunk).  The block issues its
+//             chunk's 16-byte non-temporal loads first, then finds the
+//             sequence that owns the row (a wave-level scan of num_draft,
+//             served from cache while the chunk is in flight), and reduces
+//             the chunk in float32 to (max of the raw logits, sum of
+//             exp2(x*c - round(max*c)), lowest-index argmax for greedy rows)
+//             with wave shuffles and LDS across the 4 waves.  No inter-block
+//             communication.
+// scan        one block per sequence: validates the sequence, merges its
+//             rows' chunk partials in a fixed order, computes p and q at the
+//             proposals, draws the Philox uniforms, runs the left-to-right
+//             acceptance test and writes everything but the final token.
+// tile_sums   one block per (sequence, 8192-element tile) of the row(s) at
+//             the stop position: sum of the unnormalised final weights.
+// select      one block per sequence: picks the tile holding t = u * Z,
+//             re-reads it, prefix-sums it across the block and emits the
+//             first token whose inclusive prefix exceeds t.
+//
+// The method (accept with probability min(1, p/q), stop at the first
+// rejection, redraw from norm(max(0, p - q)) or take a bonus token from the
+// next target distribution) follows "Draft Model（草稿模型）"
+// (compassingai.com) section 2 and its one-step algorithm box; the one-hot
+// proposal follows "5.2 Draft 模型与无模型方案" (AIInfraGuide) section 4.3;
+// temperature on both rows follows the gitcode.csdn.net tutorial section 4.3.
+// The path is a memory-bound streaming reduction: no matrix cores are used.
+// Blocks never wait on one another: ordering comes only from kernel
+// boundaries, so there are no device-scope fences (each one writes back a
+// whole L2 on this chip) and no spin loops.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sv_internal.h"
+
+namespace sv {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kNV = 8;   // 16-byte vectors per thread per 32 KB chunk
+constexpr int kSample = 0, kGreedy = 1, kOnehot = 2;
+constexpr int kStBadLayout = 1, kStKTooLarge = 2, kStBadMode = 4, kStBadTemp = 8, kStNoDraft = 16,
+              kStBadToken = 32, kStNonfinite = 64, kStZeroResidual = 128;
+constexpr float kMinTemperature = 1e-6f;
+constexpr uint32_t kNaNBits = 0x7FC00000u;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
+// multiply/xor S-box with the key bumped by the Weyl constants between rounds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo_a = 0xD2511F53u * c0, hi_a = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo_b = 0xCD9E8D57u * c2, hi_b = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi_b ^ c1 ^ k0;
+    const uint32_t n2 = hi_a ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo_b;
+    c2 = n2;
+    c3 = lo_a;
+  }
+  return c0;
+}
+
+// uniform in [0, 1) on the 2^-24 grid for (sequence, position, purpose)
+__device__ __forceinline__ float draw_uniform(const Params& P, uint32_t seq_id, uint32_t pos, uint32_t purpose) {
+  const uint32_t w = philox_word0(pos, purpose, seq_id, 0u, P.seed_lo, P.seed_hi);
+  return (float)(w >> 8) * 0x1p-24f;
+}
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float load_logit(const void* base, int64_t idx, int bf16) {
+  if (bf16) return __uint_as_float(((uint32_t)((const uint16_t*)base)[idx]) << 16);
+  return ((const float*)base)[idx];
+}
+
+// Merge two (max, scaled sum, argmax) triples.  s is relative to
+// round(m * c); the result is relative to round(max(m, m2) * c).  The
+// products are rounded on their own (the library is built without implicit
+// fusion), so a partial is rescaled by exactly the reference it was summed
+// against.  NaN in a sum propagates; two empty (-inf) sides add their sums.
+template <bool ARG>
+__device__ __forceinline__ void merge_stats(float& m, float& s, int& idx, float m2, float s2, int idx2, float c) {
+  const float mn = fmaxf(m, m2);
+  if (ARG) idx = (m2 > m) ? idx2 : ((m > m2) ? idx : min(idx, idx2));
+  if (mn == -INFINITY) {
+    s = s + s2;
+  } else {
+    const float mc = mn * c;
+    s = s * fexp2(m * c - mc) + s2 * fexp2(m2 * c - mc);
+  }
+  m = mn;
+}
+
+template <bool ARG>
+__device__ __forceinline__ void wave_merge(float& m, float& s, int& idx, float c) {
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, kWave);
+    const float s2 = __shfl_xor(s, off, kWave);
+    const int i2 = ARG ? __shfl_xor(idx, off, kWave) : 0;
+    merge_stats<ARG>(m, s, idx, m2, s2, i2, c);
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int64_t o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// which sequence owns a row, with its temperature and mode.  Every wave
+// works it out on its own (no LDS, no barrier): lane l takes a window of
+// consecutive sequences, sums their row counts (K_s + 1 target rows or K_s
+// draft rows), a wave scan gives each lane its first row, and the lane whose
+// interval holds the row names the owner.  Returns -1 if no sequence owns
+// the row (inconsistent num_draft: the scan kernel then reports a bad
+// layout).
+//
+// Batches of up to 256 sequences use a 4-sequence window per lane that is
+// loaded before the chunk's own loads are issued: vector loads complete in
+// issue order, so the lookup then never waits for the chunk.
+// ---------------------------------------------------------------------------
+constexpr int kWin = 4;
+
+struct SeqWindow {
+  int k[kWin];
+  float T[kWin];
+  int md[kWin];
+};
+
+// Raw loads only (index clamped, no branches): nothing reads these registers
+// until the chunk's loads have been issued.
+__device__ __forceinline__ SeqWindow load_window(const Params& P) {
+  SeqWindow w;
+  const int base = (threadIdx.x & (kWave - 1)) * kWin;
+#pragma unroll
+  for (int i = 0; i < kWin; ++i) {
+    const int s = min(base + i, P.B - 1);
+    w.k[i] = P.num_draft[s];
+    w.T[i] = P.temperature[s];
+    w.md[i] = P.mode[s];
+  }
+  return w;
+}
+
+struct Owner {
+  int s;
+  float T;
+  int md;
+};
+
+// lowest lane that claims the row (a consistent layout has exactly one)
+__device__ __forceinline__ Owner owner_from_lanes(int owner, float T, int md) {
+  const unsigned long long hits = __ballot(owner >= 0);
+  Owner o{-1, 1.f, kSample};
+  if (hits == 0ull) return o;
+  const int src = (int)__builtin_ctzll(hits);
+  o.s = __builtin_amdgcn_readfirstlane(__shfl(owner, src, kWave));
+  o.T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(__shfl(T, src, kWave))));
+  o.md = __builtin_amdgcn_readfirstlane(__shfl(md, src, kWave));
+  return o;
+}
+
+// 32-bit unsigned arithmetic (wraps instead of overflowing on a corrupt
+// num_draft; a consistent layout has fewer than 2^31 rows).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ Owner owner_in_window(const SeqWindow& w, const Params& P, int plus_one, int r) {
+  const int base = (threadIdx.x & (kWave - 1)) * kWin;
+  uint32_t cnt[kWin];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < kWin; ++i) {
+    cnt[i] = (base + i < P.B) ? (uint32_t)w.k[i] + (uint32_t)plus_one : 0u;
+    sum += cnt[i];
+  }
+  uint32_t start = wave_incl_scan_u32(sum) - sum;
+  int owner = -1;
+  float T = 1.f;
+  int md = kSample;
+  const uint32_t ur = (uint32_t)r;
+#pragma unroll
+  for (int i = 0; i < kWin; ++i) {
+    // (ur - start) < cnt  <=>  start <= ur < start + cnt, without overflow
+    if (ur - start < cnt[i]) {
+      owner = base + i;
+      T = w.T[i];
+      md = w.md[i];
+    }
+    start += cnt[i];
+  }
+  return owner_from_lanes(owner, T, md);
+}
+
+// any batch size: lane l takes sequences [l*per, (l+1)*per)
+__device__ __forceinline__ Owner owner_general(const Params& P, int plus_one, int64_t r) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int per = (P.B + kWave - 1) / kWave;
+  const int lo = min(P.B, lane * per), hi = min(P.B, lo + per);
+  int64_t sum = 0;
+  for (int s = lo; s < hi; ++s) sum += (int64_t)P.num_draft[s] + plus_one;
+  int64_t start = wave_incl_scan_i64(sum) - sum;
+  int owner = -1;
+  for (int s = lo; s < hi; ++s) {
+    const int64_t cnt = (int64_t)P.num_draft[s] + plus_one;
+    if (r >= start && r < start + cnt) owner = s;
+    start += cnt;
+  }
+  const float T = (owner >= 0) ? P.temperature[owner] : 1.f;
+  const int md = (owner >= 0) ? (int)P.mode[owner] : kSample;
+  return owner_from_lanes(owner, T, md);
+}
+
+// ---------------------------------------------------------------------------
+// thread-local statistics of a chunk
+// ---------------------------------------------------------------------------
+
+template <bool BF16>
+__device__ __forceinline__ void load_chunk(const char* rowp, int c0, u32x4 (&v)[kNV]) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int ES = BF16 ? 2 : 4;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kNV; ++u) {
+    const int e = c0 + (u * kThreads + t) * VEC;
+    v[u] = __builtin_nontemporal_load((const u32x4*)(rowp + (int64_t)e * ES));
+  }
+}
+
+// Full 32 KB chunk in registers: thread t holds vectors (u*256 + t), u < 8.
+template <bool BF16, bool ARG>
+__device__ __forceinline__ void stats_from_regs(const u32x4 (&v)[kNV], int c0, float c, float& m_out, float& s_out,
+                                                int& i_out) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int N = kNV * VEC;
+  const int t = threadIdx.x;
+  float f[N];
+#pragma unroll
+  for (int u = 0; u < kNV; ++u) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w = v[u][q];
+      if (BF16) {
+        f[u * VEC + 2 * q] = bf_lo(w);
+        f[u * VEC + 2 * q + 1] = bf_hi(w);
+      } else {
+        f[u * VEC + q] = __uint_as_float(w);
+      }
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < N; ++k) mx = fmaxf(mx, f[k]);
+  const float mc = (mx == -INFINITY) ? 0.f : mx * c;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+  for (int k = 0; k < N; k += 4) {
+    a0 += fexp2(fmaf(f[k + 0], c, -mc));
+    a1 += fexp2(fmaf(f[k + 1], c, -mc));
+    a2 += fexp2(fmaf(f[k + 2], c, -mc));
+    a3 += fexp2(fmaf(f[k + 3], c, -mc));
+  }
+  s_out = (a0 + a1) + (a2 + a3);
+  m_out = mx;
+  int idx = 0x7FFFFFFF;
+  if (ARG) {
+#pragma unroll
+    for (int k = N - 1; k >= 0; --k) {
+      const int e = c0 + ((k / VEC) * kThreads + t) * VEC + (k % VEC);
+      if (f[k] == mx) idx = e;
+    }
+  }
+  i_out = idx;
+}
+
+// Any chunk (partial last chunk of a row, or rows that are not 16-byte
+// aligned): two passes (max, then sum), element e = c0 + j*256 + t.
+template <bool ARG>
+__device__ __forceinline__ void stats_scalar(const void* row, int bf16, int c0, int c1, float c, float& m_out,
+                                             float& s_out, int& i_out) {
+  float mx = -INFINITY;
+  int idx = 0x7FFFFFFF;
+  for (int e = c0 + (int)threadIdx.x; e < c1; e += kThreads) {
+    const float x = load_logit(row, e, bf16);
+    if (ARG && x > mx) idx = e;
+    mx = fmaxf(mx, x);
+  }
+  const float mc = (mx == -INFINITY) ? 0.f : mx * c;
+  float acc = 0.f;
+  for (int e = c0 + (int)threadIdx.x; e < c1; e += kThreads) acc += fexp2(fmaf(load_logit(row, e, bf16), c, -mc));
+  m_out = mx;
+  s_out = acc;
+  i_out = idx;
+}
+
+// ---------------------------------------------------------------------------
+// block helpers (256 threads)
+// ---------------------------------------------------------------------------
+
+// exclusive prefix of one float per thread in thread order; *total = sum
+__device__ __forceinline__ float block_excl_scan(float v, float* s_w, float* total) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  float inc = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float o = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += o;
+  }
+  if (lane == kWave - 1) s_w[wv] = inc;
+  __syncthreads();
+  float before = 0.f;
+  for (int w = 0; w < wv; ++w) before += s_w[w];
+  float tot = 0.f;
+  for (int w = 0; w < kWaves; ++w) tot += s_w[w];
+  *total = tot;
+  __syncthreads();
+  return before + inc - v;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* s_w) {
+  v = wave_sum(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) s_w[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < kWaves; ++w) tot += s_w[w];
+  __syncthreads();
+  return tot;
+}
+
+__device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* s_w) {
+  v = wave_sum_i64(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) s_w[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int64_t tot = 0;
+  for (int w = 0; w < kWaves; ++w) tot += s_w[w];
+  __syncthreads();
+  return tot;
+}
+
+// ---------------------------------------------------------------------------
+// final weights w for the final draw
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float final_weight(int kind, float x, float y, int k, const SeqFinal& f) {
+  const float p = fexp2(fmaf(x, f.c, -f.mct)) * f.inv_st;
+  if (kind == kFinalResidual) {
+    const float q = fexp2(fmaf(y, f.c, -f.mcd)) * f.inv_sd;
+    return fmaxf(p - q, 0.f);
+  }
+  if (kind == kFinalOnehot && k == f.xhat) return 0.f;
+  return p;
+}
+
+// Sum of w over tile j, this thread's share (coalesced: thread t owns
+// elements base + (u*256 + t)*VEC .. +VEC).
+template <bool BF16>
+__device__ __forceinline__ float tile_part_vec(const Params& P, const SeqFinal& f, int kind, int j) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int NV = kTileVec / VEC;
+  constexpr int ES = BF16 ? 2 : 4;
+  const int t = threadIdx.x;
+  const int base = j * kTileElems;
+  const int end = min(P.V, base + kTileElems);
+  const char* tp = (const char*)P.tgt + (int64_t)f.trow * P.ld_t * ES;
+  const char* dp = (kind == kFinalResidual) ? (const char*)P.dft + (int64_t)f.drow * P.ld_d * ES : nullptr;
+  float acc = 0.f;
+  if (base + kTileElems <= end) {
+    u32x4 vt[NV], vd[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = base + (u * kThreads + t) * VEC;
+      vt[u] = __builtin_nontemporal_load((const u32x4*)(tp + (int64_t)e * ES));
+      if (kind == kFinalResidual) vd[u] = __builtin_nontemporal_load((const u32x4*)(dp + (int64_t)e * ES));
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = base + (u * kThreads + t) * VEC;
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) {
+        float x, y = 0.f;
+        if (BF16) {
+          x = (q & 1) ? bf_hi(vt[u][q >> 1]) : bf_lo(vt[u][q >> 1]);
+          if (kind == kFinalResidual) y = (q & 1) ? bf_hi(vd[u][q >> 1]) : bf_lo(vd[u][q >> 1]);
+        } else {
+          x = __uint_as_float(vt[u][q]);
+          if (kind == kFinalResidual) y = __uint_as_float(vd[u][q]);
+        }
+        acc += final_weight(kind, x, y, e + q, f);
+      }
+    }
+  } else {
+    for (int u = 0; u < NV; ++u) {
+      for (int q = 0; q < VEC; ++q) {
+        const int e = base + (u * kThreads + t) * VEC + q;
+        if (e < end) {
+          const float x = load_logit(P.tgt, (int64_t)f.trow * P.ld_t + e, BF16);
+          const float y = (kind == kFinalResidual) ? load_logit(P.dft, (int64_t)f.drow * P.ld_d + e, BF16) : 0.f;
+          acc += final_weight(kind, x, y, e, f);
+        }
+      }
+    }
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float tile_part_scalar(const Params& P, const SeqFinal& f, int kind, int j) {
+  const int base = j * kTileElems;
+  const int end = min(P.V, base + kTileElems);
+  float acc = 0.f;
+  for (int u = 0; u < kTileVec; ++u) {
+    const int e = base + u * kThreads + (int)threadIdx.x;
+    if (e < end) {
+      const float x = load_logit(P.tgt, (int64_t)f.trow * P.ld_t + e, P.t_bf16);
+      const float y = (kind == kFinalResidual) ? load_logit(P.dft, (int64_t)f.drow * P.ld_d + e, P.d_bf16) : 0.f;
+      acc += final_weight(kind, x, y, e, f);
+    }
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float tile_part(const Params& P, const SeqFinal& f, int kind, int j) {
+  const bool vec = P.t_vec && (kind != kFinalResidual || (P.d_vec && P.d_bf16 == P.t_bf16));
+  if (vec) return P.t_bf16 ? tile_part_vec<true>(P, f, kind, j) : tile_part_vec<false>(P, f, kind, j);
+  return tile_part_scalar(P, f, kind, j);
+}
+
+// clear the outputs of a sequence that is not verified
+__device__ void clear_sequence(const Params& P, int s, int off_t, int off_d, int K, int st) {
+  const int t = threadIdx.x;
+  for (int j = t; j <= K; j += kThreads) P.emitted[off_t + j] = -1;
+  for (int j = t; j < K; j += kThreads) {
+    if (P.p_at) P.p_at[off_d + j] = __uint_as_float(kNaNBits);
+    if (P.q_at) P.q_at[off_d + j] = __uint_as_float(kNaNBits);
+  }
+  if (t == 0) {
+    P.accepted_len[s] = -1;
+    if (P.status) P.status[s] = st;
+    P.fin[s].kind = kFinalDone;
+  }
+}
+
+// Block-wide merge of the threads' (max, sum, argmax) and the partial write.
+template <bool ARG>
+__device__ __forceinline__ void finish_chunk(const Params& P, float m, float sum, int idx, float c) {
+  __shared__ float s_m[kWaves], s_s[kWaves];
+  __shared__ int s_i[kWaves];
+  wave_merge<ARG>(m, sum, idx, c);
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  if (lane == 0) {
+    s_m[wv] = m;
+    s_s[wv] = sum;
+    s_i[wv] = idx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = s_m[0], S = s_s[0];
+    int I = s_i[0];
+    for (int q = 1; q < kWaves; ++q) merge_stats<true>(M, S, I, s_m[q], s_s[q], s_i[q], c);
+    P.partials[blockIdx.x] = Partial{M, S, I, 0};    // block index == partial index
+  }
+}
+
+__device__ __forceinline__ float row_scale(int md, float T) { return (md == kGreedy) ? kLog2e : kLog2e / T; }
+
+// A full, 16-byte aligned 32 KB chunk: the owner window's loads and the
+// chunk's loads are issued back to back in one basic block, then consumed.
+template <bool BF>
+__device__ __forceinline__ void row_stats_full(const Params& P, const char* rowp, int row, int c0, int plus_one,
+                                               bool is_draft) {
+  u32x4 v[kNV];
+  if (P.B <= kWave * kWin) {
+    // issue order: the window's loads, then the chunk's loads, then any use
+    // (vector loads complete in issue order, so the lookup only waits for the
+    // window while the chunk is still in flight)
+    const SeqWindow win = load_window(P);
+    __builtin_amdgcn_sched_barrier(0);
+    load_chunk<BF>(rowp, c0, v);
+    __builtin_amdgcn_sched_barrier(0);
+    const Owner own = owner_in_window(win, P, plus_one, row);
+    if (own.s < 0) return;                 // every wave agrees: inconsistent layout
+    const float c = row_scale(own.md, own.T);
+    float m, sum;
+    int idx;
+    if (own.md == kGreedy && !is_draft) {
+      stats_from_regs<BF, true>(v, c0, c, m, sum, idx);
+      finish_chunk<true>(P, m, sum, idx, c);
+    } else {
+      stats_from_regs<BF, false>(v, c0, c, m, sum, idx);
+      finish_chunk<false>(P, m, sum, idx, c);
+    }
+  } else {
+    load_chunk<BF>(rowp, c0, v);
+    const Owner own = owner_general(P, plus_one, row);
+    if (own.s < 0) return;
+    const float c = row_scale(own.md, own.T);
+    float m, sum;
+    int idx;
+    if (own.md == kGreedy && !is_draft) {
+      stats_from_regs<BF, true>(v, c0, c, m, sum, idx);
+      finish_chunk<true>(P, m, sum, idx, c);
+    } else {
+      stats_from_regs<BF, false>(v, c0, c, m, sum, idx);
+      finish_chunk<false>(P, m, sum, idx, c);
+    }
+  }
+}
+
+// The partial last chunk of a row, or a row that is not 16-byte aligned.
+__device__ __forceinline__ void row_stats_tail(const Params& P, const char* rowp, int bf, int row, int c0, int c1,
+                                               int plus_one, bool is_draft) {
+  const Owner own = owner_general(P, plus_one, row);
+  if (own.s < 0) return;
+  const float c = row_scale(own.md, own.T);
+  float m, sum;
+  int idx;
+  if (own.md == kGreedy && !is_draft) {
+    stats_scalar<true>(rowp, bf, c0, c1, c, m, sum, idx);
+    finish_chunk<true>(P, m, sum, idx, c);
+  } else {
+    stats_scalar<false>(rowp, bf, c0, c1, c, m, sum, idx);
+    finish_chunk<false>(P, m, sum, idx, c);
+  }
+}
+
+template <bool TB, bool DB>
+__device__ __forceinline__ void row_stats_body(const Params& P) {
+  const int b = blockIdx.x;
+  const int nblk_t = P.n_t * P.nch_t;
+  const bool is_draft = b >= nblk_t;
+  const int bb = is_draft ? b - nblk_t : b;
+  const int nch = is_draft ? P.nch_d : P.nch_t;
+  const int row = bb / nch;
+  const int chunk = bb - row * nch;
+  const int ce = is_draft ? P.ce_d : P.ce_t;
+  const bool bf = is_draft ? DB : TB;
+  const int vec = is_draft ? P.d_vec : P.t_vec;
+  const void* base = is_draft ? P.dft : P.tgt;
+  const int64_t ld = is_draft ? P.ld_d : P.ld_t;
+  const char* rowp = (const char*)base + (int64_t)row * ld * (bf ? 2 : 4);
+  const int c0 = chunk * ce;
+  const int plus_one = is_draft ? 0 : 1;
+  if (vec && c0 + ce <= P.V) {
+    if (is_draft) row_stats_full<DB>(P, rowp, row, c0, plus_one, true);
+    else row_stats_full<TB>(P, rowp, row, c0, plus_one, false);
+  } else {
+    row_stats_tail(P, rowp, bf, row, c0, min(P.V, c0 + ce), plus_one, is_draft);
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// kernels
+// ---------------------------------------------------------------------------
+
+template <bool TB, bool DB>
+__global__ void __launch_bounds__(kThreads) k_row_stats(Params P) {
+  row_stats_body<TB, DB>(P);
+}
+
+struct ScanShared {
+  float M[2 * kMaxK + 1];
+  float S[2 * kMaxK + 1];
+  int I[2 * kMaxK + 1];
+  int acc[kMaxK];
+  int tok[kMaxK];
+  int64_t w64[kWaves];
+  int A;
+  int bad;
+};
+
+__global__ void __launch_bounds__(kThreads) k_scan(Params P) {
+  __shared__ ScanShared sh;
+  const int s = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), wv = t / kWave;
+
+  // 1. layout: sum of all K, sum before s, any negative K
+  int64_t tot = 0, bef = 0;
+  int neg = 0;
+  for (int j = t; j < P.B; j += kThreads) {
+    const int64_t k = P.num_draft[j];
+    tot += k;
+    if (j < s) bef += k;
+    neg |= (k < 0);
+  }
+  tot = block_sum_i64(tot, sh.w64);
+  bef = block_sum_i64(bef, sh.w64);
+  neg = __syncthreads_or(neg);
+  if (neg || tot != (int64_t)P.total_draft) {
+    // every output slot is cleared; block s clears its share
+    for (int64_t e = (int64_t)s * kThreads + t; e < (int64_t)P.total_draft + P.B; e += (int64_t)P.B * kThreads)
+      P.emitted[e] = -1;
+    for (int64_t e = (int64_t)s * kThreads + t; e < P.total_draft; e += (int64_t)P.B * kThreads) {
+      if (P.p_at) P.p_at[e] = __uint_as_float(kNaNBits);
+      if (P.q_at) P.q_at[e] = __uint_as_float(kNaNBits);
+    }
+    if (t == 0) {
+      P.accepted_len[s] = -1;
+      if (P.status) P.status[s] = kStBadLayout;
+      P.fin[s].kind = kFinalDone;
+    }
+    return;
+  }
+  const int K = P.num_draft[s];
+  const int off_d = (int)bef;
+  const int off_t = off_d + s;
+
+  // 2. per-sequence checks
+  const int md = P.mode[s];
+  const float T = P.temperature[s];
+  int st = 0;
+  if (K > P.max_k) st |= kStKTooLarge;
+  if (md != kSample && md != kGreedy && md != kOnehot) st |= kStBadMode;
+  if ((md == kSample || md == kOnehot) && !(isfinite(T) && T >= kMinTemperature)) st |= kStBadTemp;
+  if (md == kSample && K > 0 && P.dft == nullptr) st |= kStNoDraft;
+  int badtok = 0;
+  for (int i = t; i < K; i += kThreads) {
+    const int x = P.tokens[off_d + i];
+    badtok |= (x < 0 || x >= P.V);
+  }
+  if (__syncthreads_or(badtok)) st |= kStBadToken;
+  if (st) {
+    clear_sequence(P, s, off_t, off_d, K, st);
+    return;
+  }
+  const float c = (md == kGreedy) ? kLog2e : kLog2e / T;
+  const uint32_t seq_id = P.seq_ids[s];
+  const int nrows = K + 1 + (md == kSample ? K : 0);
+
+  // 3. merge each row's chunk partials in a fixed order
+  for (int r = wv; r < nrows; r += kWaves) {
+    const bool isd = r > K;
+    const int nch = isd ? P.nch_d : P.nch_t;
+    const int64_t pbase = isd ? (int64_t)P.n_t * P.nch_t + (int64_t)(off_d + (r - K - 1)) * P.nch_d
+                              : (int64_t)(off_t + r) * P.nch_t;
+    float m = -INFINITY, sum = 0.f;
+    int idx = 0x7FFFFFFF;
+    for (int ch = lane; ch < nch; ch += kWave) {
+      const Partial pp = P.partials[pbase + ch];
+      merge_stats<true>(m, sum, idx, pp.m, pp.s, pp.idx, c);
+    }
+    wave_merge<true>(m, sum, idx, c);
+    if (lane == 0) {
+      sh.M[r] = m;
+      sh.S[r] = sum;
+      sh.I[r] = idx;
+    }
+  }
+  __syncthreads();
+
+  // 4. every used row must be finite with a positive sum
+  int bad = 0;
+  for (int r = t; r < nrows; r += kThreads) {
+    const float m = sh.M[r], S = sh.S[r];
+    if (!(isfinite(m) && isfinite(S) && S > 0.f)) bad = 1;
+  }
+  if (__syncthreads_or(bad)) {
+    clear_sequence(P, s, off_t, off_d, K, kStNonfinite);
+    return;
+  }
+
+  // 5. p and q at the proposals, uniforms, accept decisions
+  if (t < K) {
+    const int x = P.tokens[off_d + t];
+    const float xt = load_logit(P.tgt, (int64_t)(off_t + t) * P.ld_t + x, P.t_bf16);
+    const float p = fexp2(fmaf(xt, c, -(sh.M[t] * c))) / sh.S[t];
+    float q = 1.f;
+    if (md == kSample) {
+      const float xd = load_logit(P.dft, (int64_t)(off_d + t) * P.ld_d + x, P.d_bf16);
+      q = fexp2(fmaf(xd, c, -(sh.M[K + 1 + t] * c))) / sh.S[K + 1 + t];
+    }
+    int acc;
+    if (md == kGreedy) {
+      acc = (x == sh.I[t]);
+    } else {
+      const float u = draw_uniform(P, seq_id, (uint32_t)t, 0u);
+      const float r = (md == kOnehot) ? p : (q > 0.f ? fminf(1.f, p / q) : 0.f);
+      acc = u < r;
+    }
+    if (P.p_at) P.p_at[off_d + t] = p;
+    if (P.q_at) P.q_at[off_d + t] = q;
+    sh.acc[t] = acc;
+    sh.tok[t] = x;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int a = K;
+    for (int i = 0; i < K; ++i) {
+      if (!sh.acc[i]) {
+        a = i;
+        break;
+      }
+    }
+    sh.A = a;
+  }
+  __syncthreads();
+  const int A = sh.A;
+
+  // 6. emitted tokens: accepted prefix, -1 after A; greedy also fills A
+  if (t <= K) {
+    if (t < A) P.emitted[off_t + t] = sh.tok[t];
+    else if (t > A) P.emitted[off_t + t] = -1;
+    else if (md == kGreedy) P.emitted[off_t + t] = sh.I[A];
+  }
+  if (t == 0) {
+    P.accepted_len[s] = A;
+    SeqFinal f{};
+    f.s = s;
+    f.A = A;
+    f.emit_pos = off_t + A;
+    f.c = c;
+    if (md == kGreedy) {
+      f.kind = kFinalDone;
+      if (P.status) P.status[s] = 0;
+    } else {
+      f.trow = off_t + A;
+      f.mct = sh.M[A] * c;
+      f.inv_st = 1.f / sh.S[A];
+      f.u = draw_uniform(P, seq_id, (uint32_t)A, 1u);
+      if (A == K) {
+        f.kind = kFinalBonus;
+      } else if (md == kOnehot) {
+        f.kind = kFinalOnehot;
+        f.xhat = sh.tok[A];
+      } else {
+        f.kind = kFinalResidual;
+        f.drow = off_d + A;
+        f.mcd = sh.M[K + 1 + A] * c;
+        f.inv_sd = 1.f / sh.S[K + 1 + A];
+      }
+    }
+    P.fin[s] = f;
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) k_tile_sums(Params P) {
+  __shared__ float s_w[kWaves];
+  const int j = blockIdx.x, s = blockIdx.y;
+  const SeqFinal f = P.fin[s];
+  if (f.kind == kFinalDone) return;
+  const float tot = block_sum(tile_part(P, f, f.kind, j), s_w);
+  if (threadIdx.x == 0) P.tilesum[(int64_t)s * P.ntiles + j] = tot;
+}
+
+__global__ void __launch_bounds__(kThreads) k_select(Params P) {
+  __shared__ float s_w[kWaves];
+  __shared__ float s_tiles[kMaxTiles];
+  __shared__ float s_Z, s_tp;
+  __shared__ int s_jj, s_fallback, s_first, s_last;
+
+  const int s = blockIdx.x;
+  const SeqFinal f = P.fin[s];
+  if (f.kind == kFinalDone) return;
+  const int t = threadIdx.x;
+
+  int kind = f.kind;
+  for (int q = t; q < P.ntiles; q += kThreads) s_tiles[q] = P.tilesum[(int64_t)s * P.ntiles + q];
+  __syncthreads();
+  if (t == 0) {
+    float Z = 0.f;
+    for (int q = 0; q < P.ntiles; ++q) Z += s_tiles[q];   // fixed order
+    s_Z = Z;
+    s_fallback = !(Z > 0.f);
+  }
+  __syncthreads();
+  const bool fallback = s_fallback;
+  if (fallback) {
+    // residual without mass (rounding only): draw from p at position A instead
+    kind = kFinalBonus;
+    float Z = 0.f;
+    for (int q = 0; q < P.ntiles; ++q) {
+      const float v = block_sum(tile_part(P, f, kind, q), s_w);
+      if (t == 0) s_tiles[q] = v;
+      Z += v;
+    }
+    if (t == 0) s_Z = Z;
+    __syncthreads();
+  }
+  if (t == 0) {
+    const float tt = f.u * s_Z;
+    float cum = 0.f;
+    int jj = -1;
+    for (int q = 0; q < P.ntiles; ++q) {
+      if (cum + s_tiles[q] > tt) {
+        jj = q;
+        break;
+      }
+      cum += s_tiles[q];
+    }
+    if (jj < 0) {
+      for (int q = P.ntiles - 1; q >= 0; --q) {
+        if (s_tiles[q] > 0.f) {
+          jj = q;
+          break;
+        }
+      }
+      cum = 0.f;
+      for (int q = 0; q < jj; ++q) cum += s_tiles[q];
+    }
+    s_jj = jj;
+    s_tp = tt - cum;
+    s_first = 0x7FFFFFFF;
+    s_last = -1;
+  }
+  __syncthreads();
+  const int jj = s_jj;
+  const float tp = s_tp;
+
+  // re-read tile jj: thread t owns kTileVec consecutive elements
+  const int e0 = jj * kTileElems + t * kTileVec;
+  float loc = 0.f;
+  int last_pos = -1;
+  for (int q = 0; q < kTileVec; ++q) {
+    const int e = e0 + q;
+    if (e < P.V) {
+      const float x = load_logit(P.tgt, (int64_t)f.trow * P.ld_t + e, P.t_bf16);
+      const float y = (kind == kFinalResidual) ? load_logit(P.dft, (int64_t)f.drow * P.ld_d + e, P.d_bf16) : 0.f;
+      const float w = final_weight(kind, x, y, e, f);
+      if (w > 0.f) last_pos = e;
+      loc += w;
+    }
+  }
+  float total;
+  const float before = block_excl_scan(loc, s_w, &total);
+  // second pass over this thread's elements (cache hits) to find the crossing
+  if (before + loc > tp) {
+    float run = before;
+    for (int q = 0; q < kTileVec; ++q) {
+      const int e = e0 + q;
+      if (e >= P.V) break;
+      const float x = load_logit(P.tgt, (int64_t)f.trow * P.ld_t + e, P.t_bf16);
+      const float y = (kind == kFinalResidual) ? load_logit(P.dft, (int64_t)f.drow * P.ld_d + e, P.d_bf16) : 0.f;
+      const float w = final_weight(kind, x, y, e, f);
+      run += w;
+      if (w > 0.f && run > tp) {
+        atomicMin(&s_first, e);   // LDS: the lowest crossing over threads wins
+        break;
+      }
+    }
+  }
+  if (last_pos >= 0) atomicMax(&s_last, last_pos);
+  __syncthreads();
+  if (t == 0) {
+    const int y = (s_first != 0x7FFFFFFF) ? s_first : s_last;
+    P.emitted[f.emit_pos] = y;
+    if (P.status) P.status[s] = fallback ? kStZeroResidual : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+hipError_t launch_row_stats(const Params& p, hipStream_t st) {
+  const int64_t blocks = (int64_t)p.n_t * p.nch_t + (int64_t)p.n_d * p.nch_d;
+  if (blocks <= 0) return hipSuccess;
+  const dim3 g((unsigned)blocks), b(kThreads);
+  if (p.t_bf16) {
+    if (p.d_bf16) hipLaunchKernelGGL((k_row_stats<true, true>), g, b, 0, st, p);
+    else hipLaunchKernelGGL((k_row_stats<true, false>), g, b, 0, st, p);
+  } else {
+    if (p.d_bf16) hipLaunchKernelGGL((k_row_stats<false, true>), g, b, 0, st, p);
+    else hipLaunchKernelGGL((k_row_stats<false, false>), g, b, 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const Params& p, hipStream_t st) {
+  hipLaunchKernelGGL(k_scan, dim3(p.B), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_sums(const Params& p, hipStream_t st) {
+  hipLaunchKernelGGL(k_tile_sums, dim3(p.ntiles, p.B), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const Params& p, hipStream_t st) {
+  hipLaunchKernelGGL(k_select, dim3(p.B), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace sv
