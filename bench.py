@@ -139,6 +139,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true", help="time without per-kernel HIP events")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 5 plain device copies of 1 GiB (the reference kernel for counter scaling)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -217,6 +219,15 @@ def main():
                     "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic,
                     "kernel": "k_row_stats", "algorithmic_bytes_per_launch": int(stats_bytes),
                     "mean_launch_ms": round(kern["row_stats"], 5)}
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_budget)
     line = {

@@ -122,8 +122,9 @@ typedef struct spec_verify_args {
 
 /* Create a context on HIP device `device` for batches of at most max_batch
  * sequences, K_s <= max_k (1..128) and vocab <= max_vocab.  Allocates the
- * context's device scratch (per-row partial statistics, per-sequence
- * records, tile sums); the caller owns every input and output
+ * context's device scratch (per-chunk partial row statistics, per-sequence
+ * final-draw records and tile sums, defaults for NULL optional inputs); the
+ * caller owns every input and output
  * buffer.  Returns SV_OK and sets *out, or an error code (then *out = NULL). */
 int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int32_t max_k, int64_t max_vocab);
 
@@ -132,9 +133,10 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
  * SV_ERR_CAPACITY: nothing is enqueued); problems that only the device can
  * see are reported per sequence through `status`.  Does not allocate, does
  * not synchronise; outputs are valid once the stream has reached this point.
- * Launches four kernels: row statistics (one block per 32 KB of every logit
- * row), scan (one block per sequence: acceptance test), tile sums and select
- * (the final draw at the stop position). */
+ * Launches four kernels: row statistics (one block per 32 KB of every
+ * logit row), scan (one block per sequence: the acceptance test), tile sums
+ * (one block per 8192-element tile of the row(s) at each stop position) and
+ * select (one block per sequence: inverse-CDF search). */
 int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* args, void* hip_stream);
 
 /* Free the context and its device memory.  NULL is accepted. */

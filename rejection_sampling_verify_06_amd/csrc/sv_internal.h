@@ -9,8 +9,7 @@ namespace sv {
 
 constexpr int kThreads = 256;           // every kernel: 4 waves of 64
 constexpr int kChunkBytes = 32768;      // bytes of one logit row streamed by one row-stats block
-constexpr int kTileElems = 8192;        // elements of a row per final-draw block
-constexpr int kTileVec = kTileElems / kThreads;   // elements per thread in a tile (32)
+constexpr int kTileElems = 8192;        // elements of a tile of the final draw
 constexpr int kMaxK = 128;
 constexpr int kMaxTiles = 256;          // => vocab <= 2,097,152
 

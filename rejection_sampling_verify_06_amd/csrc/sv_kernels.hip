@@ -258,15 +258,48 @@ __device__ __forceinline__ Owner owner_general(const Params& P, int plus_one, in
 // thread-local statistics of a chunk
 // ---------------------------------------------------------------------------
 
-template <bool BF16>
-__device__ __forceinline__ void load_chunk(const char* rowp, int c0, u32x4 (&v)[kNV]) {
+// Thread t loads vectors (u*256 + t), u < 8, of the chunk starting at c0.
+// TAIL: the chunk ends at c1 before its 32 KB are up; vectors past c1 are
+// loaded from the row's first 16 bytes instead (in bounds: the row has at
+// least one vector) and replaced by -inf in mask_chunk.
+template <bool BF16, bool TAIL>
+__device__ __forceinline__ void load_chunk(const char* rowp, int c0, int c1, u32x4 (&v)[kNV]) {
   constexpr int VEC = BF16 ? 8 : 4;
   constexpr int ES = BF16 ? 2 : 4;
   const int t = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < kNV; ++u) {
     const int e = c0 + (u * kThreads + t) * VEC;
-    v[u] = __builtin_nontemporal_load((const u32x4*)(rowp + (int64_t)e * ES));
+    const int a = (!TAIL || e + VEC <= c1) ? e : 0;
+    v[u] = __builtin_nontemporal_load((const u32x4*)(rowp + (int64_t)a * ES));
+  }
+}
+
+// Replace what lies past c1 by -inf; the one vector that straddles c1 is
+// rebuilt from element loads.
+template <bool BF16>
+__device__ __forceinline__ void mask_chunk(const char* rowp, int c0, int c1, u32x4 (&v)[kNV]) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kNV; ++u) {
+    const int e = c0 + (u * kThreads + t) * VEC;
+    if (e + VEC > c1) {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (BF16) {
+          const int e0 = e + 2 * q, e1 = e0 + 1;
+          const uint32_t lo = (e0 < c1) ? (uint32_t)((const uint16_t*)rowp)[e0] : 0xFF80u;
+          const uint32_t hi = (e1 < c1) ? (uint32_t)((const uint16_t*)rowp)[e1] : 0xFF80u;
+          w[q] = lo | (hi << 16);
+        } else {
+          const int e0 = e + q;
+          w[q] = (e0 < c1) ? ((const uint32_t*)rowp)[e0] : 0xFF800000u;
+        }
+      }
+      v[u] = u32x4{w[0], w[1], w[2], w[3]};
+    }
   }
 }
 
@@ -316,23 +349,40 @@ __device__ __forceinline__ void stats_from_regs(const u32x4 (&v)[kNV], int c0, f
   i_out = idx;
 }
 
-// Any chunk (partial last chunk of a row, or rows that are not 16-byte
-// aligned): two passes (max, then sum), element e = c0 + j*256 + t.
+// Rows that are not 16-byte aligned (or shorter than one vector): element
+// e = c0 + j*256 + t, eight loads in flight per thread, each batch merged
+// into the running (max, sum, argmax).
 template <bool ARG>
 __device__ __forceinline__ void stats_scalar(const void* row, int bf16, int c0, int c1, float c, float& m_out,
                                              float& s_out, int& i_out) {
-  float mx = -INFINITY;
+  constexpr int NB = 8;
+  float m = -INFINITY, s = 0.f;
   int idx = 0x7FFFFFFF;
-  for (int e = c0 + (int)threadIdx.x; e < c1; e += kThreads) {
-    const float x = load_logit(row, e, bf16);
-    if (ARG && x > mx) idx = e;
-    mx = fmaxf(mx, x);
+  for (int b0 = c0 + (int)threadIdx.x; b0 < c1; b0 += NB * kThreads) {
+    float x[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int e = b0 + j * kThreads;
+      const float v = load_logit(row, min(e, c1 - 1), bf16);
+      x[j] = (e < c1) ? v : -INFINITY;
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bm = fmaxf(bm, x[j]);
+    int bi = 0x7FFFFFFF;
+    if (ARG) {
+#pragma unroll
+      for (int j = NB - 1; j >= 0; --j)
+        if (x[j] == bm) bi = b0 + j * kThreads;
+    }
+    const float bmc = (bm == -INFINITY) ? 0.f : bm * c;
+    float bs = 0.f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) bs += fexp2(fmaf(x[j], c, -bmc));
+    merge_stats<ARG>(m, s, idx, bm, bs, bi, c);
   }
-  const float mc = (mx == -INFINITY) ? 0.f : mx * c;
-  float acc = 0.f;
-  for (int e = c0 + (int)threadIdx.x; e < c1; e += kThreads) acc += fexp2(fmaf(load_logit(row, e, bf16), c, -mc));
-  m_out = mx;
-  s_out = acc;
+  m_out = m;
+  s_out = s;
   i_out = idx;
 }
 
@@ -381,8 +431,10 @@ __device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* s_w) {
 }
 
 // ---------------------------------------------------------------------------
-// final weights w for the final draw
+// the final draw at the stop position: tiles of 8192 elements, 256 threads
 // ---------------------------------------------------------------------------
+constexpr int kTileVec = kTileElems / kThreads;   // 32 elements per thread per tile
+
 __device__ __forceinline__ float final_weight(int kind, float x, float y, int k, const SeqFinal& f) {
   const float p = fexp2(fmaf(x, f.c, -f.mct)) * f.inv_st;
   if (kind == kFinalResidual) {
@@ -393,91 +445,163 @@ __device__ __forceinline__ float final_weight(int kind, float x, float y, int k,
   return p;
 }
 
-// Sum of w over tile j, this thread's share (coalesced: thread t owns
-// elements base + (u*256 + t)*VEC .. +VEC).
-template <bool BF16>
-__device__ __forceinline__ float tile_part_vec(const Params& P, const SeqFinal& f, int kind, int j) {
+// This thread's share of the weight of tile j (coalesced: thread t owns
+// elements base + (u*256 + t)*VEC .. +VEC); every load is issued before use.
+// TAIL (the row's last tile): vectors past V are loaded from the row's
+// first 16 bytes instead and then replaced by -inf logits (weight 0); the
+// one vector that straddles V is rebuilt from element loads.
+template <bool BF16, int KIND, bool TAIL>
+__device__ __forceinline__ float tile_part_vec(const Params& P, const SeqFinal& f, int j) {
   constexpr int VEC = BF16 ? 8 : 4;
   constexpr int NV = kTileVec / VEC;
   constexpr int ES = BF16 ? 2 : 4;
   const int t = threadIdx.x;
   const int base = j * kTileElems;
-  const int end = min(P.V, base + kTileElems);
+  const int V = P.V;
   const char* tp = (const char*)P.tgt + (int64_t)f.trow * P.ld_t * ES;
-  const char* dp = (kind == kFinalResidual) ? (const char*)P.dft + (int64_t)f.drow * P.ld_d * ES : nullptr;
+  const char* dp = (KIND == kFinalResidual) ? (const char*)P.dft + (int64_t)f.drow * P.ld_d * ES : nullptr;
+  u32x4 vt[NV], vd[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int e = base + (u * kThreads + t) * VEC;
+    const int a = (!TAIL || e + VEC <= V) ? e : 0;
+    vt[u] = __builtin_nontemporal_load((const u32x4*)(tp + (int64_t)a * ES));
+    if (KIND == kFinalResidual) vd[u] = __builtin_nontemporal_load((const u32x4*)(dp + (int64_t)a * ES));
+  }
+  if (TAIL) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = base + (u * kThreads + t) * VEC;
+      if (e + VEC > V) {
+        uint32_t wt[4], wd[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (BF16) {
+            const int e0 = e + 2 * q, e1 = e0 + 1;
+            wt[q] = ((e0 < V) ? (uint32_t)((const uint16_t*)tp)[e0] : 0xFF80u) |
+                    (((e1 < V) ? (uint32_t)((const uint16_t*)tp)[e1] : 0xFF80u) << 16);
+            if (KIND == kFinalResidual)
+              wd[q] = ((e0 < V) ? (uint32_t)((const uint16_t*)dp)[e0] : 0xFF80u) |
+                      (((e1 < V) ? (uint32_t)((const uint16_t*)dp)[e1] : 0xFF80u) << 16);
+          } else {
+            const int e0 = e + q;
+            wt[q] = (e0 < V) ? ((const uint32_t*)tp)[e0] : 0xFF800000u;
+            if (KIND == kFinalResidual) wd[q] = (e0 < V) ? ((const uint32_t*)dp)[e0] : 0xFF800000u;
+          }
+        }
+        vt[u] = u32x4{wt[0], wt[1], wt[2], wt[3]};
+        if (KIND == kFinalResidual) vd[u] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+      }
+    }
+  }
   float acc = 0.f;
-  if (base + kTileElems <= end) {
-    u32x4 vt[NV], vd[NV];
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int e = base + (u * kThreads + t) * VEC;
-      vt[u] = __builtin_nontemporal_load((const u32x4*)(tp + (int64_t)e * ES));
-      if (kind == kFinalResidual) vd[u] = __builtin_nontemporal_load((const u32x4*)(dp + (int64_t)e * ES));
-    }
+  for (int u = 0; u < NV; ++u) {
+    const int e = base + (u * kThreads + t) * VEC;
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int e = base + (u * kThreads + t) * VEC;
-#pragma unroll
-      for (int q = 0; q < VEC; ++q) {
-        float x, y = 0.f;
-        if (BF16) {
-          x = (q & 1) ? bf_hi(vt[u][q >> 1]) : bf_lo(vt[u][q >> 1]);
-          if (kind == kFinalResidual) y = (q & 1) ? bf_hi(vd[u][q >> 1]) : bf_lo(vd[u][q >> 1]);
-        } else {
-          x = __uint_as_float(vt[u][q]);
-          if (kind == kFinalResidual) y = __uint_as_float(vd[u][q]);
-        }
-        acc += final_weight(kind, x, y, e + q, f);
+    for (int q = 0; q < VEC; ++q) {
+      float x, y = 0.f;
+      if (BF16) {
+        x = (q & 1) ? bf_hi(vt[u][q >> 1]) : bf_lo(vt[u][q >> 1]);
+        if (KIND == kFinalResidual) y = (q & 1) ? bf_hi(vd[u][q >> 1]) : bf_lo(vd[u][q >> 1]);
+      } else {
+        x = __uint_as_float(vt[u][q]);
+        if (KIND == kFinalResidual) y = __uint_as_float(vd[u][q]);
       }
-    }
-  } else {
-    for (int u = 0; u < NV; ++u) {
-      for (int q = 0; q < VEC; ++q) {
-        const int e = base + (u * kThreads + t) * VEC + q;
-        if (e < end) {
-          const float x = load_logit(P.tgt, (int64_t)f.trow * P.ld_t + e, BF16);
-          const float y = (kind == kFinalResidual) ? load_logit(P.dft, (int64_t)f.drow * P.ld_d + e, BF16) : 0.f;
-          acc += final_weight(kind, x, y, e, f);
-        }
-      }
+      acc += final_weight(KIND, x, y, e + q, f);
     }
   }
   return acc;
 }
 
-__device__ __forceinline__ float tile_part_scalar(const Params& P, const SeqFinal& f, int kind, int j) {
+// Rows that are not 16-byte aligned, shorter than a vector, or a residual
+// whose two rows differ in type: element loads clamped to V - 1, weights
+// past V zeroed.
+__device__ __forceinline__ float tile_part_generic(const Params& P, const SeqFinal& f, int kind, int j) {
   const int base = j * kTileElems;
-  const int end = min(P.V, base + kTileElems);
+  const int64_t toff = (int64_t)f.trow * P.ld_t, doff = (int64_t)f.drow * P.ld_d;
   float acc = 0.f;
-  for (int u = 0; u < kTileVec; ++u) {
-    const int e = base + u * kThreads + (int)threadIdx.x;
-    if (e < end) {
-      const float x = load_logit(P.tgt, (int64_t)f.trow * P.ld_t + e, P.t_bf16);
-      const float y = (kind == kFinalResidual) ? load_logit(P.dft, (int64_t)f.drow * P.ld_d + e, P.d_bf16) : 0.f;
-      acc += final_weight(kind, x, y, e, f);
+  for (int u0 = 0; u0 < kTileVec; u0 += 8) {
+    float x[8], y[8];
+    int ee[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      ee[q] = base + (u0 + q) * kThreads + (int)threadIdx.x;
+      const int e = min(ee[q], P.V - 1);
+      x[q] = load_logit(P.tgt, toff + e, P.t_bf16);
+      y[q] = (kind == kFinalResidual) ? load_logit(P.dft, doff + e, P.d_bf16) : 0.f;
     }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc += (ee[q] < P.V) ? final_weight(kind, x[q], y[q], ee[q], f) : 0.f;
   }
   return acc;
+}
+
+template <bool BF16, int KIND>
+__device__ __forceinline__ float tile_part_k(const Params& P, const SeqFinal& f, int j) {
+  if ((j + 1) * kTileElems <= P.V) return tile_part_vec<BF16, KIND, false>(P, f, j);
+  return tile_part_vec<BF16, KIND, true>(P, f, j);
 }
 
 __device__ __forceinline__ float tile_part(const Params& P, const SeqFinal& f, int kind, int j) {
-  const bool vec = P.t_vec && (kind != kFinalResidual || (P.d_vec && P.d_bf16 == P.t_bf16));
-  if (vec) return P.t_bf16 ? tile_part_vec<true>(P, f, kind, j) : tile_part_vec<false>(P, f, kind, j);
-  return tile_part_scalar(P, f, kind, j);
+  const int vecmin = P.t_bf16 ? 8 : 4;
+  const bool vec = P.t_vec && P.V >= vecmin && (kind != kFinalResidual || (P.d_vec && P.d_bf16 == P.t_bf16));
+  if (vec) {
+    if (P.t_bf16) {
+      if (kind == kFinalResidual) return tile_part_k<true, kFinalResidual>(P, f, j);
+      if (kind == kFinalOnehot) return tile_part_k<true, kFinalOnehot>(P, f, j);
+      return tile_part_k<true, kFinalBonus>(P, f, j);
+    }
+    if (kind == kFinalResidual) return tile_part_k<false, kFinalResidual>(P, f, j);
+    if (kind == kFinalOnehot) return tile_part_k<false, kFinalOnehot>(P, f, j);
+    return tile_part_k<false, kFinalBonus>(P, f, j);
+  }
+  return tile_part_generic(P, f, kind, j);
+}
+
+// Weights of the kTileVec consecutive elements thread t owns in tile jj
+// (for the inverse-CDF search); all loads issued before use.
+template <bool TBF, bool DBF, bool RES>
+__device__ __forceinline__ void run_weights(const Params& P, const SeqFinal& f, int kind, int e0, float (&w)[kTileVec]) {
+  const int64_t toff = (int64_t)f.trow * P.ld_t, doff = (int64_t)f.drow * P.ld_d;
+  float y[kTileVec];
+#pragma unroll
+  for (int q = 0; q < kTileVec; ++q) {
+    const int e = min(e0 + q, P.V - 1);
+    w[q] = TBF ? __uint_as_float(((uint32_t)((const uint16_t*)P.tgt)[toff + e]) << 16) : ((const float*)P.tgt)[toff + e];
+    if (RES) y[q] = DBF ? __uint_as_float(((uint32_t)((const uint16_t*)P.dft)[doff + e]) << 16) : ((const float*)P.dft)[doff + e];
+  }
+#pragma unroll
+  for (int q = 0; q < kTileVec; ++q)
+    w[q] = (e0 + q < P.V) ? final_weight(kind, w[q], RES ? y[q] : 0.f, e0 + q, f) : 0.f;
+}
+
+__device__ __forceinline__ void run_weights_any(const Params& P, const SeqFinal& f, int kind, int e0, float (&w)[kTileVec]) {
+  if (kind == kFinalResidual) {
+    if (P.t_bf16) {
+      if (P.d_bf16) run_weights<true, true, true>(P, f, kind, e0, w);
+      else run_weights<true, false, true>(P, f, kind, e0, w);
+    } else {
+      if (P.d_bf16) run_weights<false, true, true>(P, f, kind, e0, w);
+      else run_weights<false, false, true>(P, f, kind, e0, w);
+    }
+  } else {
+    if (P.t_bf16) run_weights<true, true, false>(P, f, kind, e0, w);
+    else run_weights<false, false, false>(P, f, kind, e0, w);
+  }
 }
 
 // clear the outputs of a sequence that is not verified
 __device__ void clear_sequence(const Params& P, int s, int off_t, int off_d, int K, int st) {
   const int t = threadIdx.x;
-  for (int j = t; j <= K; j += kThreads) P.emitted[off_t + j] = -1;
-  for (int j = t; j < K; j += kThreads) {
+  for (int j = t; j <= K; j += blockDim.x) P.emitted[off_t + j] = -1;
+  for (int j = t; j < K; j += blockDim.x) {
     if (P.p_at) P.p_at[off_d + j] = __uint_as_float(kNaNBits);
     if (P.q_at) P.q_at[off_d + j] = __uint_as_float(kNaNBits);
   }
   if (t == 0) {
     P.accepted_len[s] = -1;
     if (P.status) P.status[s] = st;
-    P.fin[s].kind = kFinalDone;
   }
 }
 
@@ -504,52 +628,44 @@ __device__ __forceinline__ void finish_chunk(const Params& P, float m, float sum
 
 __device__ __forceinline__ float row_scale(int md, float T) { return (md == kGreedy) ? kLog2e : kLog2e / T; }
 
-// A full, 16-byte aligned 32 KB chunk: the owner window's loads and the
-// chunk's loads are issued back to back in one basic block, then consumed.
-template <bool BF>
-__device__ __forceinline__ void row_stats_full(const Params& P, const char* rowp, int row, int c0, int plus_one,
-                                               bool is_draft) {
+template <bool BF, bool ARG>
+__device__ __forceinline__ void chunk_from_regs(const Params& P, const u32x4 (&v)[kNV], int c0, float c) {
+  float m, sum;
+  int idx;
+  stats_from_regs<BF, ARG>(v, c0, c, m, sum, idx);
+  finish_chunk<ARG>(P, m, sum, idx, c);
+}
+
+// A 16-byte aligned chunk (full, or the row's last when TAIL): the owner
+// window's loads and the chunk's loads are issued back to back, then used.
+template <bool BF, bool TAIL>
+__device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp, int row, int c0, int c1,
+                                              int plus_one, bool is_draft) {
   u32x4 v[kNV];
+  Owner own;
   if (P.B <= kWave * kWin) {
     // issue order: the window's loads, then the chunk's loads, then any use
     // (vector loads complete in issue order, so the lookup only waits for the
     // window while the chunk is still in flight)
     const SeqWindow win = load_window(P);
     __builtin_amdgcn_sched_barrier(0);
-    load_chunk<BF>(rowp, c0, v);
+    load_chunk<BF, TAIL>(rowp, c0, c1, v);
     __builtin_amdgcn_sched_barrier(0);
-    const Owner own = owner_in_window(win, P, plus_one, row);
-    if (own.s < 0) return;                 // every wave agrees: inconsistent layout
-    const float c = row_scale(own.md, own.T);
-    float m, sum;
-    int idx;
-    if (own.md == kGreedy && !is_draft) {
-      stats_from_regs<BF, true>(v, c0, c, m, sum, idx);
-      finish_chunk<true>(P, m, sum, idx, c);
-    } else {
-      stats_from_regs<BF, false>(v, c0, c, m, sum, idx);
-      finish_chunk<false>(P, m, sum, idx, c);
-    }
+    own = owner_in_window(win, P, plus_one, row);
   } else {
-    load_chunk<BF>(rowp, c0, v);
-    const Owner own = owner_general(P, plus_one, row);
-    if (own.s < 0) return;
-    const float c = row_scale(own.md, own.T);
-    float m, sum;
-    int idx;
-    if (own.md == kGreedy && !is_draft) {
-      stats_from_regs<BF, true>(v, c0, c, m, sum, idx);
-      finish_chunk<true>(P, m, sum, idx, c);
-    } else {
-      stats_from_regs<BF, false>(v, c0, c, m, sum, idx);
-      finish_chunk<false>(P, m, sum, idx, c);
-    }
+    load_chunk<BF, TAIL>(rowp, c0, c1, v);
+    own = owner_general(P, plus_one, row);
   }
+  if (own.s < 0) return;                   // every wave agrees: inconsistent layout
+  if (TAIL) mask_chunk<BF>(rowp, c0, c1, v);
+  const float c = row_scale(own.md, own.T);
+  if (own.md == kGreedy && !is_draft) chunk_from_regs<BF, true>(P, v, c0, c);
+  else chunk_from_regs<BF, false>(P, v, c0, c);
 }
 
-// The partial last chunk of a row, or a row that is not 16-byte aligned.
-__device__ __forceinline__ void row_stats_tail(const Params& P, const char* rowp, int bf, int row, int c0, int c1,
-                                               int plus_one, bool is_draft) {
+// Rows that are not 16-byte aligned, or shorter than one vector.
+__device__ __forceinline__ void row_stats_scalar(const Params& P, const char* rowp, int bf, int row, int c0, int c1,
+                                                 int plus_one, bool is_draft) {
   const Owner own = owner_general(P, plus_one, row);
   if (own.s < 0) return;
   const float c = row_scale(own.md, own.T);
@@ -564,6 +680,19 @@ __device__ __forceinline__ void row_stats_tail(const Params& P, const char* rowp
   }
 }
 
+template <bool BF>
+__device__ __forceinline__ void row_stats_seg(const Params& P, const char* rowp, int vec, int row, int c0, int ce,
+                                              int plus_one, bool is_draft) {
+  constexpr int VEC = BF ? 8 : 4;
+  const int c1 = min(P.V, c0 + ce);
+  if (vec && P.V >= VEC) {
+    if (c0 + ce <= P.V) row_stats_vec<BF, false>(P, rowp, row, c0, c1, plus_one, is_draft);
+    else row_stats_vec<BF, true>(P, rowp, row, c0, c1, plus_one, is_draft);
+  } else {
+    row_stats_scalar(P, rowp, BF, row, c0, c1, plus_one, is_draft);
+  }
+}
+
 template <bool TB, bool DB>
 __device__ __forceinline__ void row_stats_body(const Params& P) {
   const int b = blockIdx.x;
@@ -573,19 +702,12 @@ __device__ __forceinline__ void row_stats_body(const Params& P) {
   const int nch = is_draft ? P.nch_d : P.nch_t;
   const int row = bb / nch;
   const int chunk = bb - row * nch;
-  const int ce = is_draft ? P.ce_d : P.ce_t;
-  const bool bf = is_draft ? DB : TB;
-  const int vec = is_draft ? P.d_vec : P.t_vec;
-  const void* base = is_draft ? P.dft : P.tgt;
-  const int64_t ld = is_draft ? P.ld_d : P.ld_t;
-  const char* rowp = (const char*)base + (int64_t)row * ld * (bf ? 2 : 4);
-  const int c0 = chunk * ce;
-  const int plus_one = is_draft ? 0 : 1;
-  if (vec && c0 + ce <= P.V) {
-    if (is_draft) row_stats_full<DB>(P, rowp, row, c0, plus_one, true);
-    else row_stats_full<TB>(P, rowp, row, c0, plus_one, false);
+  if (is_draft) {
+    const char* rowp = (const char*)P.dft + (int64_t)row * P.ld_d * (DB ? 2 : 4);
+    row_stats_seg<DB>(P, rowp, P.d_vec, row, chunk * P.ce_d, P.ce_d, 0, true);
   } else {
-    row_stats_tail(P, rowp, bf, row, c0, min(P.V, c0 + ce), plus_one, is_draft);
+    const char* rowp = (const char*)P.tgt + (int64_t)row * P.ld_t * (TB ? 2 : 4);
+    row_stats_seg<TB>(P, rowp, P.t_vec, row, chunk * P.ce_t, P.ce_t, 1, false);
   }
 }
 
@@ -607,19 +729,27 @@ struct ScanShared {
   int acc[kMaxK];
   int tok[kMaxK];
   int64_t w64[kWaves];
+  float w[kWaves];
+  SeqFinal f;
   int A;
-  int bad;
 };
 
-__global__ void __launch_bounds__(kThreads) k_scan(Params P) {
-  __shared__ ScanShared sh;
-  const int s = blockIdx.x;
+// The acceptance scan of sequence s by one 256-thread block.  Fills sh.f
+// (kind kFinalDone when no final draw is left) and, when writer, stores
+// every output of the sequence but the final token.
+__device__ void scan_sequence(const Params& P, int s, ScanShared& sh, bool writer) {
   const int t = threadIdx.x;
   const int lane = t & (kWave - 1), wv = t / kWave;
+  if (t == 0) sh.f.kind = kFinalDone;
 
-  // 1. layout: sum of all K, sum before s, any negative K
+  // ---- layout: sum of all K, sum before s, any negative K ----
+  const int K = P.num_draft[s];
+  const int md = P.mode[s];
+  const float T = P.temperature[s];
+  const uint32_t seq_id = P.seq_ids[s];
   int64_t tot = 0, bef = 0;
   int neg = 0;
+#pragma unroll 4
   for (int j = t; j < P.B; j += kThreads) {
     const int64_t k = P.num_draft[j];
     tot += k;
@@ -630,47 +760,45 @@ __global__ void __launch_bounds__(kThreads) k_scan(Params P) {
   bef = block_sum_i64(bef, sh.w64);
   neg = __syncthreads_or(neg);
   if (neg || tot != (int64_t)P.total_draft) {
-    // every output slot is cleared; block s clears its share
-    for (int64_t e = (int64_t)s * kThreads + t; e < (int64_t)P.total_draft + P.B; e += (int64_t)P.B * kThreads)
-      P.emitted[e] = -1;
-    for (int64_t e = (int64_t)s * kThreads + t; e < P.total_draft; e += (int64_t)P.B * kThreads) {
-      if (P.p_at) P.p_at[e] = __uint_as_float(kNaNBits);
-      if (P.q_at) P.q_at[e] = __uint_as_float(kNaNBits);
+    if (writer) {
+      // every output slot is cleared; sequence s's writer clears its share
+      for (int64_t e = (int64_t)s * kThreads + t; e < (int64_t)P.total_draft + P.B; e += (int64_t)P.B * kThreads)
+        P.emitted[e] = -1;
+      for (int64_t e = (int64_t)s * kThreads + t; e < P.total_draft; e += (int64_t)P.B * kThreads) {
+        if (P.p_at) P.p_at[e] = __uint_as_float(kNaNBits);
+        if (P.q_at) P.q_at[e] = __uint_as_float(kNaNBits);
+      }
+      if (t == 0) {
+        P.accepted_len[s] = -1;
+        if (P.status) P.status[s] = kStBadLayout;
+      }
     }
-    if (t == 0) {
-      P.accepted_len[s] = -1;
-      if (P.status) P.status[s] = kStBadLayout;
-      P.fin[s].kind = kFinalDone;
-    }
+    __syncthreads();
     return;
   }
-  const int K = P.num_draft[s];
   const int off_d = (int)bef;
   const int off_t = off_d + s;
 
-  // 2. per-sequence checks
-  const int md = P.mode[s];
-  const float T = P.temperature[s];
+  // ---- per-sequence checks ----
   int st = 0;
   if (K > P.max_k) st |= kStKTooLarge;
   if (md != kSample && md != kGreedy && md != kOnehot) st |= kStBadMode;
   if ((md == kSample || md == kOnehot) && !(isfinite(T) && T >= kMinTemperature)) st |= kStBadTemp;
   if (md == kSample && K > 0 && P.dft == nullptr) st |= kStNoDraft;
-  int badtok = 0;
-  for (int i = t; i < K; i += kThreads) {
-    const int x = P.tokens[off_d + i];
-    badtok |= (x < 0 || x >= P.V);
+  if (st == 0) {
+    // K <= max_k <= kMaxK < kThreads: one proposal per thread
+    const int x = (t < K) ? P.tokens[off_d + t] : 0;
+    if (__syncthreads_or(t < K && (x < 0 || x >= P.V))) st = kStBadToken;
   }
-  if (__syncthreads_or(badtok)) st |= kStBadToken;
-  if (st) {
-    clear_sequence(P, s, off_t, off_d, K, st);
+  if (st) {                                   // uniform over the block
+    if (writer) clear_sequence(P, s, off_t, off_d, K, st);
+    __syncthreads();
     return;
   }
   const float c = (md == kGreedy) ? kLog2e : kLog2e / T;
-  const uint32_t seq_id = P.seq_ids[s];
   const int nrows = K + 1 + (md == kSample ? K : 0);
 
-  // 3. merge each row's chunk partials in a fixed order
+  // ---- each row's chunk partials, merged in a fixed order (one wave per row) ----
   for (int r = wv; r < nrows; r += kWaves) {
     const bool isd = r > K;
     const int nch = isd ? P.nch_d : P.nch_t;
@@ -691,27 +819,25 @@ __global__ void __launch_bounds__(kThreads) k_scan(Params P) {
   }
   __syncthreads();
 
-  // 4. every used row must be finite with a positive sum
+  // ---- every used row must be finite with a positive sum ----
   int bad = 0;
   for (int r = t; r < nrows; r += kThreads) {
     const float m = sh.M[r], S = sh.S[r];
     if (!(isfinite(m) && isfinite(S) && S > 0.f)) bad = 1;
   }
   if (__syncthreads_or(bad)) {
-    clear_sequence(P, s, off_t, off_d, K, kStNonfinite);
+    if (writer) clear_sequence(P, s, off_t, off_d, K, kStNonfinite);
+    __syncthreads();
     return;
   }
 
-  // 5. p and q at the proposals, uniforms, accept decisions
+  // ---- p and q at the proposals, uniforms, accept decisions ----
   if (t < K) {
     const int x = P.tokens[off_d + t];
     const float xt = load_logit(P.tgt, (int64_t)(off_t + t) * P.ld_t + x, P.t_bf16);
+    const float xd = (md == kSample) ? load_logit(P.dft, (int64_t)(off_d + t) * P.ld_d + x, P.d_bf16) : 0.f;
     const float p = fexp2(fmaf(xt, c, -(sh.M[t] * c))) / sh.S[t];
-    float q = 1.f;
-    if (md == kSample) {
-      const float xd = load_logit(P.dft, (int64_t)(off_d + t) * P.ld_d + x, P.d_bf16);
-      q = fexp2(fmaf(xd, c, -(sh.M[K + 1 + t] * c))) / sh.S[K + 1 + t];
-    }
+    const float q = (md == kSample) ? fexp2(fmaf(xd, c, -(sh.M[K + 1 + t] * c))) / sh.S[K + 1 + t] : 1.f;
     int acc;
     if (md == kGreedy) {
       acc = (x == sh.I[t]);
@@ -720,8 +846,10 @@ __global__ void __launch_bounds__(kThreads) k_scan(Params P) {
       const float r = (md == kOnehot) ? p : (q > 0.f ? fminf(1.f, p / q) : 0.f);
       acc = u < r;
     }
-    if (P.p_at) P.p_at[off_d + t] = p;
-    if (P.q_at) P.q_at[off_d + t] = q;
+    if (writer) {
+      if (P.p_at) P.p_at[off_d + t] = p;
+      if (P.q_at) P.q_at[off_d + t] = q;
+    }
     sh.acc[t] = acc;
     sh.tok[t] = x;
   }
@@ -735,47 +863,55 @@ __global__ void __launch_bounds__(kThreads) k_scan(Params P) {
       }
     }
     sh.A = a;
+    SeqFinal f{};
+    f.s = s;
+    f.A = a;
+    f.emit_pos = off_t + a;
+    f.c = c;
+    if (md == kGreedy) {
+      f.kind = kFinalDone;
+    } else {
+      f.trow = off_t + a;
+      f.mct = sh.M[a] * c;
+      f.inv_st = 1.f / sh.S[a];
+      f.u = draw_uniform(P, seq_id, (uint32_t)a, 1u);
+      if (a == K) {
+        f.kind = kFinalBonus;
+      } else if (md == kOnehot) {
+        f.kind = kFinalOnehot;
+        f.xhat = sh.tok[a];
+      } else {
+        f.kind = kFinalResidual;
+        f.drow = off_d + a;
+        f.mcd = sh.M[K + 1 + a] * c;
+        f.inv_sd = 1.f / sh.S[K + 1 + a];
+      }
+    }
+    sh.f = f;
+    if (writer) P.accepted_len[s] = a;
   }
   __syncthreads();
   const int A = sh.A;
 
-  // 6. emitted tokens: accepted prefix, -1 after A; greedy also fills A
-  if (t <= K) {
+  // ---- emitted tokens: accepted prefix, -1 after A; greedy fills A too ----
+  if (writer && t <= K) {
     if (t < A) P.emitted[off_t + t] = sh.tok[t];
     else if (t > A) P.emitted[off_t + t] = -1;
     else if (md == kGreedy) P.emitted[off_t + t] = sh.I[A];
   }
-  if (t == 0) {
-    P.accepted_len[s] = A;
-    SeqFinal f{};
-    f.s = s;
-    f.A = A;
-    f.emit_pos = off_t + A;
-    f.c = c;
-    if (md == kGreedy) {
-      f.kind = kFinalDone;
-      if (P.status) P.status[s] = 0;
-    } else {
-      f.trow = off_t + A;
-      f.mct = sh.M[A] * c;
-      f.inv_st = 1.f / sh.S[A];
-      f.u = draw_uniform(P, seq_id, (uint32_t)A, 1u);
-      if (A == K) {
-        f.kind = kFinalBonus;
-      } else if (md == kOnehot) {
-        f.kind = kFinalOnehot;
-        f.xhat = sh.tok[A];
-      } else {
-        f.kind = kFinalResidual;
-        f.drow = off_d + A;
-        f.mcd = sh.M[K + 1 + A] * c;
-        f.inv_sd = 1.f / sh.S[K + 1 + A];
-      }
-    }
-    P.fin[s] = f;
-  }
+  if (writer && md == kGreedy && t == 0 && P.status) P.status[s] = 0;
 }
 
+// One block per sequence: the acceptance scan; records the final draw.
+__global__ void __launch_bounds__(kThreads) k_scan(Params P) {
+  __shared__ ScanShared sh;
+  const int s = blockIdx.x;
+  scan_sequence(P, s, sh, true);
+  if (threadIdx.x == 0) P.fin[s] = sh.f;
+}
+
+// grid (ntiles, B): the final weights of one tile of the row(s) at the stop
+// position of sequence s.
 __global__ void __launch_bounds__(kThreads) k_tile_sums(Params P) {
   __shared__ float s_w[kWaves];
   const int j = blockIdx.x, s = blockIdx.y;
@@ -785,6 +921,7 @@ __global__ void __launch_bounds__(kThreads) k_tile_sums(Params P) {
   if (threadIdx.x == 0) P.tilesum[(int64_t)s * P.ntiles + j] = tot;
 }
 
+// One block per sequence: the tile holding t = u * Z, then the token in it.
 __global__ void __launch_bounds__(kThreads) k_select(Params P) {
   __shared__ float s_w[kWaves];
   __shared__ float s_tiles[kMaxTiles];
@@ -851,32 +988,24 @@ __global__ void __launch_bounds__(kThreads) k_select(Params P) {
 
   // re-read tile jj: thread t owns kTileVec consecutive elements
   const int e0 = jj * kTileElems + t * kTileVec;
+  float xv[kTileVec];
+  run_weights_any(P, f, kind, e0, xv);
   float loc = 0.f;
   int last_pos = -1;
+#pragma unroll
   for (int q = 0; q < kTileVec; ++q) {
-    const int e = e0 + q;
-    if (e < P.V) {
-      const float x = load_logit(P.tgt, (int64_t)f.trow * P.ld_t + e, P.t_bf16);
-      const float y = (kind == kFinalResidual) ? load_logit(P.dft, (int64_t)f.drow * P.ld_d + e, P.d_bf16) : 0.f;
-      const float w = final_weight(kind, x, y, e, f);
-      if (w > 0.f) last_pos = e;
-      loc += w;
-    }
+    if (xv[q] > 0.f) last_pos = e0 + q;
+    loc += xv[q];
   }
   float total;
   const float before = block_excl_scan(loc, s_w, &total);
-  // second pass over this thread's elements (cache hits) to find the crossing
+  // the first element (with weight) whose running prefix passes tp
   if (before + loc > tp) {
     float run = before;
     for (int q = 0; q < kTileVec; ++q) {
-      const int e = e0 + q;
-      if (e >= P.V) break;
-      const float x = load_logit(P.tgt, (int64_t)f.trow * P.ld_t + e, P.t_bf16);
-      const float y = (kind == kFinalResidual) ? load_logit(P.dft, (int64_t)f.drow * P.ld_d + e, P.d_bf16) : 0.f;
-      const float w = final_weight(kind, x, y, e, f);
-      run += w;
-      if (w > 0.f && run > tp) {
-        atomicMin(&s_first, e);   // LDS: the lowest crossing over threads wins
+      run += xv[q];
+      if (xv[q] > 0.f && run > tp) {
+        atomicMin(&s_first, e0 + q);   // LDS: the lowest crossing over threads wins
         break;
       }
     }
