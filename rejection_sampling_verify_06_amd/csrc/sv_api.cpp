@@ -63,6 +63,7 @@ struct spec_verify_ctx {
   void* mem = nullptr;
   size_t bytes = 0;
   sv::Partial* partials = nullptr;
+  float* xval = nullptr;
   sv::SeqFinal* fin = nullptr;
   float* tilesum = nullptr;
   // defaults for NULL temperature / mode / seq_ids: 1.0, SV_SAMPLE, s
@@ -128,6 +129,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
 
   size_t off = 0;
   const size_t o_part = off;   off = align_up(off + sizeof(sv::Partial) * c->max_rows * c->max_nch, 256);
+  const size_t o_xval = off;   off = align_up(off + sizeof(float) * c->max_rows, 256);
   const size_t o_fin = off;    off = align_up(off + sizeof(sv::SeqFinal) * max_batch, 256);
   const size_t o_tile = off;   off = align_up(off + sizeof(float) * (size_t)max_batch * c->max_tiles, 256);
   const size_t o_dt = off;     off = align_up(off + sizeof(float) * (size_t)max_batch, 256);
@@ -148,6 +150,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
   }
   char* b = (char*)c->mem;
   c->partials = (sv::Partial*)(b + o_part);
+  c->xval = (float*)(b + o_xval);
   c->fin = (sv::SeqFinal*)(b + o_fin);
   c->tilesum = (float*)(b + o_tile);
   c->def_temperature = (float*)(b + o_dt);
@@ -267,6 +270,7 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
   p.q_at = a->q_at_proposal;
   p.status = a->status;
   p.partials = ctx->partials;
+  p.xval = ctx->xval;
   p.fin = ctx->fin;
   p.tilesum = ctx->tilesum;
   // one row-stats block streams 32 KB of a row

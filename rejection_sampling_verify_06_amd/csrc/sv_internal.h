@@ -76,6 +76,7 @@ struct Params {
   int32_t* status;
   // scratch owned by the context
   Partial* partials;  // target row r chunk k at r*nch_t + k; draft row r at n_t*nch_t + r*nch_d + k
+  float* xval;        // [n_t + n_d]: each row's logit at its proposed token
   SeqFinal* fin;      // [B]
   float* tilesum;     // [B * ntiles]
   int32_t nch_t;      // chunks per target row

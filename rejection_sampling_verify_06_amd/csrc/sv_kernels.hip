@@ -179,20 +179,24 @@ __device__ __forceinline__ SeqWindow load_window(const Params& P) {
 }
 
 struct Owner {
-  int s;
+  int s;       // owning sequence, -1 if none
   float T;
   int md;
+  int first;   // first row of the owner's rows in this segment
+  int K;       // the owner's K_s
 };
 
 // lowest lane that claims the row (a consistent layout has exactly one)
-__device__ __forceinline__ Owner owner_from_lanes(int owner, float T, int md) {
+__device__ __forceinline__ Owner owner_from_lanes(int owner, float T, int md, int first, int K) {
   const unsigned long long hits = __ballot(owner >= 0);
-  Owner o{-1, 1.f, kSample};
+  Owner o{-1, 1.f, kSample, 0, 0};
   if (hits == 0ull) return o;
   const int src = (int)__builtin_ctzll(hits);
   o.s = __builtin_amdgcn_readfirstlane(__shfl(owner, src, kWave));
   o.T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(__shfl(T, src, kWave))));
   o.md = __builtin_amdgcn_readfirstlane(__shfl(md, src, kWave));
+  o.first = __builtin_amdgcn_readfirstlane(__shfl(first, src, kWave));
+  o.K = __builtin_amdgcn_readfirstlane(__shfl(K, src, kWave));
   return o;
 }
 
@@ -218,7 +222,7 @@ __device__ __forceinline__ Owner owner_in_window(const SeqWindow& w, const Param
     sum += cnt[i];
   }
   uint32_t start = wave_incl_scan_u32(sum) - sum;
-  int owner = -1;
+  int owner = -1, first = 0, K = 0;
   float T = 1.f;
   int md = kSample;
   const uint32_t ur = (uint32_t)r;
@@ -229,10 +233,12 @@ __device__ __forceinline__ Owner owner_in_window(const SeqWindow& w, const Param
       owner = base + i;
       T = w.T[i];
       md = w.md[i];
+      first = (int)start;
+      K = w.k[i];
     }
     start += cnt[i];
   }
-  return owner_from_lanes(owner, T, md);
+  return owner_from_lanes(owner, T, md, first, K);
 }
 
 // any batch size: lane l takes sequences [l*per, (l+1)*per)
@@ -243,15 +249,19 @@ __device__ __forceinline__ Owner owner_general(const Params& P, int plus_one, in
   int64_t sum = 0;
   for (int s = lo; s < hi; ++s) sum += (int64_t)P.num_draft[s] + plus_one;
   int64_t start = wave_incl_scan_i64(sum) - sum;
-  int owner = -1;
+  int owner = -1, first = 0, K = 0;
   for (int s = lo; s < hi; ++s) {
     const int64_t cnt = (int64_t)P.num_draft[s] + plus_one;
-    if (r >= start && r < start + cnt) owner = s;
+    if (r >= start && r < start + cnt) {
+      owner = s;
+      first = (int)start;
+      K = P.num_draft[s];
+    }
     start += cnt;
   }
   const float T = (owner >= 0) ? P.temperature[owner] : 1.f;
   const int md = (owner >= 0) ? (int)P.mode[owner] : kSample;
-  return owner_from_lanes(owner, T, md);
+  return owner_from_lanes(owner, T, md, first, K);
 }
 
 // ---------------------------------------------------------------------------
@@ -559,40 +569,121 @@ __device__ __forceinline__ float tile_part(const Params& P, const SeqFinal& f, i
   return tile_part_generic(P, f, kind, j);
 }
 
-// Weights of the kTileVec consecutive elements thread t owns in tile jj
-// (for the inverse-CDF search); all loads issued before use.
-template <bool TBF, bool DBF, bool RES>
-__device__ __forceinline__ void run_weights(const Params& P, const SeqFinal& f, int kind, int e0, float (&w)[kTileVec]) {
-  const int64_t toff = (int64_t)f.trow * P.ld_t, doff = (int64_t)f.drow * P.ld_d;
-  float y[kTileVec];
+// The weights of tile jj into LDS in element order (index e + e/32, so that
+// each thread's run of 32 consecutive weights is bank-conflict free), loaded
+// with the same coalesced, masked vector loads as tile_part_vec.
+__device__ __forceinline__ int lds_pad(int e) { return e + (e >> 5); }
+constexpr int kTileLds = kTileElems + kTileElems / 32;
+
+template <bool BF16, int KIND, bool TAIL>
+__device__ __forceinline__ void tile_weights_lds_vec(const Params& P, const SeqFinal& f, int j, float* lw) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int NV = kTileVec / VEC;
+  constexpr int ES = BF16 ? 2 : 4;
+  const int t = threadIdx.x;
+  const int base = j * kTileElems;
+  const int V = P.V;
+  const char* tp = (const char*)P.tgt + (int64_t)f.trow * P.ld_t * ES;
+  const char* dp = (KIND == kFinalResidual) ? (const char*)P.dft + (int64_t)f.drow * P.ld_d * ES : nullptr;
+  u32x4 vt[NV], vd[NV];
 #pragma unroll
-  for (int q = 0; q < kTileVec; ++q) {
-    const int e = min(e0 + q, P.V - 1);
-    w[q] = TBF ? __uint_as_float(((uint32_t)((const uint16_t*)P.tgt)[toff + e]) << 16) : ((const float*)P.tgt)[toff + e];
-    if (RES) y[q] = DBF ? __uint_as_float(((uint32_t)((const uint16_t*)P.dft)[doff + e]) << 16) : ((const float*)P.dft)[doff + e];
+  for (int u = 0; u < NV; ++u) {
+    const int e = base + (u * kThreads + t) * VEC;
+    const int a = (!TAIL || e + VEC <= V) ? e : 0;
+    vt[u] = __builtin_nontemporal_load((const u32x4*)(tp + (int64_t)a * ES));
+    if (KIND == kFinalResidual) vd[u] = __builtin_nontemporal_load((const u32x4*)(dp + (int64_t)a * ES));
+  }
+  if (TAIL) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int e = base + (u * kThreads + t) * VEC;
+      if (e + VEC > V) {
+        uint32_t wt[4], wd[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (BF16) {
+            const int e0 = e + 2 * q, e1 = e0 + 1;
+            wt[q] = ((e0 < V) ? (uint32_t)((const uint16_t*)tp)[e0] : 0xFF80u) |
+                    (((e1 < V) ? (uint32_t)((const uint16_t*)tp)[e1] : 0xFF80u) << 16);
+            if (KIND == kFinalResidual)
+              wd[q] = ((e0 < V) ? (uint32_t)((const uint16_t*)dp)[e0] : 0xFF80u) |
+                      (((e1 < V) ? (uint32_t)((const uint16_t*)dp)[e1] : 0xFF80u) << 16);
+          } else {
+            const int e0 = e + q;
+            wt[q] = (e0 < V) ? ((const uint32_t*)tp)[e0] : 0xFF800000u;
+            if (KIND == kFinalResidual) wd[q] = (e0 < V) ? ((const uint32_t*)dp)[e0] : 0xFF800000u;
+          }
+        }
+        vt[u] = u32x4{wt[0], wt[1], wt[2], wt[3]};
+        if (KIND == kFinalResidual) vd[u] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+      }
+    }
   }
 #pragma unroll
-  for (int q = 0; q < kTileVec; ++q)
-    w[q] = (e0 + q < P.V) ? final_weight(kind, w[q], RES ? y[q] : 0.f, e0 + q, f) : 0.f;
+  for (int u = 0; u < NV; ++u) {
+    const int el = (u * kThreads + t) * VEC;    // element index within the tile
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) {
+      float x, y = 0.f;
+      if (BF16) {
+        x = (q & 1) ? bf_hi(vt[u][q >> 1]) : bf_lo(vt[u][q >> 1]);
+        if (KIND == kFinalResidual) y = (q & 1) ? bf_hi(vd[u][q >> 1]) : bf_lo(vd[u][q >> 1]);
+      } else {
+        x = __uint_as_float(vt[u][q]);
+        if (KIND == kFinalResidual) y = __uint_as_float(vd[u][q]);
+      }
+      lw[lds_pad(el + q)] = final_weight(KIND, x, y, base + el + q, f);
+    }
+  }
 }
 
-__device__ __forceinline__ void run_weights_any(const Params& P, const SeqFinal& f, int kind, int e0, float (&w)[kTileVec]) {
-  if (kind == kFinalResidual) {
+// Any row alignment: element e = base + u*256 + t, loads clamped, weights past V zeroed.
+__device__ __forceinline__ void tile_weights_lds_generic(const Params& P, const SeqFinal& f, int kind, int j,
+                                                         float* lw) {
+  const int base = j * kTileElems;
+  const int64_t toff = (int64_t)f.trow * P.ld_t, doff = (int64_t)f.drow * P.ld_d;
+  for (int u0 = 0; u0 < kTileVec; u0 += 8) {
+    float x[8], y[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = min(base + (u0 + q) * kThreads + (int)threadIdx.x, P.V - 1);
+      x[q] = load_logit(P.tgt, toff + e, P.t_bf16);
+      y[q] = (kind == kFinalResidual) ? load_logit(P.dft, doff + e, P.d_bf16) : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int el = (u0 + q) * kThreads + (int)threadIdx.x;
+      lw[lds_pad(el)] = (base + el < P.V) ? final_weight(kind, x[q], y[q], base + el, f) : 0.f;
+    }
+  }
+}
+
+template <bool BF16, int KIND>
+__device__ __forceinline__ void tile_weights_lds_k(const Params& P, const SeqFinal& f, int j, float* lw) {
+  if ((j + 1) * kTileElems <= P.V) tile_weights_lds_vec<BF16, KIND, false>(P, f, j, lw);
+  else tile_weights_lds_vec<BF16, KIND, true>(P, f, j, lw);
+}
+
+__device__ __forceinline__ void tile_weights_lds(const Params& P, const SeqFinal& f, int kind, int j, float* lw) {
+  const int vecmin = P.t_bf16 ? 8 : 4;
+  const bool vec = P.t_vec && P.V >= vecmin && (kind != kFinalResidual || (P.d_vec && P.d_bf16 == P.t_bf16));
+  if (vec) {
     if (P.t_bf16) {
-      if (P.d_bf16) run_weights<true, true, true>(P, f, kind, e0, w);
-      else run_weights<true, false, true>(P, f, kind, e0, w);
+      if (kind == kFinalResidual) tile_weights_lds_k<true, kFinalResidual>(P, f, j, lw);
+      else if (kind == kFinalOnehot) tile_weights_lds_k<true, kFinalOnehot>(P, f, j, lw);
+      else tile_weights_lds_k<true, kFinalBonus>(P, f, j, lw);
     } else {
-      if (P.d_bf16) run_weights<false, true, true>(P, f, kind, e0, w);
-      else run_weights<false, false, true>(P, f, kind, e0, w);
+      if (kind == kFinalResidual) tile_weights_lds_k<false, kFinalResidual>(P, f, j, lw);
+      else if (kind == kFinalOnehot) tile_weights_lds_k<false, kFinalOnehot>(P, f, j, lw);
+      else tile_weights_lds_k<false, kFinalBonus>(P, f, j, lw);
     }
   } else {
-    if (P.t_bf16) run_weights<true, true, false>(P, f, kind, e0, w);
-    else run_weights<false, false, false>(P, f, kind, e0, w);
+    tile_weights_lds_generic(P, f, kind, j, lw);
   }
 }
 
 // clear the outputs of a sequence that is not verified
-__device__ void clear_sequence(const Params& P, int s, int off_t, int off_d, int K, int st) {
+__device__ __forceinline__ void clear_sequence(const Params& P, int s, int off_t, int off_d, int K, int st) {
   const int t = threadIdx.x;
   for (int j = t; j <= K; j += blockDim.x) P.emitted[off_t + j] = -1;
   for (int j = t; j < K; j += blockDim.x) {
@@ -628,6 +719,41 @@ __device__ __forceinline__ void finish_chunk(const Params& P, float m, float sum
 
 __device__ __forceinline__ float row_scale(int md, float T) { return (md == kGreedy) ? kLog2e : kLog2e / T; }
 
+// The proposed token that row `row` judges (target rows 0..K-1 and draft
+// rows of a sequence), or -1 (bonus row, or an index that the host-declared
+// total_draft does not cover, which only a corrupt num_draft can produce).
+__device__ __forceinline__ int row_proposal(const Params& P, const Owner& own, int row, bool is_draft) {
+  const int i = row - own.first;
+  if (i < 0 || i >= own.K) return -1;
+  const int off_d = is_draft ? own.first : own.first - own.s;
+  const int idx = off_d + i;
+  if (idx < 0 || idx >= P.total_draft) return -1;
+  return P.tokens[idx];
+}
+
+// The logit at the proposal, taken from the chunk held in registers by the
+// thread that loaded it, stored for the scan kernel (xval[row]).
+template <bool BF>
+__device__ __forceinline__ void record_proposal_logit(const Params& P, const u32x4 (&v)[kNV], int c0, int c1, int x,
+                                                      int64_t grow) {
+  constexpr int VEC = BF ? 8 : 4;
+  if (x < c0 || x >= c1) return;
+  const int o = x - c0;
+  const int vi = o / VEC;
+  if ((vi & (kThreads - 1)) != (int)threadIdx.x) return;
+  const int u = vi / kThreads;
+  const int q = o % VEC;
+  const int word = BF ? (q >> 1) : q;
+  // constant register indices only (a runtime index would spill v to scratch)
+  uint32_t w = 0;
+#pragma unroll
+  for (int uu = 0; uu < kNV; ++uu)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      if (uu == u && qq == word) w = v[uu][qq];
+  P.xval[grow] = BF ? ((q & 1) ? bf_hi(w) : bf_lo(w)) : __uint_as_float(w);
+}
+
 template <bool BF, bool ARG>
 __device__ __forceinline__ void chunk_from_regs(const Params& P, const u32x4 (&v)[kNV], int c0, float c) {
   float m, sum;
@@ -657,7 +783,9 @@ __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp,
     own = owner_general(P, plus_one, row);
   }
   if (own.s < 0) return;                   // every wave agrees: inconsistent layout
+  const int x = row_proposal(P, own, row, is_draft);
   if (TAIL) mask_chunk<BF>(rowp, c0, c1, v);
+  record_proposal_logit<BF>(P, v, c0, c1, x, is_draft ? (int64_t)P.n_t + row : (int64_t)row);
   const float c = row_scale(own.md, own.T);
   if (own.md == kGreedy && !is_draft) chunk_from_regs<BF, true>(P, v, c0, c);
   else chunk_from_regs<BF, false>(P, v, c0, c);
@@ -668,6 +796,9 @@ __device__ __forceinline__ void row_stats_scalar(const Params& P, const char* ro
                                                  int plus_one, bool is_draft) {
   const Owner own = owner_general(P, plus_one, row);
   if (own.s < 0) return;
+  const int x = row_proposal(P, own, row, is_draft);
+  if (threadIdx.x == 0 && x >= c0 && x < c1)
+    P.xval[is_draft ? (int64_t)P.n_t + row : (int64_t)row] = load_logit(rowp, x, bf);
   const float c = row_scale(own.md, own.T);
   float m, sum;
   int idx;
@@ -722,83 +853,40 @@ __global__ void __launch_bounds__(kThreads) k_row_stats(Params P) {
   row_stats_body<TB, DB>(P);
 }
 
+constexpr int kScanStage = 1024;   // chunk partials a scan block stages in LDS
+
 struct ScanShared {
+  Partial part[kScanStage];
   float M[2 * kMaxK + 1];
   float S[2 * kMaxK + 1];
   int I[2 * kMaxK + 1];
   int acc[kMaxK];
   int tok[kMaxK];
-  int64_t w64[kWaves];
-  float w[kWaves];
+  int64_t red[3][kWaves];
   SeqFinal f;
   int A;
 };
 
-// The acceptance scan of sequence s by one 256-thread block.  Fills sh.f
-// (kind kFinalDone when no final draw is left) and, when writer, stores
-// every output of the sequence but the final token.
-__device__ void scan_sequence(const Params& P, int s, ScanShared& sh, bool writer) {
+// Inconsistent num_draft: every output slot is cleared; block s clears its share.
+__device__ __forceinline__ void clear_bad_layout(const Params& P, int s) {
   const int t = threadIdx.x;
-  const int lane = t & (kWave - 1), wv = t / kWave;
-  if (t == 0) sh.f.kind = kFinalDone;
+  for (int64_t e = (int64_t)s * kThreads + t; e < (int64_t)P.total_draft + P.B; e += (int64_t)P.B * kThreads)
+    P.emitted[e] = -1;
+  for (int64_t e = (int64_t)s * kThreads + t; e < P.total_draft; e += (int64_t)P.B * kThreads) {
+    if (P.p_at) P.p_at[e] = __uint_as_float(kNaNBits);
+    if (P.q_at) P.q_at[e] = __uint_as_float(kNaNBits);
+  }
+  if (t == 0) {
+    P.accepted_len[s] = -1;
+    if (P.status) P.status[s] = kStBadLayout;
+  }
+}
 
-  // ---- layout: sum of all K, sum before s, any negative K ----
-  const int K = P.num_draft[s];
-  const int md = P.mode[s];
-  const float T = P.temperature[s];
-  const uint32_t seq_id = P.seq_ids[s];
-  int64_t tot = 0, bef = 0;
-  int neg = 0;
-#pragma unroll 4
-  for (int j = t; j < P.B; j += kThreads) {
-    const int64_t k = P.num_draft[j];
-    tot += k;
-    if (j < s) bef += k;
-    neg |= (k < 0);
-  }
-  tot = block_sum_i64(tot, sh.w64);
-  bef = block_sum_i64(bef, sh.w64);
-  neg = __syncthreads_or(neg);
-  if (neg || tot != (int64_t)P.total_draft) {
-    if (writer) {
-      // every output slot is cleared; sequence s's writer clears its share
-      for (int64_t e = (int64_t)s * kThreads + t; e < (int64_t)P.total_draft + P.B; e += (int64_t)P.B * kThreads)
-        P.emitted[e] = -1;
-      for (int64_t e = (int64_t)s * kThreads + t; e < P.total_draft; e += (int64_t)P.B * kThreads) {
-        if (P.p_at) P.p_at[e] = __uint_as_float(kNaNBits);
-        if (P.q_at) P.q_at[e] = __uint_as_float(kNaNBits);
-      }
-      if (t == 0) {
-        P.accepted_len[s] = -1;
-        if (P.status) P.status[s] = kStBadLayout;
-      }
-    }
-    __syncthreads();
-    return;
-  }
-  const int off_d = (int)bef;
-  const int off_t = off_d + s;
-
-  // ---- per-sequence checks ----
-  int st = 0;
-  if (K > P.max_k) st |= kStKTooLarge;
-  if (md != kSample && md != kGreedy && md != kOnehot) st |= kStBadMode;
-  if ((md == kSample || md == kOnehot) && !(isfinite(T) && T >= kMinTemperature)) st |= kStBadTemp;
-  if (md == kSample && K > 0 && P.dft == nullptr) st |= kStNoDraft;
-  if (st == 0) {
-    // K <= max_k <= kMaxK < kThreads: one proposal per thread
-    const int x = (t < K) ? P.tokens[off_d + t] : 0;
-    if (__syncthreads_or(t < K && (x < 0 || x >= P.V))) st = kStBadToken;
-  }
-  if (st) {                                   // uniform over the block
-    if (writer) clear_sequence(P, s, off_t, off_d, K, st);
-    __syncthreads();
-    return;
-  }
-  const float c = (md == kGreedy) ? kLog2e : kLog2e / T;
-  const int nrows = K + 1 + (md == kSample ? K : 0);
-
-  // ---- each row's chunk partials, merged in a fixed order (one wave per row) ----
+// Rows with more chunk partials than the LDS stage holds: merge each row
+// straight from global memory (one wave per row).
+__device__ __forceinline__ void merge_rows_global(const Params& P, ScanShared& sh, int K, int nrows,
+                                                            int off_t, int off_d, float c) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   for (int r = wv; r < nrows; r += kWaves) {
     const bool isd = r > K;
     const int nch = isd ? P.nch_d : P.nch_t;
@@ -817,6 +905,108 @@ __device__ void scan_sequence(const Params& P, int s, ScanShared& sh, bool write
       sh.I[r] = idx;
     }
   }
+}
+
+// The acceptance scan of sequence s by one 256-thread block: stores every
+// output of the sequence but the final token and fills sh.f (kind
+// kFinalDone when no final draw is left).  Two dependent rounds of loads:
+// the layout sums, then the proposals, their logits and the rows' partials.
+__device__ __forceinline__ void scan_sequence(const Params& P, int s, ScanShared& sh) {
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), wv = t / kWave;
+  if (t == 0) sh.f.kind = kFinalDone;
+
+  // ---- round 1: the sequence's own inputs and the layout sums ----
+  const int K = P.num_draft[s];
+  const int md = P.mode[s];
+  const float T = P.temperature[s];
+  const uint32_t seq_id = P.seq_ids[s];
+  int64_t tot = 0, bef = 0, neg = 0;
+#pragma unroll 4
+  for (int j = t; j < P.B; j += kThreads) {
+    const int64_t k = P.num_draft[j];
+    tot += k;
+    bef += (j < s) ? k : 0;
+    neg |= (k < 0);
+  }
+  tot = wave_sum_i64(tot);
+  bef = wave_sum_i64(bef);
+  neg = wave_sum_i64(neg);
+  if (lane == 0) {
+    sh.red[0][wv] = tot;
+    sh.red[1][wv] = bef;
+    sh.red[2][wv] = neg;
+  }
+  __syncthreads();
+  tot = bef = neg = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    tot += sh.red[0][w];
+    bef += sh.red[1][w];
+    neg += sh.red[2][w];
+  }
+  if (neg != 0 || tot != (int64_t)P.total_draft) {
+    clear_bad_layout(P, s);
+    __syncthreads();
+    return;
+  }
+  const int off_d = (int)bef;
+  const int off_t = off_d + s;
+
+  int st = 0;
+  if (K > P.max_k) st |= kStKTooLarge;
+  if (md != kSample && md != kGreedy && md != kOnehot) st |= kStBadMode;
+  if ((md == kSample || md == kOnehot) && !(isfinite(T) && T >= kMinTemperature)) st |= kStBadTemp;
+  if (md == kSample && K > 0 && P.dft == nullptr) st |= kStNoDraft;
+  if (st) {                                   // uniform over the block
+    clear_sequence(P, s, off_t, off_d, K, st);
+    __syncthreads();
+    return;
+  }
+  const float c = (md == kGreedy) ? kLog2e : kLog2e / T;
+  const bool sample = md == kSample;
+  const int nrows = K + 1 + (sample ? K : 0);
+
+  // ---- round 2: proposals, their logits, the rows' chunk partials ----
+  // K <= max_k <= kMaxK < kThreads: one proposal per thread
+  const int x = (t < K) ? P.tokens[off_d + t] : 0;
+  const float xt = (t < K) ? P.xval[off_t + t] : 0.f;
+  const float xd = (t < K && sample) ? P.xval[(int64_t)P.n_t + off_d + t] : 0.f;
+  const int nt_items = (K + 1) * P.nch_t;
+  const int nitems = nt_items + (sample ? K * P.nch_d : 0);
+  const bool staged = nitems <= kScanStage;
+  if (staged) {
+    const Partial* pt = P.partials + (int64_t)off_t * P.nch_t;
+    const Partial* pd = P.partials + (int64_t)P.n_t * P.nch_t + (int64_t)off_d * P.nch_d;
+#pragma unroll 4
+    for (int l = t; l < nitems; l += kThreads) sh.part[l] = (l < nt_items) ? pt[l] : pd[l - nt_items];
+  }
+  if (__syncthreads_or(t < K && (x < 0 || x >= P.V))) {
+    clear_sequence(P, s, off_t, off_d, K, kStBadToken);
+    __syncthreads();
+    return;
+  }
+  if (staged) {
+    for (int r = wv; r < nrows; r += kWaves) {
+      const bool isd = r > K;
+      const int nch = isd ? P.nch_d : P.nch_t;
+      const int base = isd ? nt_items + (r - K - 1) * P.nch_d : r * P.nch_t;
+      float m = -INFINITY, sum = 0.f;
+      int idx = 0x7FFFFFFF;
+      for (int ch = lane; ch < nch; ch += kWave) {
+        const Partial pp = sh.part[base + ch];
+        merge_stats<true>(m, sum, idx, pp.m, pp.s, pp.idx, c);
+      }
+      wave_merge<true>(m, sum, idx, c);
+      if (lane == 0) {
+        sh.M[r] = m;
+        sh.S[r] = sum;
+        sh.I[r] = idx;
+      }
+    }
+  } else {
+    merge_rows_global(P, sh, K, nrows, off_t, off_d, c);
+  }
   __syncthreads();
 
   // ---- every used row must be finite with a positive sum ----
@@ -826,18 +1016,15 @@ __device__ void scan_sequence(const Params& P, int s, ScanShared& sh, bool write
     if (!(isfinite(m) && isfinite(S) && S > 0.f)) bad = 1;
   }
   if (__syncthreads_or(bad)) {
-    if (writer) clear_sequence(P, s, off_t, off_d, K, kStNonfinite);
+    clear_sequence(P, s, off_t, off_d, K, kStNonfinite);
     __syncthreads();
     return;
   }
 
   // ---- p and q at the proposals, uniforms, accept decisions ----
   if (t < K) {
-    const int x = P.tokens[off_d + t];
-    const float xt = load_logit(P.tgt, (int64_t)(off_t + t) * P.ld_t + x, P.t_bf16);
-    const float xd = (md == kSample) ? load_logit(P.dft, (int64_t)(off_d + t) * P.ld_d + x, P.d_bf16) : 0.f;
     const float p = fexp2(fmaf(xt, c, -(sh.M[t] * c))) / sh.S[t];
-    const float q = (md == kSample) ? fexp2(fmaf(xd, c, -(sh.M[K + 1 + t] * c))) / sh.S[K + 1 + t] : 1.f;
+    const float q = sample ? fexp2(fmaf(xd, c, -(sh.M[K + 1 + t] * c))) / sh.S[K + 1 + t] : 1.f;
     int acc;
     if (md == kGreedy) {
       acc = (x == sh.I[t]);
@@ -846,10 +1033,8 @@ __device__ void scan_sequence(const Params& P, int s, ScanShared& sh, bool write
       const float r = (md == kOnehot) ? p : (q > 0.f ? fminf(1.f, p / q) : 0.f);
       acc = u < r;
     }
-    if (writer) {
-      if (P.p_at) P.p_at[off_d + t] = p;
-      if (P.q_at) P.q_at[off_d + t] = q;
-    }
+    if (P.p_at) P.p_at[off_d + t] = p;
+    if (P.q_at) P.q_at[off_d + t] = q;
     sh.acc[t] = acc;
     sh.tok[t] = x;
   }
@@ -888,25 +1073,25 @@ __device__ void scan_sequence(const Params& P, int s, ScanShared& sh, bool write
       }
     }
     sh.f = f;
-    if (writer) P.accepted_len[s] = a;
+    P.accepted_len[s] = a;
   }
   __syncthreads();
   const int A = sh.A;
 
   // ---- emitted tokens: accepted prefix, -1 after A; greedy fills A too ----
-  if (writer && t <= K) {
+  if (t <= K) {
     if (t < A) P.emitted[off_t + t] = sh.tok[t];
     else if (t > A) P.emitted[off_t + t] = -1;
     else if (md == kGreedy) P.emitted[off_t + t] = sh.I[A];
   }
-  if (writer && md == kGreedy && t == 0 && P.status) P.status[s] = 0;
+  if (md == kGreedy && t == 0 && P.status) P.status[s] = 0;
 }
 
 // One block per sequence: the acceptance scan; records the final draw.
 __global__ void __launch_bounds__(kThreads) k_scan(Params P) {
   __shared__ ScanShared sh;
   const int s = blockIdx.x;
-  scan_sequence(P, s, sh, true);
+  scan_sequence(P, s, sh);
   if (threadIdx.x == 0) P.fin[s] = sh.f;
 }
 
@@ -921,75 +1106,132 @@ __global__ void __launch_bounds__(kThreads) k_tile_sums(Params P) {
   if (threadIdx.x == 0) P.tilesum[(int64_t)s * P.ntiles + j] = tot;
 }
 
-// One block per sequence: the tile holding t = u * Z, then the token in it.
-__global__ void __launch_bounds__(kThreads) k_select(Params P) {
-  __shared__ float s_w[kWaves];
-  __shared__ float s_tiles[kMaxTiles];
-  __shared__ float s_Z, s_tp;
-  __shared__ int s_jj, s_fallback, s_first, s_last;
+struct SelShared {
+  float lw[kTileLds];          // the chosen tile's weights, element order (padded)
+  float w[kWaves];
+  float tiles[kMaxTiles];
+  float tp;
+  int jj, fallback, first, last;
+};
 
-  const int s = blockIdx.x;
-  const SeqFinal f = P.fin[s];
-  if (f.kind == kFinalDone) return;
+// The residual had no mass (rounding only): the token is drawn from p at
+// position A instead.  Recomputes every tile's sum of p and picks the tile.
+__device__ __forceinline__ void select_fallback(const Params& P, const SeqFinal& f, SelShared& sh) {
   const int t = threadIdx.x;
-
-  int kind = f.kind;
-  for (int q = t; q < P.ntiles; q += kThreads) s_tiles[q] = P.tilesum[(int64_t)s * P.ntiles + q];
+  for (int q = 0; q < P.ntiles; ++q) {
+    const float v = block_sum(tile_part(P, f, kFinalBonus, q), sh.w);
+    if (t == 0) sh.tiles[q] = v;
+  }
   __syncthreads();
   if (t == 0) {
     float Z = 0.f;
-    for (int q = 0; q < P.ntiles; ++q) Z += s_tiles[q];   // fixed order
-    s_Z = Z;
-    s_fallback = !(Z > 0.f);
-  }
-  __syncthreads();
-  const bool fallback = s_fallback;
-  if (fallback) {
-    // residual without mass (rounding only): draw from p at position A instead
-    kind = kFinalBonus;
-    float Z = 0.f;
-    for (int q = 0; q < P.ntiles; ++q) {
-      const float v = block_sum(tile_part(P, f, kind, q), s_w);
-      if (t == 0) s_tiles[q] = v;
-      Z += v;
-    }
-    if (t == 0) s_Z = Z;
-    __syncthreads();
-  }
-  if (t == 0) {
-    const float tt = f.u * s_Z;
+    for (int q = 0; q < P.ntiles; ++q) Z += sh.tiles[q];
+    const float tt = f.u * Z;
     float cum = 0.f;
     int jj = -1;
     for (int q = 0; q < P.ntiles; ++q) {
-      if (cum + s_tiles[q] > tt) {
+      if (cum + sh.tiles[q] > tt) {
         jj = q;
         break;
       }
-      cum += s_tiles[q];
+      cum += sh.tiles[q];
     }
     if (jj < 0) {
       for (int q = P.ntiles - 1; q >= 0; --q) {
-        if (s_tiles[q] > 0.f) {
+        if (sh.tiles[q] > 0.f) {
           jj = q;
           break;
         }
       }
       cum = 0.f;
-      for (int q = 0; q < jj; ++q) cum += s_tiles[q];
+      for (int q = 0; q < jj; ++q) cum += sh.tiles[q];
     }
-    s_jj = jj;
-    s_tp = tt - cum;
-    s_first = 0x7FFFFFFF;
-    s_last = -1;
+    sh.jj = jj;
+    sh.tp = tt - cum;
   }
   __syncthreads();
-  const int jj = s_jj;
-  const float tp = s_tp;
+}
 
-  // re-read tile jj: thread t owns kTileVec consecutive elements
+// One block per sequence: the tile holding t = u * Z, then the token in it.
+// Two dependent rounds of loads: the record and the tile sums together, then
+// the chosen tile.
+__global__ void __launch_bounds__(kThreads) k_select(Params P) {
+  __shared__ SelShared sh;
+  constexpr int kTPL = kMaxTiles / kWave;      // tile sums per lane of wave 0
+  const int s = blockIdx.x;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), wv = t / kWave;
+  const SeqFinal f = P.fin[s];
+  float tv[kTPL];
+  if (wv == 0) {
+#pragma unroll
+    for (int k = 0; k < kTPL; ++k) {
+      const int j = lane + k * kWave;
+      tv[k] = (j < P.ntiles) ? P.tilesum[(int64_t)s * P.ntiles + j] : 0.f;
+    }
+  }
+  if (f.kind == kFinalDone) return;
+  if (wv == 0) {
+    // prefix sums over tiles (lane-major within each group of 64), total Z
+    float pre[kTPL];
+    float carry = 0.f;
+#pragma unroll
+    for (int k = 0; k < kTPL; ++k) {
+      float v = tv[k];
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const float o = __shfl_up(v, off, kWave);
+        if (lane >= off) v += o;
+      }
+      pre[k] = carry + v;
+      carry += __shfl(v, kWave - 1, kWave);
+    }
+    const float Z = carry;
+    const float tt = f.u * Z;
+    // first tile whose inclusive prefix exceeds tt; else the last tile with mass
+    int jj = -1, jlast = -1;
+#pragma unroll
+    for (int k = kTPL - 1; k >= 0; --k) {
+      const unsigned long long hit = __ballot(pre[k] > tt && lane + k * kWave < P.ntiles);
+      if (hit) jj = k * kWave + (int)__builtin_ctzll(hit);
+      const unsigned long long pos = __ballot(tv[k] > 0.f);
+      if (pos && jlast < 0) jlast = k * kWave + 63 - (int)__builtin_clzll(pos);
+    }
+    if (jj < 0) jj = jlast;
+    // exclusive prefix of tile jj
+    float before = 0.f;
+#pragma unroll
+    for (int k = 0; k < kTPL; ++k) {
+      const float ex = pre[k] - tv[k];
+      const float b = __shfl(ex, (jj < 0 ? 0 : jj) & (kWave - 1), kWave);
+      if (jj >= 0 && jj / kWave == k) before = b;
+    }
+    if (lane == 0) {
+      sh.fallback = !(Z > 0.f);
+      sh.jj = jj;
+      sh.tp = tt - before;
+      sh.first = 0x7FFFFFFF;
+      sh.last = -1;
+    }
+  }
+  __syncthreads();
+  const bool fallback = sh.fallback;
+  int kind = f.kind;
+  if (fallback) {
+    kind = kFinalBonus;
+    select_fallback(P, f, sh);
+  }
+  const int jj = sh.jj;
+  const float tp = sh.tp;
+
+  // re-read tile jj with coalesced loads into LDS; then thread t takes the
+  // kTileVec consecutive weights starting at element t * kTileVec
+  tile_weights_lds(P, f, kind, jj, sh.lw);
+  __syncthreads();
   const int e0 = jj * kTileElems + t * kTileVec;
   float xv[kTileVec];
-  run_weights_any(P, f, kind, e0, xv);
+#pragma unroll
+  for (int q = 0; q < kTileVec; ++q) xv[q] = sh.lw[lds_pad(t * kTileVec + q)];
   float loc = 0.f;
   int last_pos = -1;
 #pragma unroll
@@ -998,22 +1240,21 @@ __global__ void __launch_bounds__(kThreads) k_select(Params P) {
     loc += xv[q];
   }
   float total;
-  const float before = block_excl_scan(loc, s_w, &total);
+  const float before = block_excl_scan(loc, sh.w, &total);
   // the first element (with weight) whose running prefix passes tp
-  if (before + loc > tp) {
-    float run = before;
-    for (int q = 0; q < kTileVec; ++q) {
-      run += xv[q];
-      if (xv[q] > 0.f && run > tp) {
-        atomicMin(&s_first, e0 + q);   // LDS: the lowest crossing over threads wins
-        break;
-      }
-    }
+  // (fully unrolled: constant register indices)
+  int found = -1;
+  float run = before;
+#pragma unroll
+  for (int q = 0; q < kTileVec; ++q) {
+    run += xv[q];
+    if (found < 0 && xv[q] > 0.f && run > tp) found = q;
   }
-  if (last_pos >= 0) atomicMax(&s_last, last_pos);
+  if (found >= 0) atomicMin(&sh.first, e0 + found);   // LDS: the lowest crossing over threads wins
+  if (last_pos >= 0) atomicMax(&sh.last, last_pos);
   __syncthreads();
   if (t == 0) {
-    const int y = (s_first != 0x7FFFFFFF) ? s_first : s_last;
+    const int y = (sh.first != 0x7FFFFFFF) ? sh.first : sh.last;
     P.emitted[f.emit_pos] = y;
     if (P.status) P.status[s] = fallback ? kStZeroResidual : 0;
   }
