@@ -1,17 +1,19 @@
 // Kernels of the batched speculative-decoding verify step for gfx950.
 //
 // row_stats   one block per (logit row, 32 KB chunk).  The block issues its
-//             chunk's 16-byte non-temporal loads first, then finds the
+//             chunk's 16-byte non-temporal loads first; wave 0 finds the
 //             sequence that owns the row (a wave-level scan of num_draft,
-//             served from cache while the chunk is in flight), and reduces
-//             the chunk in float32 to (max of the raw logits, sum of
-//             exp2(x*c - round(max*c)), lowest-index argmax for greedy rows)
-//             with wave shuffles and LDS across the 4 waves.  No inter-block
+//             served from cache while the chunk is in flight).  The chunk is
+//             reduced in float32 to (max of the raw logits, sum of
+//             exp2(x*c - round(max*c)), lowest-index argmax for greedy rows):
+//             block max first, then one sum against it.  No inter-block
 //             communication.
-// scan        one block per sequence: validates the sequence, merges its
-//             rows' chunk partials in a fixed order, computes p and q at the
-//             proposals, draws the Philox uniforms, runs the left-to-right
-//             acceptance test and writes everything but the final token.
+// scan        one 64-lane wave per sequence: validates the sequence, merges
+//             each row's chunk partials in chunk order (lane r: row r),
+//             computes p and q at the proposals, draws the Philox uniforms,
+//             runs the left-to-right acceptance test (lane i: position i, the
+//             stop position from a ballot) and writes everything but the
+//             final token.
 // tile_sums   one block per (sequence, 8192-element tile) of the row(s) at
 //             the stop position: sum of the unnormalised final weights.
 // select      one block per sequence: picks the tile holding t = u * Z,
@@ -311,52 +313,6 @@ __device__ __forceinline__ void mask_chunk(const char* rowp, int c0, int c1, u32
       v[u] = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
-}
-
-// Full 32 KB chunk in registers: thread t holds vectors (u*256 + t), u < 8.
-template <bool BF16, bool ARG>
-__device__ __forceinline__ void stats_from_regs(const u32x4 (&v)[kNV], int c0, float c, float& m_out, float& s_out,
-                                                int& i_out) {
-  constexpr int VEC = BF16 ? 8 : 4;
-  constexpr int N = kNV * VEC;
-  const int t = threadIdx.x;
-  float f[N];
-#pragma unroll
-  for (int u = 0; u < kNV; ++u) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t w = v[u][q];
-      if (BF16) {
-        f[u * VEC + 2 * q] = bf_lo(w);
-        f[u * VEC + 2 * q + 1] = bf_hi(w);
-      } else {
-        f[u * VEC + q] = __uint_as_float(w);
-      }
-    }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < N; ++k) mx = fmaxf(mx, f[k]);
-  const float mc = (mx == -INFINITY) ? 0.f : mx * c;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-  for (int k = 0; k < N; k += 4) {
-    a0 += fexp2(fmaf(f[k + 0], c, -mc));
-    a1 += fexp2(fmaf(f[k + 1], c, -mc));
-    a2 += fexp2(fmaf(f[k + 2], c, -mc));
-    a3 += fexp2(fmaf(f[k + 3], c, -mc));
-  }
-  s_out = (a0 + a1) + (a2 + a3);
-  m_out = mx;
-  int idx = 0x7FFFFFFF;
-  if (ARG) {
-#pragma unroll
-    for (int k = N - 1; k >= 0; --k) {
-      const int e = c0 + ((k / VEC) * kThreads + t) * VEC + (k % VEC);
-      if (f[k] == mx) idx = e;
-    }
-  }
-  i_out = idx;
 }
 
 // Rows that are not 16-byte aligned (or shorter than one vector): element
@@ -734,61 +690,137 @@ __device__ __forceinline__ int row_proposal(const Params& P, const Owner& own, i
 // The logit at the proposal, taken from the chunk held in registers by the
 // thread that loaded it, stored for the scan kernel (xval[row]).
 template <bool BF>
-__device__ __forceinline__ void record_proposal_logit(const Params& P, const u32x4 (&v)[kNV], int c0, int c1, int x,
-                                                      int64_t grow) {
+__device__ __forceinline__ void record_proposal_logit(const Params& P, const float (&f)[kNV * (BF ? 8 : 4)], int c0,
+                                                      int c1, int x, int64_t grow) {
   constexpr int VEC = BF ? 8 : 4;
+  constexpr int N = kNV * VEC;
   if (x < c0 || x >= c1) return;
   const int o = x - c0;
   const int vi = o / VEC;
   if ((vi & (kThreads - 1)) != (int)threadIdx.x) return;
-  const int u = vi / kThreads;
-  const int q = o % VEC;
-  const int word = BF ? (q >> 1) : q;
-  // constant register indices only (a runtime index would spill v to scratch)
-  uint32_t w = 0;
+  const int k = (vi / kThreads) * VEC + o % VEC;
+  // constant register indices only (a runtime index would spill f to scratch)
+  float val = 0.f;
 #pragma unroll
-  for (int uu = 0; uu < kNV; ++uu)
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq)
-      if (uu == u && qq == word) w = v[uu][qq];
-  P.xval[grow] = BF ? ((q & 1) ? bf_hi(w) : bf_lo(w)) : __uint_as_float(w);
+  for (int kk = 0; kk < N; ++kk)
+    if (kk == k) val = f[kk];
+  P.xval[grow] = val;
 }
 
-template <bool BF, bool ARG>
-__device__ __forceinline__ void chunk_from_regs(const Params& P, const u32x4 (&v)[kNV], int c0, float c) {
-  float m, sum;
-  int idx;
-  stats_from_regs<BF, ARG>(v, c0, c, m, sum, idx);
-  finish_chunk<ARG>(P, m, sum, idx, c);
+template <bool BF>
+__device__ __forceinline__ void unpack_chunk(const u32x4 (&v)[kNV], float (&f)[kNV * (BF ? 8 : 4)]) {
+#pragma unroll
+  for (int u = 0; u < kNV; ++u)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (BF) {
+        f[u * 8 + 2 * q] = bf_lo(v[u][q]);
+        f[u * 8 + 2 * q + 1] = bf_hi(v[u][q]);
+      } else {
+        f[u * 4 + q] = __uint_as_float(v[u][q]);
+      }
+    }
 }
 
-// A 16-byte aligned chunk (full, or the row's last when TAIL): the owner
-// window's loads and the chunk's loads are issued back to back, then used.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// What wave 0 of a row-statistics block hands to the other waves.
+struct StatsShared {
+  float m[kWaves];
+  float s[kWaves];
+  int i[kWaves];
+  Owner own;
+  int x;          // token the row judges, or -1
+};
+
+__device__ __forceinline__ void publish_owner(const Params& P, StatsShared& sh, const Owner& own, int row,
+                                              bool is_draft) {
+  const int x = (own.s >= 0) ? row_proposal(P, own, row, is_draft) : -1;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    sh.own = own;
+    sh.x = x;
+  }
+}
+
+// A 16-byte aligned chunk (full, or the row's last when TAIL).  Every wave
+// issues its share of the chunk's loads at once; wave 0 alone also looks up
+// the owning sequence (its window loads go first, so the lookup overlaps the
+// chunk's flight) and publishes it in LDS.  The block first agrees on the
+// chunk maximum M, then every thread sums exp2(x*c - round(M*c)) against that
+// common reference, so the block's partial is a plain sum (no rescaling).
 template <bool BF, bool TAIL>
 __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp, int row, int c0, int c1,
                                               int plus_one, bool is_draft) {
+  constexpr int VEC = BF ? 8 : 4;
+  constexpr int N = kNV * VEC;
+  __shared__ StatsShared sh;
+  const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
   u32x4 v[kNV];
-  Owner own;
-  if (P.B <= kWave * kWin) {
-    // issue order: the window's loads, then the chunk's loads, then any use
-    // (vector loads complete in issue order, so the lookup only waits for the
-    // window while the chunk is still in flight)
-    const SeqWindow win = load_window(P);
-    __builtin_amdgcn_sched_barrier(0);
-    load_chunk<BF, TAIL>(rowp, c0, c1, v);
-    __builtin_amdgcn_sched_barrier(0);
-    own = owner_in_window(win, P, plus_one, row);
+  if (wv == 0) {
+    if (P.B <= kWave * kWin) {
+      const SeqWindow win = load_window(P);
+      __builtin_amdgcn_sched_barrier(0);
+      load_chunk<BF, TAIL>(rowp, c0, c1, v);
+      __builtin_amdgcn_sched_barrier(0);
+      publish_owner(P, sh, owner_in_window(win, P, plus_one, row), row, is_draft);
+    } else {
+      load_chunk<BF, TAIL>(rowp, c0, c1, v);
+      publish_owner(P, sh, owner_general(P, plus_one, row), row, is_draft);
+    }
   } else {
     load_chunk<BF, TAIL>(rowp, c0, c1, v);
-    own = owner_general(P, plus_one, row);
   }
-  if (own.s < 0) return;                   // every wave agrees: inconsistent layout
-  const int x = row_proposal(P, own, row, is_draft);
   if (TAIL) mask_chunk<BF>(rowp, c0, c1, v);
-  record_proposal_logit<BF>(P, v, c0, c1, x, is_draft ? (int64_t)P.n_t + row : (int64_t)row);
+  float f[N];
+  unpack_chunk<BF>(v, f);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < N; ++k) mx = fmaxf(mx, f[k]);
+  mx = wave_max(mx);
+  if (lane == 0) sh.m[wv] = mx;
+  __syncthreads();
+  const Owner own = sh.own;
+  if (own.s < 0) return;                   // the whole block: inconsistent layout
+  const float M = fmaxf(fmaxf(sh.m[0], sh.m[1]), fmaxf(sh.m[2], sh.m[3]));
   const float c = row_scale(own.md, own.T);
-  if (own.md == kGreedy && !is_draft) chunk_from_regs<BF, true>(P, v, c0, c);
-  else chunk_from_regs<BF, false>(P, v, c0, c);
+  const float mc = (M == -INFINITY) ? 0.f : M * c;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+  for (int k = 0; k < N; k += 4) {
+    a0 += fexp2(fmaf(f[k + 0], c, -mc));
+    a1 += fexp2(fmaf(f[k + 1], c, -mc));
+    a2 += fexp2(fmaf(f[k + 2], c, -mc));
+    a3 += fexp2(fmaf(f[k + 3], c, -mc));
+  }
+  const float sum = wave_sum((a0 + a1) + (a2 + a3));
+  int idx = 0x7FFFFFFF;
+  if (own.md == kGreedy && !is_draft) {    // lowest index attaining M
+#pragma unroll
+    for (int k = N - 1; k >= 0; --k)
+      if (f[k] == M) idx = c0 + ((k / VEC) * kThreads + t) * VEC + (k % VEC);
+    idx = wave_min_i(idx);
+  }
+  record_proposal_logit<BF>(P, f, c0, c1, sh.x, is_draft ? (int64_t)P.n_t + row : (int64_t)row);
+  if (lane == 0) {
+    sh.s[wv] = sum;
+    sh.i[wv] = idx;
+  }
+  __syncthreads();
+  if (t == 0) {
+    const float S = (sh.s[0] + sh.s[1]) + (sh.s[2] + sh.s[3]);
+    const int I = min(min(sh.i[0], sh.i[1]), min(sh.i[2], sh.i[3]));
+    P.partials[blockIdx.x] = Partial{M, S, I, 0};    // block index == partial index
+  }
 }
 
 // Rows that are not 16-byte aligned, or shorter than one vector.
@@ -853,26 +885,26 @@ __global__ void __launch_bounds__(kThreads) k_row_stats(Params P) {
   row_stats_body<TB, DB>(P);
 }
 
-constexpr int kScanStage = 1024;   // chunk partials a scan block stages in LDS
+// ---------------------------------------------------------------------------
+// scan: one 64-lane wave per sequence, so no cross-wave barriers.  Lane r
+// merges the chunk partials of row r on its own; lane i judges position i.
+// ---------------------------------------------------------------------------
+constexpr int kScanThreads = kWave;
+constexpr int kMergeUnroll = 16;      // chunk partials a lane has in flight at once
 
 struct ScanShared {
-  Partial part[kScanStage];
-  float M[2 * kMaxK + 1];
+  float M[2 * kMaxK + 1];   // rows 0..K: target, K+1..2K: draft
   float S[2 * kMaxK + 1];
   int I[2 * kMaxK + 1];
-  int acc[kMaxK];
   int tok[kMaxK];
-  int64_t red[3][kWaves];
-  SeqFinal f;
-  int A;
 };
 
 // Inconsistent num_draft: every output slot is cleared; block s clears its share.
 __device__ __forceinline__ void clear_bad_layout(const Params& P, int s) {
-  const int t = threadIdx.x;
-  for (int64_t e = (int64_t)s * kThreads + t; e < (int64_t)P.total_draft + P.B; e += (int64_t)P.B * kThreads)
-    P.emitted[e] = -1;
-  for (int64_t e = (int64_t)s * kThreads + t; e < P.total_draft; e += (int64_t)P.B * kThreads) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int64_t stride = (int64_t)P.B * nt;
+  for (int64_t e = (int64_t)s * nt + t; e < (int64_t)P.total_draft + P.B; e += stride) P.emitted[e] = -1;
+  for (int64_t e = (int64_t)s * nt + t; e < P.total_draft; e += stride) {
     if (P.p_at) P.p_at[e] = __uint_as_float(kNaNBits);
     if (P.q_at) P.q_at[e] = __uint_as_float(kNaNBits);
   }
@@ -882,39 +914,50 @@ __device__ __forceinline__ void clear_bad_layout(const Params& P, int s) {
   }
 }
 
-// Rows with more chunk partials than the LDS stage holds: merge each row
-// straight from global memory (one wave per row).
-__device__ __forceinline__ void merge_rows_global(const Params& P, ScanShared& sh, int K, int nrows,
-                                                            int off_t, int off_d, float c) {
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  for (int r = wv; r < nrows; r += kWaves) {
-    const bool isd = r > K;
-    const int nch = isd ? P.nch_d : P.nch_t;
-    const int64_t pbase = isd ? (int64_t)P.n_t * P.nch_t + (int64_t)(off_d + (r - K - 1)) * P.nch_d
-                              : (int64_t)(off_t + r) * P.nch_t;
-    float m = -INFINITY, sum = 0.f;
-    int idx = 0x7FFFFFFF;
-    for (int ch = lane; ch < nch; ch += kWave) {
-      const Partial pp = P.partials[pbase + ch];
-      merge_stats<true>(m, sum, idx, pp.m, pp.s, pp.idx, c);
+// Row statistics from the row's chunk partials: M = max of the chunk maxima,
+// S = sum of s_k * exp2(round(m_k*c) - round(M*c)), I = lowest index attaining
+// M.  The chunks are taken in order; kMergeUnroll loads are issued before any
+// is used (indices clamped into the row, surplus entries ignored).
+__device__ __forceinline__ void merge_row(const Partial* pp, int nch, float c, float& M, float& S, int& I) {
+  M = -INFINITY;
+  S = 0.f;
+  I = 0x7FFFFFFF;
+  for (int k0 = 0; k0 < nch; k0 += kMergeUnroll) {
+    Partial q[kMergeUnroll];
+#pragma unroll
+    for (int k = 0; k < kMergeUnroll; ++k) q[k] = pp[min(k0 + k, nch - 1)];
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMergeUnroll; ++k)
+      if (k0 + k < nch) m = fmaxf(m, q[k].m);
+    // fold the running (M, S) into this group's reference
+    const float mn = fmaxf(M, m);
+    const float mnc = (mn == -INFINITY) ? 0.f : mn * c;
+    float sum = (M == -INFINITY) ? S : S * fexp2(M * c - mnc);
+    int idx = (M == mn) ? I : 0x7FFFFFFF;
+#pragma unroll
+    for (int k = 0; k < kMergeUnroll; ++k) {
+      if (k0 + k < nch) {
+        sum += (q[k].m == -INFINITY) ? q[k].s : q[k].s * fexp2(q[k].m * c - mnc);
+        if (q[k].m == mn) idx = min(idx, q[k].idx);
+      }
     }
-    wave_merge<true>(m, sum, idx, c);
-    if (lane == 0) {
-      sh.M[r] = m;
-      sh.S[r] = sum;
-      sh.I[r] = idx;
-    }
+    M = mn;
+    S = sum;
+    I = idx;
   }
 }
 
-// The acceptance scan of sequence s by one 256-thread block: stores every
-// output of the sequence but the final token and fills sh.f (kind
-// kFinalDone when no final draw is left).  Two dependent rounds of loads:
-// the layout sums, then the proposals, their logits and the rows' partials.
-__device__ __forceinline__ void scan_sequence(const Params& P, int s, ScanShared& sh) {
-  const int t = threadIdx.x;
-  const int lane = t & (kWave - 1), wv = t / kWave;
-  if (t == 0) sh.f.kind = kFinalDone;
+// The acceptance scan of sequence s: stores every output of the sequence but
+// the final token and returns what the final draw needs (kind kFinalDone when
+// nothing is left).  Two dependent rounds of loads: the layout sums with the
+// sequence's own inputs, then the proposals, their logits and the rows'
+// partials.
+__device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanShared& sh) {
+  const int lane = threadIdx.x;
+  SeqFinal f{};
+  f.kind = kFinalDone;
+  f.s = s;
 
   // ---- round 1: the sequence's own inputs and the layout sums ----
   const int K = P.num_draft[s];
@@ -923,7 +966,7 @@ __device__ __forceinline__ void scan_sequence(const Params& P, int s, ScanShared
   const uint32_t seq_id = P.seq_ids[s];
   int64_t tot = 0, bef = 0, neg = 0;
 #pragma unroll 4
-  for (int j = t; j < P.B; j += kThreads) {
+  for (int j = lane; j < P.B; j += kScanThreads) {
     const int64_t k = P.num_draft[j];
     tot += k;
     bef += (j < s) ? k : 0;
@@ -932,23 +975,9 @@ __device__ __forceinline__ void scan_sequence(const Params& P, int s, ScanShared
   tot = wave_sum_i64(tot);
   bef = wave_sum_i64(bef);
   neg = wave_sum_i64(neg);
-  if (lane == 0) {
-    sh.red[0][wv] = tot;
-    sh.red[1][wv] = bef;
-    sh.red[2][wv] = neg;
-  }
-  __syncthreads();
-  tot = bef = neg = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    tot += sh.red[0][w];
-    bef += sh.red[1][w];
-    neg += sh.red[2][w];
-  }
   if (neg != 0 || tot != (int64_t)P.total_draft) {
     clear_bad_layout(P, s);
-    __syncthreads();
-    return;
+    return f;
   }
   const int off_d = (int)bef;
   const int off_t = off_d + s;
@@ -958,141 +987,121 @@ __device__ __forceinline__ void scan_sequence(const Params& P, int s, ScanShared
   if (md != kSample && md != kGreedy && md != kOnehot) st |= kStBadMode;
   if ((md == kSample || md == kOnehot) && !(isfinite(T) && T >= kMinTemperature)) st |= kStBadTemp;
   if (md == kSample && K > 0 && P.dft == nullptr) st |= kStNoDraft;
-  if (st) {                                   // uniform over the block
+  if (st) {
     clear_sequence(P, s, off_t, off_d, K, st);
-    __syncthreads();
-    return;
+    return f;
   }
   const float c = (md == kGreedy) ? kLog2e : kLog2e / T;
   const bool sample = md == kSample;
   const int nrows = K + 1 + (sample ? K : 0);
 
-  // ---- round 2: proposals, their logits, the rows' chunk partials ----
-  // K <= max_k <= kMaxK < kThreads: one proposal per thread
-  const int x = (t < K) ? P.tokens[off_d + t] : 0;
-  const float xt = (t < K) ? P.xval[off_t + t] : 0.f;
-  const float xd = (t < K && sample) ? P.xval[(int64_t)P.n_t + off_d + t] : 0.f;
-  const int nt_items = (K + 1) * P.nch_t;
-  const int nitems = nt_items + (sample ? K * P.nch_d : 0);
-  const bool staged = nitems <= kScanStage;
-  if (staged) {
-    const Partial* pt = P.partials + (int64_t)off_t * P.nch_t;
-    const Partial* pd = P.partials + (int64_t)P.n_t * P.nch_t + (int64_t)off_d * P.nch_d;
-#pragma unroll 4
-    for (int l = t; l < nitems; l += kThreads) sh.part[l] = (l < nt_items) ? pt[l] : pd[l - nt_items];
+  // ---- round 2: position `lane`'s proposal and the logits at it, then the
+  // rows' chunk partials (lane r: row r); everything issued before any use ----
+  int x0 = 0;
+  float xt0 = 0.f, xd0 = 0.f;
+  if (lane < K) {
+    x0 = P.tokens[off_d + lane];
+    xt0 = P.xval[off_t + lane];
+    if (sample) xd0 = P.xval[(int64_t)P.n_t + off_d + lane];
   }
-  if (__syncthreads_or(t < K && (x < 0 || x >= P.V))) {
-    clear_sequence(P, s, off_t, off_d, K, kStBadToken);
-    __syncthreads();
-    return;
-  }
-  if (staged) {
-    for (int r = wv; r < nrows; r += kWaves) {
-      const bool isd = r > K;
-      const int nch = isd ? P.nch_d : P.nch_t;
-      const int base = isd ? nt_items + (r - K - 1) * P.nch_d : r * P.nch_t;
-      float m = -INFINITY, sum = 0.f;
-      int idx = 0x7FFFFFFF;
-      for (int ch = lane; ch < nch; ch += kWave) {
-        const Partial pp = sh.part[base + ch];
-        merge_stats<true>(m, sum, idx, pp.m, pp.s, pp.idx, c);
-      }
-      wave_merge<true>(m, sum, idx, c);
-      if (lane == 0) {
-        sh.M[r] = m;
-        sh.S[r] = sum;
-        sh.I[r] = idx;
-      }
-    }
-  } else {
-    merge_rows_global(P, sh, K, nrows, off_t, off_d, c);
-  }
-  __syncthreads();
-
-  // ---- every used row must be finite with a positive sum ----
   int bad = 0;
-  for (int r = t; r < nrows; r += kThreads) {
-    const float m = sh.M[r], S = sh.S[r];
-    if (!(isfinite(m) && isfinite(S) && S > 0.f)) bad = 1;
+  for (int r = lane; r < nrows; r += kScanThreads) {
+    const bool isd = r > K;
+    const Partial* pp = isd ? P.partials + (int64_t)P.n_t * P.nch_t + (int64_t)(off_d + r - K - 1) * P.nch_d
+                            : P.partials + (int64_t)(off_t + r) * P.nch_t;
+    float M, S;
+    int I;
+    merge_row(pp, isd ? P.nch_d : P.nch_t, c, M, S, I);
+    sh.M[r] = M;
+    sh.S[r] = S;
+    sh.I[r] = I;
+    bad |= !(isfinite(M) && isfinite(S) && S > 0.f);
   }
-  if (__syncthreads_or(bad)) {
+  int badtok = 0;
+  if (lane < K) {
+    sh.tok[lane] = x0;
+    badtok = (x0 < 0 || x0 >= P.V);
+  }
+  for (int i = lane + kScanThreads; i < K; i += kScanThreads) {   // K > 64 only
+    const int x = P.tokens[off_d + i];
+    sh.tok[i] = x;
+    badtok |= (x < 0 || x >= P.V);
+  }
+  if (__any(badtok)) {
+    clear_sequence(P, s, off_t, off_d, K, kStBadToken);
+    return f;
+  }
+  if (__any(bad)) {
     clear_sequence(P, s, off_t, off_d, K, kStNonfinite);
-    __syncthreads();
-    return;
+    return f;
   }
+  __syncthreads();   // the rows' statistics and tokens, written by other lanes
 
   // ---- p and q at the proposals, uniforms, accept decisions ----
-  if (t < K) {
-    const float p = fexp2(fmaf(xt, c, -(sh.M[t] * c))) / sh.S[t];
-    const float q = sample ? fexp2(fmaf(xd, c, -(sh.M[K + 1 + t] * c))) / sh.S[K + 1 + t] : 1.f;
-    int acc;
-    if (md == kGreedy) {
-      acc = (x == sh.I[t]);
-    } else {
-      const float u = draw_uniform(P, seq_id, (uint32_t)t, 0u);
-      const float r = (md == kOnehot) ? p : (q > 0.f ? fminf(1.f, p / q) : 0.f);
-      acc = u < r;
-    }
-    if (P.p_at) P.p_at[off_d + t] = p;
-    if (P.q_at) P.q_at[off_d + t] = q;
-    sh.acc[t] = acc;
-    sh.tok[t] = x;
-  }
-  __syncthreads();
-  if (t == 0) {
-    int a = K;
-    for (int i = 0; i < K; ++i) {
-      if (!sh.acc[i]) {
-        a = i;
-        break;
-      }
-    }
-    sh.A = a;
-    SeqFinal f{};
-    f.s = s;
-    f.A = a;
-    f.emit_pos = off_t + a;
-    f.c = c;
-    if (md == kGreedy) {
-      f.kind = kFinalDone;
-    } else {
-      f.trow = off_t + a;
-      f.mct = sh.M[a] * c;
-      f.inv_st = 1.f / sh.S[a];
-      f.u = draw_uniform(P, seq_id, (uint32_t)a, 1u);
-      if (a == K) {
-        f.kind = kFinalBonus;
-      } else if (md == kOnehot) {
-        f.kind = kFinalOnehot;
-        f.xhat = sh.tok[a];
+  int A = K;
+  for (int i0 = 0; i0 < K; i0 += kScanThreads) {
+    const int i = i0 + lane;
+    int reject = 0;
+    if (i < K) {
+      const float xt = (i0 == 0) ? xt0 : P.xval[off_t + i];
+      const float xd = (i0 == 0) ? xd0 : (sample ? P.xval[(int64_t)P.n_t + off_d + i] : 0.f);
+      const float p = fexp2(fmaf(xt, c, -(sh.M[i] * c))) / sh.S[i];
+      const float q = sample ? fexp2(fmaf(xd, c, -(sh.M[K + 1 + i] * c))) / sh.S[K + 1 + i] : 1.f;
+      int acc;
+      if (md == kGreedy) {
+        acc = (sh.tok[i] == sh.I[i]);
       } else {
-        f.kind = kFinalResidual;
-        f.drow = off_d + a;
-        f.mcd = sh.M[K + 1 + a] * c;
-        f.inv_sd = 1.f / sh.S[K + 1 + a];
+        const float u = draw_uniform(P, seq_id, (uint32_t)i, 0u);
+        const float r = (md == kOnehot) ? p : (q > 0.f ? fminf(1.f, p / q) : 0.f);
+        acc = u < r;
       }
+      if (P.p_at) P.p_at[off_d + i] = p;
+      if (P.q_at) P.q_at[off_d + i] = q;
+      reject = !acc;
     }
-    sh.f = f;
-    P.accepted_len[s] = a;
+    const unsigned long long rj = __ballot(reject);
+    if (A == K && rj != 0ull) A = i0 + (int)__builtin_ctzll(rj);
   }
-  __syncthreads();
-  const int A = sh.A;
 
   // ---- emitted tokens: accepted prefix, -1 after A; greedy fills A too ----
-  if (t <= K) {
-    if (t < A) P.emitted[off_t + t] = sh.tok[t];
-    else if (t > A) P.emitted[off_t + t] = -1;
-    else if (md == kGreedy) P.emitted[off_t + t] = sh.I[A];
+  for (int j = lane; j <= K; j += kScanThreads) {
+    if (j < A) P.emitted[off_t + j] = sh.tok[j];
+    else if (j > A) P.emitted[off_t + j] = -1;
+    else if (md == kGreedy) P.emitted[off_t + j] = sh.I[A];
   }
-  if (md == kGreedy && t == 0 && P.status) P.status[s] = 0;
+  if (lane == 0) {
+    P.accepted_len[s] = A;
+    if (md == kGreedy && P.status) P.status[s] = 0;
+  }
+  f.A = A;
+  f.emit_pos = off_t + A;
+  f.c = c;
+  if (md != kGreedy) {
+    f.trow = off_t + A;
+    f.mct = sh.M[A] * c;
+    f.inv_st = 1.f / sh.S[A];
+    f.u = draw_uniform(P, seq_id, (uint32_t)A, 1u);
+    if (A == K) {
+      f.kind = kFinalBonus;
+    } else if (md == kOnehot) {
+      f.kind = kFinalOnehot;
+      f.xhat = sh.tok[A];
+    } else {
+      f.kind = kFinalResidual;
+      f.drow = off_d + A;
+      f.mcd = sh.M[K + 1 + A] * c;
+      f.inv_sd = 1.f / sh.S[K + 1 + A];
+    }
+  }
+  return f;
 }
 
-// One block per sequence: the acceptance scan; records the final draw.
-__global__ void __launch_bounds__(kThreads) k_scan(Params P) {
+// One wave per sequence: the acceptance scan; records the final draw.
+__global__ void __launch_bounds__(kScanThreads) k_scan(Params P) {
   __shared__ ScanShared sh;
   const int s = blockIdx.x;
-  scan_sequence(P, s, sh);
-  if (threadIdx.x == 0) P.fin[s] = sh.f;
+  const SeqFinal f = scan_sequence(P, s, sh);
+  if (threadIdx.x == 0) P.fin[s] = f;
 }
 
 // grid (ntiles, B): the final weights of one tile of the row(s) at the stop
@@ -1279,7 +1288,7 @@ hipError_t launch_row_stats(const Params& p, hipStream_t st) {
 }
 
 hipError_t launch_scan(const Params& p, hipStream_t st) {
-  hipLaunchKernelGGL(k_scan, dim3(p.B), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(k_scan, dim3(p.B), dim3(kScanThreads), 0, st, p);
   return hipGetLastError();
 }
 
