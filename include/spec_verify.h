@@ -133,10 +133,13 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
  * SV_ERR_CAPACITY: nothing is enqueued); problems that only the device can
  * see are reported per sequence through `status`.  Does not allocate, does
  * not synchronise; outputs are valid once the stream has reached this point.
- * Launches four kernels: row statistics (one block per 32 KB of every
- * logit row), scan (one block per sequence: the acceptance test), tile sums
- * (one block per 8192-element tile of the row(s) at each stop position) and
- * select (one block per sequence: inverse-CDF search). */
+ * Launches two or three kernels: row statistics (one block per 32 KB of
+ * every logit row); final (per sequence: the acceptance test, then the sums
+ * of the final weights over 8192-element tiles of the row(s) at the stop
+ * position and, when one block holds the whole sequence, the inverse-CDF
+ * search); for batches below 128 the tiles of a sequence are spread over
+ * several blocks and a select kernel (one block per sequence) does the
+ * search. */
 int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* args, void* hip_stream);
 
 /* Free the context and its device memory.  NULL is accepted. */
@@ -147,13 +150,14 @@ const char* spec_verify_last_error(void);
 
 /* ---- measurement hooks ---------------------------------------------------
  * spec_verify_timing_enable(ctx, n) makes the next n calls of
- * spec_verify_run record a HIP event before and after each of its four
- * kernels on the call's stream (n = 0 turns it off; events are created here,
+ * spec_verify_run record a HIP event before and after each of its kernel
+ * slots on the call's stream (n = 0 turns it off; events are created here,
  * never inside run).  spec_verify_timing_read waits for those events and
- * returns the number of recorded calls and, per kernel, the summed elapsed
+ * returns the number of recorded calls and, per slot, the summed elapsed
  * milliseconds (ms_per_kernel has SV_NUM_KERNELS entries: row statistics,
- * scan, tile sums, select), then resets the record. */
-#define SV_NUM_KERNELS 4
+ * final, select; a slot whose kernel was not launched reads about 0), then
+ * resets the record. */
+#define SV_NUM_KERNELS 3
 int spec_verify_timing_enable(spec_verify_ctx* ctx, int32_t max_calls);
 int spec_verify_timing_read(spec_verify_ctx* ctx, int32_t* calls, double* ms_per_kernel);
 

@@ -18,8 +18,8 @@ SV_ST_NO_DRAFT_LOGITS = 16
 SV_ST_BAD_TOKEN = 32
 SV_ST_NONFINITE = 64
 SV_ST_ZERO_RESIDUAL = 128
-SV_NUM_KERNELS = 4
-KERNEL_NAMES = ("row_stats", "scan", "tile_sums", "select")
+SV_NUM_KERNELS = 3
+KERNEL_NAMES = ("row_stats", "final", "select")
 
 EXPORTED = (
     "spec_verify_create", "spec_verify_run", "spec_verify_destroy", "spec_verify_last_error",

@@ -279,6 +279,12 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
   p.nch_t = (p.V + p.ce_t - 1) / p.ce_t;
   p.nch_d = (p.V + p.ce_d - 1) / p.ce_d;
   p.ntiles = (p.V + sv::kTileElems - 1) / sv::kTileElems;
+  p.nsplit = 1;
+  if (p.B < sv::kFuseMinBatch) {
+    const int want = (sv::kSplitTargetBlocks + p.B - 1) / p.B;
+    p.nsplit = want < p.ntiles ? want : p.ntiles;
+    if (p.nsplit < 1) p.nsplit = 1;
+  }
   if ((int64_t)(p.n_t + p.n_d) > ctx->max_rows || p.nch_t > ctx->max_nch || p.nch_d > ctx->max_nch ||
       p.ntiles > ctx->max_tiles) {
     set_err("spec_verify_run: scratch capacity exceeded");
@@ -293,9 +299,8 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
   const bool timed = ctx->timing_used < ctx->timing_cap;
   hipEvent_t* ev = timed ? &ctx->events[(size_t)ctx->timing_used * (SV_NUM_KERNELS + 1)] : nullptr;
   typedef hipError_t (*Launch)(const sv::Params&, hipStream_t);
-  static const Launch kLaunch[SV_NUM_KERNELS] = {sv::launch_row_stats, sv::launch_scan, sv::launch_tile_sums,
-                                                 sv::launch_select};
-  static const char* kName[SV_NUM_KERNELS] = {"row_stats", "scan", "tile_sums", "select"};
+  static const Launch kLaunch[SV_NUM_KERNELS] = {sv::launch_row_stats, sv::launch_final, sv::launch_select};
+  static const char* kName[SV_NUM_KERNELS] = {"row_stats", "final", "select"};
   if (timed && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail("hipEventRecord", e);
   for (int k = 0; k < SV_NUM_KERNELS; ++k) {
     if ((e = kLaunch[k](p, st)) != hipSuccess) return hip_fail(kName[k], e);

@@ -7,11 +7,16 @@
 
 namespace sv {
 
-constexpr int kThreads = 256;           // every kernel: 4 waves of 64
+constexpr int kThreads = 256;           // row-statistics blocks: 4 waves of 64
 constexpr int kChunkBytes = 32768;      // bytes of one logit row streamed by one row-stats block
 constexpr int kTileElems = 8192;        // elements of a tile of the final draw
 constexpr int kMaxK = 128;
 constexpr int kMaxTiles = 256;          // => vocab <= 2,097,152
+// The final kernel runs one 1024-thread block per sequence when the batch
+// alone fills the chip; smaller batches split each sequence's tiles over
+// about kSplitTargetBlocks / B blocks and finish in a select kernel.
+constexpr int kFuseMinBatch = 128;
+constexpr int kSplitTargetBlocks = 256;
 
 // Row statistics of one chunk of one row: max of the raw logits m, the sum
 // s = sum exp2(x*c - round(m*c)), and the lowest index attaining m.
@@ -29,7 +34,7 @@ enum FinalKind : int32_t {
   kFinalBonus = 3         // w = p_K
 };
 
-// What the final draw needs, written by the scan kernel for every sequence.
+// What the final draw needs, written by the acceptance scan for every sequence.
 struct SeqFinal {
   int32_t kind;
   int32_t A;
@@ -84,12 +89,13 @@ struct Params {
   int32_t ce_t;       // elements per target chunk (32 KB)
   int32_t ce_d;       // elements per draft chunk (32 KB)
   int32_t ntiles;     // tiles per row for the final draw
+  int32_t nsplit;     // final-kernel blocks per sequence
 };
 
-// The four kernels of one verify step, in stream order.
+// The kernels of one verify step, in stream order (select only when
+// nsplit > 1).
 hipError_t launch_row_stats(const Params& p, hipStream_t st);
-hipError_t launch_scan(const Params& p, hipStream_t st);
-hipError_t launch_tile_sums(const Params& p, hipStream_t st);
+hipError_t launch_final(const Params& p, hipStream_t st);
 hipError_t launch_select(const Params& p, hipStream_t st);
 
 }  // namespace sv

@@ -8,17 +8,19 @@
 //             exp2(x*c - round(max*c)), lowest-index argmax for greedy rows):
 //             block max first, then one sum against it.  No inter-block
 //             communication.
-// scan        one 64-lane wave per sequence: validates the sequence, merges
-//             each row's chunk partials in chunk order (lane r: row r),
-//             computes p and q at the proposals, draws the Philox uniforms,
-//             runs the left-to-right acceptance test (lane i: position i, the
-//             stop position from a ballot) and writes everything but the
-//             final token.
-// tile_sums   one block per (sequence, 8192-element tile) of the row(s) at
-//             the stop position: sum of the unnormalised final weights.
-// select      one block per sequence: picks the tile holding t = u * Z,
-//             re-reads it, prefix-sums it across the block and emits the
-//             first token whose inclusive prefix exceeds t.
+// final       grid (nsplit, B) of 1024-thread blocks.  Wave 0 runs the
+//             acceptance scan of its sequence: validates it, merges each
+//             row's chunk partials in chunk order (lane r: row r), computes
+//             p and q at the proposals, draws the Philox uniforms and runs
+//             the left-to-right test (lane i: position i, the stop position
+//             from a ballot); split 0 writes everything but the final token.
+//             The block then sums the final weights over 8192-element tiles
+//             of the row(s) at the stop position.  With one block per
+//             sequence (batches of 128 and more) the same block picks the
+//             tile holding t = u * Z, re-reads it and emits the first token
+//             whose inclusive prefix exceeds t.
+// select      (batches below 128 only) one block per sequence: the tile sums
+//             written by the split final blocks, then the same search.
 //
 // The method (accept with probability min(1, p/q), stop at the first
 // rejection, redraw from norm(max(0, p - q)) or take a bonus token from the
@@ -122,15 +124,81 @@ __device__ __forceinline__ void wave_merge(float& m, float& s, int& idx, float c
   }
 }
 
+// ---------------------------------------------------------------------------
+// wave reductions and scans with DPP lane moves (quad permutes, row shifts
+// and mirrors, the row broadcasts of this ISA family): six VALU steps
+// instead of a chain of LDS-routed shuffles.  Reductions leave the result in
+// lane 63 and broadcast it with readlane.
+// ---------------------------------------------------------------------------
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// lanes that the row mask leaves out (or whose source is out of the row)
+// receive `old`
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, true);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(dpp_i<CTRL, ROW_MASK>(__float_as_int(old), __float_as_int(v)));
+}
+__device__ __forceinline__ float lane63_f(float v) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63)); }
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += dpp_f<kDppQuadXor1>(0.f, v);
+  v += dpp_f<kDppQuadXor2>(0.f, v);
+  v += dpp_f<kDppRowHalfMirror>(0.f, v);
+  v += dpp_f<kDppRowMirror>(0.f, v);
+  v += dpp_f<kDppRowBcast15, 0xA>(0.f, v);
+  v += dpp_f<kDppRowBcast31, 0xC>(0.f, v);
+  return lane63_f(v);
 }
 
-__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += (uint32_t)dpp_i<kDppQuadXor1>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppQuadXor2>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowHalfMirror>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowMirror>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowBcast15, 0xA>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowBcast31, 0xC>(0, (int)v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  const float n = -INFINITY;
+  v = fmaxf(v, dpp_f<kDppQuadXor1>(n, v));
+  v = fmaxf(v, dpp_f<kDppQuadXor2>(n, v));
+  v = fmaxf(v, dpp_f<kDppRowHalfMirror>(n, v));
+  v = fmaxf(v, dpp_f<kDppRowMirror>(n, v));
+  v = fmaxf(v, dpp_f<kDppRowBcast15, 0xA>(n, v));
+  v = fmaxf(v, dpp_f<kDppRowBcast31, 0xC>(n, v));
+  return lane63_f(v);
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+  const int n = 0x7FFFFFFF;
+  v = min(v, dpp_i<kDppQuadXor1>(n, v));
+  v = min(v, dpp_i<kDppQuadXor2>(n, v));
+  v = min(v, dpp_i<kDppRowHalfMirror>(n, v));
+  v = min(v, dpp_i<kDppRowMirror>(n, v));
+  v = min(v, dpp_i<kDppRowBcast15, 0xA>(n, v));
+  v = min(v, dpp_i<kDppRowBcast31, 0xC>(n, v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// inclusive prefix over the lanes (Hillis-Steele inside rows of 16, then
+// the row broadcasts carry the row totals forward)
+__device__ __forceinline__ float wave_incl_scan_f(float v) {
+  v += dpp_f<kDppRowShr1>(0.f, v);
+  v += dpp_f<kDppRowShr2>(0.f, v);
+  v += dpp_f<kDppRowShr4>(0.f, v);
+  v += dpp_f<kDppRowShr8>(0.f, v);
+  v += dpp_f<kDppRowBcast15, 0xA>(0.f, v);
+  v += dpp_f<kDppRowBcast31, 0xC>(0.f, v);
   return v;
 }
 
@@ -194,23 +262,23 @@ __device__ __forceinline__ Owner owner_from_lanes(int owner, float T, int md, in
   Owner o{-1, 1.f, kSample, 0, 0};
   if (hits == 0ull) return o;
   const int src = (int)__builtin_ctzll(hits);
-  o.s = __builtin_amdgcn_readfirstlane(__shfl(owner, src, kWave));
-  o.T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(__shfl(T, src, kWave))));
-  o.md = __builtin_amdgcn_readfirstlane(__shfl(md, src, kWave));
-  o.first = __builtin_amdgcn_readfirstlane(__shfl(first, src, kWave));
-  o.K = __builtin_amdgcn_readfirstlane(__shfl(K, src, kWave));
+  o.s = __builtin_amdgcn_readlane(owner, src);
+  o.T = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(T), src));
+  o.md = __builtin_amdgcn_readlane(md, src);
+  o.first = __builtin_amdgcn_readlane(first, src);
+  o.K = __builtin_amdgcn_readlane(K, src);
   return o;
 }
 
 // 32-bit unsigned arithmetic (wraps instead of overflowing on a corrupt
 // num_draft; a consistent layout has fewer than 2^31 rows).
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
+  v += (uint32_t)dpp_i<kDppRowShr1>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowShr2>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowShr4>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowShr8>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowBcast15, 0xA>(0, (int)v);
+  v += (uint32_t)dpp_i<kDppRowBcast31, 0xC>(0, (int)v);
   return v;
 }
 
@@ -353,53 +421,13 @@ __device__ __forceinline__ void stats_scalar(const void* row, int bf16, int c0, 
 }
 
 // ---------------------------------------------------------------------------
-// block helpers (256 threads)
+// the final draw at the stop position A.  The row(s) at A are cut into tiles
+// of 8192 elements; a 1024-thread block holds 8 elements of a tile per thread.
 // ---------------------------------------------------------------------------
-
-// exclusive prefix of one float per thread in thread order; *total = sum
-__device__ __forceinline__ float block_excl_scan(float v, float* s_w, float* total) {
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-  float inc = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float o = __shfl_up(inc, off, kWave);
-    if (lane >= off) inc += o;
-  }
-  if (lane == kWave - 1) s_w[wv] = inc;
-  __syncthreads();
-  float before = 0.f;
-  for (int w = 0; w < wv; ++w) before += s_w[w];
-  float tot = 0.f;
-  for (int w = 0; w < kWaves; ++w) tot += s_w[w];
-  *total = tot;
-  __syncthreads();
-  return before + inc - v;
-}
-
-__device__ __forceinline__ float block_sum(float v, float* s_w) {
-  v = wave_sum(v);
-  if ((threadIdx.x & (kWave - 1)) == 0) s_w[threadIdx.x / kWave] = v;
-  __syncthreads();
-  float tot = 0.f;
-  for (int w = 0; w < kWaves; ++w) tot += s_w[w];
-  __syncthreads();
-  return tot;
-}
-
-__device__ __forceinline__ int64_t block_sum_i64(int64_t v, int64_t* s_w) {
-  v = wave_sum_i64(v);
-  if ((threadIdx.x & (kWave - 1)) == 0) s_w[threadIdx.x / kWave] = v;
-  __syncthreads();
-  int64_t tot = 0;
-  for (int w = 0; w < kWaves; ++w) tot += s_w[w];
-  __syncthreads();
-  return tot;
-}
-
-// ---------------------------------------------------------------------------
-// the final draw at the stop position: tiles of 8192 elements, 256 threads
-// ---------------------------------------------------------------------------
-constexpr int kTileVec = kTileElems / kThreads;   // 32 elements per thread per tile
+constexpr int kFinThreads = 1024;
+constexpr int kFinWaves = kFinThreads / kWave;
+constexpr int kPerThread = kTileElems / kFinThreads;   // 8
+constexpr int kTileUnroll = 4;                         // tiles whose loads are in flight together
 
 __device__ __forceinline__ float final_weight(int kind, float x, float y, int k, const SeqFinal& f) {
   const float p = fexp2(fmaf(x, f.c, -f.mct)) * f.inv_st;
@@ -411,238 +439,369 @@ __device__ __forceinline__ float final_weight(int kind, float x, float y, int k,
   return p;
 }
 
-// This thread's share of the weight of tile j (coalesced: thread t owns
-// elements base + (u*256 + t)*VEC .. +VEC); every load is issued before use.
-// TAIL (the row's last tile): vectors past V are loaded from the row's
-// first 16 bytes instead and then replaced by -inf logits (weight 0); the
-// one vector that straddles V is rebuilt from element loads.
-template <bool BF16, int KIND, bool TAIL>
-__device__ __forceinline__ float tile_part_vec(const Params& P, const SeqFinal& f, int j) {
-  constexpr int VEC = BF16 ? 8 : 4;
-  constexpr int NV = kTileVec / VEC;
-  constexpr int ES = BF16 ? 2 : 4;
-  const int t = threadIdx.x;
-  const int base = j * kTileElems;
-  const int V = P.V;
-  const char* tp = (const char*)P.tgt + (int64_t)f.trow * P.ld_t * ES;
-  const char* dp = (KIND == kFinalResidual) ? (const char*)P.dft + (int64_t)f.drow * P.ld_d * ES : nullptr;
-  u32x4 vt[NV], vd[NV];
+struct FinShared {
+  float tw[kMaxTiles][kFinWaves];   // each wave's share of each tile's sum
+  float tile[kMaxTiles];            // tile sums
+  float sw[kFinWaves];
+  int first[kFinWaves];
+  int last[kFinWaves];
+  float tp;                         // remainder of u * Z inside tile jj
+  int jj;
+  int fallback;
+};
+
+// The final weights of the VEC elements e.. of one 16-byte vector (target
+// words vt, draft words vd).
+template <bool BF, int KIND>
+__device__ __forceinline__ void vec_weights(const u32x4& vt, const u32x4& vd, int e, const SeqFinal& f,
+                                            float (&w)[BF ? 8 : 4]) {
+  constexpr int VEC = BF ? 8 : 4;
 #pragma unroll
-  for (int u = 0; u < NV; ++u) {
-    const int e = base + (u * kThreads + t) * VEC;
-    const int a = (!TAIL || e + VEC <= V) ? e : 0;
-    vt[u] = __builtin_nontemporal_load((const u32x4*)(tp + (int64_t)a * ES));
-    if (KIND == kFinalResidual) vd[u] = __builtin_nontemporal_load((const u32x4*)(dp + (int64_t)a * ES));
+  for (int q = 0; q < VEC; ++q) {
+    float x, y = 0.f;
+    if (BF) {
+      x = (q & 1) ? bf_hi(vt[q >> 1]) : bf_lo(vt[q >> 1]);
+      if (KIND == kFinalResidual) y = (q & 1) ? bf_hi(vd[q >> 1]) : bf_lo(vd[q >> 1]);
+    } else {
+      x = __uint_as_float(vt[q]);
+      if (KIND == kFinalResidual) y = __uint_as_float(vd[q]);
+    }
+    w[q] = final_weight(KIND, x, y, e + q, f);
   }
-  if (TAIL) {
+}
+
+// The vector of elements e..e+VEC of a 16-byte aligned row: entries at or
+// past V read as -inf (weight 0); a vector that straddles V is assembled
+// from element loads, one wholly past V is not loaded at all.
+template <bool BF>
+__device__ __forceinline__ u32x4 load_vec_masked(const char* rowp, int e, int V) {
+  constexpr int VEC = BF ? 8 : 4;
+  constexpr int ES = BF ? 2 : 4;
+  if (e + VEC <= V) return __builtin_nontemporal_load((const u32x4*)(rowp + (int64_t)e * ES));
+  uint32_t w[4];
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int e = base + (u * kThreads + t) * VEC;
-      if (e + VEC > V) {
-        uint32_t wt[4], wd[4];
+  for (int q = 0; q < 4; ++q) {
+    if (BF) {
+      const int e0 = e + 2 * q, e1 = e0 + 1;
+      const uint32_t lo = (e0 < V) ? (uint32_t)((const uint16_t*)rowp)[e0] : 0xFF80u;
+      const uint32_t hi = (e1 < V) ? (uint32_t)((const uint16_t*)rowp)[e1] : 0xFF80u;
+      w[q] = lo | (hi << 16);
+    } else {
+      const int e0 = e + q;
+      w[q] = (e0 < V) ? ((const uint32_t*)rowp)[e0] : 0xFF800000u;
+    }
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// Sums of the full tiles jb, jb+step, ... (< nfull) into sh.tw.  Thread t
+// owns vectors (n*1024 + t), n < NV, of a tile (coalesced); the loads of
+// kTileUnroll tiles are issued before any is used (indices clamped to the
+// last full tile for the loads, surplus tiles skipped after).
+template <bool BF, int KIND>
+__device__ __forceinline__ void tiles_full_vec(const Params& P, const SeqFinal& f, int j0, int step, int nfull,
+                                               FinShared& sh) {
+  constexpr int VEC = BF ? 8 : 4;
+  constexpr int NV = kPerThread / VEC;
+  constexpr int ES = BF ? 2 : 4;
+  const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
+  const char* tp = (const char*)P.tgt + (int64_t)f.trow * P.ld_t * ES;
+  const char* dp = (KIND == kFinalResidual) ? (const char*)P.dft + (int64_t)f.drow * P.ld_d * ES : tp;
+  for (int jb = j0; jb < nfull; jb += kTileUnroll * step) {
+    u32x4 vt[kTileUnroll][NV], vd[kTileUnroll][NV];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (BF16) {
-            const int e0 = e + 2 * q, e1 = e0 + 1;
-            wt[q] = ((e0 < V) ? (uint32_t)((const uint16_t*)tp)[e0] : 0xFF80u) |
-                    (((e1 < V) ? (uint32_t)((const uint16_t*)tp)[e1] : 0xFF80u) << 16);
-            if (KIND == kFinalResidual)
-              wd[q] = ((e0 < V) ? (uint32_t)((const uint16_t*)dp)[e0] : 0xFF80u) |
-                      (((e1 < V) ? (uint32_t)((const uint16_t*)dp)[e1] : 0xFF80u) << 16);
-          } else {
-            const int e0 = e + q;
-            wt[q] = (e0 < V) ? ((const uint32_t*)tp)[e0] : 0xFF800000u;
-            if (KIND == kFinalResidual) wd[q] = (e0 < V) ? ((const uint32_t*)dp)[e0] : 0xFF800000u;
-          }
+    for (int u = 0; u < kTileUnroll; ++u) {
+      const int j = min(jb + u * step, nfull - 1);
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        const int64_t e = (int64_t)j * kTileElems + (n * kFinThreads + t) * VEC;
+        vt[u][n] = __builtin_nontemporal_load((const u32x4*)(tp + e * ES));
+        if (KIND == kFinalResidual) vd[u][n] = __builtin_nontemporal_load((const u32x4*)(dp + e * ES));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kTileUnroll; ++u) {
+      const int j = jb + u * step;
+      if (j < nfull) {
+        float acc = 0.f;
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+          float w[VEC];
+          vec_weights<BF, KIND>(vt[u][n], vd[u][n], j * kTileElems + (n * kFinThreads + t) * VEC, f, w);
+#pragma unroll
+          for (int q = 0; q < VEC; ++q) acc += w[q];
         }
-        vt[u] = u32x4{wt[0], wt[1], wt[2], wt[3]};
-        if (KIND == kFinalResidual) vd[u] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+        acc = wave_sum(acc);
+        if (lane == 0) sh.tw[j][wv] = acc;
       }
     }
   }
+}
+
+// The row's last tile when it is not full (element layout as above).
+template <bool BF, int KIND>
+__device__ __forceinline__ void tile_tail_vec(const Params& P, const SeqFinal& f, int j, FinShared& sh) {
+  constexpr int VEC = BF ? 8 : 4;
+  constexpr int NV = kPerThread / VEC;
+  constexpr int ES = BF ? 2 : 4;
+  const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
+  const char* tp = (const char*)P.tgt + (int64_t)f.trow * P.ld_t * ES;
+  const char* dp = (KIND == kFinalResidual) ? (const char*)P.dft + (int64_t)f.drow * P.ld_d * ES : tp;
   float acc = 0.f;
 #pragma unroll
-  for (int u = 0; u < NV; ++u) {
-    const int e = base + (u * kThreads + t) * VEC;
+  for (int n = 0; n < NV; ++n) {
+    const int e = j * kTileElems + (n * kFinThreads + t) * VEC;
+    if (e < P.V) {
+      const u32x4 vt = load_vec_masked<BF>(tp, e, P.V);
+      const u32x4 vd = (KIND == kFinalResidual) ? load_vec_masked<BF>(dp, e, P.V) : vt;
+      float w[VEC];
+      vec_weights<BF, KIND>(vt, vd, e, f, w);
 #pragma unroll
-    for (int q = 0; q < VEC; ++q) {
-      float x, y = 0.f;
-      if (BF16) {
-        x = (q & 1) ? bf_hi(vt[u][q >> 1]) : bf_lo(vt[u][q >> 1]);
-        if (KIND == kFinalResidual) y = (q & 1) ? bf_hi(vd[u][q >> 1]) : bf_lo(vd[u][q >> 1]);
-      } else {
-        x = __uint_as_float(vt[u][q]);
-        if (KIND == kFinalResidual) y = __uint_as_float(vd[u][q]);
-      }
-      acc += final_weight(KIND, x, y, e + q, f);
+      for (int q = 0; q < VEC; ++q) acc += w[q];
     }
   }
-  return acc;
+  acc = wave_sum(acc);
+  if (lane == 0) sh.tw[j][wv] = acc;
 }
 
 // Rows that are not 16-byte aligned, shorter than a vector, or a residual
 // whose two rows differ in type: element loads clamped to V - 1, weights
-// past V zeroed.
-__device__ __forceinline__ float tile_part_generic(const Params& P, const SeqFinal& f, int kind, int j) {
-  const int base = j * kTileElems;
+// past V zeroed.  Thread t takes elements j*8192 + q*1024 + t.
+__device__ __forceinline__ void tile_generic(const Params& P, const SeqFinal& f, int kind, int j, FinShared& sh) {
+  const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
   const int64_t toff = (int64_t)f.trow * P.ld_t, doff = (int64_t)f.drow * P.ld_d;
+  float x[kPerThread], y[kPerThread];
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int e = min(j * kTileElems + q * kFinThreads + t, P.V - 1);
+    x[q] = load_logit(P.tgt, toff + e, P.t_bf16);
+    y[q] = (kind == kFinalResidual) ? load_logit(P.dft, doff + e, P.d_bf16) : 0.f;
+  }
   float acc = 0.f;
-  for (int u0 = 0; u0 < kTileVec; u0 += 8) {
-    float x[8], y[8];
-    int ee[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      ee[q] = base + (u0 + q) * kThreads + (int)threadIdx.x;
-      const int e = min(ee[q], P.V - 1);
-      x[q] = load_logit(P.tgt, toff + e, P.t_bf16);
-      y[q] = (kind == kFinalResidual) ? load_logit(P.dft, doff + e, P.d_bf16) : 0.f;
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc += (ee[q] < P.V) ? final_weight(kind, x[q], y[q], ee[q], f) : 0.f;
+  for (int q = 0; q < kPerThread; ++q) {
+    const int e = j * kTileElems + q * kFinThreads + t;
+    acc += (e < P.V) ? final_weight(kind, x[q], y[q], e, f) : 0.f;
   }
-  return acc;
+  acc = wave_sum(acc);
+  if (lane == 0) sh.tw[j][wv] = acc;
 }
 
-template <bool BF16, int KIND>
-__device__ __forceinline__ float tile_part_k(const Params& P, const SeqFinal& f, int j) {
-  if ((j + 1) * kTileElems <= P.V) return tile_part_vec<BF16, KIND, false>(P, f, j);
-  return tile_part_vec<BF16, KIND, true>(P, f, j);
-}
-
-__device__ __forceinline__ float tile_part(const Params& P, const SeqFinal& f, int kind, int j) {
+__device__ __forceinline__ bool final_vec_ok(const Params& P, int kind) {
   const int vecmin = P.t_bf16 ? 8 : 4;
-  const bool vec = P.t_vec && P.V >= vecmin && (kind != kFinalResidual || (P.d_vec && P.d_bf16 == P.t_bf16));
-  if (vec) {
+  return P.t_vec && P.V >= vecmin && (kind != kFinalResidual || (P.d_vec && P.d_bf16 == P.t_bf16));
+}
+
+template <bool BF, int KIND>
+__device__ __forceinline__ void tiles_vec(const Params& P, const SeqFinal& f, int j0, int step, FinShared& sh) {
+  const int nfull = P.V / kTileElems;
+  tiles_full_vec<BF, KIND>(P, f, j0, step, nfull, sh);
+  const int jt = P.ntiles - 1;
+  if (jt >= nfull && jt >= j0 && (jt - j0) % step == 0) tile_tail_vec<BF, KIND>(P, f, jt, sh);
+}
+
+// Per-wave sums of tiles j0, j0+step, ... of the final weights into sh.tw.
+__device__ __forceinline__ void tile_sums_pass(const Params& P, const SeqFinal& f, int kind, int j0, int step,
+                                               FinShared& sh) {
+  if (final_vec_ok(P, kind)) {
     if (P.t_bf16) {
-      if (kind == kFinalResidual) return tile_part_k<true, kFinalResidual>(P, f, j);
-      if (kind == kFinalOnehot) return tile_part_k<true, kFinalOnehot>(P, f, j);
-      return tile_part_k<true, kFinalBonus>(P, f, j);
-    }
-    if (kind == kFinalResidual) return tile_part_k<false, kFinalResidual>(P, f, j);
-    if (kind == kFinalOnehot) return tile_part_k<false, kFinalOnehot>(P, f, j);
-    return tile_part_k<false, kFinalBonus>(P, f, j);
-  }
-  return tile_part_generic(P, f, kind, j);
-}
-
-// The weights of tile jj into LDS in element order (index e + e/32, so that
-// each thread's run of 32 consecutive weights is bank-conflict free), loaded
-// with the same coalesced, masked vector loads as tile_part_vec.
-__device__ __forceinline__ int lds_pad(int e) { return e + (e >> 5); }
-constexpr int kTileLds = kTileElems + kTileElems / 32;
-
-template <bool BF16, int KIND, bool TAIL>
-__device__ __forceinline__ void tile_weights_lds_vec(const Params& P, const SeqFinal& f, int j, float* lw) {
-  constexpr int VEC = BF16 ? 8 : 4;
-  constexpr int NV = kTileVec / VEC;
-  constexpr int ES = BF16 ? 2 : 4;
-  const int t = threadIdx.x;
-  const int base = j * kTileElems;
-  const int V = P.V;
-  const char* tp = (const char*)P.tgt + (int64_t)f.trow * P.ld_t * ES;
-  const char* dp = (KIND == kFinalResidual) ? (const char*)P.dft + (int64_t)f.drow * P.ld_d * ES : nullptr;
-  u32x4 vt[NV], vd[NV];
-#pragma unroll
-  for (int u = 0; u < NV; ++u) {
-    const int e = base + (u * kThreads + t) * VEC;
-    const int a = (!TAIL || e + VEC <= V) ? e : 0;
-    vt[u] = __builtin_nontemporal_load((const u32x4*)(tp + (int64_t)a * ES));
-    if (KIND == kFinalResidual) vd[u] = __builtin_nontemporal_load((const u32x4*)(dp + (int64_t)a * ES));
-  }
-  if (TAIL) {
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int e = base + (u * kThreads + t) * VEC;
-      if (e + VEC > V) {
-        uint32_t wt[4], wd[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (BF16) {
-            const int e0 = e + 2 * q, e1 = e0 + 1;
-            wt[q] = ((e0 < V) ? (uint32_t)((const uint16_t*)tp)[e0] : 0xFF80u) |
-                    (((e1 < V) ? (uint32_t)((const uint16_t*)tp)[e1] : 0xFF80u) << 16);
-            if (KIND == kFinalResidual)
-              wd[q] = ((e0 < V) ? (uint32_t)((const uint16_t*)dp)[e0] : 0xFF80u) |
-                      (((e1 < V) ? (uint32_t)((const uint16_t*)dp)[e1] : 0xFF80u) << 16);
-          } else {
-            const int e0 = e + q;
-            wt[q] = (e0 < V) ? ((const uint32_t*)tp)[e0] : 0xFF800000u;
-            if (KIND == kFinalResidual) wd[q] = (e0 < V) ? ((const uint32_t*)dp)[e0] : 0xFF800000u;
-          }
-        }
-        vt[u] = u32x4{wt[0], wt[1], wt[2], wt[3]};
-        if (KIND == kFinalResidual) vd[u] = u32x4{wd[0], wd[1], wd[2], wd[3]};
-      }
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < NV; ++u) {
-    const int el = (u * kThreads + t) * VEC;    // element index within the tile
-#pragma unroll
-    for (int q = 0; q < VEC; ++q) {
-      float x, y = 0.f;
-      if (BF16) {
-        x = (q & 1) ? bf_hi(vt[u][q >> 1]) : bf_lo(vt[u][q >> 1]);
-        if (KIND == kFinalResidual) y = (q & 1) ? bf_hi(vd[u][q >> 1]) : bf_lo(vd[u][q >> 1]);
-      } else {
-        x = __uint_as_float(vt[u][q]);
-        if (KIND == kFinalResidual) y = __uint_as_float(vd[u][q]);
-      }
-      lw[lds_pad(el + q)] = final_weight(KIND, x, y, base + el + q, f);
-    }
-  }
-}
-
-// Any row alignment: element e = base + u*256 + t, loads clamped, weights past V zeroed.
-__device__ __forceinline__ void tile_weights_lds_generic(const Params& P, const SeqFinal& f, int kind, int j,
-                                                         float* lw) {
-  const int base = j * kTileElems;
-  const int64_t toff = (int64_t)f.trow * P.ld_t, doff = (int64_t)f.drow * P.ld_d;
-  for (int u0 = 0; u0 < kTileVec; u0 += 8) {
-    float x[8], y[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int e = min(base + (u0 + q) * kThreads + (int)threadIdx.x, P.V - 1);
-      x[q] = load_logit(P.tgt, toff + e, P.t_bf16);
-      y[q] = (kind == kFinalResidual) ? load_logit(P.dft, doff + e, P.d_bf16) : 0.f;
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int el = (u0 + q) * kThreads + (int)threadIdx.x;
-      lw[lds_pad(el)] = (base + el < P.V) ? final_weight(kind, x[q], y[q], base + el, f) : 0.f;
-    }
-  }
-}
-
-template <bool BF16, int KIND>
-__device__ __forceinline__ void tile_weights_lds_k(const Params& P, const SeqFinal& f, int j, float* lw) {
-  if ((j + 1) * kTileElems <= P.V) tile_weights_lds_vec<BF16, KIND, false>(P, f, j, lw);
-  else tile_weights_lds_vec<BF16, KIND, true>(P, f, j, lw);
-}
-
-__device__ __forceinline__ void tile_weights_lds(const Params& P, const SeqFinal& f, int kind, int j, float* lw) {
-  const int vecmin = P.t_bf16 ? 8 : 4;
-  const bool vec = P.t_vec && P.V >= vecmin && (kind != kFinalResidual || (P.d_vec && P.d_bf16 == P.t_bf16));
-  if (vec) {
-    if (P.t_bf16) {
-      if (kind == kFinalResidual) tile_weights_lds_k<true, kFinalResidual>(P, f, j, lw);
-      else if (kind == kFinalOnehot) tile_weights_lds_k<true, kFinalOnehot>(P, f, j, lw);
-      else tile_weights_lds_k<true, kFinalBonus>(P, f, j, lw);
+      if (kind == kFinalResidual) tiles_vec<true, kFinalResidual>(P, f, j0, step, sh);
+      else if (kind == kFinalOnehot) tiles_vec<true, kFinalOnehot>(P, f, j0, step, sh);
+      else tiles_vec<true, kFinalBonus>(P, f, j0, step, sh);
     } else {
-      if (kind == kFinalResidual) tile_weights_lds_k<false, kFinalResidual>(P, f, j, lw);
-      else if (kind == kFinalOnehot) tile_weights_lds_k<false, kFinalOnehot>(P, f, j, lw);
-      else tile_weights_lds_k<false, kFinalBonus>(P, f, j, lw);
+      if (kind == kFinalResidual) tiles_vec<false, kFinalResidual>(P, f, j0, step, sh);
+      else if (kind == kFinalOnehot) tiles_vec<false, kFinalOnehot>(P, f, j0, step, sh);
+      else tiles_vec<false, kFinalBonus>(P, f, j0, step, sh);
     }
   } else {
-    tile_weights_lds_generic(P, f, kind, j, lw);
+    for (int j = j0; j < P.ntiles; j += step) tile_generic(P, f, kind, j, sh);
   }
 }
 
-// clear the outputs of a sequence that is not verified
-__device__ __forceinline__ void clear_sequence(const Params& P, int s, int off_t, int off_d, int K, int st) {
+// Tile sums from the per-wave shares (fixed order); thread j adds up tile j.
+__device__ __forceinline__ float tile_total(const FinShared& sh, int j) {
+  float z = 0.f;
+#pragma unroll
+  for (int w = 0; w < kFinWaves; ++w) z += sh.tw[j][w];
+  return z;
+}
+
+// Weights of the 8 consecutive elements jj*8192 + t*8 .. +7 (thread t).
+template <bool BF, int KIND>
+__device__ __forceinline__ void slice_vec(const Params& P, const SeqFinal& f, int jj, float (&w)[kPerThread]) {
+  constexpr int VEC = BF ? 8 : 4;
+  constexpr int NV = kPerThread / VEC;
+  constexpr int ES = BF ? 2 : 4;
+  const char* tp = (const char*)P.tgt + (int64_t)f.trow * P.ld_t * ES;
+  const char* dp = (KIND == kFinalResidual) ? (const char*)P.dft + (int64_t)f.drow * P.ld_d * ES : tp;
+  const int e0 = jj * kTileElems + (int)threadIdx.x * kPerThread;
+#pragma unroll
+  for (int n = 0; n < NV; ++n) {
+    const int e = e0 + n * VEC;
+    float wv[VEC];
+    if (e < P.V) {
+      const u32x4 vt = load_vec_masked<BF>(tp, e, P.V);
+      const u32x4 vd = (KIND == kFinalResidual) ? load_vec_masked<BF>(dp, e, P.V) : vt;
+      vec_weights<BF, KIND>(vt, vd, e, f, wv);
+    } else {
+#pragma unroll
+      for (int q = 0; q < VEC; ++q) wv[q] = 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < VEC; ++q) w[n * VEC + q] = wv[q];
+  }
+}
+
+__device__ __forceinline__ void slice_generic(const Params& P, const SeqFinal& f, int kind, int jj,
+                                              float (&w)[kPerThread]) {
+  const int64_t toff = (int64_t)f.trow * P.ld_t, doff = (int64_t)f.drow * P.ld_d;
+  const int e0 = jj * kTileElems + (int)threadIdx.x * kPerThread;
+  float x[kPerThread], y[kPerThread];
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int e = min(e0 + q, P.V - 1);
+    x[q] = load_logit(P.tgt, toff + e, P.t_bf16);
+    y[q] = (kind == kFinalResidual) ? load_logit(P.dft, doff + e, P.d_bf16) : 0.f;
+  }
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) w[q] = (e0 + q < P.V) ? final_weight(kind, x[q], y[q], e0 + q, f) : 0.f;
+}
+
+__device__ __forceinline__ void slice_weights(const Params& P, const SeqFinal& f, int kind, int jj,
+                                              float (&w)[kPerThread]) {
+  if (final_vec_ok(P, kind)) {
+    if (P.t_bf16) {
+      if (kind == kFinalResidual) slice_vec<true, kFinalResidual>(P, f, jj, w);
+      else if (kind == kFinalOnehot) slice_vec<true, kFinalOnehot>(P, f, jj, w);
+      else slice_vec<true, kFinalBonus>(P, f, jj, w);
+    } else {
+      if (kind == kFinalResidual) slice_vec<false, kFinalResidual>(P, f, jj, w);
+      else if (kind == kFinalOnehot) slice_vec<false, kFinalOnehot>(P, f, jj, w);
+      else slice_vec<false, kFinalBonus>(P, f, jj, w);
+    }
+  } else {
+    slice_generic(P, f, kind, jj, w);
+  }
+}
+
+// Wave 0: prefix sums over the tile sums in sh.tile (lane-major within each
+// group of 64), total Z, the first tile whose inclusive prefix exceeds
+// tt = u * Z (else the last tile with mass), and the remainder tp of tt in it.
+__device__ __forceinline__ void pick_tile(const Params& P, const SeqFinal& f, FinShared& sh) {
+  constexpr int kTPL = kMaxTiles / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  float tv[kTPL], pre[kTPL];
+  float carry = 0.f;
+#pragma unroll
+  for (int k = 0; k < kTPL; ++k) {
+    const int j = lane + k * kWave;
+    tv[k] = (j < P.ntiles) ? sh.tile[j] : 0.f;
+    const float v = wave_incl_scan_f(tv[k]);
+    pre[k] = carry + v;
+    carry += lane63_f(v);
+  }
+  const float Z = carry;
+  const float tt = f.u * Z;
+  int jj = -1, jlast = -1;
+#pragma unroll
+  for (int k = kTPL - 1; k >= 0; --k) {
+    const unsigned long long hit = __ballot(pre[k] > tt && lane + k * kWave < P.ntiles);
+    if (hit) jj = k * kWave + (int)__builtin_ctzll(hit);
+    const unsigned long long pos = __ballot(tv[k] > 0.f);
+    if (pos && jlast < 0) jlast = k * kWave + 63 - (int)__builtin_clzll(pos);
+  }
+  if (jj < 0) jj = jlast;
+  jj = min(max(jj, 0), P.ntiles - 1);
+  float before = 0.f;
+#pragma unroll
+  for (int k = 0; k < kTPL; ++k) {
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pre[k] - tv[k]), jj & (kWave - 1)));
+    if (jj / kWave == k) before = b;
+  }
+  if (lane == 0) {
+    sh.fallback = !(Z > 0.f);
+    sh.jj = jj;
+    sh.tp = tt - before;
+  }
+}
+
+// The token of the final draw: thread t re-reads its 8 consecutive weights of
+// tile jj, a block-wide exclusive prefix over the threads' sums locates the
+// first element (with weight) whose running prefix passes tp; ballots pick
+// the lowest such thread, and, failing one (rounding), the last element with
+// weight.  Writes the token and the sequence's status.
+__device__ __forceinline__ void select_token(const Params& P, const SeqFinal& f, int kind, bool fallback,
+                                             FinShared& sh) {
+  const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
+  const int jj = sh.jj;
+  const float tp = sh.tp;
+  float w[kPerThread];
+  slice_weights(P, f, kind, jj, w);
+  float loc = 0.f;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) loc += w[q];
+  const float inc = wave_incl_scan_f(loc);
+  if (lane == kWave - 1) sh.sw[wv] = inc;
+  __syncthreads();
+  float run = inc - loc;
+  for (int q = 0; q < wv; ++q) run += sh.sw[q];
+  int found = -1, lastp = -1;
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    run += w[q];
+    if (found < 0 && w[q] > 0.f && run > tp) found = q;
+    if (w[q] > 0.f) lastp = q;
+  }
+  const unsigned long long fm = __ballot(found >= 0);
+  const unsigned long long lm = __ballot(lastp >= 0);
+  const int fl = fm ? (int)__builtin_ctzll(fm) : 0;
+  const int ll = lm ? 63 - (int)__builtin_clzll(lm) : 0;
+  const int ff = __builtin_amdgcn_readlane(found, fl);
+  const int lq = __builtin_amdgcn_readlane(lastp, ll);
+  const int base = jj * kTileElems + wv * kWave * kPerThread;
+  if (lane == 0) {
+    sh.first[wv] = fm ? base + fl * kPerThread + ff : 0x7FFFFFFF;
+    sh.last[wv] = lm ? base + ll * kPerThread + lq : -1;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int y = 0x7FFFFFFF, z = -1;
+#pragma unroll
+    for (int q = 0; q < kFinWaves; ++q) {
+      y = min(y, sh.first[q]);
+      z = max(z, sh.last[q]);
+    }
+    P.emitted[f.emit_pos] = (y != 0x7FFFFFFF) ? y : z;
+    if (P.status) P.status[f.s] = fallback ? kStZeroResidual : 0;
+  }
+}
+
+// Given the tile sums in sh.tile: the tile, then the token.  A residual with
+// no mass (rounding only) falls back to p at the stop position: the block
+// recomputes every tile sum of p and picks again.
+__device__ __forceinline__ void finish_draw(const Params& P, const SeqFinal& f, FinShared& sh) {
   const int t = threadIdx.x;
-  for (int j = t; j <= K; j += blockDim.x) P.emitted[off_t + j] = -1;
-  for (int j = t; j < K; j += blockDim.x) {
+  if (t < kWave) pick_tile(P, f, sh);
+  __syncthreads();
+  const bool fallback = sh.fallback;
+  int kind = f.kind;
+  if (fallback) {
+    kind = kFinalBonus;
+    tile_sums_pass(P, f, kind, 0, 1, sh);
+    __syncthreads();
+    if (t < P.ntiles) sh.tile[t] = tile_total(sh, t);
+    __syncthreads();
+    if (t < kWave) pick_tile(P, f, sh);
+    __syncthreads();
+  }
+  select_token(P, f, kind, fallback, sh);
+}
+
+// clear the outputs of a sequence that is not verified (one wave)
+__device__ __forceinline__ void clear_sequence(const Params& P, int s, int off_t, int off_d, int K, int st) {
+  const int t = threadIdx.x & (kWave - 1);
+  for (int j = t; j <= K; j += kWave) P.emitted[off_t + j] = -1;
+  for (int j = t; j < K; j += kWave) {
     if (P.p_at) P.p_at[off_d + j] = __uint_as_float(kNaNBits);
     if (P.q_at) P.q_at[off_d + j] = __uint_as_float(kNaNBits);
   }
@@ -720,18 +879,6 @@ __device__ __forceinline__ void unpack_chunk(const u32x4 (&v)[kNV], float (&f)[k
         f[u * 4 + q] = __uint_as_float(v[u][q]);
       }
     }
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
-}
-
-__device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, kWave));
-  return v;
 }
 
 // What wave 0 of a row-statistics block hands to the other waves.
@@ -886,7 +1033,7 @@ __global__ void __launch_bounds__(kThreads) k_row_stats(Params P) {
 }
 
 // ---------------------------------------------------------------------------
-// scan: one 64-lane wave per sequence, so no cross-wave barriers.  Lane r
+// acceptance scan: one 64-lane wave per sequence, so no barriers.  Lane r
 // merges the chunk partials of row r on its own; lane i judges position i.
 // ---------------------------------------------------------------------------
 constexpr int kScanThreads = kWave;
@@ -899,9 +1046,10 @@ struct ScanShared {
   int tok[kMaxK];
 };
 
-// Inconsistent num_draft: every output slot is cleared; block s clears its share.
+// Inconsistent num_draft: every output slot is cleared; the scanning wave of
+// sequence s clears its share.
 __device__ __forceinline__ void clear_bad_layout(const Params& P, int s) {
-  const int t = threadIdx.x, nt = blockDim.x;
+  const int t = threadIdx.x & (kWave - 1), nt = kWave;
   const int64_t stride = (int64_t)P.B * nt;
   for (int64_t e = (int64_t)s * nt + t; e < (int64_t)P.total_draft + P.B; e += stride) P.emitted[e] = -1;
   for (int64_t e = (int64_t)s * nt + t; e < P.total_draft; e += stride) {
@@ -948,12 +1096,12 @@ __device__ __forceinline__ void merge_row(const Partial* pp, int nch, float c, f
   }
 }
 
-// The acceptance scan of sequence s: stores every output of the sequence but
-// the final token and returns what the final draw needs (kind kFinalDone when
-// nothing is left).  Two dependent rounds of loads: the layout sums with the
-// sequence's own inputs, then the proposals, their logits and the rows'
-// partials.
-__device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanShared& sh) {
+// The acceptance scan of sequence s by one wave: with `write`, stores every
+// output of the sequence but the final token; returns what the final draw
+// needs (kind kFinalDone when nothing is left).  Two dependent rounds of
+// loads: the layout sums with the sequence's own inputs, then the proposals,
+// their logits and the rows' partials.
+__device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanShared& sh, bool write) {
   const int lane = threadIdx.x;
   SeqFinal f{};
   f.kind = kFinalDone;
@@ -964,19 +1112,25 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
   const int md = P.mode[s];
   const float T = P.temperature[s];
   const uint32_t seq_id = P.seq_ids[s];
-  int64_t tot = 0, bef = 0, neg = 0;
+  // 32-bit sums: a count outside 0..kLayoutKMax cannot belong to a layout
+  // of total_draft (<= 4096 * 128) rows and is flagged on its own, so the
+  // in-range sums stay below 2^31
+  constexpr int kLayoutKMax = 1 << 19;
+  uint32_t tot = 0, bef = 0;
+  int out_of_range = 0;
 #pragma unroll 4
   for (int j = lane; j < P.B; j += kScanThreads) {
-    const int64_t k = P.num_draft[j];
-    tot += k;
-    bef += (j < s) ? k : 0;
-    neg |= (k < 0);
+    const int k = P.num_draft[j];
+    const bool ok = k >= 0 && k <= kLayoutKMax;
+    out_of_range |= !ok;
+    const uint32_t kk = ok ? (uint32_t)k : 0u;
+    tot += kk;
+    bef += (j < s) ? kk : 0u;
   }
-  tot = wave_sum_i64(tot);
-  bef = wave_sum_i64(bef);
-  neg = wave_sum_i64(neg);
-  if (neg != 0 || tot != (int64_t)P.total_draft) {
-    clear_bad_layout(P, s);
+  tot = wave_sum_u32(tot);
+  bef = wave_sum_u32(bef);
+  if (__any(out_of_range) || tot != (uint32_t)P.total_draft) {
+    if (write) clear_bad_layout(P, s);
     return f;
   }
   const int off_d = (int)bef;
@@ -988,7 +1142,7 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
   if ((md == kSample || md == kOnehot) && !(isfinite(T) && T >= kMinTemperature)) st |= kStBadTemp;
   if (md == kSample && K > 0 && P.dft == nullptr) st |= kStNoDraft;
   if (st) {
-    clear_sequence(P, s, off_t, off_d, K, st);
+    if (write) clear_sequence(P, s, off_t, off_d, K, st);
     return f;
   }
   const float c = (md == kGreedy) ? kLog2e : kLog2e / T;
@@ -1028,14 +1182,16 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
     badtok |= (x < 0 || x >= P.V);
   }
   if (__any(badtok)) {
-    clear_sequence(P, s, off_t, off_d, K, kStBadToken);
+    if (write) clear_sequence(P, s, off_t, off_d, K, kStBadToken);
     return f;
   }
   if (__any(bad)) {
-    clear_sequence(P, s, off_t, off_d, K, kStNonfinite);
+    if (write) clear_sequence(P, s, off_t, off_d, K, kStNonfinite);
     return f;
   }
-  __syncthreads();   // the rows' statistics and tokens, written by other lanes
+  // the rows' statistics and tokens were written to LDS by other lanes of
+  // this wave: keep the compiler from moving the reads above the writes
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
   // ---- p and q at the proposals, uniforms, accept decisions ----
   int A = K;
@@ -1055,8 +1211,8 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
         const float r = (md == kOnehot) ? p : (q > 0.f ? fminf(1.f, p / q) : 0.f);
         acc = u < r;
       }
-      if (P.p_at) P.p_at[off_d + i] = p;
-      if (P.q_at) P.q_at[off_d + i] = q;
+      if (write && P.p_at) P.p_at[off_d + i] = p;
+      if (write && P.q_at) P.q_at[off_d + i] = q;
       reject = !acc;
     }
     const unsigned long long rj = __ballot(reject);
@@ -1064,12 +1220,12 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
   }
 
   // ---- emitted tokens: accepted prefix, -1 after A; greedy fills A too ----
-  for (int j = lane; j <= K; j += kScanThreads) {
+  for (int j = lane; write && j <= K; j += kScanThreads) {
     if (j < A) P.emitted[off_t + j] = sh.tok[j];
     else if (j > A) P.emitted[off_t + j] = -1;
     else if (md == kGreedy) P.emitted[off_t + j] = sh.I[A];
   }
-  if (lane == 0) {
+  if (write && lane == 0) {
     P.accepted_len[s] = A;
     if (md == kGreedy && P.status) P.status[s] = 0;
   }
@@ -1096,177 +1252,50 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
   return f;
 }
 
-// One wave per sequence: the acceptance scan; records the final draw.
-__global__ void __launch_bounds__(kScanThreads) k_scan(Params P) {
-  __shared__ ScanShared sh;
-  const int s = blockIdx.x;
-  const SeqFinal f = scan_sequence(P, s, sh);
-  if (threadIdx.x == 0) P.fin[s] = f;
-}
-
-// grid (ntiles, B): the final weights of one tile of the row(s) at the stop
-// position of sequence s.
-__global__ void __launch_bounds__(kThreads) k_tile_sums(Params P) {
-  __shared__ float s_w[kWaves];
-  const int j = blockIdx.x, s = blockIdx.y;
-  const SeqFinal f = P.fin[s];
-  if (f.kind == kFinalDone) return;
-  const float tot = block_sum(tile_part(P, f, f.kind, j), s_w);
-  if (threadIdx.x == 0) P.tilesum[(int64_t)s * P.ntiles + j] = tot;
-}
-
-struct SelShared {
-  float lw[kTileLds];          // the chosen tile's weights, element order (padded)
-  float w[kWaves];
-  float tiles[kMaxTiles];
-  float tp;
-  int jj, fallback, first, last;
-};
-
-// The residual had no mass (rounding only): the token is drawn from p at
-// position A instead.  Recomputes every tile's sum of p and picks the tile.
-__device__ __forceinline__ void select_fallback(const Params& P, const SeqFinal& f, SelShared& sh) {
+// Final kernel, grid (nsplit, B), 1024 threads.  Wave 0 runs the acceptance
+// scan of sequence s (split 0 writes its outputs and the record); then the
+// block sums the final weights of its tiles (j = split mod nsplit) of the
+// row(s) at the stop position.  With one block per sequence the same block
+// picks the token; otherwise the tile sums go to HBM for k_select.
+__global__ void __launch_bounds__(kFinThreads) k_final(Params P) {
+  __shared__ ScanShared ssh;
+  __shared__ FinShared sh;
+  __shared__ SeqFinal sf;
+  const int split = blockIdx.x, s = blockIdx.y;
   const int t = threadIdx.x;
-  for (int q = 0; q < P.ntiles; ++q) {
-    const float v = block_sum(tile_part(P, f, kFinalBonus, q), sh.w);
-    if (t == 0) sh.tiles[q] = v;
+  if (t < kWave) {
+    const SeqFinal f = scan_sequence(P, s, ssh, split == 0);
+    if (t == 0) {
+      sf = f;
+      if (split == 0) P.fin[s] = f;
+    }
   }
   __syncthreads();
-  if (t == 0) {
-    float Z = 0.f;
-    for (int q = 0; q < P.ntiles; ++q) Z += sh.tiles[q];
-    const float tt = f.u * Z;
-    float cum = 0.f;
-    int jj = -1;
-    for (int q = 0; q < P.ntiles; ++q) {
-      if (cum + sh.tiles[q] > tt) {
-        jj = q;
-        break;
-      }
-      cum += sh.tiles[q];
-    }
-    if (jj < 0) {
-      for (int q = P.ntiles - 1; q >= 0; --q) {
-        if (sh.tiles[q] > 0.f) {
-          jj = q;
-          break;
-        }
-      }
-      cum = 0.f;
-      for (int q = 0; q < jj; ++q) cum += sh.tiles[q];
-    }
-    sh.jj = jj;
-    sh.tp = tt - cum;
-  }
+  const SeqFinal f = sf;
+  if (f.kind == kFinalDone) return;
+  tile_sums_pass(P, f, f.kind, split, P.nsplit, sh);
   __syncthreads();
+  if (t < P.ntiles && t % P.nsplit == split) {
+    const float z = tile_total(sh, t);
+    if (P.nsplit == 1) sh.tile[t] = z;
+    else P.tilesum[(int64_t)s * P.ntiles + t] = z;
+  }
+  if (P.nsplit > 1) return;
+  __syncthreads();
+  finish_draw(P, f, sh);
 }
 
-// One block per sequence: the tile holding t = u * Z, then the token in it.
-// Two dependent rounds of loads: the record and the tile sums together, then
-// the chosen tile.
-__global__ void __launch_bounds__(kThreads) k_select(Params P) {
-  __shared__ SelShared sh;
-  constexpr int kTPL = kMaxTiles / kWave;      // tile sums per lane of wave 0
+// One block per sequence when the final kernel was split: the tile sums from
+// HBM, then the tile and the token.
+__global__ void __launch_bounds__(kFinThreads) k_select(Params P) {
+  __shared__ FinShared sh;
   const int s = blockIdx.x;
   const int t = threadIdx.x;
-  const int lane = t & (kWave - 1), wv = t / kWave;
   const SeqFinal f = P.fin[s];
-  float tv[kTPL];
-  if (wv == 0) {
-#pragma unroll
-    for (int k = 0; k < kTPL; ++k) {
-      const int j = lane + k * kWave;
-      tv[k] = (j < P.ntiles) ? P.tilesum[(int64_t)s * P.ntiles + j] : 0.f;
-    }
-  }
   if (f.kind == kFinalDone) return;
-  if (wv == 0) {
-    // prefix sums over tiles (lane-major within each group of 64), total Z
-    float pre[kTPL];
-    float carry = 0.f;
-#pragma unroll
-    for (int k = 0; k < kTPL; ++k) {
-      float v = tv[k];
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const float o = __shfl_up(v, off, kWave);
-        if (lane >= off) v += o;
-      }
-      pre[k] = carry + v;
-      carry += __shfl(v, kWave - 1, kWave);
-    }
-    const float Z = carry;
-    const float tt = f.u * Z;
-    // first tile whose inclusive prefix exceeds tt; else the last tile with mass
-    int jj = -1, jlast = -1;
-#pragma unroll
-    for (int k = kTPL - 1; k >= 0; --k) {
-      const unsigned long long hit = __ballot(pre[k] > tt && lane + k * kWave < P.ntiles);
-      if (hit) jj = k * kWave + (int)__builtin_ctzll(hit);
-      const unsigned long long pos = __ballot(tv[k] > 0.f);
-      if (pos && jlast < 0) jlast = k * kWave + 63 - (int)__builtin_clzll(pos);
-    }
-    if (jj < 0) jj = jlast;
-    // exclusive prefix of tile jj
-    float before = 0.f;
-#pragma unroll
-    for (int k = 0; k < kTPL; ++k) {
-      const float ex = pre[k] - tv[k];
-      const float b = __shfl(ex, (jj < 0 ? 0 : jj) & (kWave - 1), kWave);
-      if (jj >= 0 && jj / kWave == k) before = b;
-    }
-    if (lane == 0) {
-      sh.fallback = !(Z > 0.f);
-      sh.jj = jj;
-      sh.tp = tt - before;
-      sh.first = 0x7FFFFFFF;
-      sh.last = -1;
-    }
-  }
+  if (t < P.ntiles) sh.tile[t] = P.tilesum[(int64_t)s * P.ntiles + t];
   __syncthreads();
-  const bool fallback = sh.fallback;
-  int kind = f.kind;
-  if (fallback) {
-    kind = kFinalBonus;
-    select_fallback(P, f, sh);
-  }
-  const int jj = sh.jj;
-  const float tp = sh.tp;
-
-  // re-read tile jj with coalesced loads into LDS; then thread t takes the
-  // kTileVec consecutive weights starting at element t * kTileVec
-  tile_weights_lds(P, f, kind, jj, sh.lw);
-  __syncthreads();
-  const int e0 = jj * kTileElems + t * kTileVec;
-  float xv[kTileVec];
-#pragma unroll
-  for (int q = 0; q < kTileVec; ++q) xv[q] = sh.lw[lds_pad(t * kTileVec + q)];
-  float loc = 0.f;
-  int last_pos = -1;
-#pragma unroll
-  for (int q = 0; q < kTileVec; ++q) {
-    if (xv[q] > 0.f) last_pos = e0 + q;
-    loc += xv[q];
-  }
-  float total;
-  const float before = block_excl_scan(loc, sh.w, &total);
-  // the first element (with weight) whose running prefix passes tp
-  // (fully unrolled: constant register indices)
-  int found = -1;
-  float run = before;
-#pragma unroll
-  for (int q = 0; q < kTileVec; ++q) {
-    run += xv[q];
-    if (found < 0 && xv[q] > 0.f && run > tp) found = q;
-  }
-  if (found >= 0) atomicMin(&sh.first, e0 + found);   // LDS: the lowest crossing over threads wins
-  if (last_pos >= 0) atomicMax(&sh.last, last_pos);
-  __syncthreads();
-  if (t == 0) {
-    const int y = (sh.first != 0x7FFFFFFF) ? sh.first : sh.last;
-    P.emitted[f.emit_pos] = y;
-    if (P.status) P.status[s] = fallback ? kStZeroResidual : 0;
-  }
+  finish_draw(P, f, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1287,18 +1316,14 @@ hipError_t launch_row_stats(const Params& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const Params& p, hipStream_t st) {
-  hipLaunchKernelGGL(k_scan, dim3(p.B), dim3(kScanThreads), 0, st, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_tile_sums(const Params& p, hipStream_t st) {
-  hipLaunchKernelGGL(k_tile_sums, dim3(p.ntiles, p.B), dim3(kThreads), 0, st, p);
+hipError_t launch_final(const Params& p, hipStream_t st) {
+  hipLaunchKernelGGL(k_final, dim3(p.nsplit, p.B), dim3(kFinThreads), 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const Params& p, hipStream_t st) {
-  hipLaunchKernelGGL(k_select, dim3(p.B), dim3(kThreads), 0, st, p);
+  if (p.nsplit <= 1) return hipSuccess;
+  hipLaunchKernelGGL(k_select, dim3(p.B), dim3(kFinThreads), 0, st, p);
   return hipGetLastError();
 }
 
