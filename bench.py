@@ -2,18 +2,20 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3]
 
-A step is one call of the library's verify step (prep, row statistics,
-final draw) over one batch of a synthetic workload whose inputs are already
-resident in HBM.  R distinct input sets rotate so that the 256 MB
+A step is one call of the library's verify step (row statistics, then the
+acceptance scan and final draw) over one batch of a synthetic workload whose
+inputs are already resident in HBM.  R distinct input sets rotate so that the 256 MB
 last-level cache cannot serve repeated reads.  Prints one JSON line:
 
   value       verified positions per second, sum_s (K_s + 1) per step
+  value       from the K timed steps, run without per-kernel events
   roofline    the row-statistics kernel (the dominant one): algorithmic
               bytes per launch (every streamed logit row read once) over its
-              mean duration from HIP events recorded around it on the
-              library's stream, against 8 TB/s; ``traffic`` is the HBM bytes
-              per launch measured by rocprofv3 FETCH_SIZE + WRITE_SIZE when a
-              counter summary for the current kernel source is committed
+              mean duration from HIP events recorded around each kernel on
+              the library's stream during K further steps, against 8 TB/s;
+              ``traffic`` is the HBM bytes per launch measured by rocprofv3
+              FETCH_SIZE + WRITE_SIZE when a counter summary for the current
+              kernel source is committed
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same
               workload, single process
 """
@@ -196,35 +198,46 @@ def main():
         if (st & 127).any():
             raise RuntimeError(f"input set {r}: unexpected status bits {np.unique(st)}")
 
-    events = not args.no_kernel_events
-    if events:
-        v.timing_enable(args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kern = {}
-    if events:
-        n, ms = v.timing_read()
-        kern = {k: ms[k] / max(n, 1) for k in ms}
-        v.timing_enable(0)
+    def timed(k0):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(k0 + i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
 
+    # the timed region: K steps, no per-kernel events (they add gaps)
+    elapsed = timed(args.warmup)
     sets_used = [(args.warmup + i) % R for i in range(args.steps)]
     pos = np.mean([batches[r].positions for r in sets_used])
     stats_bytes = np.mean([row_bytes(batches[r])["row_stats"] for r in sets_used])
     fin_bytes = np.mean([fin_b[r] for r in sets_used])
     ms_step = elapsed * 1e3 / args.steps
     value = pos * args.steps / elapsed
+    # four more repetitions of the same K steps, for the median
+    reps = [ms_step] + [timed(args.warmup + args.steps * (r + 1)) * 1e3 / args.steps for r in range(4)]
+
+    # per-kernel HIP events on the library's stream, K more steps
+    events = not args.no_kernel_events
+    kern = {}
+    ev_ms_step = None
+    if events:
+        k0 = args.warmup + 5 * args.steps
+        v.timing_enable(args.steps)
+        ev_ms_step = timed(k0) * 1e3 / args.steps
+        n, ms = v.timing_read()
+        kern = {k: ms[k] / max(n, 1) for k in ms}
+        v.timing_enable(0)
+        ev_sets = [(k0 + i) % R for i in range(args.steps)]
+        ev_stats_bytes = np.mean([row_bytes(batches[r])["row_stats"] for r in ev_sets])
 
     roofline = None
     if events and kern.get("row_stats", 0) > 0:
-        ach = stats_bytes / (kern["row_stats"] * 1e-3) / 1e9
+        ach = ev_stats_bytes / (kern["row_stats"] * 1e-3) / 1e9
         traffic = load_traffic(args.workload)
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                    "kernel": "k_row_stats", "algorithmic_bytes_per_launch": int(stats_bytes),
+                    "kernel": "k_row_stats", "algorithmic_bytes_per_launch": int(ev_stats_bytes),
                     "mean_launch_ms": round(kern["row_stats"], 5)}
 
     if args.copy_calibration:
@@ -247,9 +260,12 @@ def main():
                    "positions_per_step": round(float(pos), 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "ms_per_step_median_of_5": round(float(np.median(reps)), 5),
         "step_bytes": {"row_stats": int(stats_bytes), "final_draw": int(fin_bytes),
-                       "step_GBps": round((stats_bytes + fin_bytes) / (ms_step * 1e-3) / 1e9, 1)},
+                       "step_GBps": round((stats_bytes + fin_bytes) / (ms_step * 1e-3) / 1e9, 1),
+                       "step_frac_of_peak": round((stats_bytes + fin_bytes) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
         "kernel_ms": {k: round(x, 5) for k, x in kern.items()},
+        "kernel_events_ms_per_step": None if ev_ms_step is None else round(ev_ms_step, 5),
         "input_generation_s": round(gen_s, 1),
     }
     print(json.dumps(line), flush=True)

@@ -427,7 +427,7 @@ __device__ __forceinline__ void stats_scalar(const void* row, int bf16, int c0, 
 constexpr int kFinThreads = 1024;
 constexpr int kFinWaves = kFinThreads / kWave;
 constexpr int kPerThread = kTileElems / kFinThreads;   // 8
-constexpr int kTileUnroll = 4;                         // tiles whose loads are in flight together
+constexpr int kTileUnroll = 2;                         // tiles whose loads are in flight together
 
 __device__ __forceinline__ float final_weight(int kind, float x, float y, int k, const SeqFinal& f) {
   const float p = fexp2(fmaf(x, f.c, -f.mct)) * f.inv_st;
