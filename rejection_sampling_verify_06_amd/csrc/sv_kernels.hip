@@ -427,7 +427,12 @@ __device__ __forceinline__ void stats_scalar(const void* row, int bf16, int c0, 
 constexpr int kFinThreads = 1024;
 constexpr int kFinWaves = kFinThreads / kWave;
 constexpr int kPerThread = kTileElems / kFinThreads;   // 8
-constexpr int kTileUnroll = 2;                         // tiles whose loads are in flight together
+// Tiles whose loads a block keeps in flight together: with a block per
+// sequence on every CU, two tiles of the two residual rows (64 KB per block
+// in bf16) stream fastest; a draw that reads one row keeps more tiles in
+// flight, since fewer blocks have work then.
+template <bool BF, int KIND>
+constexpr int tile_unroll() { return KIND == kFinalResidual ? 2 : (BF ? 8 : 4); }
 
 __device__ __forceinline__ float final_weight(int kind, float x, float y, int k, const SeqFinal& f) {
   const float p = fexp2(fmaf(x, f.c, -f.mct)) * f.inv_st;
@@ -501,6 +506,7 @@ __device__ __forceinline__ u32x4 load_vec_masked(const char* rowp, int e, int V)
 template <bool BF, int KIND>
 __device__ __forceinline__ void tiles_full_vec(const Params& P, const SeqFinal& f, int j0, int step, int nfull,
                                                FinShared& sh) {
+  constexpr int kTileUnroll = tile_unroll<BF, KIND>();
   constexpr int VEC = BF ? 8 : 4;
   constexpr int NV = kPerThread / VEC;
   constexpr int ES = BF ? 2 : 4;
@@ -626,15 +632,15 @@ __device__ __forceinline__ float tile_total(const FinShared& sh, int j) {
   return z;
 }
 
-// Weights of the 8 consecutive elements jj*8192 + t*8 .. +7 (thread t).
-template <bool BF, int KIND>
-__device__ __forceinline__ void slice_vec(const Params& P, const SeqFinal& f, int jj, float (&w)[kPerThread]) {
+// Weights of the PT consecutive elements base + t*PT .. +PT-1 (thread t).
+template <bool BF, int KIND, int PT>
+__device__ __forceinline__ void slice_vec(const Params& P, const SeqFinal& f, int base, float (&w)[PT]) {
   constexpr int VEC = BF ? 8 : 4;
-  constexpr int NV = kPerThread / VEC;
+  constexpr int NV = PT / VEC;
   constexpr int ES = BF ? 2 : 4;
   const char* tp = (const char*)P.tgt + (int64_t)f.trow * P.ld_t * ES;
   const char* dp = (KIND == kFinalResidual) ? (const char*)P.dft + (int64_t)f.drow * P.ld_d * ES : tp;
-  const int e0 = jj * kTileElems + (int)threadIdx.x * kPerThread;
+  const int e0 = base + (int)threadIdx.x * PT;
 #pragma unroll
   for (int n = 0; n < NV; ++n) {
     const int e = e0 + n * VEC;
@@ -652,42 +658,44 @@ __device__ __forceinline__ void slice_vec(const Params& P, const SeqFinal& f, in
   }
 }
 
-__device__ __forceinline__ void slice_generic(const Params& P, const SeqFinal& f, int kind, int jj,
-                                              float (&w)[kPerThread]) {
+template <int PT>
+__device__ __forceinline__ void slice_generic(const Params& P, const SeqFinal& f, int kind, int base,
+                                              float (&w)[PT]) {
   const int64_t toff = (int64_t)f.trow * P.ld_t, doff = (int64_t)f.drow * P.ld_d;
-  const int e0 = jj * kTileElems + (int)threadIdx.x * kPerThread;
-  float x[kPerThread], y[kPerThread];
+  const int e0 = base + (int)threadIdx.x * PT;
+  float x[PT], y[PT];
 #pragma unroll
-  for (int q = 0; q < kPerThread; ++q) {
+  for (int q = 0; q < PT; ++q) {
     const int e = min(e0 + q, P.V - 1);
     x[q] = load_logit(P.tgt, toff + e, P.t_bf16);
     y[q] = (kind == kFinalResidual) ? load_logit(P.dft, doff + e, P.d_bf16) : 0.f;
   }
 #pragma unroll
-  for (int q = 0; q < kPerThread; ++q) w[q] = (e0 + q < P.V) ? final_weight(kind, x[q], y[q], e0 + q, f) : 0.f;
+  for (int q = 0; q < PT; ++q) w[q] = (e0 + q < P.V) ? final_weight(kind, x[q], y[q], e0 + q, f) : 0.f;
 }
 
-__device__ __forceinline__ void slice_weights(const Params& P, const SeqFinal& f, int kind, int jj,
-                                              float (&w)[kPerThread]) {
+template <int PT>
+__device__ __forceinline__ void slice_weights(const Params& P, const SeqFinal& f, int kind, int base,
+                                              float (&w)[PT]) {
   if (final_vec_ok(P, kind)) {
     if (P.t_bf16) {
-      if (kind == kFinalResidual) slice_vec<true, kFinalResidual>(P, f, jj, w);
-      else if (kind == kFinalOnehot) slice_vec<true, kFinalOnehot>(P, f, jj, w);
-      else slice_vec<true, kFinalBonus>(P, f, jj, w);
+      if (kind == kFinalResidual) slice_vec<true, kFinalResidual, PT>(P, f, base, w);
+      else if (kind == kFinalOnehot) slice_vec<true, kFinalOnehot, PT>(P, f, base, w);
+      else slice_vec<true, kFinalBonus, PT>(P, f, base, w);
     } else {
-      if (kind == kFinalResidual) slice_vec<false, kFinalResidual>(P, f, jj, w);
-      else if (kind == kFinalOnehot) slice_vec<false, kFinalOnehot>(P, f, jj, w);
-      else slice_vec<false, kFinalBonus>(P, f, jj, w);
+      if (kind == kFinalResidual) slice_vec<false, kFinalResidual, PT>(P, f, base, w);
+      else if (kind == kFinalOnehot) slice_vec<false, kFinalOnehot, PT>(P, f, base, w);
+      else slice_vec<false, kFinalBonus, PT>(P, f, base, w);
     }
   } else {
-    slice_generic(P, f, kind, jj, w);
+    slice_generic<PT>(P, f, kind, base, w);
   }
 }
 
-// Wave 0: prefix sums over the tile sums in sh.tile (lane-major within each
-// group of 64), total Z, the first tile whose inclusive prefix exceeds
-// tt = u * Z (else the last tile with mass), and the remainder tp of tt in it.
-__device__ __forceinline__ void pick_tile(const Params& P, const SeqFinal& f, FinShared& sh) {
+// Wave 0: prefix sums over the n unit sums in sh.tile (lane-major within each
+// group of 64), total Z, the first unit whose inclusive prefix exceeds
+// tt = u * Z (else the last unit with mass), and the remainder tp of tt in it.
+__device__ __forceinline__ void pick_unit(const SeqFinal& f, int n, FinShared& sh) {
   constexpr int kTPL = kMaxTiles / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   float tv[kTPL], pre[kTPL];
@@ -695,7 +703,7 @@ __device__ __forceinline__ void pick_tile(const Params& P, const SeqFinal& f, Fi
 #pragma unroll
   for (int k = 0; k < kTPL; ++k) {
     const int j = lane + k * kWave;
-    tv[k] = (j < P.ntiles) ? sh.tile[j] : 0.f;
+    tv[k] = (j < n) ? sh.tile[j] : 0.f;
     const float v = wave_incl_scan_f(tv[k]);
     pre[k] = carry + v;
     carry += lane63_f(v);
@@ -705,13 +713,13 @@ __device__ __forceinline__ void pick_tile(const Params& P, const SeqFinal& f, Fi
   int jj = -1, jlast = -1;
 #pragma unroll
   for (int k = kTPL - 1; k >= 0; --k) {
-    const unsigned long long hit = __ballot(pre[k] > tt && lane + k * kWave < P.ntiles);
+    const unsigned long long hit = __ballot(pre[k] > tt && lane + k * kWave < n);
     if (hit) jj = k * kWave + (int)__builtin_ctzll(hit);
     const unsigned long long pos = __ballot(tv[k] > 0.f);
     if (pos && jlast < 0) jlast = k * kWave + 63 - (int)__builtin_clzll(pos);
   }
   if (jj < 0) jj = jlast;
-  jj = min(max(jj, 0), P.ntiles - 1);
+  jj = min(max(jj, 0), n - 1);
   float before = 0.f;
 #pragma unroll
   for (int k = 0; k < kTPL; ++k) {
@@ -725,21 +733,24 @@ __device__ __forceinline__ void pick_tile(const Params& P, const SeqFinal& f, Fi
   }
 }
 
-// The token of the final draw: thread t re-reads its 8 consecutive weights of
-// tile jj, a block-wide exclusive prefix over the threads' sums locates the
-// first element (with weight) whose running prefix passes tp; ballots pick
-// the lowest such thread, and, failing one (rounding), the last element with
+// The token of the final draw inside unit jj (elements jj*span .. +span-1,
+// span = 1024*PT): thread t re-reads its PT consecutive weights, a
+// block-wide exclusive prefix over the threads' sums locates the first
+// element (with weight) whose running prefix passes tp; ballots pick the
+// lowest such thread, and, failing one (rounding), the last element with
 // weight.  Writes the token and the sequence's status.
+template <int PT>
 __device__ __forceinline__ void select_token(const Params& P, const SeqFinal& f, int kind, bool fallback,
                                              FinShared& sh) {
   const int t = threadIdx.x, wv = t / kWave, lane = t & (kWave - 1);
   const int jj = sh.jj;
   const float tp = sh.tp;
-  float w[kPerThread];
-  slice_weights(P, f, kind, jj, w);
+  const int base = jj * (kFinThreads * PT);
+  float w[PT];
+  slice_weights<PT>(P, f, kind, base, w);
   float loc = 0.f;
 #pragma unroll
-  for (int q = 0; q < kPerThread; ++q) loc += w[q];
+  for (int q = 0; q < PT; ++q) loc += w[q];
   const float inc = wave_incl_scan_f(loc);
   if (lane == kWave - 1) sh.sw[wv] = inc;
   __syncthreads();
@@ -747,7 +758,7 @@ __device__ __forceinline__ void select_token(const Params& P, const SeqFinal& f,
   for (int q = 0; q < wv; ++q) run += sh.sw[q];
   int found = -1, lastp = -1;
 #pragma unroll
-  for (int q = 0; q < kPerThread; ++q) {
+  for (int q = 0; q < PT; ++q) {
     run += w[q];
     if (found < 0 && w[q] > 0.f && run > tp) found = q;
     if (w[q] > 0.f) lastp = q;
@@ -758,10 +769,10 @@ __device__ __forceinline__ void select_token(const Params& P, const SeqFinal& f,
   const int ll = lm ? 63 - (int)__builtin_clzll(lm) : 0;
   const int ff = __builtin_amdgcn_readlane(found, fl);
   const int lq = __builtin_amdgcn_readlane(lastp, ll);
-  const int base = jj * kTileElems + wv * kWave * kPerThread;
+  const int wbase = base + wv * kWave * PT;
   if (lane == 0) {
-    sh.first[wv] = fm ? base + fl * kPerThread + ff : 0x7FFFFFFF;
-    sh.last[wv] = lm ? base + ll * kPerThread + lq : -1;
+    sh.first[wv] = fm ? wbase + fl * PT + ff : 0x7FFFFFFF;
+    sh.last[wv] = lm ? wbase + ll * PT + lq : -1;
   }
   __syncthreads();
   if (t == 0) {
@@ -776,12 +787,12 @@ __device__ __forceinline__ void select_token(const Params& P, const SeqFinal& f,
   }
 }
 
-// Given the tile sums in sh.tile: the tile, then the token.  A residual with
-// no mass (rounding only) falls back to p at the stop position: the block
-// recomputes every tile sum of p and picks again.
+// Residual draws, given the tile sums in sh.tile: the tile, then the token.
+// A residual with no mass (rounding only) falls back to p at the stop
+// position: the block recomputes every tile sum of p and picks again.
 __device__ __forceinline__ void finish_draw(const Params& P, const SeqFinal& f, FinShared& sh) {
   const int t = threadIdx.x;
-  if (t < kWave) pick_tile(P, f, sh);
+  if (t < kWave) pick_unit(f, P.ntiles, sh);
   __syncthreads();
   const bool fallback = sh.fallback;
   int kind = f.kind;
@@ -791,11 +802,50 @@ __device__ __forceinline__ void finish_draw(const Params& P, const SeqFinal& f, 
     __syncthreads();
     if (t < P.ntiles) sh.tile[t] = tile_total(sh, t);
     __syncthreads();
-    if (t < kWave) pick_tile(P, f, sh);
+    if (t < kWave) pick_unit(f, P.ntiles, sh);
     __syncthreads();
   }
-  select_token(P, f, kind, fallback, sh);
+  select_token<kPerThread>(P, f, kind, fallback, sh);
 }
+
+// Bonus and one-hot draws read one row, whose chunk sums of p follow from
+// row_stats' partials: chunk k holds s_k * exp2(round(m_k c) - round(M c)) / S
+// (s_k is relative to round(m_k c)); a one-hot draw takes p(x) of the proposed
+// token out of its chunk.  So the chunk holding t = u * Z is found without
+// reading the row, and only that chunk (32 KB) is re-read.  Wave 0 fills
+// sh.tile with the chunk sums of `kind` and picks.
+__device__ __forceinline__ void pick_chunk(const Params& P, const SeqFinal& f, int kind, FinShared& sh) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const Partial* pp = P.partials + (int64_t)f.trow * P.nch_t;
+  const bool onehot = kind == kFinalOnehot;
+  const int xchunk = onehot ? f.xhat / P.ce_t : -1;
+  const float px = onehot ? fexp2(fmaf(P.xval[f.trow], f.c, -f.mct)) * f.inv_st : 0.f;
+  for (int k = lane; k < P.nch_t; k += kWave) {
+    const Partial q = pp[k];
+    float z = (q.m == -INFINITY) ? 0.f : q.s * fexp2(q.m * f.c - f.mct) * f.inv_st;
+    if (k == xchunk) z = fmaxf(z - px, 0.f);
+    sh.tile[k] = z;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  pick_unit(f, P.nch_t, sh);
+}
+
+__device__ __forceinline__ void finish_draw_chunks(const Params& P, const SeqFinal& f, FinShared& sh) {
+  const int t = threadIdx.x;
+  if (t < kWave) pick_chunk(P, f, f.kind, sh);
+  __syncthreads();
+  const bool fallback = sh.fallback;
+  int kind = f.kind;
+  if (fallback) {           // one-hot residual with no mass: p itself
+    kind = kFinalBonus;
+    if (t < kWave) pick_chunk(P, f, kind, sh);
+    __syncthreads();
+  }
+  // a 32 KB chunk is 16384 bf16 or 8192 float32 logits
+  if (P.t_bf16) select_token<kChunkBytes / 2 / kFinThreads>(P, f, kind, fallback, sh);
+  else select_token<kChunkBytes / 4 / kFinThreads>(P, f, kind, fallback, sh);
+}
+
 
 // clear the outputs of a sequence that is not verified (one wave)
 __device__ __forceinline__ void clear_sequence(const Params& P, int s, int off_t, int off_d, int K, int st) {
@@ -1273,6 +1323,10 @@ __global__ void __launch_bounds__(kFinThreads) k_final(Params P) {
   __syncthreads();
   const SeqFinal f = sf;
   if (f.kind == kFinalDone) return;
+  if (f.kind != kFinalResidual) {   // bonus or one-hot: from the chunk partials
+    if (split == 0) finish_draw_chunks(P, f, sh);
+    return;
+  }
   tile_sums_pass(P, f, f.kind, split, P.nsplit, sh);
   __syncthreads();
   if (t < P.ntiles && t % P.nsplit == split) {
@@ -1292,7 +1346,7 @@ __global__ void __launch_bounds__(kFinThreads) k_select(Params P) {
   const int s = blockIdx.x;
   const int t = threadIdx.x;
   const SeqFinal f = P.fin[s];
-  if (f.kind == kFinalDone) return;
+  if (f.kind != kFinalResidual) return;   // drawn by the final kernel (or nothing to draw)
   if (t < P.ntiles) sh.tile[t] = P.tilesum[(int64_t)s * P.ntiles + t];
   __syncthreads();
   finish_draw(P, f, sh);
