@@ -57,13 +57,14 @@ struct spec_verify_ctx {
   int32_t max_batch = 0;
   int32_t max_k = 0;
   int64_t max_vocab = 0;
-  int64_t max_rows = 0;     // target + draft rows
+  int64_t max_rows = 0;     // sequence slots: max_batch * (2 * max_k + 1)
   int32_t max_nch = 0;      // chunks per row at the smallest chunk (8192 elements)
   int32_t max_tiles = 0;
   void* mem = nullptr;
   size_t bytes = 0;
   sv::Partial* partials = nullptr;
   float* xval = nullptr;
+  int32_t* ptok = nullptr;
   sv::SeqFinal* fin = nullptr;
   float* tilesum = nullptr;
   // defaults for NULL temperature / mode / seq_ids: 1.0, SV_SAMPLE, s
@@ -130,6 +131,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
   size_t off = 0;
   const size_t o_part = off;   off = align_up(off + sizeof(sv::Partial) * c->max_rows * c->max_nch, 256);
   const size_t o_xval = off;   off = align_up(off + sizeof(float) * c->max_rows, 256);
+  const size_t o_ptok = off;   off = align_up(off + sizeof(int32_t) * (size_t)max_batch * max_k, 256);
   const size_t o_fin = off;    off = align_up(off + sizeof(sv::SeqFinal) * max_batch, 256);
   const size_t o_tile = off;   off = align_up(off + sizeof(float) * (size_t)max_batch * c->max_tiles, 256);
   const size_t o_dt = off;     off = align_up(off + sizeof(float) * (size_t)max_batch, 256);
@@ -151,6 +153,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
   char* b = (char*)c->mem;
   c->partials = (sv::Partial*)(b + o_part);
   c->xval = (float*)(b + o_xval);
+  c->ptok = (int32_t*)(b + o_ptok);
   c->fin = (sv::SeqFinal*)(b + o_fin);
   c->tilesum = (float*)(b + o_tile);
   c->def_temperature = (float*)(b + o_dt);
@@ -271,6 +274,7 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
   p.status = a->status;
   p.partials = ctx->partials;
   p.xval = ctx->xval;
+  p.ptok = ctx->ptok;
   p.fin = ctx->fin;
   p.tilesum = ctx->tilesum;
   // one row-stats block streams 32 KB of a row
@@ -279,6 +283,8 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
   p.nch_t = (p.V + p.ce_t - 1) / p.ce_t;
   p.nch_d = (p.V + p.ce_d - 1) / p.ce_d;
   p.ntiles = (p.V + sv::kTileElems - 1) / sv::kTileElems;
+  p.slots = 2 * ctx->max_k + 1;
+  p.nch_max = p.nch_t > p.nch_d ? p.nch_t : p.nch_d;
   p.nsplit = 1;
   if (p.B < sv::kFuseMinBatch) {
     const int want = (sv::kSplitTargetBlocks + p.B - 1) / p.B;

@@ -79,9 +79,12 @@ struct Params {
   float* p_at;
   float* q_at;
   int32_t* status;
-  // scratch owned by the context
-  Partial* partials;  // target row r chunk k at r*nch_t + k; draft row r at n_t*nch_t + r*nch_d + k
-  float* xval;        // [n_t + n_d]: each row's logit at its proposed token
+  // scratch owned by the context, indexed by sequence slot: target position
+  // i of sequence s in slot s*slots + i, draft position i in slot
+  // s*slots + max_k + 1 + i
+  Partial* partials;  // chunk k of slot r at r*nch_max + k
+  float* xval;        // per slot: the row's logit at its proposed token
+  int32_t* ptok;      // [B * max_k]: the proposed tokens, copied by row statistics
   SeqFinal* fin;      // [B]
   float* tilesum;     // [B * ntiles]
   int32_t nch_t;      // chunks per target row
@@ -90,6 +93,8 @@ struct Params {
   int32_t ce_d;       // elements per draft chunk (32 KB)
   int32_t ntiles;     // tiles per row for the final draw
   int32_t nsplit;     // final-kernel blocks per sequence
+  int32_t slots;      // 2 * max_k + 1 slots per sequence
+  int32_t nch_max;    // max(nch_t, nch_d): partials per slot
 };
 
 // The kernels of one verify step, in stream order (select only when

@@ -521,8 +521,9 @@ __device__ __forceinline__ void tiles_full_vec(const Params& P, const SeqFinal& 
 #pragma unroll
       for (int n = 0; n < NV; ++n) {
         const int64_t e = (int64_t)j * kTileElems + (n * kFinThreads + t) * VEC;
-        vt[u][n] = __builtin_nontemporal_load((const u32x4*)(tp + e * ES));
-        if (KIND == kFinalResidual) vd[u][n] = __builtin_nontemporal_load((const u32x4*)(dp + e * ES));
+        // plain loads: the tile the search re-reads may still be cached
+        vt[u][n] = *((const u32x4*)(tp + e * ES));
+        if (KIND == kFinalResidual) vd[u][n] = *((const u32x4*)(dp + e * ES));
       }
     }
 #pragma unroll
@@ -816,10 +817,11 @@ __device__ __forceinline__ void finish_draw(const Params& P, const SeqFinal& f, 
 // sh.tile with the chunk sums of `kind` and picks.
 __device__ __forceinline__ void pick_chunk(const Params& P, const SeqFinal& f, int kind, FinShared& sh) {
   const int lane = threadIdx.x & (kWave - 1);
-  const Partial* pp = P.partials + (int64_t)f.trow * P.nch_t;
+  const int64_t sb = (int64_t)f.s * P.slots + f.A;     // target slot A
+  const Partial* pp = P.partials + sb * P.nch_max;
   const bool onehot = kind == kFinalOnehot;
   const int xchunk = onehot ? f.xhat / P.ce_t : -1;
-  const float px = onehot ? fexp2(fmaf(P.xval[f.trow], f.c, -f.mct)) * f.inv_st : 0.f;
+  const float px = onehot ? fexp2(fmaf(P.xval[sb], f.c, -f.mct)) * f.inv_st : 0.f;
   for (int k = lane; k < P.nch_t; k += kWave) {
     const Partial q = pp[k];
     float z = (q.m == -INFINITY) ? 0.f : q.s * fexp2(q.m * f.c - f.mct) * f.inv_st;
@@ -863,7 +865,7 @@ __device__ __forceinline__ void clear_sequence(const Params& P, int s, int off_t
 
 // Block-wide merge of the threads' (max, sum, argmax) and the partial write.
 template <bool ARG>
-__device__ __forceinline__ void finish_chunk(const Params& P, float m, float sum, int idx, float c) {
+__device__ __forceinline__ void finish_chunk(const Params& P, float m, float sum, int idx, float c, int64_t pidx) {
   __shared__ float s_m[kWaves], s_s[kWaves];
   __shared__ int s_i[kWaves];
   wave_merge<ARG>(m, sum, idx, c);
@@ -878,7 +880,7 @@ __device__ __forceinline__ void finish_chunk(const Params& P, float m, float sum
     float M = s_m[0], S = s_s[0];
     int I = s_i[0];
     for (int q = 1; q < kWaves; ++q) merge_stats<true>(M, S, I, s_m[q], s_s[q], s_i[q], c);
-    P.partials[blockIdx.x] = Partial{M, S, I, 0};    // block index == partial index
+    if (pidx >= 0) P.partials[pidx] = Partial{M, S, I, 0};
   }
 }
 
@@ -894,6 +896,22 @@ __device__ __forceinline__ int row_proposal(const Params& P, const Owner& own, i
   const int idx = off_d + i;
   if (idx < 0 || idx >= P.total_draft) return -1;
   return P.tokens[idx];
+}
+
+// The row's slot among its sequence's 2*max_k + 1: target position i at
+// slot i, draft position i at slot max_k + 1 + i; -1 past them (K > max_k,
+// which the scan reports).  Chunk k of slot r of sequence s keeps its
+// partial at (s*slots + r)*nch_max + k, so the scan finds a sequence's rows
+// without knowing its offset in the packed layout.
+__device__ __forceinline__ int row_slot_base(const Params& P, const Owner& own, int row, bool is_draft) {
+  const int i = row - own.first;
+  int slot = -1;
+  if (is_draft) {
+    if (i >= 0 && i < own.K && i < P.max_k) slot = P.max_k + 1 + i;
+  } else {
+    if (i >= 0 && i <= own.K && i <= P.max_k) slot = i;
+  }
+  return slot < 0 ? -1 : own.s * P.slots + slot;    // < 4096 * 257
 }
 
 // The logit at the proposal, taken from the chunk held in registers by the
@@ -938,14 +956,21 @@ struct StatsShared {
   int i[kWaves];
   Owner own;
   int x;          // token the row judges, or -1
+  int sb;         // the row's slot index s*slots + r, or -1
 };
 
+// Wave 0: the owner, the row's slot and proposal into LDS; chunk 0 of a
+// target row also records the proposal token in the sequence's slot list.
 __device__ __forceinline__ void publish_owner(const Params& P, StatsShared& sh, const Owner& own, int row,
-                                              bool is_draft) {
+                                              bool is_draft, int chunk) {
   const int x = (own.s >= 0) ? row_proposal(P, own, row, is_draft) : -1;
+  const int sb = (own.s >= 0) ? row_slot_base(P, own, row, is_draft) : -1;
   if ((threadIdx.x & (kWave - 1)) == 0) {
     sh.own = own;
     sh.x = x;
+    sh.sb = sb;
+    const int i = row - own.first;
+    if (chunk == 0 && !is_draft && sb >= 0 && i < own.K && i < P.max_k) P.ptok[(int64_t)own.s * P.max_k + i] = x;
   }
 }
 
@@ -956,7 +981,7 @@ __device__ __forceinline__ void publish_owner(const Params& P, StatsShared& sh, 
 // chunk maximum M, then every thread sums exp2(x*c - round(M*c)) against that
 // common reference, so the block's partial is a plain sum (no rescaling).
 template <bool BF, bool TAIL>
-__device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp, int row, int c0, int c1,
+__device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp, int row, int chunk, int c0, int c1,
                                               int plus_one, bool is_draft) {
   constexpr int VEC = BF ? 8 : 4;
   constexpr int N = kNV * VEC;
@@ -969,10 +994,10 @@ __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp,
       __builtin_amdgcn_sched_barrier(0);
       load_chunk<BF, TAIL>(rowp, c0, c1, v);
       __builtin_amdgcn_sched_barrier(0);
-      publish_owner(P, sh, owner_in_window(win, P, plus_one, row), row, is_draft);
+      publish_owner(P, sh, owner_in_window(win, P, plus_one, row), row, is_draft, chunk);
     } else {
       load_chunk<BF, TAIL>(rowp, c0, c1, v);
-      publish_owner(P, sh, owner_general(P, plus_one, row), row, is_draft);
+      publish_owner(P, sh, owner_general(P, plus_one, row), row, is_draft, chunk);
     }
   } else {
     load_chunk<BF, TAIL>(rowp, c0, c1, v);
@@ -980,13 +1005,16 @@ __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp,
   if (TAIL) mask_chunk<BF>(rowp, c0, c1, v);
   float f[N];
   unpack_chunk<BF>(v, f);
-  float mx = -INFINITY;
+  float tmx = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < N; ++k) mx = fmaxf(mx, f[k]);
-  mx = wave_max(mx);
+  for (int k = 0; k < N; ++k) tmx = fmaxf(tmx, f[k]);
+  const float mx = wave_max(tmx);
   if (lane == 0) sh.m[wv] = mx;
   __syncthreads();
-  const Owner own = sh.own;
+  Owner own;                               // block-uniform: scalar registers
+  own.s = __builtin_amdgcn_readfirstlane(sh.own.s);
+  own.T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sh.own.T)));
+  own.md = __builtin_amdgcn_readfirstlane(sh.own.md);
   if (own.s < 0) return;                   // the whole block: inconsistent layout
   const float M = fmaxf(fmaxf(sh.m[0], sh.m[1]), fmaxf(sh.m[2], sh.m[3]));
   const float c = row_scale(own.md, own.T);
@@ -1002,12 +1030,15 @@ __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp,
   const float sum = wave_sum((a0 + a1) + (a2 + a3));
   int idx = 0x7FFFFFFF;
   if (own.md == kGreedy && !is_draft) {    // lowest index attaining M
+    if (mx == M) {                          // only waves that hold M search
 #pragma unroll
-    for (int k = N - 1; k >= 0; --k)
-      if (f[k] == M) idx = c0 + ((k / VEC) * kThreads + t) * VEC + (k % VEC);
+      for (int k = N - 1; k >= 0; --k)
+        if (f[k] == M) idx = c0 + ((k / VEC) * kThreads + t) * VEC + (k % VEC);
+    }
     idx = wave_min_i(idx);
   }
-  record_proposal_logit<BF>(P, f, c0, c1, sh.x, is_draft ? (int64_t)P.n_t + row : (int64_t)row);
+  const int sb = __builtin_amdgcn_readfirstlane(sh.sb);
+  if (sb >= 0) record_proposal_logit<BF>(P, f, c0, c1, __builtin_amdgcn_readfirstlane(sh.x), sb);
   if (lane == 0) {
     sh.s[wv] = sum;
     sh.i[wv] = idx;
@@ -1016,40 +1047,46 @@ __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp,
   if (t == 0) {
     const float S = (sh.s[0] + sh.s[1]) + (sh.s[2] + sh.s[3]);
     const int I = min(min(sh.i[0], sh.i[1]), min(sh.i[2], sh.i[3]));
-    P.partials[blockIdx.x] = Partial{M, S, I, 0};    // block index == partial index
+    if (sb >= 0) P.partials[(int64_t)sb * P.nch_max + chunk] = Partial{M, S, I, 0};
   }
 }
 
 // Rows that are not 16-byte aligned, or shorter than one vector.
-__device__ __forceinline__ void row_stats_scalar(const Params& P, const char* rowp, int bf, int row, int c0, int c1,
-                                                 int plus_one, bool is_draft) {
+__device__ __forceinline__ void row_stats_scalar(const Params& P, const char* rowp, int bf, int row, int chunk, int c0,
+                                                 int c1, int plus_one, bool is_draft) {
   const Owner own = owner_general(P, plus_one, row);
   if (own.s < 0) return;
   const int x = row_proposal(P, own, row, is_draft);
-  if (threadIdx.x == 0 && x >= c0 && x < c1)
-    P.xval[is_draft ? (int64_t)P.n_t + row : (int64_t)row] = load_logit(rowp, x, bf);
+  const int sb = row_slot_base(P, own, row, is_draft);
+  if (threadIdx.x == 0 && sb >= 0) {
+    if (x >= c0 && x < c1) P.xval[sb] = load_logit(rowp, x, bf);
+    const int i = row - own.first;
+    if (chunk == 0 && !is_draft && i < own.K && i < P.max_k) P.ptok[(int64_t)own.s * P.max_k + i] = x;
+  }
+  const int64_t pidx = sb < 0 ? -1 : (int64_t)sb * P.nch_max + chunk;
   const float c = row_scale(own.md, own.T);
   float m, sum;
   int idx;
   if (own.md == kGreedy && !is_draft) {
     stats_scalar<true>(rowp, bf, c0, c1, c, m, sum, idx);
-    finish_chunk<true>(P, m, sum, idx, c);
+    finish_chunk<true>(P, m, sum, idx, c, pidx);
   } else {
     stats_scalar<false>(rowp, bf, c0, c1, c, m, sum, idx);
-    finish_chunk<false>(P, m, sum, idx, c);
+    finish_chunk<false>(P, m, sum, idx, c, pidx);
   }
 }
 
 template <bool BF>
-__device__ __forceinline__ void row_stats_seg(const Params& P, const char* rowp, int vec, int row, int c0, int ce,
+__device__ __forceinline__ void row_stats_seg(const Params& P, const char* rowp, int vec, int row, int chunk, int ce,
                                               int plus_one, bool is_draft) {
   constexpr int VEC = BF ? 8 : 4;
+  const int c0 = chunk * ce;
   const int c1 = min(P.V, c0 + ce);
   if (vec && P.V >= VEC) {
-    if (c0 + ce <= P.V) row_stats_vec<BF, false>(P, rowp, row, c0, c1, plus_one, is_draft);
-    else row_stats_vec<BF, true>(P, rowp, row, c0, c1, plus_one, is_draft);
+    if (c0 + ce <= P.V) row_stats_vec<BF, false>(P, rowp, row, chunk, c0, c1, plus_one, is_draft);
+    else row_stats_vec<BF, true>(P, rowp, row, chunk, c0, c1, plus_one, is_draft);
   } else {
-    row_stats_scalar(P, rowp, BF, row, c0, c1, plus_one, is_draft);
+    row_stats_scalar(P, rowp, BF, row, chunk, c0, c1, plus_one, is_draft);
   }
 }
 
@@ -1064,10 +1101,10 @@ __device__ __forceinline__ void row_stats_body(const Params& P) {
   const int chunk = bb - row * nch;
   if (is_draft) {
     const char* rowp = (const char*)P.dft + (int64_t)row * P.ld_d * (DB ? 2 : 4);
-    row_stats_seg<DB>(P, rowp, P.d_vec, row, chunk * P.ce_d, P.ce_d, 0, true);
+    row_stats_seg<DB>(P, rowp, P.d_vec, row, chunk, P.ce_d, 0, true);
   } else {
     const char* rowp = (const char*)P.tgt + (int64_t)row * P.ld_t * (TB ? 2 : 4);
-    row_stats_seg<TB>(P, rowp, P.t_vec, row, chunk * P.ce_t, P.ce_t, 1, false);
+    row_stats_seg<TB>(P, rowp, P.t_vec, row, chunk, P.ce_t, 1, false);
   }
 }
 
@@ -1087,12 +1124,13 @@ __global__ void __launch_bounds__(kThreads) k_row_stats(Params P) {
 // merges the chunk partials of row r on its own; lane i judges position i.
 // ---------------------------------------------------------------------------
 constexpr int kScanThreads = kWave;
-constexpr int kMergeUnroll = 16;      // chunk partials a lane has in flight at once
+constexpr int kMergeUnroll = 8;       // chunk partials a lane has in flight at once
 
 struct ScanShared {
-  float M[2 * kMaxK + 1];   // rows 0..K: target, K+1..2K: draft
+  float M[2 * kMaxK + 1];   // per slot: target positions 0..K at 0..K, draft position i at max_k + 1 + i
   float S[2 * kMaxK + 1];
   int I[2 * kMaxK + 1];
+  float X[2 * kMaxK + 1];   // the slot's logit at its proposal
   int tok[kMaxK];
 };
 
@@ -1112,10 +1150,34 @@ __device__ __forceinline__ void clear_bad_layout(const Params& P, int s) {
   }
 }
 
-// Row statistics from the row's chunk partials: M = max of the chunk maxima,
-// S = sum of s_k * exp2(round(m_k*c) - round(M*c)), I = lowest index attaining
-// M.  The chunks are taken in order; kMergeUnroll loads are issued before any
-// is used (indices clamped into the row, surplus entries ignored).
+// Row statistics from a group of chunk partials folded into a running
+// (M, S, I): M = max of the chunk maxima, S = sum of
+// s_k * exp2(round(m_k*c) - round(M*c)), I = lowest index attaining M.
+// Entries k >= n are ignored.
+__device__ __forceinline__ void merge_group(const Partial (&q)[kMergeUnroll], int n, float c, float& M, float& S,
+                                            int& I) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMergeUnroll; ++k)
+    if (k < n) m = fmaxf(m, q[k].m);
+  const float mn = fmaxf(M, m);
+  const float mnc = (mn == -INFINITY) ? 0.f : mn * c;
+  float sum = (M == -INFINITY) ? S : S * fexp2(M * c - mnc);
+  int idx = (M == mn) ? I : 0x7FFFFFFF;
+#pragma unroll
+  for (int k = 0; k < kMergeUnroll; ++k) {
+    if (k < n) {
+      sum += (q[k].m == -INFINITY) ? q[k].s : q[k].s * fexp2(q[k].m * c - mnc);
+      if (q[k].m == mn) idx = min(idx, q[k].idx);
+    }
+  }
+  M = mn;
+  S = sum;
+  I = idx;
+}
+
+// The whole row from its partials in chunk order, kMergeUnroll loads in
+// flight at a time (indices clamped into the row).
 __device__ __forceinline__ void merge_row(const Partial* pp, int nch, float c, float& M, float& S, int& I) {
   M = -INFINITY;
   S = 0.f;
@@ -1124,47 +1186,49 @@ __device__ __forceinline__ void merge_row(const Partial* pp, int nch, float c, f
     Partial q[kMergeUnroll];
 #pragma unroll
     for (int k = 0; k < kMergeUnroll; ++k) q[k] = pp[min(k0 + k, nch - 1)];
-    float m = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kMergeUnroll; ++k)
-      if (k0 + k < nch) m = fmaxf(m, q[k].m);
-    // fold the running (M, S) into this group's reference
-    const float mn = fmaxf(M, m);
-    const float mnc = (mn == -INFINITY) ? 0.f : mn * c;
-    float sum = (M == -INFINITY) ? S : S * fexp2(M * c - mnc);
-    int idx = (M == mn) ? I : 0x7FFFFFFF;
-#pragma unroll
-    for (int k = 0; k < kMergeUnroll; ++k) {
-      if (k0 + k < nch) {
-        sum += (q[k].m == -INFINITY) ? q[k].s : q[k].s * fexp2(q[k].m * c - mnc);
-        if (q[k].m == mn) idx = min(idx, q[k].idx);
-      }
-    }
-    M = mn;
-    S = sum;
-    I = idx;
+    merge_group(q, nch - k0, c, M, S, I);
   }
 }
 
 // The acceptance scan of sequence s by one wave: with `write`, stores every
 // output of the sequence but the final token; returns what the final draw
-// needs (kind kFinalDone when nothing is left).  Two dependent rounds of
-// loads: the layout sums with the sequence's own inputs, then the proposals,
-// their logits and the rows' partials.
+// needs (kind kFinalDone when nothing is left).  When a slot's chunks fit one
+// lane (<= 8) or two (<= 16, then at most 32 slots), lanes own slots (one or
+// two lanes per slot) and every load (the sequence's inputs, the layout sums,
+// each slot's partials, proposal logit and proposal token) is issued before
+// any is used: one round trip.  Otherwise lane r merges slot r in a loop.
 __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanShared& sh, bool write) {
   const int lane = threadIdx.x;
   SeqFinal f{};
   f.kind = kFinalDone;
   f.s = s;
+  const int mk = P.max_k;
+  const int R = P.slots;                       // 2 * max_k + 1
+  const int64_t sbase = (int64_t)s * R;
+  const int lps = (P.nch_max > kMergeUnroll && R <= kScanThreads / 2) ? 2 : 1;   // lanes per slot
+  const bool fast = R * lps <= kScanThreads && P.nch_max <= kMergeUnroll * lps;
 
-  // ---- round 1: the sequence's own inputs and the layout sums ----
   const int K = P.num_draft[s];
   const int md = P.mode[s];
   const float T = P.temperature[s];
   const uint32_t seq_id = P.seq_ids[s];
-  // 32-bit sums: a count outside 0..kLayoutKMax cannot belong to a layout
-  // of total_draft (<= 4096 * 128) rows and is flagged on its own, so the
-  // in-range sums stay below 2^31
+  Partial q[kMergeUnroll];
+  float xv = 0.f;
+  int tk = 0;
+  const int myslot = min(lane / lps, R - 1);
+  const int part = lane % lps;                 // which 8 chunks of the slot
+  const int mynch = (myslot > mk) ? P.nch_d : P.nch_t;
+  const int myn = min(max(mynch - part * kMergeUnroll, 0), kMergeUnroll);
+  if (fast) {
+    const Partial* pp = P.partials + (sbase + myslot) * P.nch_max + part * kMergeUnroll;
+#pragma unroll
+    for (int k = 0; k < kMergeUnroll; ++k) q[k] = pp[min(k, max(myn - 1, 0))];
+    xv = P.xval[sbase + myslot];
+    tk = P.ptok[(int64_t)s * mk + min(lane, mk - 1)];
+  }
+  // layout sums in 32 bits: a count outside 0..kLayoutKMax cannot belong to a
+  // layout of total_draft (<= 4096 * 128) rows and is flagged on its own, so
+  // the in-range sums stay below 2^31
   constexpr int kLayoutKMax = 1 << 19;
   uint32_t tot = 0, bef = 0;
   int out_of_range = 0;
@@ -1187,7 +1251,7 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
   const int off_t = off_d + s;
 
   int st = 0;
-  if (K > P.max_k) st |= kStKTooLarge;
+  if (K > mk) st |= kStKTooLarge;
   if (md != kSample && md != kGreedy && md != kOnehot) st |= kStBadMode;
   if ((md == kSample || md == kOnehot) && !(isfinite(T) && T >= kMinTemperature)) st |= kStBadTemp;
   if (md == kSample && K > 0 && P.dft == nullptr) st |= kStNoDraft;
@@ -1197,39 +1261,61 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
   }
   const float c = (md == kGreedy) ? kLog2e : kLog2e / T;
   const bool sample = md == kSample;
-  const int nrows = K + 1 + (sample ? K : 0);
 
-  // ---- round 2: position `lane`'s proposal and the logits at it, then the
-  // rows' chunk partials (lane r: row r); everything issued before any use ----
-  int x0 = 0;
-  float xt0 = 0.f, xd0 = 0.f;
-  if (lane < K) {
-    x0 = P.tokens[off_d + lane];
-    xt0 = P.xval[off_t + lane];
-    if (sample) xd0 = P.xval[(int64_t)P.n_t + off_d + lane];
-  }
-  int bad = 0;
-  for (int r = lane; r < nrows; r += kScanThreads) {
-    const bool isd = r > K;
-    const Partial* pp = isd ? P.partials + (int64_t)P.n_t * P.nch_t + (int64_t)(off_d + r - K - 1) * P.nch_d
-                            : P.partials + (int64_t)(off_t + r) * P.nch_t;
-    float M, S;
-    int I;
-    merge_row(pp, isd ? P.nch_d : P.nch_t, c, M, S, I);
-    sh.M[r] = M;
-    sh.S[r] = S;
-    sh.I[r] = I;
-    bad |= !(isfinite(M) && isfinite(S) && S > 0.f);
-  }
-  int badtok = 0;
-  if (lane < K) {
-    sh.tok[lane] = x0;
-    badtok = (x0 < 0 || x0 >= P.V);
-  }
-  for (int i = lane + kScanThreads; i < K; i += kScanThreads) {   // K > 64 only
-    const int x = P.tokens[off_d + i];
-    sh.tok[i] = x;
-    badtok |= (x < 0 || x >= P.V);
+  // ---- each used slot's statistics (lane r: slot r), the proposal tokens ----
+  int bad = 0, badtok = 0;
+  if (fast) {
+    const int r = lane / lps;
+    const bool used = (r <= K) || (sample && r > mk && r <= mk + K);
+    float M = -INFINITY, S = 0.f;
+    int I = 0x7FFFFFFF;
+    merge_group(q, myn, c, M, S, I);
+    if (lps == 2) {         // chunks 0..7 (even lane) then 8..15 (odd lane), same order in both lanes
+      const float M2 = dpp_f<kDppQuadXor1>(0.f, M);
+      const float S2 = dpp_f<kDppQuadXor1>(0.f, S);
+      const int I2 = dpp_i<kDppQuadXor1>(0, I);
+      const float Ma = part ? M2 : M, Sa = part ? S2 : S;
+      const int Ia = part ? I2 : I;
+      const float Mb = part ? M : M2, Sb = part ? S : S2;
+      const int Ib = part ? I : I2;
+      const float mn = fmaxf(Ma, Mb);
+      const float mnc = (mn == -INFINITY) ? 0.f : mn * c;
+      const float sa = (Ma == -INFINITY) ? Sa : Sa * fexp2(Ma * c - mnc);
+      const float sb = (Mb == -INFINITY) ? Sb : Sb * fexp2(Mb * c - mnc);
+      M = mn;
+      S = sa + sb;
+      I = min(Ma == mn ? Ia : 0x7FFFFFFF, Mb == mn ? Ib : 0x7FFFFFFF);
+    }
+    if (used && part == 0 && r < R) {
+      sh.M[r] = M;
+      sh.S[r] = S;
+      sh.I[r] = I;
+      sh.X[r] = xv;
+      bad = !(isfinite(M) && isfinite(S) && S > 0.f);
+    }
+    if (lane < K) {
+      sh.tok[lane] = tk;
+      badtok = (tk < 0 || tk >= P.V);
+    }
+  } else {
+    for (int r = lane; r < R; r += kScanThreads) {
+      const bool used = (r <= K) || (sample && r > mk && r <= mk + K);
+      if (!used) continue;
+      const int nch = (r > mk) ? P.nch_d : P.nch_t;
+      float M, S;
+      int I;
+      merge_row(P.partials + (sbase + r) * P.nch_max, nch, c, M, S, I);
+      sh.M[r] = M;
+      sh.S[r] = S;
+      sh.I[r] = I;
+      sh.X[r] = P.xval[sbase + r];
+      bad |= !(isfinite(M) && isfinite(S) && S > 0.f);
+    }
+    for (int i = lane; i < K; i += kScanThreads) {
+      const int x = P.ptok[(int64_t)s * mk + i];
+      sh.tok[i] = x;
+      badtok |= (x < 0 || x >= P.V);
+    }
   }
   if (__any(badtok)) {
     if (write) clear_sequence(P, s, off_t, off_d, K, kStBadToken);
@@ -1239,7 +1325,7 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
     if (write) clear_sequence(P, s, off_t, off_d, K, kStNonfinite);
     return f;
   }
-  // the rows' statistics and tokens were written to LDS by other lanes of
+  // the slots' statistics and tokens were written to LDS by other lanes of
   // this wave: keep the compiler from moving the reads above the writes
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
@@ -1249,20 +1335,19 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
     const int i = i0 + lane;
     int reject = 0;
     if (i < K) {
-      const float xt = (i0 == 0) ? xt0 : P.xval[off_t + i];
-      const float xd = (i0 == 0) ? xd0 : (sample ? P.xval[(int64_t)P.n_t + off_d + i] : 0.f);
-      const float p = fexp2(fmaf(xt, c, -(sh.M[i] * c))) / sh.S[i];
-      const float q = sample ? fexp2(fmaf(xd, c, -(sh.M[K + 1 + i] * c))) / sh.S[K + 1 + i] : 1.f;
+      const int d = mk + 1 + i;
+      const float p = fexp2(fmaf(sh.X[i], c, -(sh.M[i] * c))) / sh.S[i];
+      const float qd = sample ? fexp2(fmaf(sh.X[d], c, -(sh.M[d] * c))) / sh.S[d] : 1.f;
       int acc;
       if (md == kGreedy) {
         acc = (sh.tok[i] == sh.I[i]);
       } else {
         const float u = draw_uniform(P, seq_id, (uint32_t)i, 0u);
-        const float r = (md == kOnehot) ? p : (q > 0.f ? fminf(1.f, p / q) : 0.f);
+        const float r = (md == kOnehot) ? p : (qd > 0.f ? fminf(1.f, p / qd) : 0.f);
         acc = u < r;
       }
       if (write && P.p_at) P.p_at[off_d + i] = p;
-      if (write && P.q_at) P.q_at[off_d + i] = q;
+      if (write && P.q_at) P.q_at[off_d + i] = qd;
       reject = !acc;
     }
     const unsigned long long rj = __ballot(reject);
@@ -1295,8 +1380,8 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
     } else {
       f.kind = kFinalResidual;
       f.drow = off_d + A;
-      f.mcd = sh.M[K + 1 + A] * c;
-      f.inv_sd = 1.f / sh.S[K + 1 + A];
+      f.mcd = sh.M[mk + 1 + A] * c;
+      f.inv_sd = 1.f / sh.S[mk + 1 + A];
     }
   }
   return f;
