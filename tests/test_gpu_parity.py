@@ -52,6 +52,7 @@ TINY = [
     (12, 64, 500, 16, "bf16", 0),      # K up to max_k
     (13, 200, 300, 8, "f32", 4),
     (14, 3, 1, 3, "f32", 0),           # a one-token vocabulary
+    (15, 6, 150000, 4, "f32", 0),      # 19 chunks per row: the scan merges in groups
 ]
 
 
@@ -269,6 +270,37 @@ def _quiet(verifier, b, torch_mod):
     rep = gu.compare(gu.oracle_for(b, verifier.max_k), out)
     assert rep.ok, rep.messages
     return rep, out, None
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_workload_bench_context(torch_mod, cfg):
+    """The full-size workloads through a context sized the way bench.py sizes
+    it (max_k = 8 here): the scan's one-round path, with two lanes per slot
+    where a row has 9..16 chunks, and the launch shapes bench.py times."""
+    import rejection_sampling_verify_06_amd as sv
+    from workloads import config_description
+    desc = config_description(cfg)
+    batches = [make_config_batch(cfg, step) for step in (0, 1)]
+    maxk = max(8, int(max(b.num_draft.max() for b in batches)))
+    v = sv.Verifier(max_batch=desc["batch"], max_k=maxk, max_vocab=desc["vocab"], device=0)
+    try:
+        for step, b in enumerate(batches):
+            gu.check_batch(v, b, torch_mod, label=f"C{cfg} step {step}, bench context")
+    finally:
+        v.close()
+
+
+def test_small_max_k_mixed(torch_mod):
+    """max_k = 8, fp32 rows of 13 chunks (two scan lanes per slot), a batch
+    below 128 (split final kernel + select) with every mode."""
+    import rejection_sampling_verify_06_amd as sv
+    v = sv.Verifier(max_batch=64, max_k=8, max_vocab=100000, device=0)
+    try:
+        for seed in (50, 51):
+            b = make_random_batch(seed, B=24, V=100000, kmax=8, dtype="f32")
+            gu.check_batch(v, b, torch_mod, label=f"max_k 8, V 100000 f32, seed {seed}")
+    finally:
+        v.close()
 
 
 def test_workload_c4_interleaved(verifier, torch_mod):
