@@ -41,9 +41,9 @@ struct SeqFinal {
   int32_t trow;       // target row of position A
   int32_t drow;       // draft row of position A (kFinalResidual)
   float mct;          // round(M_t * c) of target row A
-  float inv_st;       // 1 / S_t
   float mcd;          // round(M_d * c) of draft row A
-  float inv_sd;       // 1 / S_d
+  float rq;           // S_t / S_d (residual weights are S_t * max(0, p - q))
+  float pad0;
   float c;
   float u;            // uniform of the final draw
   int32_t xhat;       // proposed token at A (kFinalOnehot)

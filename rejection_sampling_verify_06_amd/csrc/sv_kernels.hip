@@ -434,14 +434,18 @@ constexpr int kPerThread = kTileElems / kFinThreads;   // 8
 template <bool BF, int KIND>
 constexpr int tile_unroll() { return KIND == kFinalResidual ? 2 : (BF ? 8 : 4); }
 
+// Final weights up to one positive factor per sequence (the inverse CDF is
+// scale-free): with e_x = exp2(x c - round(M_t c)) = S_t p(x), a residual
+// weight is max(0, e_x - (S_t/S_d) e_y) = S_t max(0, p - q), formed with a
+// single rounding; bonus and one-hot weights are e_x = S_t p.
 __device__ __forceinline__ float final_weight(int kind, float x, float y, int k, const SeqFinal& f) {
-  const float p = fexp2(fmaf(x, f.c, -f.mct)) * f.inv_st;
+  const float ex = fexp2(fmaf(x, f.c, -f.mct));
   if (kind == kFinalResidual) {
-    const float q = fexp2(fmaf(y, f.c, -f.mcd)) * f.inv_sd;
-    return fmaxf(p - q, 0.f);
+    const float ey = fexp2(fmaf(y, f.c, -f.mcd));
+    return fmaxf(fmaf(-f.rq, ey, ex), 0.f);
   }
   if (kind == kFinalOnehot && k == f.xhat) return 0.f;
-  return p;
+  return ex;
 }
 
 struct FinShared {
@@ -809,10 +813,11 @@ __device__ __forceinline__ void finish_draw(const Params& P, const SeqFinal& f, 
   select_token<kPerThread>(P, f, kind, fallback, sh);
 }
 
-// Bonus and one-hot draws read one row, whose chunk sums of p follow from
-// row_stats' partials: chunk k holds s_k * exp2(round(m_k c) - round(M c)) / S
-// (s_k is relative to round(m_k c)); a one-hot draw takes p(x) of the proposed
-// token out of its chunk.  So the chunk holding t = u * Z is found without
+// Bonus and one-hot draws read one row, whose chunk sums of the weights e_x
+// (S p, the scale the token search uses) follow from row_stats' partials:
+// chunk k holds s_k * exp2(round(m_k c) - round(M c)) (s_k is relative to
+// round(m_k c)); a one-hot draw takes e_x of the proposed token out of its
+// chunk.  So the chunk holding t = u * Z is found without
 // reading the row, and only that chunk (32 KB) is re-read.  Wave 0 fills
 // sh.tile with the chunk sums of `kind` and picks.
 __device__ __forceinline__ void pick_chunk(const Params& P, const SeqFinal& f, int kind, FinShared& sh) {
@@ -821,10 +826,10 @@ __device__ __forceinline__ void pick_chunk(const Params& P, const SeqFinal& f, i
   const Partial* pp = P.partials + sb * P.nch_max;
   const bool onehot = kind == kFinalOnehot;
   const int xchunk = onehot ? f.xhat / P.ce_t : -1;
-  const float px = onehot ? fexp2(fmaf(P.xval[sb], f.c, -f.mct)) * f.inv_st : 0.f;
+  const float px = onehot ? fexp2(fmaf(P.xval[sb], f.c, -f.mct)) : 0.f;
   for (int k = lane; k < P.nch_t; k += kWave) {
     const Partial q = pp[k];
-    float z = (q.m == -INFINITY) ? 0.f : q.s * fexp2(q.m * f.c - f.mct) * f.inv_st;
+    float z = (q.m == -INFINITY) ? 0.f : q.s * fexp2(q.m * f.c - f.mct);
     if (k == xchunk) z = fmaxf(z - px, 0.f);
     sh.tile[k] = z;
   }
@@ -1370,7 +1375,6 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
   if (md != kGreedy) {
     f.trow = off_t + A;
     f.mct = sh.M[A] * c;
-    f.inv_st = 1.f / sh.S[A];
     f.u = draw_uniform(P, seq_id, (uint32_t)A, 1u);
     if (A == K) {
       f.kind = kFinalBonus;
@@ -1381,7 +1385,7 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
       f.kind = kFinalResidual;
       f.drow = off_d + A;
       f.mcd = sh.M[mk + 1 + A] * c;
-      f.inv_sd = 1.f / sh.S[mk + 1 + A];
+      f.rq = sh.S[A] / sh.S[mk + 1 + A];
     }
   }
   return f;
