@@ -58,19 +58,33 @@ def row_bytes(batch) -> dict:
     return {"row_stats": stats}
 
 
-def final_bytes(batch, accepted_len) -> int:
+def final_bytes(batch, accepted_len) -> dict:
+    """Bytes of the final draw, from each sequence's outcome.
+
+    read:    what this library reads — both rows at a SAMPLE rejection; one
+             32 KB chunk of the target row for a bonus or one-hot draw (its
+             chunk sums come from the row statistics); nothing for GREEDY.
+    formula: the method's own count (the whole target row for a bonus or
+             one-hot draw as well), for context.
+    early_exit: a sequential scan that stops at the first rejection reads
+             target rows 0..A and draft rows 0..min(A, K-1), plus the final
+             rows; the dense single pass reads every row."""
     bt = 2 if batch.dtype == "bf16" else 4
+    bd = bt if batch.draft is not None else 0
     V = batch.vocab
-    total = 0
+    read = formula = early = 0
     for s in range(batch.batch):
         m = int(batch.mode[s])
-        if m == 1:
-            continue
         A, K = int(accepted_len[s]), int(batch.num_draft[s])
         if A < 0:
             continue
-        total += V * bt * (2 if (m == 0 and A < K) else 1)
-    return total
+        early += V * (A + 1) * bt + (V * min(A + 1, K) * bd if m == 0 else 0)
+        if m == 1:
+            continue
+        residual = m == 0 and A < K
+        read += V * (bt + bd) if residual else min(32768, V * bt)
+        formula += V * bt * (2 if residual else 1)
+    return {"read": read, "formula": formula, "early_exit": early + read}
 
 
 def to_device(batch, torch):
@@ -125,6 +139,70 @@ def cpu_baseline(cfg: int, budget_s: float) -> dict:
                       f"sequences of step 0 with seeds 0..{passes - 1}, {dt:.1f} s, numpy float64, one process"}
 
 
+def step_traffic(workload: str, ms_step: float):
+    """HBM bytes of a whole step (every kernel) from the committed counter
+    summary, over the step time: the metric's own GB/s; None when the
+    counters were taken on another kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    with open(COUNTERS_FILE) as f:
+        c = json.load(f)
+    w = c.get("workloads", {}).get(workload)
+    if c.get("kernel_source_sha") != kernel_source_sha() or w is None or "step_hbm_bytes" not in w:
+        return None
+    gbps = w["step_hbm_bytes"] / (ms_step * 1e-3) / 1e9
+    return {"hbm_bytes": w["step_hbm_bytes"], "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
+def cpu_baseline_parallel(cfg: int, budget_s: float, workers: int) -> dict:
+    """The same oracle over `workers` processes, each taking every
+    workers-th sequence of step 0 pass after pass until the budget is spent.
+    Runs in a child interpreter that never touches the GPU."""
+    import multiprocessing as mp
+    with mp.get_context("fork").Pool(workers) as pool:
+        res = pool.starmap(_oracle_worker, [(cfg, budget_s, w, workers) for w in range(workers)])
+    pos = sum(r[0] for r in res)
+    wall = max(r[1] for r in res)
+    return {"value": round(pos / wall, 3), "unit": "positions/s", "cores": workers, "kind": "oracle",
+            "sample": f"{pos} positions of step 0 (sequences split over {workers} processes, passes with new seeds), "
+                      f"{wall:.1f} s, numpy float64"}
+
+
+def _oracle_worker(cfg, budget_s, w, n):
+    import oracle
+    from workloads import make_config_batch
+    b = make_config_batch(cfg, 0)
+    off_d = np.concatenate(([0], np.cumsum(b.num_draft)[:-1])).astype(np.int64)
+    off_t = off_d + np.arange(b.batch)
+    mine = list(range(w, b.batch, n)) or [w % b.batch]
+    done = passes = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        for s in mine:
+            K = int(b.num_draft[s])
+            sl_t = slice(int(off_t[s]), int(off_t[s]) + K + 1)
+            sl_d = slice(int(off_d[s]), int(off_d[s]) + K)
+            oracle.verify_batch(target=b.target[sl_t], draft=None if b.draft is None else b.draft[sl_d],
+                                dtype=b.dtype, vocab=b.vocab, num_draft=b.num_draft[s:s + 1],
+                                draft_tokens=b.draft_tokens[sl_d], temperature=b.temperature[s:s + 1],
+                                mode=b.mode[s:s + 1], seq_ids=b.seq_ids[s:s + 1], seed=passes)
+            done += K + 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        passes += 1
+    return done, time.perf_counter() - t0
+
+
+def run_parallel_baseline_child(cfg: int, budget_s: float, workers: int):
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-parallel-child", str(cfg),
+                        "--cpu-budget", str(budget_s), "--cpu-workers", str(workers)],
+                       capture_output=True, text=True, timeout=budget_s * 4 + 120)
+    if r.returncode != 0:
+        return {"error": (r.stderr or "")[-300:]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def load_traffic(workload: str):
     """HBM bytes per row-statistics launch from the committed counter summary,
     or None when it was taken on another kernel source or another workload."""
@@ -147,10 +225,16 @@ def main():
     ap.add_argument("--rotate", type=int, default=None, help="input sets kept resident and cycled")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1),
+                    help="processes for the parallel oracle baseline (0: skip it)")
+    ap.add_argument("--cpu-parallel-child", type=int, default=None, help=argparse.SUPPRESS)
     ap.add_argument("--no-kernel-events", action="store_true", help="time without per-kernel HIP events")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain device copies of 1 GiB (the reference kernel for counter scaling)")
     args = ap.parse_args()
+    if args.cpu_parallel_child is not None:      # child interpreter: CPU only
+        print(json.dumps(cpu_baseline_parallel(args.cpu_parallel_child, args.cpu_budget, args.cpu_workers)))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -211,7 +295,9 @@ def main():
     sets_used = [(args.warmup + i) % R for i in range(args.steps)]
     pos = np.mean([batches[r].positions for r in sets_used])
     stats_bytes = np.mean([row_bytes(batches[r])["row_stats"] for r in sets_used])
-    fin_bytes = np.mean([fin_b[r] for r in sets_used])
+    fin_bytes = np.mean([fin_b[r]["read"] for r in sets_used])
+    fin_formula = np.mean([fin_b[r]["formula"] for r in sets_used])
+    early_bytes = np.mean([fin_b[r]["early_exit"] for r in sets_used])
     ms_step = elapsed * 1e3 / args.steps
     value = pos * args.steps / elapsed
     # four more repetitions of the same K steps, for the median
@@ -250,6 +336,8 @@ def main():
         del src, dst
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_budget)
+    cpu_par = None if (args.no_cpu_baseline or args.cpu_workers < 1) else \
+        run_parallel_baseline_child(cfg, args.cpu_budget, args.cpu_workers)
     line = {
         "metric": METRIC, "value": round(float(value), 1), "unit": "positions/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
@@ -262,8 +350,11 @@ def main():
         "cpu_baseline": cpu,
         "ms_per_step_median_of_5": round(float(np.median(reps)), 5),
         "step_bytes": {"row_stats": int(stats_bytes), "final_draw": int(fin_bytes),
+                       "final_draw_formula": int(fin_formula), "early_exit_lower_bound": int(early_bytes),
                        "step_GBps": round((stats_bytes + fin_bytes) / (ms_step * 1e-3) / 1e9, 1),
                        "step_frac_of_peak": round((stats_bytes + fin_bytes) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+        "step_traffic": step_traffic(args.workload, ms_step),
+        "cpu_baseline_parallel": cpu_par,
         "kernel_ms": {k: round(x, 5) for k, x in kern.items()},
         "kernel_events_ms_per_step": None if ev_ms_step is None else round(ev_ms_step, 5),
         "input_generation_s": round(gen_s, 1),
