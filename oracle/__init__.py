@@ -1,4 +1,5 @@
-"""CPU oracle of the batched speculative-decoding verify step.
+"""CPU oracle of the batched speculative-decoding verify step and of the
+N-gram (prompt-lookup) proposer that feeds its one-hot mode.
 
 TEST INFRASTRUCTURE ONLY.  This package is a plain, slow, float64 statement
 of what the verify step computes, used to check the HIP library.  Only the
@@ -21,3 +22,4 @@ from .verify import (  # noqa: F401
     verify_sequence, verify_batch, verify_batch_from,
 )
 from .compare import CompareReport, compare  # noqa: F401
+from .ngram import ngram_propose, ngram_propose_batch, valid_starts  # noqa: F401
