@@ -161,6 +161,56 @@ const char* spec_verify_last_error(void);
 int spec_verify_timing_enable(spec_verify_ctx* ctx, int32_t max_calls);
 int spec_verify_timing_read(spec_verify_ctx* ctx, int32_t* calls, double* ms_per_kernel);
 
+/* ---- N-gram (prompt-lookup) proposer -------------------------------------
+ * "5.2 Draft 模型与无模型方案" (AIInfraGuide), sections 4.1-4.3 and the lookup
+ * experiment of section 6: for each sequence, the last n token ids of its
+ * history are looked up earlier in the same history and the tokens that
+ * followed become a deterministic proposal, which the target then verifies
+ * as a one-hot draft (spec_verify_run with mode SV_ONEHOT).
+ *
+ * With history h of length L and window n, a start s is an occurrence when
+ * h[s .. s+n-1] equals h[L-n .. L-1] and s + n < L - n (the occurrence ends
+ * before the tail and at least one token follows it outside the tail).  The
+ * chosen occurrence has the largest n in [min_n, max_n], then the largest s;
+ * the proposal is h[s+n .. min(s+n+max_tokens, L-n) - 1] (never copied from
+ * the tail).  No occurrence: an empty proposal.
+ *
+ * All pointers are device pointers owned by the caller.
+ *   history        [total_len] int32 token ids; sequence b is
+ *                  history[hist_offsets[b] .. hist_offsets[b+1] - 1]
+ *   hist_offsets   [batch + 1] int64
+ *   total_len      host value: the length of `history`; bounds every read
+ *   min_n, max_n   1 <= min_n <= max_n <= SV_NGRAM_MAX_N
+ *   max_tokens     1 .. SV_NGRAM_MAX_TOKENS
+ *   draft_tokens   out [batch * max_tokens] int32: sequence b's proposal at
+ *                  b * max_tokens, -1 after it
+ *   num_draft      out [batch] int32: proposal length (0: none)
+ *   match_n        out [batch] int32 or NULL: the window that matched (0:
+ *                  none; -1: sequence b's offsets are out of order or outside
+ *                  total_len, and nothing of it was read)
+ * spec_verify_ngram_propose checks the host-side values (SV_ERR_INVALID:
+ * nothing is enqueued), enqueues one kernel on `hip_stream` (one block per
+ * sequence), allocates nothing and does not synchronise.  It needs no
+ * context. */
+#define SV_NGRAM_MAX_N 16
+#define SV_NGRAM_MAX_TOKENS 128
+typedef struct spec_verify_ngram_args {
+  int32_t batch;
+  const int32_t* history;
+  const int64_t* hist_offsets;
+  int64_t total_len;
+  int32_t min_n;
+  int32_t max_n;
+  int32_t max_tokens;
+  int32_t* draft_tokens;
+  int32_t* num_draft;
+  int32_t* match_n;
+} spec_verify_ngram_args;
+int spec_verify_ngram_propose(const spec_verify_ngram_args* args, void* hip_stream);
+
+/* sizeof(spec_verify_ngram_args) as compiled into the library. */
+int64_t spec_verify_ngram_args_size(void);
+
 /* Library version string. */
 const char* spec_verify_version(void);
 

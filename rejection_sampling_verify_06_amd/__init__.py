@@ -25,7 +25,7 @@ from ._lib import (  # noqa: F401
     KERNEL_NAMES, LibraryMissing,
 )
 
-__all__ = ["Verifier", "VerifyError", "verify", "LibraryMissing", "KERNEL_NAMES"]
+__all__ = ["Verifier", "VerifyError", "verify", "propose_ngram", "NgramProposer", "LibraryMissing", "KERNEL_NAMES"]
 
 
 class VerifyError(RuntimeError):
@@ -203,6 +203,60 @@ def verify(target, draft, draft_tokens, num_draft, temperature=None, mode=None, 
     if v is None:
         v = _CACHE[key] = Verifier(max(B, 1), kmax, int(target.shape[1]), dev)
     return v.run(target, draft, draft_tokens, num_draft, temperature, mode, seq_ids, seed, want_pq=want_pq)
+
+
+class NgramProposer:
+    """N-gram (prompt-lookup) proposals for a ragged batch of histories
+    (spec_verify_ngram_propose).  Holds only its packed argument struct, so a
+    caller that reuses the output tensors can re-run it cheaply."""
+
+    def __init__(self):
+        self._lib = _lib.load()
+
+    def make_outputs(self, batch: int, max_tokens: int, device, want_match: bool = True) -> dict:
+        import torch
+        return {"draft_tokens": torch.empty((batch, max_tokens), dtype=torch.int32, device=device),
+                "num_draft": torch.empty(batch, dtype=torch.int32, device=device),
+                "match_n": torch.empty(batch, dtype=torch.int32, device=device) if want_match else None}
+
+    def build_args(self, history, offsets, min_n: int, max_n: int, max_tokens: int, out: dict):
+        import torch
+        dev = offsets.device
+        B = int(offsets.numel()) - 1
+        if B < 0:
+            raise ValueError("offsets needs batch + 1 entries")
+        _need(offsets, "offsets", (torch.int64,), torch, device=dev)
+        _need(history, "history", (torch.int32,), torch, device=dev)
+        _need(out["draft_tokens"], "draft_tokens", (torch.int32,), torch, B * max_tokens, dev)
+        _need(out["num_draft"], "num_draft", (torch.int32,), torch, B, dev)
+        _need(out.get("match_n"), "match_n", (torch.int32,), torch, B, dev)
+        a = _lib.SpecVerifyNgramArgs()
+        a.batch = B
+        a.history = _ptr(history) if history.numel() else None
+        a.hist_offsets = _ptr(offsets)
+        a.total_len = int(history.numel())
+        a.min_n, a.max_n, a.max_tokens = int(min_n), int(max_n), int(max_tokens)
+        a.draft_tokens = _ptr(out["draft_tokens"])
+        a.num_draft = _ptr(out["num_draft"])
+        a.match_n = _ptr(out.get("match_n"))
+        return a
+
+    def run_args(self, args, stream=None):
+        import torch
+        st = stream if stream is not None else torch.cuda.current_stream()
+        _check(self._lib.spec_verify_ngram_propose(ctypes.byref(args), ctypes.c_void_p(st.cuda_stream)))
+
+    def run(self, history, offsets, min_n: int = 2, max_n: int = 4, max_tokens: int = 5, stream=None) -> dict:
+        B = int(offsets.numel()) - 1
+        out = self.make_outputs(B, max_tokens, offsets.device)
+        self.run_args(self.build_args(history, offsets, min_n, max_n, max_tokens, out), stream)
+        return out
+
+
+def propose_ngram(history, offsets, min_n: int = 2, max_n: int = 4, max_tokens: int = 5) -> dict:
+    """One-shot N-gram proposals: draft_tokens [B, max_tokens] (-1 padded),
+    num_draft [B], match_n [B] (0: no occurrence)."""
+    return NgramProposer().run(history, offsets, min_n, max_n, max_tokens)
 
 
 def library_loaded_path() -> str:

@@ -21,10 +21,13 @@ SV_ST_ZERO_RESIDUAL = 128
 SV_NUM_KERNELS = 3
 KERNEL_NAMES = ("row_stats", "final", "select")
 
+SV_NGRAM_MAX_N = 16
+SV_NGRAM_MAX_TOKENS = 128
+
 EXPORTED = (
     "spec_verify_create", "spec_verify_run", "spec_verify_destroy", "spec_verify_last_error",
     "spec_verify_timing_enable", "spec_verify_timing_read", "spec_verify_version",
-    "spec_verify_args_size",
+    "spec_verify_args_size", "spec_verify_ngram_propose", "spec_verify_ngram_args_size",
 )
 
 
@@ -50,6 +53,21 @@ class SpecVerifyArgs(ctypes.Structure):
         ("p_at_proposal", ctypes.c_void_p),
         ("q_at_proposal", ctypes.c_void_p),
         ("status", ctypes.c_void_p),
+    ]
+
+
+class SpecVerifyNgramArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("history", ctypes.c_void_p),
+        ("hist_offsets", ctypes.c_void_p),
+        ("total_len", ctypes.c_int64),
+        ("min_n", ctypes.c_int32),
+        ("max_n", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int32),
+        ("draft_tokens", ctypes.c_void_p),
+        ("num_draft", ctypes.c_void_p),
+        ("match_n", ctypes.c_void_p),
     ]
 
 
@@ -89,8 +107,14 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_version.restype = ctypes.c_char_p
     lib.spec_verify_args_size.argtypes = []
     lib.spec_verify_args_size.restype = ctypes.c_int64
+    lib.spec_verify_ngram_propose.argtypes = [ctypes.POINTER(SpecVerifyNgramArgs), P]
+    lib.spec_verify_ngram_propose.restype = ctypes.c_int
+    lib.spec_verify_ngram_args_size.argtypes = []
+    lib.spec_verify_ngram_args_size.restype = ctypes.c_int64
     if lib.spec_verify_args_size() != ctypes.sizeof(SpecVerifyArgs):
         raise RuntimeError("spec_verify_args layout differs between the library and the binding")
+    if lib.spec_verify_ngram_args_size() != ctypes.sizeof(SpecVerifyNgramArgs):
+        raise RuntimeError("spec_verify_ngram_args layout differs between the library and the binding")
     _LIB = lib
     return lib
 

@@ -316,6 +316,50 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
   return SV_OK;
 }
 
+int64_t spec_verify_ngram_args_size(void) { return (int64_t)sizeof(spec_verify_ngram_args); }
+
+int spec_verify_ngram_propose(const spec_verify_ngram_args* a, void* hip_stream) {
+  if (!a) {
+    set_err("spec_verify_ngram_propose: args is NULL");
+    return SV_ERR_INVALID;
+  }
+  if (a->batch < 0) {
+    set_err("spec_verify_ngram_propose: batch %d < 0", a->batch);
+    return SV_ERR_INVALID;
+  }
+  if (a->batch == 0) return SV_OK;
+  if (a->min_n < 1 || a->max_n < a->min_n || a->max_n > SV_NGRAM_MAX_N) {
+    set_err("spec_verify_ngram_propose: need 1 <= min_n (%d) <= max_n (%d) <= %d", a->min_n, a->max_n,
+            SV_NGRAM_MAX_N);
+    return SV_ERR_INVALID;
+  }
+  if (a->max_tokens < 1 || a->max_tokens > SV_NGRAM_MAX_TOKENS) {
+    set_err("spec_verify_ngram_propose: max_tokens %d outside 1..%d", a->max_tokens, SV_NGRAM_MAX_TOKENS);
+    return SV_ERR_INVALID;
+  }
+  if (a->total_len < 0 || (a->total_len > 0 && !a->history) || !a->hist_offsets || !a->draft_tokens ||
+      !a->num_draft) {
+    set_err("spec_verify_ngram_propose: history (when total_len > 0), hist_offsets, draft_tokens and num_draft "
+            "are required");
+    return SV_ERR_INVALID;
+  }
+  static_assert(SV_NGRAM_MAX_N == sv::kNgramMaxN, "window limit");
+  sv::NgramParams p;
+  p.B = a->batch;
+  p.history = a->history;
+  p.offsets = a->hist_offsets;
+  p.total_len = a->total_len;
+  p.min_n = a->min_n;
+  p.max_n = a->max_n;
+  p.max_tokens = a->max_tokens;
+  p.draft = a->draft_tokens;
+  p.num_draft = a->num_draft;
+  p.match_n = a->match_n;
+  hipError_t e = sv::launch_ngram(p, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail("ngram", e);
+  return SV_OK;
+}
+
 int spec_verify_timing_enable(spec_verify_ctx* ctx, int32_t max_calls) {
   if (!ctx || max_calls < 0) {
     set_err("spec_verify_timing_enable: bad arguments");

@@ -97,6 +97,24 @@ struct Params {
   int32_t nch_max;    // max(nch_t, nch_d): partials per slot
 };
 
+// N-gram proposer (sv_ngram.hip).
+constexpr int kNgramMaxN = 16;          // longest lookup window
+
+struct NgramParams {
+  int32_t B;
+  const int32_t* history;   // [total_len]
+  const int64_t* offsets;   // [B + 1]
+  int64_t total_len;
+  int32_t min_n;
+  int32_t max_n;
+  int32_t max_tokens;
+  int32_t* draft;           // [B * max_tokens]
+  int32_t* num_draft;       // [B]
+  int32_t* match_n;         // [B] or NULL
+};
+
+hipError_t launch_ngram(const NgramParams& p, hipStream_t st);
+
 // The kernels of one verify step, in stream order (select only when
 // nsplit > 1).
 hipError_t launch_row_stats(const Params& p, hipStream_t st);

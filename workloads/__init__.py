@@ -1,7 +1,9 @@
-"""Seeded synthetic inputs for the batched speculative-decoding verify step.
+"""Seeded synthetic inputs for the batched speculative-decoding verify step
+and for the N-gram proposer that feeds its one-hot mode.
 
 This package produces the *inputs* of the verify step (logits rows, proposed
-tokens, per-sequence draft lengths, temperatures and modes) and nothing else.
+tokens, per-sequence draft lengths, temperatures and modes) and of the
+proposer (ragged token histories), and nothing else.
 It holds none of the verify arithmetic (no softmax, no acceptance test, no
 residual sampling), so that the CPU oracle and the HIP library can both be fed
 from it without sharing any of the method's code.
@@ -9,5 +11,5 @@ from it without sharing any of the method's code.
 from .synth import (  # noqa: F401
     MODE_SAMPLE, MODE_GREEDY, MODE_ONEHOT, Batch, CONFIG_NAMES,
     make_config_batch, make_random_batch, bf16_round, bf16_widen,
-    config_description,
+    config_description, NgramBatch, NGRAM_WORKLOAD, make_ngram_batch, make_ngram_workload,
 )

@@ -334,3 +334,69 @@ def make_random_batch(seed: int, B: int, V: int, kmax: int, dtype: str = "f32",
         seq_ids=(np.arange(B, dtype=np.uint64) + seq_id_base).astype(np.uint32),
         seed=int(seed if philox_seed is None else philox_seed),
     )
+
+
+# ---------------------------------------------------------------------------
+# token histories for the N-gram (prompt-lookup) proposer
+# ---------------------------------------------------------------------------
+
+@dataclass
+class NgramBatch:
+    name: str
+    history: np.ndarray       # int32 [total_len]
+    offsets: np.ndarray       # int64 [B + 1]
+    min_n: int
+    max_n: int
+    max_tokens: int
+
+    @property
+    def batch(self) -> int:
+        return len(self.offsets) - 1
+
+    @property
+    def total_len(self) -> int:
+        return int(self.offsets[-1])
+
+
+NGRAM_WORKLOAD = "NG: B=256 histories of U{1024..16384} tokens, V=152064 Zipf ids, half the output copied from the prompt; windows 2..4, 5 proposed tokens"
+
+
+def _ngram_history(rng: np.random.Generator, L: int, vocab: int, ids: np.ndarray, p_tail_hit: float) -> np.ndarray:
+    """A prompt of Zipf-distributed ids, then an output in which runs of
+    fresh ids alternate with copies of 8..64-token spans of what came before;
+    with probability p_tail_hit the history ends inside a copied span."""
+    ranks = rng.zipf(1.2, size=L)
+    h = ids[np.minimum(ranks - 1, vocab - 1)].astype(np.int32)
+    pos = L // 2
+    while pos < L:
+        span = int(rng.integers(8, 65))
+        if rng.random() < 0.5 and pos > span:
+            src = int(rng.integers(0, pos - span))
+            n = min(span, L - pos)
+            h[pos:pos + n] = h[src:src + n]
+        pos += span
+    if rng.random() < p_tail_hit and L > 80:
+        span = int(rng.integers(4, 16))
+        src = int(rng.integers(0, L - 2 * span - 40))
+        h[L - span:] = h[src:src + span]
+    return h
+
+
+def make_ngram_batch(seed: int, B: int = 256, min_len: int = 1024, max_len: int = 16384, vocab: int = 152064,
+                     p_tail_hit: float = 0.7, min_n: int = 2, max_n: int = 4, max_tokens: int = 5,
+                     lengths: Optional[Sequence[int]] = None, name: Optional[str] = None) -> NgramBatch:
+    """Seeded ragged batch of histories (PCG64 seeded with (2000, seed))."""
+    rng = np.random.default_rng(np.random.PCG64([2000, seed]))
+    ids = rng.permutation(vocab).astype(np.int32)            # which id has which Zipf rank
+    if lengths is None:
+        lengths = rng.integers(min_len, max_len + 1, B)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    parts = [_ngram_history(rng, int(L), vocab, ids, p_tail_hit) for L in lengths]
+    offsets = np.concatenate(([0], np.cumsum(lengths))).astype(np.int64)
+    hist = np.concatenate(parts).astype(np.int32) if len(parts) else np.zeros(0, np.int32)
+    return NgramBatch(name=name or f"ngram(seed={seed},B={len(lengths)},L={min_len}..{max_len})", history=hist,
+                      offsets=offsets, min_n=min_n, max_n=max_n, max_tokens=max_tokens)
+
+
+def make_ngram_workload(step: int = 0) -> NgramBatch:
+    return make_ngram_batch(step, name=NGRAM_WORKLOAD)
