@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -36,14 +37,22 @@ sys.path.insert(0, ROOT)
 METRIC = "verified positions/sec (B·(K+1) over V) + achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
 WORKLOADS = {"C0": 0, "C1": 1, "C2": 2, "C3": 3, "C4": 4}
+NGRAM_ROTATE = 32          # 32 x ~8.6 MB of histories: more than the 256 MB last-level cache
 ROTATE = {0: 64, 1: 64, 2: 6, 3: 2, 4: 6}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "row_stats_counters.json")
+NGRAM_COUNTERS_FILE = os.path.join(ROOT, "profiles", "ngram_counters.json")
 KERNEL_SOURCE = os.path.join(ROOT, "rejection_sampling_verify_06_amd", "csrc", "sv_kernels.hip")
+NGRAM_SOURCE = os.path.join(ROOT, "rejection_sampling_verify_06_amd", "csrc", "sv_ngram.hip")
 
 
-def kernel_source_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_sha(path: str = KERNEL_SOURCE) -> str:
+    """Hash of a kernel source's code: comments and blank lines are left out,
+    so that counters stay attached to the code they were taken on."""
+    with open(path) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def row_bytes(batch) -> dict:
@@ -203,14 +212,135 @@ def run_parallel_baseline_child(cfg: int, budget_s: float, workers: int):
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
-def load_traffic(workload: str):
-    """HBM bytes per row-statistics launch from the committed counter summary,
-    or None when it was taken on another kernel source or another workload."""
-    if not os.path.exists(COUNTERS_FILE):
+def ngram_scan_bytes(b, match_n) -> int:
+    """Bytes a scan from the end of each history must read to decide, from
+    the window lengths the proposer returned: when the longest window a
+    history allows matched, everything from the most recent valid occurrence
+    of that window up to the end; otherwise the whole history (4 bytes per
+    token id)."""
+    total = 0
+    for i in range(b.batch):
+        h = b.history[b.offsets[i]:b.offsets[i + 1]]
+        L = len(h)
+        nmax = min(b.max_n, (L - 1) // 2)
+        n = int(match_n[i])
+        if n >= 1 and n == nmax:
+            last = L - 2 * n - 1                  # largest start leaving a token before the tail
+            ok = np.ones(last + 1, dtype=bool)
+            for j in range(n):
+                ok &= h[j:j + last + 1] == h[L - n + j]
+            total += 4 * (L - int(np.nonzero(ok)[0][-1]))
+        else:
+            total += 4 * L
+    return total
+
+
+def copy_calibration(torch):
+    """Five plain device copies of 1 GiB: the reference kernel that scales
+    the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def bench_ngram(args):
+    import torch
+    import rejection_sampling_verify_06_amd as sv
+    from workloads import make_ngram_workload, NGRAM_WORKLOAD
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sv.library_loaded_path()
+    dev = torch.device("cuda", 0)
+    R = args.rotate or NGRAM_ROTATE
+    t_gen = time.perf_counter()
+    batches = [make_ngram_workload(i) for i in range(R)]
+    gen_s = time.perf_counter() - t_gen
+    prop = sv.NgramProposer()
+    packed, outs = [], []
+    for b in batches:
+        h = torch.from_numpy(b.history).to(dev)
+        o = torch.from_numpy(b.offsets).to(dev)
+        out = prop.make_outputs(b.batch, b.max_tokens, dev)
+        outs.append((h, o, out))
+        packed.append(prop.build_args(h, o, b.min_n, b.max_n, b.max_tokens, out))
+
+    def step(i):
+        prop.run_args(packed[i % R])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    sets = [(args.warmup + i) % R for i in range(args.steps)]
+    seqs = np.mean([batches[r].batch for r in sets])
+    toks = np.mean([batches[r].total_len for r in sets])
+    ms_step = elapsed * 1e3 / args.steps
+    # per-launch duration from HIP events on the stream the kernel runs on
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(st)
+        step(args.warmup + args.steps + i)
+        ev[i][1].record(st)
+    torch.cuda.synchronize()
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ev_sets = sorted(set((args.warmup + args.steps + i) % R for i in range(args.steps)))
+    scan = {r: ngram_scan_bytes(batches[r], outs[r][2]["match_n"].cpu().numpy()) for r in ev_sets}
+    scan_bytes = np.mean([scan[(args.warmup + args.steps + i) % R] for i in range(args.steps)])
+    hist_bytes = np.mean([4 * batches[(args.warmup + args.steps + i) % R].total_len for i in range(args.steps)])
+    ach = scan_bytes / (launch_ms * 1e-3) / 1e9
+    if args.copy_calibration:
+        copy_calibration(torch)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        b = batches[0]
+        t1 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t1 < args.cpu_budget:
+            oracle.ngram_propose_batch(b.history, b.offsets, b.min_n, b.max_n, b.max_tokens)
+            done += 1
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(done * b.batch / dt, 1), "unit": "histories/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} passes over the {b.batch} histories of set 0 ({b.total_len} tokens), {dt:.1f} s, "
+                         f"numpy, one process"}
+    line = {
+        "metric": "N-gram proposals/sec (histories searched per second)", "value": round(float(seqs / (ms_step * 1e-3)), 1),
+        "unit": "histories/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32", "data": "synthetic",
+        "config": {"workload": NGRAM_WORKLOAD, "histories": int(seqs), "tokens_per_step": int(toks),
+                   "rotating_input_sets": R},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(ach / PEAK_HBM_GBPS, 4),
+                     "traffic": load_traffic("NG", NGRAM_COUNTERS_FILE, NGRAM_SOURCE), "kernel": "k_ngram",
+                     "algorithmic_bytes_per_launch": int(scan_bytes), "history_bytes_per_launch": int(hist_bytes),
+                     "mean_launch_ms": round(launch_ms, 5)},
+        "cpu_baseline": cpu,
+        "tokens_per_s": round(float(toks / (ms_step * 1e-3)), 1),
+        "input_generation_s": round(gen_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def load_traffic(workload: str, path: str = COUNTERS_FILE, source: str = KERNEL_SOURCE):
+    """HBM bytes per launch of the dominant kernel from a committed counter
+    summary, or None when it was taken on another kernel source or another
+    workload."""
+    if not os.path.exists(path):
         return None
-    with open(COUNTERS_FILE) as f:
+    with open(path) as f:
         c = json.load(f)
-    if c.get("kernel_source_sha") != kernel_source_sha():
+    if c.get("kernel_source_sha") != kernel_source_sha(source):
         return None
     w = c.get("workloads", {}).get(workload)
     return None if w is None else w.get("hbm_bytes_per_launch")
@@ -221,7 +351,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="C3", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="C3", choices=sorted(WORKLOADS) + ["NG"],
+                    help="C0..C4: the verify step; NG: the N-gram proposer")
     ap.add_argument("--rotate", type=int, default=None, help="input sets kept resident and cycled")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -242,6 +373,9 @@ def main():
               f"step of a sequence-sharded batch needs no communication, so a multi-GPU run would just repeat "
               f"this line per device.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "NG":
+        return bench_ngram(args)
 
     import torch
     import rejection_sampling_verify_06_amd as sv
@@ -327,13 +461,7 @@ def main():
                     "mean_launch_ms": round(kern["row_stats"], 5)}
 
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_budget)
     cpu_par = None if (args.no_cpu_baseline or args.cpu_workers < 1) else \

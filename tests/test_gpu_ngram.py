@@ -61,12 +61,13 @@ def test_page_example(torch_mod):
 
 
 def test_long_histories_across_rounds(torch_mod):
-    """Matches inside and beyond the first 2048-position round, the longest
-    window found late, and the early stop once the longest window is found."""
+    """Matches inside and beyond the first 8192-position round (histories up
+    to three rounds long), the longest window found late, and the early stop
+    once the longest window is found."""
     rng = np.random.default_rng(7)
     parts, lengths = [], []
     for i in range(64):
-        L = int(rng.integers(2100, 12000))
+        L = int(rng.integers(2100, 25000))
         h = rng.integers(0, 50000, L).astype(np.int32)
         n = int(rng.integers(2, 9))
         tail = h[L - n:].copy()

@@ -122,3 +122,21 @@ def test_pins_catch_planted_mistakes(mutant):
         except AssertionError:
             caught = True
     assert caught, mutant.__name__
+
+
+def test_bench_scan_bytes_match_oracle_starts():
+    """bench.py counts the bytes a scan from the end must read from the
+    proposer's window lengths alone; on a seeded batch they must equal the
+    depth down to the oracle's chosen start (whole history otherwise)."""
+    import bench
+    from workloads import make_ngram_batch
+    b = make_ngram_batch(11, B=40, min_len=1, max_len=3000, vocab=200, p_tail_hit=0.6)
+    _, _, win = oracle.ngram_propose_batch(b.history, b.offsets, b.min_n, b.max_n, b.max_tokens)
+    want = 0
+    for i in range(b.batch):
+        h = b.history[b.offsets[i]:b.offsets[i + 1]]
+        L = len(h)
+        n, _, s = oracle.ngram_propose(h, b.min_n, b.max_n, b.max_tokens)
+        want += 4 * ((L - s) if n is not None and n == min(b.max_n, (L - 1) // 2) else L)
+    assert (win == min(b.max_n, 4)).sum() > 0            # some histories stop early
+    assert bench.ngram_scan_bytes(b, win) == want
