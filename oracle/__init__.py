@@ -1,5 +1,6 @@
-"""CPU oracle of the batched speculative-decoding verify step and of the
-N-gram (prompt-lookup) proposer that feeds its one-hot mode.
+"""CPU oracle of the batched speculative-decoding verify step, of the
+N-gram (prompt-lookup) proposer that feeds its one-hot mode, and of the
+acceptance statistics and draft-length controllers fed by its results.
 
 TEST INFRASTRUCTURE ONLY.  This package is a plain, slow, float64 statement
 of what the verify step computes, used to check the HIP library.  Only the
@@ -23,3 +24,6 @@ from .verify import (  # noqa: F401
 )
 from .compare import CompareReport, compare  # noqa: F401
 from .ngram import ngram_propose, ngram_propose_batch, valid_starts  # noqa: F401
+from .stats import (  # noqa: F401
+    WINDOW, MULTIPLICATIVE, OPTIMAL_K, Controller, acceptance_counters, acceptance_summary, adapt_step, adapt_batch,
+)
