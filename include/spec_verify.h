@@ -211,6 +211,105 @@ int spec_verify_ngram_propose(const spec_verify_ngram_args* args, void* hip_stre
 /* sizeof(spec_verify_ngram_args) as compiled into the library. */
 int64_t spec_verify_ngram_args_size(void);
 
+/* ---- acceptance statistics ------------------------------------------------
+ * "5.2 Draft 模型与无模型方案" (AIInfraGuide), section 7: over R verify rounds
+ * that proposed D draft tokens of which C were accepted, the draft acceptance
+ * rate is C / D and the mean acceptance length 1 + C / R (a complete round
+ * also commits its corrected or bonus token); candidate coverage is the
+ * share of rounds that had any candidate; per position, the conditional
+ * acceptance rate (among rounds that reached the position) differs from the
+ * rate of being accepted all the way through it.
+ *
+ * A round is one sequence of one verify call: K = num_draft[s], A =
+ * accepted_len[s].  spec_verify_stats_accumulate ADDS one call's rounds to
+ * `stats`, device uint64 [SV_STATS_WORDS(max_k)], owned by the caller, who
+ * zeroes it to start an observation window (with a fill kernel or a copy;
+ * the library never clears it):
+ *   [0] R rounds counted             [4] rounds with K > 0 and A = K
+ *   [1] D = sum K                    [5] rounds not counted: A < 0 (not
+ *   [2] C = sum A                        verified), K outside 0..max_k, A > K
+ *   [3] rounds with K > 0            [6] emitted tokens sum (A + 1)   [7] 0
+ *   [8 + i]            rounds with K > i                 (proposed at i)
+ *   [8 + max_k + i]    rounds with K > i and A >= i      (reached i)
+ *   [8 + 2 max_k + i]  rounds with A > i                 (accepted at i)
+ * Counts are exact (integer sums, no atomics).  num_draft and accepted_len
+ * are device int32 [batch] (for instance the verify call's own arrays, on
+ * the same stream).  One block of the kernel walks the batch: meant for the
+ * batch of one decode step.
+ *
+ * spec_verify_stats_summary writes device float64 [SV_STATS_SUMMARY_WORDS]:
+ *   [0] C / D   [1] 1 + C / R   [2] [3] / R (coverage)   [3] [4] / [3]
+ *   [4 + i]          conditional acceptance at i: accepted_i / reached_i
+ *   [4 + max_k + i]  accepted through i:          accepted_i / proposed_i
+ * NaN where the denominator is 0; each value is one correctly rounded
+ * float64 division of the counts (plus 1.0 for [1]).
+ * Both enqueue one kernel on `hip_stream`, allocate nothing and do not
+ * synchronise; SV_ERR_INVALID (nothing enqueued) for max_k outside
+ * 1..SV_STATS_MAX_K, batch < 0 or a missing buffer. */
+#define SV_STATS_MAX_K 128
+#define SV_STATS_WORDS(max_k) (8 + 3 * (max_k))
+#define SV_STATS_SUMMARY_WORDS(max_k) (4 + 2 * (max_k))
+int spec_verify_stats_accumulate(int32_t batch, int32_t max_k, const int32_t* num_draft,
+                                 const int32_t* accepted_len, uint64_t* stats, void* hip_stream);
+int spec_verify_stats_summary(int32_t max_k, const uint64_t* stats, double* summary, void* hip_stream);
+
+/* ---- draft-length controllers ---------------------------------------------
+ * One controller per sequence slot, fed after each round with (K, A) and
+ * giving the proposal length of the next round.  The ratio a controller sees
+ * is A / max(K, 1) (accepted draft tokens only); a round with A < 0 changes
+ * nothing.  Decisions are taken in float64.
+ *   SV_ADAPT_WINDOW          keep the last `window` ratios; once at least
+ *       `min_samples` are held, their mean (summed oldest first) above
+ *       target + 0.1 lengthens by one, below target - 0.1 shortens by one,
+ *       within [min_k, max_k] (gitcode.csdn.net tutorial, section 5.2
+ *       动态草稿长度策略; the page's defaults are window 100, min_samples 10,
+ *       target 0.7, length 5 in 1..10).
+ *   SV_ADAPT_MULTIPLICATIVE  above target + 0.1 the length L becomes
+ *       min(max_k, int(L (1 + rate))), below target - 0.1
+ *       max(min_k, int(L (1 - rate))); int truncates (same tutorial,
+ *       section 4.4; defaults target 0.7, rate 0.1, lengths 1..5).
+ *   SV_ADAPT_OPTIMAL_K       a = max(ratio, 0.01), k* = floor(ln(1/(1-a))/a)
+ *       (unbounded at a = 1), L becomes min(clamp(k*, 2, 16), max(L, 2));
+ *       min_k, max_k, window and rate are not used ("Speculative Decoding
+ *       在分布式推理中的应用", wmrh.cn, section 三, adapt_draft_length).
+ *
+ * state: device memory owned by the caller, SV_ADAPT_STATE_BYTES(batch,
+ * window) bytes, 16-byte aligned: int32 [batch][4] {length, count, head, 0},
+ * then float64 [batch][window] ratio rings.  spec_verify_adapt_reset sets
+ * every length to init_k and empties the rings (call it first, and again
+ * after changing kind or window); spec_verify_adapt reads num_draft and
+ * accepted_len (device int32 [batch]), updates the state and writes next_k
+ * (device int32 [batch]; also for unchanged lengths).  Sequence b always
+ * uses slot b.  Each call enqueues one kernel on `hip_stream`, allocates
+ * nothing and does not synchronise; SV_ERR_INVALID (nothing enqueued) for a
+ * bad kind, bounds outside 1 <= min_k <= max_k <= SV_ADAPT_MAX_LENGTH,
+ * window outside 1..SV_ADAPT_MAX_WINDOW or min_samples < 1 (window kind),
+ * target or rate outside [0, 1], init_k outside 1..SV_ADAPT_MAX_LENGTH, or a
+ * missing or misaligned buffer. */
+enum { SV_ADAPT_WINDOW = 0, SV_ADAPT_MULTIPLICATIVE = 1, SV_ADAPT_OPTIMAL_K = 2 };
+#define SV_ADAPT_MAX_WINDOW 256
+#define SV_ADAPT_MAX_LENGTH 4096
+#define SV_ADAPT_STATE_BYTES(batch, window) ((int64_t)(batch) * (16 + 8 * (int64_t)(window)))
+typedef struct spec_verify_adapt_args {
+  int32_t batch;
+  int32_t kind;
+  int32_t min_k;
+  int32_t max_k;
+  int32_t window;
+  int32_t min_samples;
+  double target;
+  double rate;
+  const int32_t* num_draft;
+  const int32_t* accepted_len;
+  void* state;
+  int32_t* next_k;
+} spec_verify_adapt_args;
+int spec_verify_adapt_reset(const spec_verify_adapt_args* args, int32_t init_k, void* hip_stream);
+int spec_verify_adapt(const spec_verify_adapt_args* args, void* hip_stream);
+
+/* sizeof(spec_verify_adapt_args) as compiled into the library. */
+int64_t spec_verify_adapt_args_size(void);
+
 /* Library version string. */
 const char* spec_verify_version(void);
 

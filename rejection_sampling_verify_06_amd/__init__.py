@@ -23,9 +23,11 @@ from ._lib import (  # noqa: F401
     SV_ST_BAD_LAYOUT, SV_ST_K_TOO_LARGE, SV_ST_BAD_MODE, SV_ST_BAD_TEMPERATURE,
     SV_ST_NO_DRAFT_LOGITS, SV_ST_BAD_TOKEN, SV_ST_NONFINITE, SV_ST_ZERO_RESIDUAL,
     KERNEL_NAMES, LibraryMissing,
+    SV_ADAPT_WINDOW, SV_ADAPT_MULTIPLICATIVE, SV_ADAPT_OPTIMAL_K,
 )
 
-__all__ = ["Verifier", "VerifyError", "verify", "propose_ngram", "NgramProposer", "LibraryMissing", "KERNEL_NAMES"]
+__all__ = ["Verifier", "VerifyError", "verify", "propose_ngram", "NgramProposer", "AcceptanceStats",
+           "DraftLengthController", "LibraryMissing", "KERNEL_NAMES"]
 
 
 class VerifyError(RuntimeError):
@@ -257,6 +259,79 @@ def propose_ngram(history, offsets, min_n: int = 2, max_n: int = 4, max_tokens: 
     """One-shot N-gram proposals: draft_tokens [B, max_tokens] (-1 padded),
     num_draft [B], match_n [B] (0: no occurrence)."""
     return NgramProposer().run(history, offsets, min_n, max_n, max_tokens)
+
+
+class AcceptanceStats:
+    """Acceptance counters kept on the device (spec_verify_stats_accumulate /
+    spec_verify_stats_summary).  `counters` is int64 storage for the C
+    interface's uint64 words; `add` queues one call's rounds, `summary`
+    queues the rates into a float64 tensor."""
+
+    def __init__(self, max_k: int, device):
+        import torch
+        self._lib = _lib.load()
+        self.max_k = int(max_k)
+        self.counters = torch.zeros(_lib.stats_words(self.max_k), dtype=torch.int64, device=device)
+
+    def reset(self):
+        self.counters.zero_()
+
+    def add(self, num_draft, accepted_len, stream=None):
+        import torch
+        B = int(num_draft.numel())
+        _need(num_draft, "num_draft", (torch.int32,), torch, B, self.counters.device)
+        _need(accepted_len, "accepted_len", (torch.int32,), torch, B, self.counters.device)
+        st = stream if stream is not None else torch.cuda.current_stream()
+        _check(self._lib.spec_verify_stats_accumulate(B, self.max_k, _ptr(num_draft), _ptr(accepted_len),
+                                                      _ptr(self.counters), ctypes.c_void_p(st.cuda_stream)))
+
+    def summary(self, out=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty(_lib.stats_summary_words(self.max_k), dtype=torch.float64, device=self.counters.device)
+        _need(out, "summary", (torch.float64,), torch, _lib.stats_summary_words(self.max_k), self.counters.device)
+        st = stream if stream is not None else torch.cuda.current_stream()
+        _check(self._lib.spec_verify_stats_summary(self.max_k, _ptr(self.counters), _ptr(out),
+                                                   ctypes.c_void_p(st.cuda_stream)))
+        return out
+
+
+class DraftLengthController:
+    """Per-sequence draft-length controllers on the device
+    (spec_verify_adapt_reset / spec_verify_adapt).  `update` takes a round's
+    num_draft and accepted_len and returns the next lengths (int32 [batch])."""
+
+    def __init__(self, batch: int, kind: int = SV_ADAPT_WINDOW, *, min_k: int = 1, max_k: int = 10,
+                 window: int = 100, min_samples: int = 10, target: float = 0.7, rate: float = 0.1,
+                 init_k: int = 5, device=None):
+        import torch
+        self._lib = _lib.load()
+        dev = torch.device("cuda", 0) if device is None else torch.device(device)
+        self.batch = int(batch)
+        nbytes = _lib.adapt_state_bytes(self.batch, window if kind == SV_ADAPT_WINDOW else 0)
+        self.state = torch.empty(max(nbytes, 16) // 8 + 1, dtype=torch.int64, device=dev)
+        self.next_k = torch.empty(self.batch, dtype=torch.int32, device=dev)
+        a = _lib.SpecVerifyAdaptArgs()
+        a.batch, a.kind, a.min_k, a.max_k = self.batch, int(kind), int(min_k), int(max_k)
+        a.window, a.min_samples, a.target, a.rate = int(window), int(min_samples), float(target), float(rate)
+        a.state, a.next_k = _ptr(self.state), _ptr(self.next_k)
+        self._args = a
+        self.reset(init_k)
+
+    def reset(self, init_k: int, stream=None):
+        import torch
+        st = stream if stream is not None else torch.cuda.current_stream()
+        _check(self._lib.spec_verify_adapt_reset(ctypes.byref(self._args), int(init_k),
+                                                 ctypes.c_void_p(st.cuda_stream)))
+
+    def update(self, num_draft, accepted_len, stream=None):
+        import torch
+        _need(num_draft, "num_draft", (torch.int32,), torch, self.batch, self.next_k.device)
+        _need(accepted_len, "accepted_len", (torch.int32,), torch, self.batch, self.next_k.device)
+        self._args.num_draft, self._args.accepted_len = _ptr(num_draft), _ptr(accepted_len)
+        st = stream if stream is not None else torch.cuda.current_stream()
+        _check(self._lib.spec_verify_adapt(ctypes.byref(self._args), ctypes.c_void_p(st.cuda_stream)))
+        return self.next_k
 
 
 def library_loaded_path() -> str:

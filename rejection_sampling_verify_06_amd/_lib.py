@@ -24,10 +24,29 @@ KERNEL_NAMES = ("row_stats", "final", "select")
 SV_NGRAM_MAX_N = 16
 SV_NGRAM_MAX_TOKENS = 128
 
+SV_STATS_MAX_K = 128
+SV_ADAPT_WINDOW, SV_ADAPT_MULTIPLICATIVE, SV_ADAPT_OPTIMAL_K = 0, 1, 2
+SV_ADAPT_MAX_WINDOW = 256
+SV_ADAPT_MAX_LENGTH = 4096
+
+
+def stats_words(max_k: int) -> int:
+    return 8 + 3 * max_k
+
+
+def stats_summary_words(max_k: int) -> int:
+    return 4 + 2 * max_k
+
+
+def adapt_state_bytes(batch: int, window: int) -> int:
+    return batch * (16 + 8 * window)
+
 EXPORTED = (
     "spec_verify_create", "spec_verify_run", "spec_verify_destroy", "spec_verify_last_error",
     "spec_verify_timing_enable", "spec_verify_timing_read", "spec_verify_version",
     "spec_verify_args_size", "spec_verify_ngram_propose", "spec_verify_ngram_args_size",
+    "spec_verify_stats_accumulate", "spec_verify_stats_summary", "spec_verify_adapt_reset", "spec_verify_adapt",
+    "spec_verify_adapt_args_size",
 )
 
 
@@ -71,6 +90,23 @@ class SpecVerifyNgramArgs(ctypes.Structure):
     ]
 
 
+class SpecVerifyAdaptArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("kind", ctypes.c_int32),
+        ("min_k", ctypes.c_int32),
+        ("max_k", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("min_samples", ctypes.c_int32),
+        ("target", ctypes.c_double),
+        ("rate", ctypes.c_double),
+        ("num_draft", ctypes.c_void_p),
+        ("accepted_len", ctypes.c_void_p),
+        ("state", ctypes.c_void_p),
+        ("next_k", ctypes.c_void_p),
+    ]
+
+
 _LIB = None
 
 
@@ -111,10 +147,22 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_ngram_propose.restype = ctypes.c_int
     lib.spec_verify_ngram_args_size.argtypes = []
     lib.spec_verify_ngram_args_size.restype = ctypes.c_int64
+    lib.spec_verify_stats_accumulate.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, P, P]
+    lib.spec_verify_stats_accumulate.restype = ctypes.c_int
+    lib.spec_verify_stats_summary.argtypes = [ctypes.c_int32, P, P, P]
+    lib.spec_verify_stats_summary.restype = ctypes.c_int
+    lib.spec_verify_adapt_reset.argtypes = [ctypes.POINTER(SpecVerifyAdaptArgs), ctypes.c_int32, P]
+    lib.spec_verify_adapt_reset.restype = ctypes.c_int
+    lib.spec_verify_adapt.argtypes = [ctypes.POINTER(SpecVerifyAdaptArgs), P]
+    lib.spec_verify_adapt.restype = ctypes.c_int
+    lib.spec_verify_adapt_args_size.argtypes = []
+    lib.spec_verify_adapt_args_size.restype = ctypes.c_int64
     if lib.spec_verify_args_size() != ctypes.sizeof(SpecVerifyArgs):
         raise RuntimeError("spec_verify_args layout differs between the library and the binding")
     if lib.spec_verify_ngram_args_size() != ctypes.sizeof(SpecVerifyNgramArgs):
         raise RuntimeError("spec_verify_ngram_args layout differs between the library and the binding")
+    if lib.spec_verify_adapt_args_size() != ctypes.sizeof(SpecVerifyAdaptArgs):
+        raise RuntimeError("spec_verify_adapt_args layout differs between the library and the binding")
     _LIB = lib
     return lib
 

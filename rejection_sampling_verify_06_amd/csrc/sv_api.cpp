@@ -360,6 +360,117 @@ int spec_verify_ngram_propose(const spec_verify_ngram_args* a, void* hip_stream)
   return SV_OK;
 }
 
+int spec_verify_stats_accumulate(int32_t batch, int32_t max_k, const int32_t* num_draft,
+                                 const int32_t* accepted_len, uint64_t* stats, void* hip_stream) {
+  if (batch < 0 || max_k < 1 || max_k > SV_STATS_MAX_K) {
+    set_err("spec_verify_stats_accumulate: need batch >= 0 (%d) and 1 <= max_k (%d) <= %d", batch, max_k,
+            SV_STATS_MAX_K);
+    return SV_ERR_INVALID;
+  }
+  if (!stats || (batch > 0 && (!num_draft || !accepted_len))) {
+    set_err("spec_verify_stats_accumulate: stats, num_draft and accepted_len are required");
+    return SV_ERR_INVALID;
+  }
+  static_assert(SV_STATS_MAX_K == sv::kStatsMaxK, "stats positions");
+  static_assert(SV_STATS_WORDS(SV_STATS_MAX_K) == sv::kStatsMaxWords, "stats layout");
+  sv::StatsParams p{};
+  p.B = batch;
+  p.max_k = max_k;
+  p.num_draft = num_draft;
+  p.accepted_len = accepted_len;
+  p.counters = stats;
+  hipError_t e = sv::launch_stats_accumulate(p, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail("stats_accumulate", e);
+  return SV_OK;
+}
+
+int spec_verify_stats_summary(int32_t max_k, const uint64_t* stats, double* summary, void* hip_stream) {
+  if (max_k < 1 || max_k > SV_STATS_MAX_K || !stats || !summary) {
+    set_err("spec_verify_stats_summary: need 1 <= max_k (%d) <= %d and both buffers", max_k, SV_STATS_MAX_K);
+    return SV_ERR_INVALID;
+  }
+  sv::StatsParams p{};
+  p.max_k = max_k;
+  p.counters = const_cast<uint64_t*>(stats);
+  p.summary = summary;
+  hipError_t e = sv::launch_stats_summary(p, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail("stats_summary", e);
+  return SV_OK;
+}
+
+int64_t spec_verify_adapt_args_size(void) { return (int64_t)sizeof(spec_verify_adapt_args); }
+
+static int adapt_params(const spec_verify_adapt_args* a, const char* who, sv::AdaptParams* p) {
+  if (!a) {
+    set_err("%s: args is NULL", who);
+    return SV_ERR_INVALID;
+  }
+  if (a->batch < 0 || a->kind < SV_ADAPT_WINDOW || a->kind > SV_ADAPT_OPTIMAL_K) {
+    set_err("%s: batch %d < 0 or unknown kind %d", who, a->batch, a->kind);
+    return SV_ERR_INVALID;
+  }
+  if (a->kind != SV_ADAPT_OPTIMAL_K && (a->min_k < 1 || a->max_k < a->min_k || a->max_k > SV_ADAPT_MAX_LENGTH)) {
+    set_err("%s: need 1 <= min_k (%d) <= max_k (%d) <= %d", who, a->min_k, a->max_k, SV_ADAPT_MAX_LENGTH);
+    return SV_ERR_INVALID;
+  }
+  if (a->kind == SV_ADAPT_WINDOW &&
+      (a->window < 1 || a->window > SV_ADAPT_MAX_WINDOW || a->min_samples < 1)) {
+    set_err("%s: need 1 <= window (%d) <= %d and min_samples (%d) >= 1", who, a->window, SV_ADAPT_MAX_WINDOW,
+            a->min_samples);
+    return SV_ERR_INVALID;
+  }
+  if (!(a->target >= 0.0 && a->target <= 1.0) || !(a->rate >= 0.0 && a->rate <= 1.0)) {
+    set_err("%s: need target (%g) and rate (%g) in [0, 1]", who, a->target, a->rate);
+    return SV_ERR_INVALID;
+  }
+  if (a->batch > 0 && (!a->state || !a->next_k || ((uintptr_t)a->state & 15))) {
+    set_err("%s: state (16-byte aligned) and next_k are required", who);
+    return SV_ERR_INVALID;
+  }
+  static_assert(SV_ADAPT_MAX_WINDOW == sv::kAdaptMaxWindow, "window limit");
+  p->B = a->batch;
+  p->kind = a->kind;
+  p->min_k = a->min_k;
+  p->max_k = a->max_k;
+  p->window = a->kind == SV_ADAPT_WINDOW ? a->window : 1;
+  p->min_samples = a->min_samples;
+  p->target = a->target;
+  p->rate = a->rate;
+  p->num_draft = a->num_draft;
+  p->accepted_len = a->accepted_len;
+  p->hdr = static_cast<int32_t*>(a->state);
+  p->win = reinterpret_cast<double*>(static_cast<char*>(a->state) + (int64_t)a->batch * 16);
+  p->next_k = a->next_k;
+  return SV_OK;
+}
+
+int spec_verify_adapt_reset(const spec_verify_adapt_args* a, int32_t init_k, void* hip_stream) {
+  sv::AdaptParams p{};
+  int rc = adapt_params(a, "spec_verify_adapt_reset", &p);
+  if (rc != SV_OK) return rc;
+  if (init_k < 1 || init_k > SV_ADAPT_MAX_LENGTH) {
+    set_err("spec_verify_adapt_reset: init_k %d outside 1..%d", init_k, SV_ADAPT_MAX_LENGTH);
+    return SV_ERR_INVALID;
+  }
+  p.init_k = init_k;
+  hipError_t e = sv::launch_adapt_reset(p, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail("adapt_reset", e);
+  return SV_OK;
+}
+
+int spec_verify_adapt(const spec_verify_adapt_args* a, void* hip_stream) {
+  sv::AdaptParams p{};
+  int rc = adapt_params(a, "spec_verify_adapt", &p);
+  if (rc != SV_OK) return rc;
+  if (a->batch > 0 && (!a->num_draft || !a->accepted_len)) {
+    set_err("spec_verify_adapt: num_draft and accepted_len are required");
+    return SV_ERR_INVALID;
+  }
+  hipError_t e = sv::launch_adapt(p, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail("adapt", e);
+  return SV_OK;
+}
+
 int spec_verify_timing_enable(spec_verify_ctx* ctx, int32_t max_calls) {
   if (!ctx || max_calls < 0) {
     set_err("spec_verify_timing_enable: bad arguments");

@@ -115,6 +115,39 @@ struct NgramParams {
 
 hipError_t launch_ngram(const NgramParams& p, hipStream_t st);
 
+// acceptance statistics and draft-length controllers
+constexpr int kStatsMaxK = kMaxK;                       // positions tracked per round
+constexpr int kStatsMaxWords = 8 + 3 * kStatsMaxK;
+constexpr int kAdaptMaxWindow = 256;
+
+struct StatsParams {
+  int B;
+  int max_k;
+  const int32_t* num_draft;
+  const int32_t* accepted_len;
+  uint64_t* counters;          // [8 + 3 max_k], accumulated
+  double* summary;             // [4 + 2 max_k]
+};
+
+struct AdaptParams {
+  int B;
+  int kind;                    // 0 window, 1 multiplicative, 2 optimal-k
+  int min_k, max_k;
+  int window, min_samples;
+  double target, rate;
+  const int32_t* num_draft;
+  const int32_t* accepted_len;
+  int32_t* hdr;                // [B][4]: length, count, head, 0
+  double* win;                 // [B][window]
+  int32_t* next_k;             // [B]
+  int init_k;                  // reset only
+};
+
+hipError_t launch_stats_accumulate(const StatsParams& p, hipStream_t st);
+hipError_t launch_stats_summary(const StatsParams& p, hipStream_t st);
+hipError_t launch_adapt(const AdaptParams& p, hipStream_t st);
+hipError_t launch_adapt_reset(const AdaptParams& p, hipStream_t st);
+
 // The kernels of one verify step, in stream order (select only when
 // nsplit > 1).
 hipError_t launch_row_stats(const Params& p, hipStream_t st);

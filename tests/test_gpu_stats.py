@@ -1,0 +1,166 @@
+"""GPU-vs-oracle parity of the acceptance statistics and the draft-length
+controllers through the C interface.  Counters and lengths are integers and
+must be identical; the summary's rates are single correctly rounded float64
+divisions on both sides and must be bitwise equal (NaN where undefined)."""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import make_config_batch
+
+from . import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_mod():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _rounds(rng, B, max_k, p_bad=0.05):
+    """Random rounds: K in 0..max_k (a few above), A in 0..K, some not verified."""
+    K = rng.integers(0, max_k + 1, B)
+    A = (rng.random(B) * (K + 1)).astype(np.int64)
+    A = np.where(rng.random(B) < 0.3, K, A)                  # many fully accepted rounds
+    bad = rng.random(B) < p_bad
+    A = np.where(bad & (rng.random(B) < 0.5), -1, A)
+    K = np.where(bad & (A >= 0), max_k + 1 + rng.integers(0, 3, B), K)
+    return K.astype(np.int32), A.astype(np.int32)
+
+
+def _dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def _same_doubles(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])
+
+
+@pytest.mark.parametrize("max_k,sizes", [(1, [1, 7]), (8, [256, 300, 2500]), (16, [33]), (128, [1024, 1025, 64]),
+                                         (70, [500])])
+def test_counters_and_summary(torch_mod, max_k, sizes):
+    import rejection_sampling_verify_06_amd as sv
+    rng = np.random.default_rng(100 + max_k)
+    st = sv.AcceptanceStats(max_k, "cuda")
+    ref = np.zeros(8 + 3 * max_k, np.uint64)
+    for B in sizes:
+        gu.log(f"[gpu] stats max_k={max_k} B={B}")
+        K, A = _rounds(rng, B, max_k)
+        st.add(_dev(torch_mod, K), _dev(torch_mod, A))
+        oracle.acceptance_counters(K, A, max_k, into=ref)
+        got = st.counters.cpu().numpy().astype(np.uint64)
+        assert np.array_equal(got, ref), np.nonzero(got != ref)[0][:10]
+        s = st.summary().cpu().numpy()
+        assert _same_doubles(s, oracle.acceptance_summary(ref, max_k))
+    st.reset()
+    assert int(st.counters.abs().sum()) == 0
+
+
+def test_empty_batch_and_fresh_counters(torch_mod):
+    import rejection_sampling_verify_06_amd as sv
+    st = sv.AcceptanceStats(4, "cuda")
+    e = torch_mod.empty(0, dtype=torch_mod.int32, device="cuda")
+    st.add(e, e)
+    assert int(st.counters.abs().sum()) == 0
+    s = st.summary().cpu().numpy()
+    assert np.isnan(s).all()
+
+
+def test_stats_of_a_verify_step(torch_mod):
+    """The counters of the verify step's own outputs, on the same stream."""
+    import rejection_sampling_verify_06_amd as sv
+    b = make_config_batch(3, 0)
+    d = gu.batch_to_device(b, torch_mod)
+    v = sv.Verifier(max_batch=b.batch, max_k=8, max_vocab=b.vocab, device=0)
+    out = v.run(d["target"], d["draft"], d["draft_tokens"], d["num_draft"], d["temperature"], d["mode"],
+                d["seq_ids"], seed=b.seed, vocab=b.vocab)
+    st = sv.AcceptanceStats(8, "cuda")
+    st.add(d["num_draft"], out["accepted_len"])
+    s = st.summary()
+    acc = out["accepted_len"].cpu().numpy()
+    ref = oracle.acceptance_counters(b.num_draft, acc, 8)
+    assert np.array_equal(st.counters.cpu().numpy().astype(np.uint64), ref)
+    assert _same_doubles(s.cpu().numpy(), oracle.acceptance_summary(ref, 8))
+    gu.log(f"      C3 step 0: R={int(ref[0])} D={int(ref[1])} C={int(ref[2])} C/D={s[0].item():.4f} "
+           f"mean length={s[1].item():.4f}")
+    v.close()
+
+
+CTRL_CASES = [
+    ("window", 0, dict(min_k=1, max_k=10, window=100, min_samples=10, target=0.7), 5),
+    ("window small", 0, dict(min_k=2, max_k=6, window=12, min_samples=10, target=0.6), 4),
+    ("window 1", 0, dict(min_k=1, max_k=8, window=1, min_samples=1, target=0.5), 3),
+    ("window max", 0, dict(min_k=1, max_k=16, window=256, min_samples=3, target=0.8), 8),
+    ("multiplicative", 1, dict(min_k=1, max_k=5, target=0.7, rate=0.1), 5),
+    ("multiplicative wide", 1, dict(min_k=1, max_k=40, target=0.5, rate=0.35), 12),
+    ("optimal-k", 2, dict(min_k=1, max_k=16, target=0.7), 16),
+]
+
+
+@pytest.mark.parametrize("name,kind,kw,init_k", CTRL_CASES, ids=[c[0] for c in CTRL_CASES])
+def test_controllers_match_oracle(torch_mod, name, kind, kw, init_k):
+    import rejection_sampling_verify_06_amd as sv
+    rng = np.random.default_rng(sum(map(ord, name)))
+    B, steps = 300, 300
+    gu.log(f"[gpu] controller {name}: B={B} steps={steps}")
+    ctl = sv.DraftLengthController(B, kind, init_k=init_k, device="cuda", **kw)
+    states = [oracle.Controller(init_k) for _ in range(B)]
+    okw = {k: v for k, v in kw.items()}
+    L = np.full(B, init_k, np.int32)
+    # each sequence has its own acceptance probability, drifting over time
+    beta = rng.random(B)
+    for t in range(steps):
+        if t % 50 == 0:
+            beta = np.clip(beta + rng.normal(0, 0.3, B), 0, 1)
+        K = np.minimum(L, 16).astype(np.int32)
+        K = np.where(rng.random(B) < 0.03, 0, K).astype(np.int32)
+        u = rng.random((B, 16))
+        A = np.array([k if (u[j, :k] < beta[j]).all() else int(np.argmin(u[j, :k] < beta[j]))
+                      for j, k in enumerate(K)], np.int32)
+        A = np.where(rng.random(B) < 0.02, -1, A).astype(np.int32)
+        got = ctl.update(_dev(torch_mod, K), _dev(torch_mod, A)).cpu().numpy()
+        want = oracle.adapt_batch(states, K, A, kind, **okw)
+        assert np.array_equal(got, want), (t, np.nonzero(got != want)[0][:5])
+        L = want
+    gu.log(f"      lengths after {steps} rounds: min {L.min()} mean {L.mean():.2f} max {L.max()}")
+
+
+def test_controller_reset_and_small_batches(torch_mod):
+    import rejection_sampling_verify_06_amd as sv
+    kw = dict(min_k=1, max_k=7, window=12, min_samples=10, target=0.7)
+    for B in (1, 3, 5):
+        ctl = sv.DraftLengthController(B, 0, init_k=5, device="cuda", **kw)
+        states = [oracle.Controller(5) for _ in range(B)]
+        K = np.full(B, 4, np.int32)
+        for t in range(14):
+            got = ctl.update(_dev(torch_mod, K), _dev(torch_mod, K)).cpu().numpy()
+            want = oracle.adapt_batch(states, K, K, 0, **kw)
+            assert np.array_equal(got, want)
+        assert (got == 7).all()
+        ctl.reset(3)
+        states = [oracle.Controller(3) for _ in range(B)]
+        A = np.ones(B, np.int32)
+        for t in range(12):
+            got = ctl.update(_dev(torch_mod, K), _dev(torch_mod, A)).cpu().numpy()
+            want = oracle.adapt_batch(states, K, A, 0, **kw)
+            assert np.array_equal(got, want)
+        assert (got == 1).all()
+
+
+def test_bad_arguments_enqueue_nothing(torch_mod):
+    import rejection_sampling_verify_06_amd as sv
+    with pytest.raises(sv.VerifyError):
+        sv.AcceptanceStats(0, "cuda").summary()
+    with pytest.raises(sv.VerifyError):
+        sv.DraftLengthController(4, 0, window=257, device="cuda")
+    with pytest.raises(sv.VerifyError):
+        sv.DraftLengthController(4, 1, min_k=3, max_k=2, device="cuda")
+    with pytest.raises(sv.VerifyError):
+        sv.DraftLengthController(4, 5, device="cuda")
+    with pytest.raises(sv.VerifyError):
+        sv.DraftLengthController(4, 0, target=1.5, device="cuda")
