@@ -332,6 +332,92 @@ def bench_ngram(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_stats(args):
+    """Acceptance statistics + sliding-window controller on C3-shaped rounds:
+    one step adds a call's 256 rounds to the counters and updates every
+    sequence's controller (window 100, filled before timing)."""
+    import torch
+    import rejection_sampling_verify_06_amd as sv
+    from workloads import make_rounds_workload, ROUNDS_WORKLOAD
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sv.library_loaded_path()
+    R = args.rotate or 32
+    max_k, window = 8, 100
+    sets = [make_rounds_workload(i) for i in range(R)]
+    B = len(sets[0][0])
+    dev_sets = [(torch.from_numpy(K).cuda(), torch.from_numpy(A).cuda()) for K, A in sets]
+    stats = sv.AcceptanceStats(max_k, "cuda")
+    ctl = sv.DraftLengthController(B, sv.SV_ADAPT_WINDOW, min_k=1, max_k=10, window=window, min_samples=10,
+                                   target=0.7, init_k=5, device="cuda")
+
+    bound = [(stats.bind(K, A), ctl.bind(K, A)) for K, A in dev_sets]
+
+    def step(i):
+        add, update = bound[i % R]
+        add()
+        update()
+
+    for i in range(window + args.warmup):            # fill the windows, then warm up
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    st = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        add, update = bound[i % R]
+        ev[i][0].record(st)
+        add()
+        ev[i][1].record(st)
+        update()
+        ev[i][2].record(st)
+    torch.cuda.synchronize()
+    stats_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    adapt_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    valid = float(np.mean([(A >= 0).sum() for _, A in sets]))
+    # algorithmic bytes: stats reads (K, A) per round and reads + writes its counters; the controller reads
+    # (K, A), its header and the window entries it sums, and writes the new entry, the header and next_k
+    stats_bytes = 8 * B + 2 * 8 * (8 + 3 * max_k)
+    adapt_bytes = 8 * B + valid * (16 + 8 * (window - 1) + 8 + 16) + 4 * B
+    ach = adapt_bytes / (adapt_ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t1 = time.perf_counter()
+        done = 0
+        states = [oracle.Controller(5) for _ in range(B)]
+        c = np.zeros(8 + 3 * max_k, np.uint64)
+        while time.perf_counter() - t1 < args.cpu_budget:
+            K, A = sets[done % R]
+            oracle.acceptance_counters(K, A, max_k, into=c)
+            oracle.adapt_batch(states, K, A, oracle.WINDOW, min_k=1, max_k=10, window=window, min_samples=10,
+                               target=0.7)
+            done += 1
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(done * B / dt, 1), "unit": "rounds/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} calls of {B} rounds (counters + window controller, windows filling from empty), "
+                         f"{dt:.1f} s, numpy/Python, one process"}
+    line = {
+        "metric": "verify rounds/sec through acceptance statistics + draft-length controller",
+        "value": round(B / (ms_step * 1e-3), 1), "unit": "rounds/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": ROUNDS_WORKLOAD, "rounds_per_call": B, "rotating_input_sets": R},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(ach / PEAK_HBM_GBPS, 6), "traffic": None, "kernel": "k_adapt",
+                     "algorithmic_bytes_per_launch": int(adapt_bytes), "mean_launch_ms": round(adapt_ms, 5)},
+        "cpu_baseline": cpu,
+        "kernel_ms": {"stats_accumulate": round(stats_ms, 5), "adapt": round(adapt_ms, 5)},
+        "stats_bytes_per_launch": int(stats_bytes),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def load_traffic(workload: str, path: str = COUNTERS_FILE, source: str = KERNEL_SOURCE):
     """HBM bytes per launch of the dominant kernel from a committed counter
     summary, or None when it was taken on another kernel source or another
@@ -351,8 +437,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="C3", choices=sorted(WORKLOADS) + ["NG"],
-                    help="C0..C4: the verify step; NG: the N-gram proposer")
+    ap.add_argument("--workload", default="C3", choices=sorted(WORKLOADS) + ["NG", "ST"],
+                    help="C0..C4: the verify step; NG: the N-gram proposer; ST: acceptance statistics and "
+                         "the draft-length controller")
     ap.add_argument("--rotate", type=int, default=None, help="input sets kept resident and cycled")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -376,6 +463,8 @@ def main():
 
     if args.workload == "NG":
         return bench_ngram(args)
+    if args.workload == "ST":
+        return bench_stats(args)
 
     import torch
     import rejection_sampling_verify_06_amd as sv

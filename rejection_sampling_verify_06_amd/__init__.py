@@ -285,6 +285,18 @@ class AcceptanceStats:
         _check(self._lib.spec_verify_stats_accumulate(B, self.max_k, _ptr(num_draft), _ptr(accepted_len),
                                                       _ptr(self.counters), ctypes.c_void_p(st.cuda_stream)))
 
+    def bind(self, num_draft, accepted_len, stream=None):
+        """Check the arguments once and return a callable that only queues
+        the accumulation (for a caller that reuses the same tensors)."""
+        import torch
+        B = int(num_draft.numel())
+        _need(num_draft, "num_draft", (torch.int32,), torch, B, self.counters.device)
+        _need(accepted_len, "accepted_len", (torch.int32,), torch, B, self.counters.device)
+        st = ctypes.c_void_p((stream if stream is not None else torch.cuda.current_stream()).cuda_stream)
+        f, a = self._lib.spec_verify_stats_accumulate, (B, self.max_k, _ptr(num_draft), _ptr(accepted_len),
+                                                       _ptr(self.counters), st)
+        return lambda: _check(f(*a))
+
     def summary(self, out=None, stream=None):
         import torch
         if out is None:
@@ -323,6 +335,19 @@ class DraftLengthController:
         st = stream if stream is not None else torch.cuda.current_stream()
         _check(self._lib.spec_verify_adapt_reset(ctypes.byref(self._args), int(init_k),
                                                  ctypes.c_void_p(st.cuda_stream)))
+
+    def bind(self, num_draft, accepted_len, stream=None):
+        """Check the arguments once and return a callable that only queues
+        the update (for a caller that reuses the same tensors)."""
+        import torch
+        _need(num_draft, "num_draft", (torch.int32,), torch, self.batch, self.next_k.device)
+        _need(accepted_len, "accepted_len", (torch.int32,), torch, self.batch, self.next_k.device)
+        a = _lib.SpecVerifyAdaptArgs()
+        ctypes.pointer(a)[0] = self._args
+        a.num_draft, a.accepted_len = _ptr(num_draft), _ptr(accepted_len)
+        st = ctypes.c_void_p((stream if stream is not None else torch.cuda.current_stream()).cuda_stream)
+        f, ref = self._lib.spec_verify_adapt, ctypes.byref(a)
+        return lambda: _check(f(ref, st))
 
     def update(self, num_draft, accepted_len, stream=None):
         import torch

@@ -56,6 +56,8 @@ __global__ void __launch_bounds__(kStThreads) k_stats_accumulate(StatsParams P) 
   __shared__ uint32_t part[kStWaves][kStatsMaxWords];
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
   const int mk = P.max_k;
+  // the counters' old values are loaded now, so that their latency overlaps the batch's
+  const uint64_t old = t < 8 + 3 * mk ? P.counters[t] : 0;   // 8 + 3 * max_k <= 392 < kStThreads
   uint32_t sR = 0, sD = 0, sC = 0, sCand = 0, sFull = 0, sBad = 0;
   PosAcc pa = {{0, 0}, {0, 0}, {0, 0}};
   for (int b0 = 0; b0 < P.B; b0 += kStThreads) {
@@ -106,10 +108,10 @@ __global__ void __launch_bounds__(kStThreads) k_stats_accumulate(StatsParams P) 
     }
   }
   __syncthreads();
-  for (int c = t; c < 8 + 3 * mk; c += kStThreads) {
-    uint64_t s = 0;
-    for (int v = 0; v < kStWaves; ++v) s += part[v][c];
-    P.counters[c] += s;
+  if (t < 8 + 3 * mk) {
+    uint64_t s = old;
+    for (int v = 0; v < kStWaves; ++v) s += part[v][t];
+    P.counters[t] = s;
   }
 }
 
@@ -153,11 +155,22 @@ __global__ void __launch_bounds__(kAdWaves * kWave) k_adapt(AdaptParams P) {
   const int A = P.accepted_len[b], K = P.num_draft[b];
   int4* hdr = reinterpret_cast<int4*>(P.hdr) + b;
   int4 h = *hdr;                                     // length, count, head, 0
+  // the whole ring is loaded with the header (lane j holds slots j, j + 64, ...),
+  // so no load waits for the header; slots not in use are never used
+  const int W = P.window;
+  double* wb = P.win + (int64_t)b * W;
+  double v[kAdaptMaxWindow / kWave];
+  if (P.kind == 0) {
+#pragma unroll
+    for (int m = 0; m < kAdaptMaxWindow / kWave; ++m) {
+      const int j = lane + m * kWave;
+      v[m] = j < W ? wb[j] : 0.0;
+    }
+  }
   int L = h.x;
   if (A >= 0) {
     const double ratio = (double)A / (double)max(K, 1);
     if (P.kind == 0) {
-      const int W = P.window;
       int count = h.y, head = h.z, slot;
       if (count < W) {                               // append
         slot = head + count;
@@ -167,12 +180,13 @@ __global__ void __launch_bounds__(kAdWaves * kWave) k_adapt(AdaptParams P) {
         slot = head;
         head = head + 1 == W ? 0 : head + 1;
       }
-      double* wb = P.win + (int64_t)b * W;
-      // entries in age order, the new ratio last
-      for (int j = lane; j < count; j += kWave) {
-        int idx = head + j;
-        if (idx >= W) idx -= W;
-        ring[w][j] = idx == slot ? ratio : wb[idx];
+      // entries in age order (age 0 oldest), the new ratio last
+#pragma unroll
+      for (int m = 0; m < kAdaptMaxWindow / kWave; ++m) {
+        const int j = lane + m * kWave;
+        int age = j - head;
+        if (age < 0) age += W;
+        if (j < W && age < count) ring[w][age] = j == slot ? ratio : v[m];
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();

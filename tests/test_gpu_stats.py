@@ -152,6 +152,25 @@ def test_controller_reset_and_small_batches(torch_mod):
         assert (got == 1).all()
 
 
+def test_bound_calls_match_unbound(torch_mod):
+    """bind() queues the same work as add() / update()."""
+    import rejection_sampling_verify_06_amd as sv
+    rng = np.random.default_rng(77)
+    K, A = _rounds(rng, 200, 8, p_bad=0.0)
+    Kd, Ad = _dev(torch_mod, K), _dev(torch_mod, A)
+    s1, s2 = sv.AcceptanceStats(8, "cuda"), sv.AcceptanceStats(8, "cuda")
+    kw = dict(min_k=1, max_k=10, window=20, min_samples=3, target=0.5, init_k=5, device="cuda")
+    c1, c2 = sv.DraftLengthController(200, 0, **kw), sv.DraftLengthController(200, 0, **kw)
+    add, upd = s2.bind(Kd, Ad), c2.bind(Kd, Ad)
+    for _ in range(6):
+        s1.add(Kd, Ad)
+        a = c1.update(Kd, Ad).clone()
+        add()
+        upd()
+        assert torch_mod.equal(a, c2.next_k)
+    assert torch_mod.equal(s1.counters, s2.counters)
+
+
 def test_bad_arguments_enqueue_nothing(torch_mod):
     import rejection_sampling_verify_06_amd as sv
     with pytest.raises(sv.VerifyError):

@@ -1,5 +1,6 @@
 """Seeded synthetic inputs for the batched speculative-decoding verify step
-and for the N-gram proposer that feeds its one-hot mode.
+for the N-gram proposer that feeds its one-hot mode, and verify-round
+outcomes for the acceptance statistics and draft-length controllers.
 
 This package produces the *inputs* of the verify step (logits rows, proposed
 tokens, per-sequence draft lengths, temperatures and modes) and of the
@@ -12,4 +13,5 @@ from .synth import (  # noqa: F401
     MODE_SAMPLE, MODE_GREEDY, MODE_ONEHOT, Batch, CONFIG_NAMES,
     make_config_batch, make_random_batch, bf16_round, bf16_widen,
     config_description, NgramBatch, NGRAM_WORKLOAD, make_ngram_batch, make_ngram_workload,
+    ROUNDS_WORKLOAD, make_rounds_workload,
 )

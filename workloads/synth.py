@@ -400,3 +400,24 @@ def make_ngram_batch(seed: int, B: int = 256, min_len: int = 1024, max_len: int 
 
 def make_ngram_workload(step: int = 0) -> NgramBatch:
     return make_ngram_batch(step, name=NGRAM_WORKLOAD)
+
+
+ROUNDS_WORKLOAD = ("ST: B=256 rounds per call, K ~ U{1..8}, each proposed token accepted with a per-sequence "
+                   "probability beta_s ~ U[0.3, 0.95] up to the first rejection, 2% of rounds not verified; "
+                   "statistics with max_k 8 and the sliding-window controller (window 100, 10 samples, target 0.7, "
+                   "lengths 1..10)")
+
+
+def make_rounds_workload(step: int = 0, B: int = 256, max_k: int = 8):
+    """Verify-round outcomes (num_draft, accepted_len) shaped like the mixed
+    C3 batch: the inputs of the acceptance statistics and the draft-length
+    controllers.  A round's acceptances are drawn directly (independent
+    per-position Bernoulli draws), not computed by a verify step."""
+    rng = np.random.default_rng([3000, step])
+    K = rng.integers(1, max_k + 1, B).astype(np.int32)
+    beta = rng.uniform(0.3, 0.95, B)
+    ok = rng.random((B, max_k)) < beta[:, None]
+    first_no = np.where(ok.all(axis=1), max_k, np.argmin(ok, axis=1))
+    A = np.minimum(first_no, K).astype(np.int32)
+    A[rng.random(B) < 0.02] = -1
+    return K, A
