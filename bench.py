@@ -36,7 +36,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified positions/sec (B·(K+1) over V) + achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
-WORKLOADS = {"C0": 0, "C1": 1, "C2": 2, "C3": 3, "C4": 4}
+WORKLOADS = {"C0": 0, "C1": 1, "C2": 2, "C3": 3, "C4": 4, "C3S": 3}
+STRICT_WORKLOADS = {"C3S"}       # the same batches, every sequence in strict sample-match mode
 NGRAM_ROTATE = 32          # 32 x ~8.6 MB of histories: more than the 256 MB last-level cache
 ROTATE = {0: 64, 1: 64, 2: 6, 3: 2, 4: 6}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "row_stats_counters.json")
@@ -53,6 +54,11 @@ def kernel_source_sha(path: str = KERNEL_SOURCE) -> str:
     lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
     code = "\n".join(ln for ln in lines if ln)
     return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
+def make_workload_batch(workload: str, step: int):
+    from workloads import make_config_batch
+    return make_config_batch(WORKLOADS[workload], step, strict=workload in STRICT_WORKLOADS)
 
 
 def row_bytes(batch) -> dict:
@@ -115,13 +121,12 @@ def to_device(batch, torch):
     )
 
 
-def cpu_baseline(cfg: int, budget_s: float) -> dict:
+def cpu_baseline(workload: str, budget_s: float) -> dict:
     """The CPU oracle as it stands, single process, on the sequences of step 0
     of the same workload, pass after pass with Philox seeds 0, 1, 2, ... (the
     logits stay, the draws change) until about ``budget_s`` seconds are spent."""
     import oracle
-    from workloads import make_config_batch
-    b = make_config_batch(cfg, 0)
+    b = make_workload_batch(workload, 0)
     off_d = np.concatenate(([0], np.cumsum(b.num_draft)[:-1])).astype(np.int64)
     off_t = off_d + np.arange(b.batch)
     done_pos = 0
@@ -163,13 +168,13 @@ def step_traffic(workload: str, ms_step: float):
     return {"hbm_bytes": w["step_hbm_bytes"], "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
-def cpu_baseline_parallel(cfg: int, budget_s: float, workers: int) -> dict:
+def cpu_baseline_parallel(workload: str, budget_s: float, workers: int) -> dict:
     """The same oracle over `workers` processes, each taking every
     workers-th sequence of step 0 pass after pass until the budget is spent.
     Runs in a child interpreter that never touches the GPU."""
     import multiprocessing as mp
     with mp.get_context("fork").Pool(workers) as pool:
-        res = pool.starmap(_oracle_worker, [(cfg, budget_s, w, workers) for w in range(workers)])
+        res = pool.starmap(_oracle_worker, [(workload, budget_s, w, workers) for w in range(workers)])
     pos = sum(r[0] for r in res)
     wall = max(r[1] for r in res)
     return {"value": round(pos / wall, 3), "unit": "positions/s", "cores": workers, "kind": "oracle",
@@ -177,10 +182,9 @@ def cpu_baseline_parallel(cfg: int, budget_s: float, workers: int) -> dict:
                       f"{wall:.1f} s, numpy float64"}
 
 
-def _oracle_worker(cfg, budget_s, w, n):
+def _oracle_worker(workload, budget_s, w, n):
     import oracle
-    from workloads import make_config_batch
-    b = make_config_batch(cfg, 0)
+    b = make_workload_batch(workload, 0)
     off_d = np.concatenate(([0], np.cumsum(b.num_draft)[:-1])).astype(np.int64)
     off_t = off_d + np.arange(b.batch)
     mine = list(range(w, b.batch, n)) or [w % b.batch]
@@ -202,9 +206,9 @@ def _oracle_worker(cfg, budget_s, w, n):
     return done, time.perf_counter() - t0
 
 
-def run_parallel_baseline_child(cfg: int, budget_s: float, workers: int):
+def run_parallel_baseline_child(workload: str, budget_s: float, workers: int):
     import subprocess
-    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-parallel-child", str(cfg),
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-parallel-child", workload,
                         "--cpu-budget", str(budget_s), "--cpu-workers", str(workers)],
                        capture_output=True, text=True, timeout=budget_s * 4 + 120)
     if r.returncode != 0:
@@ -438,14 +442,14 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="C3", choices=sorted(WORKLOADS) + ["NG", "ST"],
-                    help="C0..C4: the verify step; NG: the N-gram proposer; ST: acceptance statistics and "
-                         "the draft-length controller")
+                    help="C0..C4: the verify step; C3S: C3 in strict sample-match mode; NG: the N-gram "
+                         "proposer; ST: acceptance statistics and the draft-length controller")
     ap.add_argument("--rotate", type=int, default=None, help="input sets kept resident and cycled")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1),
                     help="processes for the parallel oracle baseline (0: skip it)")
-    ap.add_argument("--cpu-parallel-child", type=int, default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-parallel-child", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--no-kernel-events", action="store_true", help="time without per-kernel HIP events")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain device copies of 1 GiB (the reference kernel for counter scaling)")
@@ -468,7 +472,7 @@ def main():
 
     import torch
     import rejection_sampling_verify_06_amd as sv
-    from workloads import make_config_batch, config_description, CONFIG_NAMES
+    from workloads import config_description
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -478,7 +482,7 @@ def main():
     R = args.rotate or ROTATE[cfg]
 
     t_gen = time.perf_counter()
-    batches = [make_config_batch(cfg, i) for i in range(R)]
+    batches = [make_workload_batch(args.workload, i) for i in range(R)]
     dev_in = [to_device(b, torch) for b in batches]
     gen_s = time.perf_counter() - t_gen
     desc = config_description(cfg)
@@ -552,15 +556,15 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, args.cpu_budget)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, args.cpu_budget)
     cpu_par = None if (args.no_cpu_baseline or args.cpu_workers < 1) else \
-        run_parallel_baseline_child(cfg, args.cpu_budget, args.cpu_workers)
+        run_parallel_baseline_child(args.workload, args.cpu_budget, args.cpu_workers)
     line = {
         "metric": METRIC, "value": round(float(value), 1), "unit": "positions/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": CONFIG_NAMES[cfg], "batch": desc["batch"], "k": desc["k"],
+        "config": {"workload": batches[0].name, "batch": desc["batch"], "k": desc["k"],
                    "vocab": desc["vocab"], "logits": desc["dtype"], "rotating_input_sets": R,
                    "positions_per_step": round(float(pos), 2)},
         "roofline": roofline,

@@ -29,11 +29,20 @@
  *   SV_GREEDY  strict greedy: accept iff x_i is the argmax of the raw target
  *              logits (lowest index on ties); emit that argmax on a mismatch
  *              and as the bonus.  The temperature is ignored.
+ *   SV_STRICT  sample match ("Speculative Decoding在分布式推理中的应用",
+ *              wmrh.cn, sections 二 and 三): the target draws its own token
+ *              y_i ~ p_i by the inverse CDF with u_i; x_i is accepted iff
+ *              y_i = x_i, and on a mismatch y_A is emitted (it is the draw
+ *              from p_A with x_A removed, at the point u_A*S minus x_A's mass
+ *              when u_A lies above x_A's interval).  All K accepted: bonus
+ *              from p_K as above.  Lossless; the acceptance probability is
+ *              p_i(x_i).  No draft logits are read.
  *
  * Randomness: u_i and the final draw's uniform come from Philox4x32-10
  * (Salmon et al., SC'11) with key = seed and counter = (position, purpose,
  * seq_id, 0); purpose 0 for u_i at positions 0..K-1, purpose 1 for the final
- * draw at position A; u = (word0 >> 8) * 2^-24.  Results are a pure function
+ * draw at position A (SV_STRICT draws its correction with u_A, purpose 0,
+ * and only its bonus with purpose 1); u = (word0 >> 8) * 2^-24.  Results are a pure function
  * of (inputs, seed, seq_ids): any call can be replayed exactly, and a batch
  * split across calls (with global seq_ids) gives the same outputs.
  *
@@ -69,7 +78,7 @@ typedef struct spec_verify_ctx spec_verify_ctx;
 enum { SV_F32 = 0, SV_BF16 = 1 };
 
 /* per-sequence verify mode (values of args->mode[s]) */
-enum { SV_SAMPLE = 0, SV_GREEDY = 1, SV_ONEHOT = 2 };
+enum { SV_SAMPLE = 0, SV_GREEDY = 1, SV_ONEHOT = 2, SV_STRICT = 3 };
 
 /* return codes */
 enum {
@@ -86,15 +95,15 @@ enum {
 enum {
   SV_ST_BAD_LAYOUT = 1,        /* num_draft has a negative entry or does not sum to total_draft (set for every sequence; every output slot is cleared) */
   SV_ST_K_TOO_LARGE = 2,       /* K_s > max_k of the context */
-  SV_ST_BAD_MODE = 4,          /* mode[s] not one of SV_SAMPLE, SV_GREEDY, SV_ONEHOT */
-  SV_ST_BAD_TEMPERATURE = 8,   /* SAMPLE/ONEHOT with temperature not finite or below SV_MIN_TEMPERATURE */
+  SV_ST_BAD_MODE = 4,          /* mode[s] not one of SV_SAMPLE, SV_GREEDY, SV_ONEHOT, SV_STRICT */
+  SV_ST_BAD_TEMPERATURE = 8,   /* SAMPLE/ONEHOT/STRICT with temperature not finite or below SV_MIN_TEMPERATURE */
   SV_ST_NO_DRAFT_LOGITS = 16,  /* SAMPLE sequence with K_s > 0 but draft_logits == NULL */
   SV_ST_BAD_TOKEN = 32,        /* a proposed token outside [0, vocab) */
   SV_ST_NONFINITE = 64,        /* a used logit row holds NaN or +inf, or is entirely -inf */
   SV_ST_ZERO_RESIDUAL = 128    /* the residual had no mass (rounding only); the token was drawn from p_A instead */
 };
 
-/* smallest accepted temperature for SAMPLE/ONEHOT (float32 1e-6) */
+/* smallest accepted temperature for SAMPLE/ONEHOT/STRICT (float32 1e-6) */
 #define SV_MIN_TEMPERATURE 1e-6f
 
 typedef struct spec_verify_args {

@@ -16,11 +16,11 @@ implementation).
 """
 from .philox import philox4x32_10, philox4x32_10_np, u24, verify_uniform, verify_uniforms_np  # noqa: F401
 from .verify import (  # noqa: F401
-    SAMPLE, GREEDY, ONEHOT,
+    SAMPLE, GREEDY, ONEHOT, STRICT,
     ST_BAD_LAYOUT, ST_K_TOO_LARGE, ST_BAD_MODE, ST_BAD_TEMPERATURE, ST_NO_DRAFT_LOGITS,
     ST_BAD_TOKEN, ST_NONFINITE, ST_ZERO_RESIDUAL, ST_ERROR_MASK,
     BAND, BatchResult, SeqResult, softmax, accept_ratio, residual, inverse_cdf, widen,
-    verify_sequence, verify_batch, verify_batch_from,
+    verify_sequence, verify_batch, verify_batch_from, cdf_interval, strict_correction,
 )
 from .compare import CompareReport, compare  # noqa: F401
 from .ngram import ngram_propose, ngram_propose_batch, valid_starts  # noqa: F401

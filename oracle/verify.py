@@ -21,6 +21,9 @@ Sources (page title, then section):
 * [AIG]  "5.2 Draft 模型与无模型方案" (AIInfraGuide): §4.3 (a deterministic
          proposal is the one-hot distribution q(y) = 1 and is verified with
          the same accept/correct rule).
+* [DIST] §二 and §三 also describe a strict check: the target samples its
+         own token at the position and the draft token is accepted iff the
+         two agree; on a mismatch the target's sample is emitted.
 
 Readings where the pages leave a step open (each is a row of the design
 notes):
@@ -39,7 +42,12 @@ notes):
   from p at that position with the same uniform and status bit 128 is set;
 * uniforms: Philox4x32-10, key = seed, counter = (position, purpose, seq_id,
   0); purpose 0 for the acceptance test at positions 0..K-1, purpose 1 for
-  the final draw at position A; u = (word0 >> 8) * 2^-24.
+  the final draw at position A; u = (word0 >> 8) * 2^-24;
+* strict mode: the target's own sample at position i is the inverse-CDF
+  draw from p_i with the acceptance uniform u_i; x_i is accepted iff that
+  draw is x_i; at a mismatch the draw itself is emitted (so the correction
+  uses u_A, purpose 0); all K accepted: the bonus from p_K with purpose 1.
+  No draft logits are used; reported q is 1.
 """
 from __future__ import annotations
 
@@ -51,13 +59,13 @@ import numpy as np
 from .philox import PURPOSE_ACCEPT, PURPOSE_SAMPLE, verify_uniform
 
 # verify modes, as encoded in the library's per-sequence mode input
-SAMPLE, GREEDY, ONEHOT = 0, 1, 2
+SAMPLE, GREEDY, ONEHOT, STRICT = 0, 1, 2, 3
 
 # per-sequence status bits, as defined by the library's C interface
 ST_BAD_LAYOUT = 1         # num_draft negative or not summing to total_draft
 ST_K_TOO_LARGE = 2        # K_s > max_k
-ST_BAD_MODE = 4           # mode not in {SAMPLE, GREEDY, ONEHOT}
-ST_BAD_TEMPERATURE = 8    # SAMPLE/ONEHOT with T not finite or below MIN_TEMPERATURE
+ST_BAD_MODE = 4           # mode not in {SAMPLE, GREEDY, ONEHOT, STRICT}
+ST_BAD_TEMPERATURE = 8    # SAMPLE/ONEHOT/STRICT with T not finite or below MIN_TEMPERATURE
 ST_NO_DRAFT_LOGITS = 16   # SAMPLE sequence with K > 0 but no draft logits given
 ST_BAD_TOKEN = 32         # a proposed token outside [0, V)
 ST_NONFINITE = 64         # NaN, +inf, or an all -inf row among the used rows
@@ -120,6 +128,34 @@ def inverse_cdf(w: np.ndarray, u) -> np.ndarray:
     k = np.searchsorted(C, t, side="right")
     last = int(np.nonzero(w > 0)[0][-1])
     return np.minimum(k, last)
+
+
+def cdf_interval(p: np.ndarray, x: int):
+    """[lo, hi): the part of [0, sum p) that the inverse CDF maps to token x."""
+    C = np.cumsum(p)
+    return (float(C[x - 1]) if x > 0 else 0.0), float(C[x])
+
+
+def strict_correction(p: np.ndarray, x: int, u: float):
+    """Strict mode, after a mismatch at a position with proposal x: the
+    target's own draw y = inverse_cdf(p, u), written as a draw from p with x
+    removed (weights w) at the point t' = t below x's interval and t - p(x)
+    above it, so that y != x by construction.  Returns (w, u') with
+    u' = t' / sum(w).  When u itself lies in x's interval (only when a
+    near-tie is followed down its other branch) t' is the boundary where
+    x's interval was, so that the tokens on both sides of x are candidates."""
+    w = p.copy()
+    w[x] = 0.0
+    lo, hi = cdf_interval(p, x)
+    t = u * float(np.cumsum(p)[-1])
+    if t < lo:
+        tr = t
+    elif t >= hi:
+        tr = t - float(p[x])
+    else:
+        tr = lo
+    Zr = float(np.cumsum(w)[-1])
+    return w, (tr / Zr if Zr > 0 else u)
 
 
 @dataclass
@@ -210,9 +246,9 @@ def verify_sequence(xt: np.ndarray, xd: Optional[np.ndarray], tokens: np.ndarray
     status = 0
     if K > max_k:
         status |= ST_K_TOO_LARGE
-    if mode not in (SAMPLE, GREEDY, ONEHOT):
+    if mode not in (SAMPLE, GREEDY, ONEHOT, STRICT):
         status |= ST_BAD_MODE
-    if mode in (SAMPLE, ONEHOT) and not (np.isfinite(T) and T >= MIN_TEMPERATURE):
+    if mode in (SAMPLE, ONEHOT, STRICT) and not (np.isfinite(T) and T >= MIN_TEMPERATURE):
         status |= ST_BAD_TEMPERATURE
     if mode == SAMPLE and K > 0 and not draft_present:
         status |= ST_NO_DRAFT_LOGITS
@@ -240,6 +276,17 @@ def verify_sequence(xt: np.ndarray, xd: Optional[np.ndarray], tokens: np.ndarray
     for i in range(K):
         if mode == GREEDY:
             acc = tok[i] == int(np.argmax(xt[i]))
+        elif mode == STRICT:
+            # the target's own sample at position i, with the acceptance uniform
+            u = verify_uniform(seed, seq_id, i, PURPOSE_ACCEPT)
+            y = int(inverse_cdf(p[i], u))
+            acc = y == tok[i]
+            res.u_acc.append(u)
+            res.ratios.append(float(p_at[i]))
+            lo, hi = cdf_interval(p[i], tok[i])
+            t = u * float(np.cumsum(p[i])[-1])
+            if p_at[i] > 0 and (abs(t - lo) < BAND or abs(t - hi) < BAND):
+                res.accept_flags.append(i)
         else:
             u = verify_uniform(seed, seq_id, i, PURPOSE_ACCEPT)
             r = accept_ratio(mode, p_at[i], q_at[i])
@@ -260,6 +307,12 @@ def verify_sequence(xt: np.ndarray, xd: Optional[np.ndarray], tokens: np.ndarray
     if mode == GREEDY:
         y = int(np.argmax(xt[A]))
         res.final = FinalDraw(kind="greedy", y=y)
+    elif mode == STRICT and A < K:
+        u = verify_uniform(seed, seq_id, A, PURPOSE_ACCEPT)
+        w, ur = strict_correction(p[A], tok[A], u)
+        res.final, st = _final_from_weights(w, ur, True, p[A])
+        res.final.kind = "strict"
+        res.status |= st
     else:
         u = verify_uniform(seed, seq_id, A, PURPOSE_SAMPLE)
         if A < K:

@@ -19,7 +19,7 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    SV_F32, SV_BF16, SV_SAMPLE, SV_GREEDY, SV_ONEHOT,
+    SV_F32, SV_BF16, SV_SAMPLE, SV_GREEDY, SV_ONEHOT, SV_STRICT,
     SV_ST_BAD_LAYOUT, SV_ST_K_TOO_LARGE, SV_ST_BAD_MODE, SV_ST_BAD_TEMPERATURE,
     SV_ST_NO_DRAFT_LOGITS, SV_ST_BAD_TOKEN, SV_ST_NONFINITE, SV_ST_ZERO_RESIDUAL,
     KERNEL_NAMES, LibraryMissing,

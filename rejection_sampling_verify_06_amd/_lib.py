@@ -8,7 +8,7 @@ from .build import library_path
 
 # values from include/spec_verify.h
 SV_F32, SV_BF16 = 0, 1
-SV_SAMPLE, SV_GREEDY, SV_ONEHOT = 0, 1, 2
+SV_SAMPLE, SV_GREEDY, SV_ONEHOT, SV_STRICT = 0, 1, 2, 3
 SV_OK, SV_ERR_INVALID, SV_ERR_NOMEM, SV_ERR_HIP, SV_ERR_CAPACITY = 0, -1, -2, -3, -4
 SV_ST_BAD_LAYOUT = 1
 SV_ST_K_TOO_LARGE = 2

@@ -24,7 +24,7 @@ struct Partial {
   float m;
   float s;
   int32_t idx;
-  int32_t pad;
+  float b;        // strict-mode target rows: the part of s from tokens below the proposal; else 0
 };
 
 enum FinalKind : int32_t {

@@ -49,7 +49,7 @@ using namespace wave;   // kWave and the DPP reductions and scans (sv_wave.h)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kNV = 8;   // 16-byte vectors per thread per 32 KB chunk
-constexpr int kSample = 0, kGreedy = 1, kOnehot = 2;
+constexpr int kSample = 0, kGreedy = 1, kOnehot = 2, kStrict = 3;
 constexpr int kStBadLayout = 1, kStKTooLarge = 2, kStBadMode = 4, kStBadTemp = 8, kStNoDraft = 16,
               kStBadToken = 32, kStNonfinite = 64, kStZeroResidual = 128;
 constexpr float kMinTemperature = 1e-6f;
@@ -794,10 +794,15 @@ __device__ __forceinline__ void clear_sequence(const Params& P, int s, int off_t
 }
 
 // Block-wide merge of the threads' (max, sum, argmax) and the partial write.
+// xs >= 0 (a strict-mode target row judging token xs): the partial also
+// carries the part of the sum from tokens below xs, summed against the
+// chunk's final maximum.
 template <bool ARG>
-__device__ __forceinline__ void finish_chunk(const Params& P, float m, float sum, int idx, float c, int64_t pidx) {
+__device__ __forceinline__ void finish_chunk(const Params& P, float m, float sum, int idx, float c, int64_t pidx,
+                                             const char* rowp, int bf, int c0, int c1, int xs) {
   __shared__ float s_m[kWaves], s_s[kWaves];
   __shared__ int s_i[kWaves];
+  __shared__ float s_M;
   wave_merge<ARG>(m, sum, idx, c);
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   if (lane == 0) {
@@ -806,11 +811,31 @@ __device__ __forceinline__ void finish_chunk(const Params& P, float m, float sum
     s_i[wv] = idx;
   }
   __syncthreads();
+  float M = s_m[0], S = s_s[0];
+  int I = s_i[0];
   if (threadIdx.x == 0) {
-    float M = s_m[0], S = s_s[0];
-    int I = s_i[0];
     for (int q = 1; q < kWaves; ++q) merge_stats<true>(M, S, I, s_m[q], s_s[q], s_i[q], c);
-    if (pidx >= 0) P.partials[pidx] = Partial{M, S, I, 0};
+    s_M = M;
+  }
+  float below = 0.f;
+  if (xs >= c0 && xs < c1) {                 // block-uniform: the chunk holds the proposal
+    __syncthreads();
+    const float Mb = s_M;
+    const float mc = (Mb == -INFINITY) ? 0.f : Mb * c;
+    float a = 0.f;
+    for (int k = c0 + (int)threadIdx.x; k < xs; k += kThreads) a += fexp2(fmaf(load_logit(rowp, k, bf), c, -mc));
+    a = wave_sum(a);
+    __syncthreads();                          // s_s reused
+    if (lane == 0) s_s[wv] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      below = s_s[0];
+      for (int q = 1; q < kWaves; ++q) below += s_s[q];
+    }
+  }
+  if (threadIdx.x == 0) {
+    if (xs >= 0 && c1 <= xs) below = S;       // the whole chunk lies below the proposal
+    if (pidx >= 0) P.partials[pidx] = Partial{M, S, I, below};
   }
 }
 
@@ -883,6 +908,7 @@ __device__ __forceinline__ void unpack_chunk(const u32x4 (&v)[kNV], float (&f)[k
 struct StatsShared {
   float m[kWaves];
   float s[kWaves];
+  float b[kWaves];
   int i[kWaves];
   Owner own;
   int x;          // token the row judges, or -1
@@ -949,6 +975,7 @@ __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp,
   const float M = fmaxf(fmaxf(sh.m[0], sh.m[1]), fmaxf(sh.m[2], sh.m[3]));
   const float c = row_scale(own.md, own.T);
   const float mc = (M == -INFINITY) ? 0.f : M * c;
+  const int x = __builtin_amdgcn_readfirstlane(sh.x);
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
   for (int k = 0; k < N; k += 4) {
@@ -958,6 +985,25 @@ __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp,
     a3 += fexp2(fmaf(f[k + 3], c, -mc));
   }
   const float sum = wave_sum((a0 + a1) + (a2 + a3));
+  // strict-mode target row whose proposal falls in this chunk (one block per
+  // such row): also the part of the sum from tokens below the proposal.  The
+  // terms are recomputed against an opaque copy of mc, so the compiler cannot
+  // keep the sum's terms alive for this pass (that costs registers in every
+  // block).
+  const bool split = own.md == kStrict && !is_draft && x >= c0 && x < c1;
+  float below = 0.f;
+  if (split) {
+    float mc2 = mc;
+    asm volatile("" : "+v"(mc2));
+    const int rel = x - (c0 + t * VEC);     // element k of this thread is below x iff its offset < rel
+    float bl = 0.f;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const int off = (k / VEC) * kThreads * VEC + (k % VEC);
+      bl += (off < rel) ? fexp2(fmaf(f[k], c, -mc2)) : 0.f;
+    }
+    below = wave_sum(bl);
+  }
   int idx = 0x7FFFFFFF;
   if (own.md == kGreedy && !is_draft) {    // lowest index attaining M
     if (mx == M) {                          // only waves that hold M search
@@ -968,16 +1014,20 @@ __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp,
     idx = wave_min_i(idx);
   }
   const int sb = __builtin_amdgcn_readfirstlane(sh.sb);
-  if (sb >= 0) record_proposal_logit<BF>(P, f, c0, c1, __builtin_amdgcn_readfirstlane(sh.x), sb);
+  if (sb >= 0) record_proposal_logit<BF>(P, f, c0, c1, x, sb);
   if (lane == 0) {
     sh.s[wv] = sum;
+    sh.b[wv] = below;
     sh.i[wv] = idx;
   }
   __syncthreads();
   if (t == 0) {
     const float S = (sh.s[0] + sh.s[1]) + (sh.s[2] + sh.s[3]);
     const int I = min(min(sh.i[0], sh.i[1]), min(sh.i[2], sh.i[3]));
-    if (sb >= 0) P.partials[(int64_t)sb * P.nch_max + chunk] = Partial{M, S, I, 0};
+    float Bl = 0.f;
+    if (split) Bl = (sh.b[0] + sh.b[1]) + (sh.b[2] + sh.b[3]);
+    else if (own.md == kStrict && !is_draft && x >= 0 && c1 <= x) Bl = S;   // the whole chunk is below
+    if (sb >= 0) P.partials[(int64_t)sb * P.nch_max + chunk] = Partial{M, S, I, Bl};
   }
 }
 
@@ -995,14 +1045,15 @@ __device__ __forceinline__ void row_stats_scalar(const Params& P, const char* ro
   }
   const int64_t pidx = sb < 0 ? -1 : (int64_t)sb * P.nch_max + chunk;
   const float c = row_scale(own.md, own.T);
+  const int xs = (own.md == kStrict && !is_draft) ? x : -1;
   float m, sum;
   int idx;
   if (own.md == kGreedy && !is_draft) {
     stats_scalar<true>(rowp, bf, c0, c1, c, m, sum, idx);
-    finish_chunk<true>(P, m, sum, idx, c, pidx);
+    finish_chunk<true>(P, m, sum, idx, c, pidx, rowp, bf, c0, c1, -1);
   } else {
     stats_scalar<false>(rowp, bf, c0, c1, c, m, sum, idx);
-    finish_chunk<false>(P, m, sum, idx, c, pidx);
+    finish_chunk<false>(P, m, sum, idx, c, pidx, rowp, bf, c0, c1, xs);
   }
 }
 
@@ -1059,6 +1110,7 @@ constexpr int kMergeUnroll = 8;       // chunk partials a lane has in flight at 
 struct ScanShared {
   float M[2 * kMaxK + 1];   // per slot: target positions 0..K at 0..K, draft position i at max_k + 1 + i
   float S[2 * kMaxK + 1];
+  float Bl[kMaxK + 1];      // target slots, strict mode: the part of S below the proposal
   int I[2 * kMaxK + 1];
   float X[2 * kMaxK + 1];   // the slot's logit at its proposal
   int tok[kMaxK];
@@ -1081,42 +1133,50 @@ __device__ __forceinline__ void clear_bad_layout(const Params& P, int s) {
 }
 
 // Row statistics from a group of chunk partials folded into a running
-// (M, S, I): M = max of the chunk maxima, S = sum of
-// s_k * exp2(round(m_k*c) - round(M*c)), I = lowest index attaining M.
-// Entries k >= n are ignored.
+// (M, S, I, B): M = max of the chunk maxima, S = sum of
+// s_k * exp2(round(m_k*c) - round(M*c)), I = lowest index attaining M, B the
+// same sum over the chunks' below-proposal parts b_k.  Entries k >= n are
+// ignored.
 __device__ __forceinline__ void merge_group(const Partial (&q)[kMergeUnroll], int n, float c, float& M, float& S,
-                                            int& I) {
+                                            int& I, float& B) {
   float m = -INFINITY;
 #pragma unroll
   for (int k = 0; k < kMergeUnroll; ++k)
     if (k < n) m = fmaxf(m, q[k].m);
   const float mn = fmaxf(M, m);
   const float mnc = (mn == -INFINITY) ? 0.f : mn * c;
-  float sum = (M == -INFINITY) ? S : S * fexp2(M * c - mnc);
+  const float r0 = (M == -INFINITY) ? 1.f : fexp2(M * c - mnc);
+  float sum = (M == -INFINITY) ? S : S * r0;
+  float bsum = (M == -INFINITY) ? B : B * r0;
   int idx = (M == mn) ? I : 0x7FFFFFFF;
 #pragma unroll
   for (int k = 0; k < kMergeUnroll; ++k) {
     if (k < n) {
-      sum += (q[k].m == -INFINITY) ? q[k].s : q[k].s * fexp2(q[k].m * c - mnc);
+      const float r = (q[k].m == -INFINITY) ? 1.f : fexp2(q[k].m * c - mnc);
+      sum += (q[k].m == -INFINITY) ? q[k].s : q[k].s * r;
+      bsum += (q[k].m == -INFINITY) ? q[k].b : q[k].b * r;
       if (q[k].m == mn) idx = min(idx, q[k].idx);
     }
   }
   M = mn;
   S = sum;
   I = idx;
+  B = bsum;
 }
 
 // The whole row from its partials in chunk order, kMergeUnroll loads in
 // flight at a time (indices clamped into the row).
-__device__ __forceinline__ void merge_row(const Partial* pp, int nch, float c, float& M, float& S, int& I) {
+__device__ __forceinline__ void merge_row(const Partial* pp, int nch, float c, float& M, float& S, int& I,
+                                          float& B) {
   M = -INFINITY;
   S = 0.f;
   I = 0x7FFFFFFF;
+  B = 0.f;
   for (int k0 = 0; k0 < nch; k0 += kMergeUnroll) {
     Partial q[kMergeUnroll];
 #pragma unroll
     for (int k = 0; k < kMergeUnroll; ++k) q[k] = pp[min(k0 + k, nch - 1)];
-    merge_group(q, nch - k0, c, M, S, I);
+    merge_group(q, nch - k0, c, M, S, I, B);
   }
 }
 
@@ -1182,8 +1242,8 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
 
   int st = 0;
   if (K > mk) st |= kStKTooLarge;
-  if (md != kSample && md != kGreedy && md != kOnehot) st |= kStBadMode;
-  if ((md == kSample || md == kOnehot) && !(isfinite(T) && T >= kMinTemperature)) st |= kStBadTemp;
+  if (md != kSample && md != kGreedy && md != kOnehot && md != kStrict) st |= kStBadMode;
+  if (md != kGreedy && !(isfinite(T) && T >= kMinTemperature)) st |= kStBadTemp;
   if (md == kSample && K > 0 && P.dft == nullptr) st |= kStNoDraft;
   if (st) {
     if (write) clear_sequence(P, s, off_t, off_d, K, st);
@@ -1197,23 +1257,25 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
   if (fast) {
     const int r = lane / lps;
     const bool used = (r <= K) || (sample && r > mk && r <= mk + K);
-    float M = -INFINITY, S = 0.f;
+    float M = -INFINITY, S = 0.f, B = 0.f;
     int I = 0x7FFFFFFF;
-    merge_group(q, myn, c, M, S, I);
+    merge_group(q, myn, c, M, S, I, B);
     if (lps == 2) {         // chunks 0..7 (even lane) then 8..15 (odd lane), same order in both lanes
       const float M2 = dpp_f<kDppQuadXor1>(0.f, M);
       const float S2 = dpp_f<kDppQuadXor1>(0.f, S);
+      const float B2 = dpp_f<kDppQuadXor1>(0.f, B);
       const int I2 = dpp_i<kDppQuadXor1>(0, I);
-      const float Ma = part ? M2 : M, Sa = part ? S2 : S;
+      const float Ma = part ? M2 : M, Sa = part ? S2 : S, Ba = part ? B2 : B;
       const int Ia = part ? I2 : I;
-      const float Mb = part ? M : M2, Sb = part ? S : S2;
+      const float Mb = part ? M : M2, Sb = part ? S : S2, Bb = part ? B : B2;
       const int Ib = part ? I : I2;
       const float mn = fmaxf(Ma, Mb);
       const float mnc = (mn == -INFINITY) ? 0.f : mn * c;
-      const float sa = (Ma == -INFINITY) ? Sa : Sa * fexp2(Ma * c - mnc);
-      const float sb = (Mb == -INFINITY) ? Sb : Sb * fexp2(Mb * c - mnc);
+      const float ra = (Ma == -INFINITY) ? 1.f : fexp2(Ma * c - mnc);
+      const float rb = (Mb == -INFINITY) ? 1.f : fexp2(Mb * c - mnc);
       M = mn;
-      S = sa + sb;
+      S = Sa * ra + Sb * rb;
+      B = Ba * ra + Bb * rb;
       I = min(Ma == mn ? Ia : 0x7FFFFFFF, Mb == mn ? Ib : 0x7FFFFFFF);
     }
     if (used && part == 0 && r < R) {
@@ -1221,6 +1283,7 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
       sh.S[r] = S;
       sh.I[r] = I;
       sh.X[r] = xv;
+      if (r <= mk) sh.Bl[r] = B;
       bad = !(isfinite(M) && isfinite(S) && S > 0.f);
     }
     if (lane < K) {
@@ -1232,12 +1295,13 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
       const bool used = (r <= K) || (sample && r > mk && r <= mk + K);
       if (!used) continue;
       const int nch = (r > mk) ? P.nch_d : P.nch_t;
-      float M, S;
+      float M, S, B;
       int I;
-      merge_row(P.partials + (sbase + r) * P.nch_max, nch, c, M, S, I);
+      merge_row(P.partials + (sbase + r) * P.nch_max, nch, c, M, S, I, B);
       sh.M[r] = M;
       sh.S[r] = S;
       sh.I[r] = I;
+      if (r <= mk) sh.Bl[r] = B;
       sh.X[r] = P.xval[sbase + r];
       bad |= !(isfinite(M) && isfinite(S) && S > 0.f);
     }
@@ -1271,6 +1335,13 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
       int acc;
       if (md == kGreedy) {
         acc = (sh.tok[i] == sh.I[i]);
+      } else if (md == kStrict) {
+        // accept iff the target's own draw y ~ p_i (inverse CDF, uniform u_i)
+        // lands on the proposal: t = u*S inside [B, B + e) of the proposal
+        const float u = draw_uniform(P, seq_id, (uint32_t)i, 0u);
+        const float e = fexp2(fmaf(sh.X[i], c, -(sh.M[i] * c)));
+        const float t = u * sh.S[i];
+        acc = (t >= sh.Bl[i]) && (t < sh.Bl[i] + e);
       } else {
         const float u = draw_uniform(P, seq_id, (uint32_t)i, 0u);
         const float r = (md == kOnehot) ? p : (qd > 0.f ? fminf(1.f, p / qd) : 0.f);
@@ -1306,6 +1377,19 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
     } else if (md == kOnehot) {
       f.kind = kFinalOnehot;
       f.xhat = sh.tok[A];
+    } else if (md == kStrict) {
+      // the emitted token is the target's own draw y (which missed the
+      // proposal): the draw from p with the proposal removed, at the point
+      // t' = t (below the proposal's interval) or t - e (above it), so the
+      // proposal itself can never come out
+      const float uA = draw_uniform(P, seq_id, (uint32_t)A, 0u);
+      const float e = fexp2(fmaf(sh.X[A], c, -(sh.M[A] * c)));
+      const float t = uA * sh.S[A];
+      const float tr = (t < sh.Bl[A]) ? t : t - e;
+      const float Zr = sh.S[A] - e;
+      f.kind = kFinalOnehot;
+      f.xhat = sh.tok[A];
+      f.u = (Zr > 0.f) ? fminf(fmaxf(tr / Zr, 0.f), 0x1.fffffep-1f) : uA;
     } else {
       f.kind = kFinalResidual;
       f.drow = off_d + A;

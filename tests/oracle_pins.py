@@ -326,3 +326,72 @@ def check_inverse_cdf_convention():
     assert int(ov.inverse_cdf(w, 0.0)) == 1            # zero-mass tokens are never chosen
     assert int(ov.inverse_cdf(w, 2 / 3)) == 3
     assert int(ov.inverse_cdf(w, 1.0)) == 3            # clamp to the last positive weight
+
+
+# ---------------------------------------------------------------------------
+# strict (sample-match) mode ([DIST] §二, §三): accept iff the target's own
+# sample equals the proposal, emit that sample on a mismatch
+# ---------------------------------------------------------------------------
+
+def _page_sample(p, u):
+    """The target's own inverse-CDF sample, written out independently:
+    first k whose inclusive cumulative sum exceeds u * total."""
+    C = np.cumsum(np.asarray(p, np.float64))
+    return np.searchsorted(C, np.asarray(u) * C[-1], side="right")
+
+
+def check_grid_strict(seed=5, V=6):
+    """Over all 2^24 uniforms: the proposal x is accepted exactly on x's
+    interval (probability p(x) to the grid), and for a sample of rejected
+    uniforms the emitted correction is the target's own sample."""
+    rng = np.random.default_rng(seed)
+    p = special.softmax(rng.standard_normal(V) * 1.4)
+    ys = _page_sample(p, GRID)
+    for x in range(V):
+        acc = ys == x
+        assert abs(acc.mean() - p[x]) <= 2.0 ** -24 + 1e-15, (x, acc.mean(), p[x])
+        rej = np.nonzero(~acc)[0]
+        for j in rng.choice(rej, size=min(3000, len(rej)), replace=False):
+            u = float(GRID[j])
+            w, ur = ov.strict_correction(p, x, u)
+            y = int(ov.inverse_cdf(w, ur))
+            assert y == ys[j] and y != x, (x, u, y, ys[j])
+
+
+def check_strict_acceptance_rate(n=40000, V=8, seed=6):
+    """Proposals drawn from q: the first position is accepted with
+    probability sum_x q(x) p(x)."""
+    rng = np.random.default_rng(seed)
+    t = (1.3 * rng.standard_normal((2, V))).astype(np.float32)
+    p = special.softmax(t[0].astype(np.float64))
+    q = special.softmax(rng.standard_normal(V) * 1.3)
+    toks = rng.choice(V, size=n, p=q)
+    res = run_replicated(t, None, None, 1.0, ov.STRICT, n, tokens_per_seq=toks.reshape(n, 1))
+    a = (res.accepted_len == 1).mean()
+    want = float((p * q).sum())
+    assert abs(a - want) < 5 * np.sqrt(want * (1 - want) / n), (a, want)
+
+
+def check_strict_wiring(seed=29, n=300, K=4, V=9):
+    """Each decision of the batch oracle is 'the target's sample at i with
+    the purpose-0 uniform of position i equals x_i', and the correction at A
+    is that same sample (purpose 0 at A, not the final-draw purpose)."""
+    t, _ = _tiny_rows(seed, K, V, scale=1.0)
+    rng = np.random.default_rng(seed)
+    p = [special.softmax(t[i].astype(np.float64) / 0.9) for i in range(K + 1)]
+    toks = np.stack([np.argsort(-p[i])[rng.integers(0, 2, n)] for i in range(K)], axis=1)   # likely tokens
+    res = run_replicated(t, None, None, 0.9, ov.STRICT, n, seed=seed, tokens_per_seq=toks)
+    em = _emitted_matrix(res, K)
+    seen_reject = 0
+    for s in range(n):
+        A = int(res.accepted_len[s])
+        for i in range(A + (1 if A < K else 0)):
+            y = int(_page_sample(p[i], verify_uniform(seed, s, i, PURPOSE_ACCEPT)))
+            assert (y == toks[s, i]) == (i < A), (s, i)
+            if i == A:
+                assert em[s, A] == y
+                seen_reject += 1
+        if A == K:
+            y = int(_page_sample(p[K], verify_uniform(seed, s, K, PURPOSE_SAMPLE)))
+            assert em[s, K] == y
+    assert seen_reject > n // 10

@@ -6,7 +6,7 @@ a CDF boundary); p/q at proposal within 1e-5 absolute; status words equal."""
 import numpy as np
 import pytest
 
-from workloads import (MODE_GREEDY, MODE_ONEHOT, MODE_SAMPLE, Batch, bf16_widen,
+from workloads import (MODE_GREEDY, MODE_ONEHOT, MODE_SAMPLE, MODE_STRICT, Batch, bf16_widen,
                        make_config_batch, make_random_batch)
 from . import gpu_util as gu
 
@@ -62,7 +62,7 @@ def test_tiny_mixed(verifier, torch_mod, seed, B, V, kmax, dtype, ld_pad):
     gu.check_batch(verifier, b, torch_mod, label=f"tiny seed={seed}")
 
 
-@pytest.mark.parametrize("mode", [MODE_SAMPLE, MODE_GREEDY, MODE_ONEHOT])
+@pytest.mark.parametrize("mode", [MODE_SAMPLE, MODE_GREEDY, MODE_ONEHOT, MODE_STRICT])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_single_mode(verifier, torch_mod, mode, dtype):
     b = make_random_batch(100 + mode, B=48, V=5000, kmax=8, dtype=dtype, modes=(mode,))

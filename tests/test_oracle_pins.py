@@ -48,6 +48,22 @@ def test_lossless_onehot_mode():
     pins.check_lossless(T=0.9, mode=ov.ONEHOT, seed=7)
 
 
+def test_lossless_strict_mode():
+    pins.check_lossless(mode=ov.STRICT)
+
+
+def test_grid_exact_strict():
+    pins.check_grid_strict()
+
+
+def test_strict_acceptance_rate():
+    pins.check_strict_acceptance_rate()
+
+
+def test_strict_wiring():
+    pins.check_strict_wiring()
+
+
 def test_k_zero_is_plain_sampling():
     pins.check_k_zero_is_plain_sampling()
 
@@ -166,3 +182,35 @@ def test_plant_onehot_residual_keeps_token(monkeypatch):
     monkeypatch.setattr(ov, "residual", lambda m, p, q, x: p.copy() if m == ov.ONEHOT else real(m, p, q, x))
     with pytest.raises(AssertionError):
         pins.check_grid_onehot()
+
+
+def test_plant_strict_without_remap(monkeypatch):
+    """The correction drawn from p without the proposal at the raw point t
+    (tokens above the proposal shift by one)."""
+    def bad(p, x, u):
+        w = p.copy()
+        w[x] = 0.0
+        return w, u * float(np.cumsum(p)[-1]) / float(np.cumsum(w)[-1])
+    monkeypatch.setattr(ov, "strict_correction", bad)
+    with pytest.raises(AssertionError):
+        pins.check_grid_strict()
+
+
+def test_plant_strict_other_uniform(monkeypatch):
+    """The correction drawn with another uniform than the position's own."""
+    real = ov.strict_correction
+    monkeypatch.setattr(ov, "strict_correction", lambda p, x, u: real(p, x, (u + 0.37) % 1.0))
+    with pytest.raises(AssertionError):
+        pins.check_strict_wiring()
+
+
+def test_plant_strict_as_onehot_rule(monkeypatch):
+    """Strict decisions taken with the one-hot rule u < p(x) (same acceptance
+    probability, different uniforms accept)."""
+    orig = ov.verify_sequence
+
+    def vs(xt, xd, tokens, T, mode, *a, **k):
+        return orig(xt, xd, tokens, T, ov.ONEHOT if mode == ov.STRICT else mode, *a, **k)
+    monkeypatch.setattr(ov, "verify_sequence", vs)
+    with pytest.raises(AssertionError):
+        pins.check_strict_wiring()

@@ -10,7 +10,7 @@ residual sampling), so that the CPU oracle and the HIP library can both be fed
 from it without sharing any of the method's code.
 """
 from .synth import (  # noqa: F401
-    MODE_SAMPLE, MODE_GREEDY, MODE_ONEHOT, Batch, CONFIG_NAMES,
+    MODE_SAMPLE, MODE_GREEDY, MODE_ONEHOT, MODE_STRICT, Batch, CONFIG_NAMES, STRICT_SUFFIX,
     make_config_batch, make_random_batch, bf16_round, bf16_widen,
     config_description, NgramBatch, NGRAM_WORKLOAD, make_ngram_batch, make_ngram_workload,
     ROUNDS_WORKLOAD, make_rounds_workload,

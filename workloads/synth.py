@@ -32,6 +32,7 @@ import numpy as np
 MODE_SAMPLE = 0   # probabilistic accept/correct against draft logits q
 MODE_GREEDY = 1   # accept iff the proposed token is the target argmax
 MODE_ONEHOT = 2   # deterministic proposal: q is one-hot on the proposed token
+MODE_STRICT = 3   # sample match: accept iff the target's own sample equals the proposal
 
 PAD_LOGIT = 30000.0  # value written into row padding (columns >= V)
 
@@ -167,6 +168,7 @@ CONFIG_NAMES = {
     3: "C3: B=256 K~U{1..8} V=152064 bf16 zipf, T~U[0.3,1.2]",
     4: "C4: B=128 K=5 V=128256 bf16 zipf, one-hot half + greedy half",
 }
+STRICT_SUFFIX = "; every sequence in strict sample-match mode, no draft logits"
 
 
 def config_description(cfg: int) -> dict:
@@ -181,7 +183,7 @@ def config_description(cfg: int) -> dict:
 
 
 def make_config_batch(cfg: int, step: int = 0, ld_pad: int = 0,
-                      interleave_modes: bool = False) -> Batch:
+                      interleave_modes: bool = False, strict: bool = False) -> Batch:
     """Batch ``step`` of benchmark workload ``cfg`` (0..4).
 
     C0  B=1, K=4, V=1000, fp32: target ~ N(0, 2^2) i.i.d.; draft = target +
@@ -269,8 +271,11 @@ def make_config_batch(cfg: int, step: int = 0, ld_pad: int = 0,
             rt += 1
 
     ld = V + ld_pad
+    if strict:      # the same proposals, verified by sample match; the draft logits are not needed
+        modes = np.full(B, MODE_STRICT, np.uint8)
+        dft = None
     return Batch(
-        name=CONFIG_NAMES[cfg], vocab=V, dtype=dtype,
+        name=CONFIG_NAMES[cfg] + (STRICT_SUFFIX if strict else ""), vocab=V, dtype=dtype,
         target=_pad(tgt, ld, dtype),
         draft=_pad(dft, ld, dtype) if dft is not None else None,
         num_draft=K, draft_tokens=toks, temperature=T, mode=modes,
