@@ -27,3 +27,4 @@ from .ngram import ngram_propose, ngram_propose_batch, valid_starts  # noqa: F40
 from .stats import (  # noqa: F401
     WINDOW, MULTIPLICATIVE, OPTIMAL_K, Controller, acceptance_counters, acceptance_summary, adapt_step, adapt_batch,
 )
+from .filter import filter_threshold, filtered_softmax, kept_by_definition, topk_threshold  # noqa: F401

@@ -56,6 +56,7 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
+from .filter import filter_threshold, filtered_softmax
 from .philox import PURPOSE_ACCEPT, PURPOSE_SAMPLE, verify_uniform
 
 # verify modes, as encoded in the library's per-sequence mode input
@@ -182,6 +183,9 @@ class SeqResult:
     ratios: List[float] = field(default_factory=list)
     final: Optional[FinalDraw] = None
     forced: Dict[int, bool] = field(default_factory=dict)
+    # top-p near-ties: (row key ("t", i) or ("d", i), an equally valid threshold)
+    filter_alts: List[tuple] = field(default_factory=list)
+    forced_tau: Dict[tuple, float] = field(default_factory=dict)
 
     @property
     def flagged(self) -> bool:
@@ -233,14 +237,18 @@ def _final_from_weights(w: np.ndarray, u: float, z_check: bool, fallback_p: Opti
 
 def verify_sequence(xt: np.ndarray, xd: Optional[np.ndarray], tokens: np.ndarray, T: float, mode: int,
                     seq_id: int, seed: int, vocab: int, max_k: int, draft_present: bool,
-                    force: Optional[Dict[int, bool]] = None) -> SeqResult:
+                    force: Optional[Dict[int, bool]] = None, top_k: int = 0, top_p: float = 1.0,
+                    force_tau: Optional[Dict[tuple, float]] = None) -> SeqResult:
     """Verify one sequence.
 
     xt: [K+1, V] float64 target logits (row i judges draft slot i, row K is
         the bonus distribution); xd: [K, V] float64 draft logits or None;
     tokens: the K proposed token ids.  ``force`` maps a position to an
     accept decision that overrides the uniform test there (used only to
-    follow the other branch of a near-tie)."""
+    follow the other branch of a near-tie).  ``top_k`` / ``top_p`` filter
+    every used row (oracle/filter.py); ``force_tau`` replaces a row's
+    threshold by a recorded alternative (the other side of a top-p
+    near-tie)."""
     K = int(tokens.shape[0])
     force = force or {}
     status = 0
@@ -262,14 +270,25 @@ def verify_sequence(xt: np.ndarray, xd: Optional[np.ndarray], tokens: np.ndarray
         return _error_result(K, ST_NONFINITE)
 
     T_eff = float(T) if mode != GREEDY else 1.0
-    p = [softmax(xt[i], T_eff) for i in range(K + 1)]
-    q = [softmax(xd[i], T_eff) for i in range(K)] if mode == SAMPLE else None
+    force_tau = force_tau or {}
+    alts: List[tuple] = []
+    filtering = mode != GREEDY and ((0 < int(top_k) < vocab) or (top_p < 1.0))
+
+    def row_dist(x, key):
+        if not filtering:
+            return softmax(x, T_eff)
+        tau, al = filter_threshold(x, T_eff, int(top_k), float(top_p))
+        alts.extend((key, a) for a in al)
+        return filtered_softmax(x, T_eff, force_tau.get(key, tau))
+
+    p = [row_dist(xt[i], ("t", i)) for i in range(K + 1)]
+    q = [row_dist(xd[i], ("d", i)) for i in range(K)] if mode == SAMPLE else None
     tok = [int(t) for t in tokens]
     p_at = np.array([p[i][tok[i]] for i in range(K)], dtype=np.float64)
     q_at = np.array([q[i][tok[i]] for i in range(K)] if mode == SAMPLE else [1.0] * K, dtype=np.float64)
 
     res = SeqResult(status=0, A=K, emitted=np.full(K + 1, -1, np.int32), p_at=p_at, q_at=q_at,
-                    forced=dict(force))
+                    forced=dict(force), filter_alts=alts, forced_tau=dict(force_tau))
 
     # left-to-right scan, stopping at the first rejection ([DM] algorithm box)
     A = K
@@ -337,12 +356,13 @@ class BatchResult:
     layout_ok: bool
     _ctx: dict = field(default_factory=dict, repr=False)
 
-    def rerun(self, s: int, force: Dict[int, bool]) -> SeqResult:
-        """Re-verify sequence s with some accept decisions forced."""
-        return _verify_one(self._ctx, s, force)
+    def rerun(self, s: int, force: Dict[int, bool], force_tau: Optional[Dict[tuple, float]] = None) -> SeqResult:
+        """Re-verify sequence s with some accept decisions (and filter
+        thresholds) forced."""
+        return _verify_one(self._ctx, s, force, force_tau)
 
 
-def _verify_one(ctx: dict, s: int, force=None) -> SeqResult:
+def _verify_one(ctx: dict, s: int, force=None, force_tau=None) -> SeqResult:
     K = int(ctx["num_draft"][s])
     ot, od = int(ctx["off_t"][s]), int(ctx["off_d"][s])
     V, dtype = ctx["vocab"], ctx["dtype"]
@@ -350,17 +370,22 @@ def _verify_one(ctx: dict, s: int, force=None) -> SeqResult:
     draft = ctx["draft"]
     mode = int(ctx["mode"][s])
     xd = widen(draft[od:od + K, :V], dtype) if (draft is not None and mode == SAMPLE) else None
+    tk = ctx["top_k"]
+    tp = ctx["top_p"]
     return verify_sequence(xt, xd, ctx["draft_tokens"][od:od + K], float(ctx["temperature"][s]), mode,
-                           int(ctx["seq_ids"][s]), ctx["seed"], V, ctx["max_k"], draft is not None, force)
+                           int(ctx["seq_ids"][s]), ctx["seed"], V, ctx["max_k"], draft is not None, force,
+                           top_k=0 if tk is None else int(tk[s]), top_p=1.0 if tp is None else float(tp[s]),
+                           force_tau=force_tau)
 
 
 def verify_batch(*, target, draft, dtype: str, vocab: int, num_draft, draft_tokens, temperature,
                  mode=None, seq_ids=None, seed: int = 0, max_k: int = 64,
-                 total_draft: Optional[int] = None) -> BatchResult:
+                 total_draft: Optional[int] = None, top_k=None, top_p=None) -> BatchResult:
     """Verify a packed ragged batch (layout as in the library's C interface:
     sequence s owns target rows off_t[s] .. off_t[s]+K_s with
     off_t[s] = sum_{j<s}(K_j+1), and draft rows / tokens off_d[s] ..
-    off_d[s]+K_s-1 with off_d[s] = sum_{j<s} K_j)."""
+    off_d[s]+K_s-1 with off_d[s] = sum_{j<s} K_j).  top_k (int [B]) and
+    top_p (float32 [B]) filter every used row of a sequence; None: off."""
     num_draft = np.asarray(num_draft, dtype=np.int64)
     B = int(num_draft.shape[0])
     draft_tokens = np.asarray(draft_tokens, dtype=np.int64)
@@ -385,7 +410,9 @@ def verify_batch(*, target, draft, dtype: str, vocab: int, num_draft, draft_toke
     off_t = off_d + np.arange(B, dtype=np.int64)
     ctx = dict(target=target, draft=draft, dtype=dtype, vocab=int(vocab), num_draft=num_draft,
                draft_tokens=draft_tokens, temperature=temperature, mode=mode, seq_ids=seq_ids,
-               seed=int(seed), max_k=int(max_k), off_t=off_t, off_d=off_d)
+               seed=int(seed), max_k=int(max_k), off_t=off_t, off_d=off_d,
+               top_k=None if top_k is None else np.asarray(top_k, np.int64),
+               top_p=None if top_p is None else np.asarray(top_p, np.float32).astype(np.float64))
     seqs: List[Optional[SeqResult]] = []
     for s in range(B):
         r = _verify_one(ctx, s)
@@ -406,4 +433,5 @@ def verify_batch_from(batch, max_k: int = 64) -> BatchResult:
     return verify_batch(target=batch.target, draft=batch.draft, dtype=batch.dtype, vocab=batch.vocab,
                         num_draft=batch.num_draft, draft_tokens=batch.draft_tokens,
                         temperature=batch.temperature, mode=batch.mode, seq_ids=batch.seq_ids,
-                        seed=batch.seed, max_k=max_k)
+                        seed=batch.seed, max_k=max_k, top_k=getattr(batch, "top_k", None),
+                        top_p=getattr(batch, "top_p", None))

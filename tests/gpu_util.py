@@ -65,7 +65,7 @@ def oracle_for(batch, max_k, draft=None, dtype=None, total_draft=None):
                                dtype=dtype or batch.dtype, vocab=batch.vocab, num_draft=batch.num_draft,
                                draft_tokens=batch.draft_tokens, temperature=batch.temperature,
                                mode=batch.mode, seq_ids=batch.seq_ids, seed=batch.seed, max_k=max_k,
-                               total_draft=total_draft)
+                               total_draft=total_draft, top_k=batch.top_k, top_p=batch.top_p)
 
 
 def compare(ref, out, strict_band=False):

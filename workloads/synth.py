@@ -62,6 +62,8 @@ class Batch:
     mode: np.ndarray                # uint8 [B]
     seq_ids: np.ndarray             # uint32 [B]
     seed: int                       # Philox key (64-bit)
+    top_k: Optional[np.ndarray] = None   # int32 [B] (top-k filter; <= 0 off) or None
+    top_p: Optional[np.ndarray] = None   # float32 [B] (nucleus filter; >= 1 off) or None
 
     @property
     def batch(self) -> int:
