@@ -46,6 +46,18 @@
  * of (inputs, seed, seq_ids): any call can be replayed exactly, and a batch
  * split across calls (with global seq_ids) gives the same outputs.
  *
+ * Filters (top_k / top_p, optional): top-k and nucleus rejection sampling
+ * keep the target's distribution ("Draft Model（草稿模型）", compassingai.com,
+ * 常见误读纠偏 误读 4; gitcode.csdn.net tutorial, section 5.4): each used row
+ * of a filtered SAMPLE, ONEHOT or STRICT sequence (target and draft alike)
+ * keeps the tokens with logit >= tau and is renormalised before the rule
+ * above; GREEDY ignores the filter.  top-k: tau is the k-th largest logit
+ * (ties at it all kept).  top-p, after top-k: a token is kept iff the mass of
+ * the strictly larger tokens is below p (the largest logit always kept).
+ * The output then follows the filtered target distribution.  A filtered
+ * call runs one more kernel (one block per used row of a filtered sequence)
+ * that reads those rows again.
+ *
  * Final draw: inverse CDF over the unnormalised weights w (residual, one-hot
  * residual or p_K): t = u * sum(w), emit the first token k whose inclusive
  * prefix sum exceeds t; tokens with w = 0 are never emitted.
@@ -127,6 +139,8 @@ typedef struct spec_verify_args {
   float* p_at_proposal;        /* device out, [total_draft] or NULL: p_i(x_i) for every i < K_s (T = 1 for GREEDY) */
   float* q_at_proposal;        /* device out, [total_draft] or NULL: q_i(x_i); 1.0 for ONEHOT and GREEDY */
   int32_t* status;             /* device out, [B] or NULL: SV_ST_* bits */
+  const int32_t* top_k;        /* device, [B], or NULL: top-k filter per sequence (<= 0 or >= vocab: off) */
+  const float* top_p;          /* device, [B], or NULL: top-p filter per sequence (>= 1 or NaN: off) */
 } spec_verify_args;
 
 /* Create a context on HIP device `device` for batches of at most max_batch
@@ -164,9 +178,9 @@ const char* spec_verify_last_error(void);
  * never inside run).  spec_verify_timing_read waits for those events and
  * returns the number of recorded calls and, per slot, the summed elapsed
  * milliseconds (ms_per_kernel has SV_NUM_KERNELS entries: row statistics,
- * final, select; a slot whose kernel was not launched reads about 0), then
- * resets the record. */
-#define SV_NUM_KERNELS 3
+ * filter, final, select; a slot whose kernel was not launched reads about
+ * 0), then resets the record. */
+#define SV_NUM_KERNELS 4
 int spec_verify_timing_enable(spec_verify_ctx* ctx, int32_t max_calls);
 int spec_verify_timing_read(spec_verify_ctx* ctx, int32_t* calls, double* ms_per_kernel);
 

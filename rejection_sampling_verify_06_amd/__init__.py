@@ -108,7 +108,7 @@ class Verifier:
     # -- the step -------------------------------------------------------------
     def build_args(self, target, draft, draft_tokens, num_draft, temperature=None, mode=None, seq_ids=None,
                    seed: int = 0, out: Optional[dict] = None, vocab: Optional[int] = None,
-                   total_draft: Optional[int] = None) -> "_lib.SpecVerifyArgs":
+                   total_draft: Optional[int] = None, top_k=None, top_p=None) -> "_lib.SpecVerifyArgs":
         """Check shapes and pack the argument struct (no device work)."""
         torch = self._torch
         dev = torch.device("cuda", self.device)
@@ -131,6 +131,8 @@ class Verifier:
         _need(temperature, "temperature", (torch.float32,), torch, B, dev)
         _need(mode, "mode", (torch.uint8,), torch, B, dev)
         _need(seq_ids, "seq_ids", (torch.int32, getattr(torch, "uint32", torch.int32)), torch, B, dev)
+        _need(top_k, "top_k", (torch.int32,), torch, B, dev)
+        _need(top_p, "top_p", (torch.float32,), torch, B, dev)
         if out is None:
             raise ValueError("out is required (see make_outputs)")
         _need(out["accepted_len"], "accepted_len", (torch.int32,), torch, B, dev)
@@ -159,6 +161,8 @@ class Verifier:
         a.p_at_proposal = _ptr(out.get("p_at"))
         a.q_at_proposal = _ptr(out.get("q_at"))
         a.status = _ptr(out.get("status"))
+        a.top_k = _ptr(top_k)
+        a.top_p = _ptr(top_p)
         return a
 
     def run_args(self, args: "_lib.SpecVerifyArgs", stream=None):
@@ -169,12 +173,13 @@ class Verifier:
 
     def run(self, target, draft, draft_tokens, num_draft, temperature=None, mode=None, seq_ids=None,
             seed: int = 0, out: Optional[dict] = None, want_pq: bool = True, want_status: bool = True,
-            vocab: Optional[int] = None, total_draft: Optional[int] = None, stream=None) -> dict:
+            vocab: Optional[int] = None, total_draft: Optional[int] = None, stream=None,
+            top_k=None, top_p=None) -> dict:
         if out is None:
             T = int(draft_tokens.numel()) if total_draft is None else int(total_draft)
             out = self.make_outputs(int(num_draft.numel()), T, want_pq, want_status)
         args = self.build_args(target, draft, draft_tokens, num_draft, temperature, mode, seq_ids, seed, out,
-                               vocab, total_draft)
+                               vocab, total_draft, top_k, top_p)
         self.run_args(args, stream)
         return out
 

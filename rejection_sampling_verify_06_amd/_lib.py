@@ -18,8 +18,8 @@ SV_ST_NO_DRAFT_LOGITS = 16
 SV_ST_BAD_TOKEN = 32
 SV_ST_NONFINITE = 64
 SV_ST_ZERO_RESIDUAL = 128
-SV_NUM_KERNELS = 3
-KERNEL_NAMES = ("row_stats", "final", "select")
+SV_NUM_KERNELS = 4
+KERNEL_NAMES = ("row_stats", "filter", "final", "select")
 
 SV_NGRAM_MAX_N = 16
 SV_NGRAM_MAX_TOKENS = 128
@@ -72,6 +72,8 @@ class SpecVerifyArgs(ctypes.Structure):
         ("p_at_proposal", ctypes.c_void_p),
         ("q_at_proposal", ctypes.c_void_p),
         ("status", ctypes.c_void_p),
+        ("top_k", ctypes.c_void_p),
+        ("top_p", ctypes.c_void_p),
     ]
 
 

@@ -64,6 +64,7 @@ struct spec_verify_ctx {
   size_t bytes = 0;
   sv::Partial* partials = nullptr;
   float* xval = nullptr;
+  float* tau = nullptr;
   int32_t* ptok = nullptr;
   sv::SeqFinal* fin = nullptr;
   float* tilesum = nullptr;
@@ -131,6 +132,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
   size_t off = 0;
   const size_t o_part = off;   off = align_up(off + sizeof(sv::Partial) * c->max_rows * c->max_nch, 256);
   const size_t o_xval = off;   off = align_up(off + sizeof(float) * c->max_rows, 256);
+  const size_t o_tau = off;    off = align_up(off + sizeof(float) * c->max_rows, 256);
   const size_t o_ptok = off;   off = align_up(off + sizeof(int32_t) * (size_t)max_batch * max_k, 256);
   const size_t o_fin = off;    off = align_up(off + sizeof(sv::SeqFinal) * max_batch, 256);
   const size_t o_tile = off;   off = align_up(off + sizeof(float) * (size_t)max_batch * c->max_tiles, 256);
@@ -153,6 +155,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
   char* b = (char*)c->mem;
   c->partials = (sv::Partial*)(b + o_part);
   c->xval = (float*)(b + o_xval);
+  c->tau = (float*)(b + o_tau);
   c->ptok = (int32_t*)(b + o_ptok);
   c->fin = (sv::SeqFinal*)(b + o_fin);
   c->tilesum = (float*)(b + o_tile);
@@ -274,6 +277,9 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
   p.status = a->status;
   p.partials = ctx->partials;
   p.xval = ctx->xval;
+  p.tau = ctx->tau;
+  p.top_k = a->top_k;
+  p.top_p = a->top_p;
   p.ptok = ctx->ptok;
   p.fin = ctx->fin;
   p.tilesum = ctx->tilesum;
@@ -305,8 +311,9 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
   const bool timed = ctx->timing_used < ctx->timing_cap;
   hipEvent_t* ev = timed ? &ctx->events[(size_t)ctx->timing_used * (SV_NUM_KERNELS + 1)] : nullptr;
   typedef hipError_t (*Launch)(const sv::Params&, hipStream_t);
-  static const Launch kLaunch[SV_NUM_KERNELS] = {sv::launch_row_stats, sv::launch_final, sv::launch_select};
-  static const char* kName[SV_NUM_KERNELS] = {"row_stats", "final", "select"};
+  static const Launch kLaunch[SV_NUM_KERNELS] = {sv::launch_row_stats, sv::launch_filter, sv::launch_final,
+                                                 sv::launch_select};
+  static const char* kName[SV_NUM_KERNELS] = {"row_stats", "filter", "final", "select"};
   if (timed && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail("hipEventRecord", e);
   for (int k = 0; k < SV_NUM_KERNELS; ++k) {
     if ((e = kLaunch[k](p, st)) != hipSuccess) return hip_fail(kName[k], e);

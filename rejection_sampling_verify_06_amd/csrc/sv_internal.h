@@ -43,13 +43,14 @@ struct SeqFinal {
   float mct;          // round(M_t * c) of target row A
   float mcd;          // round(M_d * c) of draft row A
   float rq;           // S_t / S_d (residual weights are S_t * max(0, p - q))
-  float pad0;
+  float taut;         // filter threshold of target row A (-inf: no filter); tokens below it weigh 0
   float c;
   float u;            // uniform of the final draw
   int32_t xhat;       // proposed token at A (kFinalOnehot)
   int32_t emit_pos;   // slot of the final token in emitted_tokens
   int32_t s;
-  int32_t pad[3];
+  float taud;         // filter threshold of draft row A
+  int32_t pad[2];
 };
 
 struct Params {
@@ -95,6 +96,9 @@ struct Params {
   int32_t nsplit;     // final-kernel blocks per sequence
   int32_t slots;      // 2 * max_k + 1 slots per sequence
   int32_t nch_max;    // max(nch_t, nch_d): partials per slot
+  const int32_t* top_k;   // [B] or NULL: top-k filter (<= 0 or >= V: off)
+  const float* top_p;     // [B] or NULL: top-p filter (>= 1 or NaN: off)
+  float* tau;             // per slot: the filter threshold (written only for filtered sequences)
 };
 
 // N-gram proposer (sv_ngram.hip).
@@ -151,6 +155,7 @@ hipError_t launch_adapt_reset(const AdaptParams& p, hipStream_t st);
 // The kernels of one verify step, in stream order (select only when
 // nsplit > 1).
 hipError_t launch_row_stats(const Params& p, hipStream_t st);
+hipError_t launch_filter(const Params& p, hipStream_t st);
 hipError_t launch_final(const Params& p, hipStream_t st);
 hipError_t launch_select(const Params& p, hipStream_t st);
 

@@ -364,9 +364,10 @@ constexpr int tile_unroll() { return KIND == kFinalResidual ? 2 : (BF ? 8 : 4); 
 // weight is max(0, e_x - (S_t/S_d) e_y) = S_t max(0, p - q), formed with a
 // single rounding; bonus and one-hot weights are e_x = S_t p.
 __device__ __forceinline__ float final_weight(int kind, float x, float y, int k, const SeqFinal& f) {
-  const float ex = fexp2(fmaf(x, f.c, -f.mct));
+  // tokens below a row's filter threshold weigh 0 (the threshold is -inf without a filter)
+  const float ex = (x >= f.taut) ? fexp2(fmaf(x, f.c, -f.mct)) : 0.f;
   if (kind == kFinalResidual) {
-    const float ey = fexp2(fmaf(y, f.c, -f.mcd));
+    const float ey = (y >= f.taud) ? fexp2(fmaf(y, f.c, -f.mcd)) : 0.f;
     return fmaxf(fmaf(-f.rq, ey, ex), 0.f);
   }
   if (kind == kFinalOnehot && k == f.xhat) return 0.f;
@@ -751,7 +752,8 @@ __device__ __forceinline__ void pick_chunk(const Params& P, const SeqFinal& f, i
   const Partial* pp = P.partials + sb * P.nch_max;
   const bool onehot = kind == kFinalOnehot;
   const int xchunk = onehot ? f.xhat / P.ce_t : -1;
-  const float px = onehot ? fexp2(fmaf(P.xval[sb], f.c, -f.mct)) : 0.f;
+  const float xv = onehot ? P.xval[sb] : 0.f;
+  const float px = (onehot && xv >= f.taut) ? fexp2(fmaf(xv, f.c, -f.mct)) : 0.f;
   for (int k = lane; k < P.nch_t; k += kWave) {
     const Partial q = pp[k];
     float z = (q.m == -INFINITY) ? 0.f : q.s * fexp2(q.m * f.c - f.mct);
@@ -1113,6 +1115,7 @@ struct ScanShared {
   float Bl[kMaxK + 1];      // target slots, strict mode: the part of S below the proposal
   int I[2 * kMaxK + 1];
   float X[2 * kMaxK + 1];   // the slot's logit at its proposal
+  float Tau[2 * kMaxK + 1]; // the slot's filter threshold (-inf: no filter)
   int tok[kMaxK];
 };
 
@@ -1202,8 +1205,10 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
   const int md = P.mode[s];
   const float T = P.temperature[s];
   const uint32_t seq_id = P.seq_ids[s];
+  const int topk = P.top_k ? P.top_k[s] : 0;
+  const float topp = P.top_p ? P.top_p[s] : 1.f;
   Partial q[kMergeUnroll];
-  float xv = 0.f;
+  float xv = 0.f, tv = -INFINITY;
   int tk = 0;
   const int myslot = min(lane / lps, R - 1);
   const int part = lane % lps;                 // which 8 chunks of the slot
@@ -1214,6 +1219,7 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
 #pragma unroll
     for (int k = 0; k < kMergeUnroll; ++k) q[k] = pp[min(k, max(myn - 1, 0))];
     xv = P.xval[sbase + myslot];
+    tv = P.tau[sbase + myslot];     // meaningful only for a filtered sequence (selected below)
     tk = P.ptok[(int64_t)s * mk + min(lane, mk - 1)];
   }
   // layout sums in 32 bits: a count outside 0..kLayoutKMax cannot belong to a
@@ -1251,6 +1257,8 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
   }
   const float c = (md == kGreedy) ? kLog2e : kLog2e / T;
   const bool sample = md == kSample;
+  // top-k / top-p: the filter kernel rewrote this sequence's partials and thresholds
+  const bool filt = md != kGreedy && ((topk > 0 && topk < P.V) || topp < 1.f);
 
   // ---- each used slot's statistics (lane r: slot r), the proposal tokens ----
   int bad = 0, badtok = 0;
@@ -1283,6 +1291,7 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
       sh.S[r] = S;
       sh.I[r] = I;
       sh.X[r] = xv;
+      sh.Tau[r] = filt ? tv : -INFINITY;
       if (r <= mk) sh.Bl[r] = B;
       bad = !(isfinite(M) && isfinite(S) && S > 0.f);
     }
@@ -1303,6 +1312,7 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
       sh.I[r] = I;
       if (r <= mk) sh.Bl[r] = B;
       sh.X[r] = P.xval[sbase + r];
+      sh.Tau[r] = filt ? P.tau[sbase + r] : -INFINITY;
       bad |= !(isfinite(M) && isfinite(S) && S > 0.f);
     }
     for (int i = lane; i < K; i += kScanThreads) {
@@ -1330,8 +1340,9 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
     int reject = 0;
     if (i < K) {
       const int d = mk + 1 + i;
-      const float p = fexp2(fmaf(sh.X[i], c, -(sh.M[i] * c))) / sh.S[i];
-      const float qd = sample ? fexp2(fmaf(sh.X[d], c, -(sh.M[d] * c))) / sh.S[d] : 1.f;
+      const float p = (sh.X[i] >= sh.Tau[i]) ? fexp2(fmaf(sh.X[i], c, -(sh.M[i] * c))) / sh.S[i] : 0.f;
+      const float qd =
+          sample ? ((sh.X[d] >= sh.Tau[d]) ? fexp2(fmaf(sh.X[d], c, -(sh.M[d] * c))) / sh.S[d] : 0.f) : 1.f;
       int acc;
       if (md == kGreedy) {
         acc = (sh.tok[i] == sh.I[i]);
@@ -1339,7 +1350,7 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
         // accept iff the target's own draw y ~ p_i (inverse CDF, uniform u_i)
         // lands on the proposal: t = u*S inside [B, B + e) of the proposal
         const float u = draw_uniform(P, seq_id, (uint32_t)i, 0u);
-        const float e = fexp2(fmaf(sh.X[i], c, -(sh.M[i] * c)));
+        const float e = (sh.X[i] >= sh.Tau[i]) ? fexp2(fmaf(sh.X[i], c, -(sh.M[i] * c))) : 0.f;
         const float t = u * sh.S[i];
         acc = (t >= sh.Bl[i]) && (t < sh.Bl[i] + e);
       } else {
@@ -1368,9 +1379,13 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
   f.A = A;
   f.emit_pos = off_t + A;
   f.c = c;
+  f.taut = -INFINITY;
+  f.taud = -INFINITY;
   if (md != kGreedy) {
     f.trow = off_t + A;
     f.mct = sh.M[A] * c;
+    f.taut = sh.Tau[A];
+    if (sample && A < K) f.taud = sh.Tau[mk + 1 + A];
     f.u = draw_uniform(P, seq_id, (uint32_t)A, 1u);
     if (A == K) {
       f.kind = kFinalBonus;
@@ -1383,7 +1398,7 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
       // t' = t (below the proposal's interval) or t - e (above it), so the
       // proposal itself can never come out
       const float uA = draw_uniform(P, seq_id, (uint32_t)A, 0u);
-      const float e = fexp2(fmaf(sh.X[A], c, -(sh.M[A] * c)));
+      const float e = (sh.X[A] >= sh.Tau[A]) ? fexp2(fmaf(sh.X[A], c, -(sh.M[A] * c))) : 0.f;
       const float t = uA * sh.S[A];
       const float tr = (t < sh.Bl[A]) ? t : t - e;
       const float Zr = sh.S[A] - e;

@@ -48,11 +48,15 @@ def batch_to_device(batch, torch, dev=0, offset_elems: int = 0, draft_as=None):
         temperature=torch.from_numpy(np.ascontiguousarray(batch.temperature, np.float32)).to(dev),
         mode=torch.from_numpy(np.ascontiguousarray(batch.mode, np.uint8)).to(dev),
         seq_ids=torch.from_numpy(np.ascontiguousarray(batch.seq_ids, np.uint32).view(np.int32)).to(dev),
+        top_k=None if batch.top_k is None else torch.from_numpy(np.ascontiguousarray(batch.top_k, np.int32)).to(dev),
+        top_p=None if batch.top_p is None else torch.from_numpy(np.ascontiguousarray(batch.top_p, np.float32)).to(dev),
     )
 
 
 def run_gpu(verifier, batch, torch, d=None, want_pq=True, seed=None, total_draft=None, **kw):
     d = d or batch_to_device(batch, torch, verifier.device)
+    kw.setdefault("top_k", d.get("top_k"))
+    kw.setdefault("top_p", d.get("top_p"))
     out = verifier.run(d["target"], d["draft"], d["draft_tokens"], d["num_draft"], d["temperature"], d["mode"],
                        d["seq_ids"], seed=batch.seed if seed is None else seed, vocab=batch.vocab,
                        want_pq=want_pq, total_draft=total_draft, **kw)

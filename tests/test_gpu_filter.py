@@ -1,0 +1,116 @@
+"""GPU-vs-oracle parity of top-k / top-p filtered verification through the C
+interface, under the usual rule (identical outputs except on flagged
+near-ties; a top-p crossing within 1e-5 of a tie group may follow the
+neighbouring threshold).  Covers every mode with per-sequence filters,
+tie-heavy bf16 rows, thresholds on the largest and the smallest logits,
+boundary bins larger than the filter's LDS buffer (refined by passes over
+the row), filters that are off, and the C3 workload with filters."""
+import numpy as np
+import pytest
+
+from workloads import (MODE_GREEDY, MODE_ONEHOT, MODE_SAMPLE, MODE_STRICT, Batch, bf16_round,
+                       make_config_batch, make_random_batch)
+
+from . import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+ALL_MODES = (MODE_SAMPLE, MODE_GREEDY, MODE_ONEHOT, MODE_STRICT)
+
+
+@pytest.fixture(scope="module")
+def torch_mod():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+@pytest.fixture(scope="module")
+def verifier(torch_mod):
+    import rejection_sampling_verify_06_amd as sv
+    v = sv.Verifier(max_batch=4096, max_k=16, max_vocab=152064, device=0)
+    yield v
+    v.close()
+
+
+def _with_filters(b: Batch, seed: int, ks, ps) -> Batch:
+    rng = np.random.default_rng(seed)
+    b.top_k = rng.choice(np.asarray(ks, np.int64), size=b.batch).astype(np.int32)
+    b.top_p = rng.choice(np.asarray(ps, np.float64), size=b.batch).astype(np.float32)
+    return b
+
+
+FILTER_CASES = [
+    # seed, B, V, kmax, dtype, ld_pad
+    (0, 24, 7, 4, "f32", 0),
+    (1, 24, 64, 6, "bf16", 0),
+    (2, 32, 1000, 6, "f32", 3),       # unaligned rows
+    (3, 32, 1000, 6, "bf16", 0),
+    (4, 16, 20000, 8, "bf16", 0),
+    (5, 12, 40000, 5, "f32", 0),
+    (6, 6, 150000, 4, "bf16", 0),
+]
+
+
+@pytest.mark.parametrize("seed,B,V,kmax,dtype,ld_pad", FILTER_CASES)
+def test_filtered_mixed(verifier, torch_mod, seed, B, V, kmax, dtype, ld_pad):
+    b = make_random_batch(500 + seed, B=B, V=V, kmax=kmax, dtype=dtype, ld_pad=ld_pad, modes=ALL_MODES)
+    ks = [0, 1, 2, 5, 50, V - 1, V, V + 3]
+    ps = [1.0, 0.95, 0.9, 0.5, 0.1, 0.0, 2.0, float("nan")]
+    _with_filters(b, seed, ks, ps)
+    gu.check_batch(verifier, b, torch_mod, label=f"filters seed={seed}")
+
+
+def test_filters_off_are_bitwise_unfiltered(verifier, torch_mod):
+    b = make_random_batch(520, B=32, V=5000, kmax=6, dtype="bf16", modes=ALL_MODES)
+    plain = gu.run_gpu(verifier, b, torch_mod)
+    b.top_k = np.where(np.arange(b.batch) % 2 == 0, 0, b.vocab).astype(np.int32)
+    b.top_p = np.where(np.arange(b.batch) % 3 == 0, 1.0, 3.0).astype(np.float32)
+    filt = gu.run_gpu(verifier, b, torch_mod)
+    for k in ("accepted_len", "emitted", "status"):
+        assert np.array_equal(plain[k], filt[k]), k
+    assert np.array_equal(plain["p_at"], filt["p_at"], equal_nan=True)
+
+
+def _tie_batch(dtype: str, V: int, seed: int, flat: bool) -> Batch:
+    """Rows on a coarse value grid (many equal logits); with ``flat`` most of
+    the row shares one value, so the boundary bin holds more candidates than
+    the filter's LDS buffer."""
+    rng = np.random.default_rng(seed)
+    B, K = 12, 3
+    n = B * (K + 1)
+    if flat:
+        tgt = np.zeros((n, V), np.float32)
+        tgt += (rng.random((n, V)) < 0.01) * np.round(rng.standard_normal((n, V)) * 4) / 4
+    else:
+        tgt = (np.round(rng.standard_normal((n, V)) * 2) / 2).astype(np.float32)
+    modes = rng.choice(np.asarray([MODE_ONEHOT, MODE_STRICT], np.uint8), size=B)
+    toks = rng.integers(0, V, size=B * K).astype(np.int32)
+    store = bf16_round(tgt) if dtype == "bf16" else tgt
+    return Batch(name=f"ties V={V} {dtype} flat={flat}", vocab=V, dtype=dtype, target=store, draft=None,
+                 num_draft=np.full(B, K, np.int32), draft_tokens=toks,
+                 temperature=rng.uniform(0.5, 1.5, B).astype(np.float32), mode=modes,
+                 seq_ids=np.arange(B, dtype=np.uint32), seed=seed)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("flat", [False, True])
+def test_ties_and_large_boundary_bins(verifier, torch_mod, dtype, flat):
+    V = 30000
+    b = _tie_batch(dtype, V, 600 + int(flat), flat)
+    _with_filters(b, 7, [0, 1, 100, 5000, 15000, 29999], [1.0, 0.999, 0.9, 0.5, 0.3, 1e-4])
+    gu.check_batch(verifier, b, torch_mod, label=f"ties {dtype} flat={flat}")
+
+
+def test_c3_with_filters_bench_context(torch_mod):
+    import rejection_sampling_verify_06_amd as sv
+    v = sv.Verifier(max_batch=256, max_k=8, max_vocab=152064, device=0)
+    try:
+        for step, (k, p) in enumerate([(50, 0.9), (0, 0.95)]):
+            b = make_config_batch(3, step)
+            b.top_k = np.full(b.batch, k, np.int32)
+            b.top_p = np.full(b.batch, p, np.float32)
+            gu.check_batch(v, b, torch_mod, label=f"C3 step {step} top_k={k} top_p={p}, bench context")
+    finally:
+        v.close()
