@@ -36,8 +36,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified positions/sec (B·(K+1) over V) + achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
-WORKLOADS = {"C0": 0, "C1": 1, "C2": 2, "C3": 3, "C4": 4, "C3S": 3}
+WORKLOADS = {"C0": 0, "C1": 1, "C2": 2, "C3": 3, "C4": 4, "C3S": 3, "C3F": 3}
 STRICT_WORKLOADS = {"C3S"}       # the same batches, every sequence in strict sample-match mode
+FILTER_WORKLOADS = {"C3F": (50, 0.9)}   # the same batches with top-k 50 and top-p 0.9 on every sequence
 NGRAM_ROTATE = 32          # 32 x ~8.6 MB of histories: more than the 256 MB last-level cache
 ROTATE = {0: 64, 1: 64, 2: 6, 3: 2, 4: 6}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "row_stats_counters.json")
@@ -58,7 +59,13 @@ def kernel_source_sha(path: str = KERNEL_SOURCE) -> str:
 
 def make_workload_batch(workload: str, step: int):
     from workloads import make_config_batch
-    return make_config_batch(WORKLOADS[workload], step, strict=workload in STRICT_WORKLOADS)
+    b = make_config_batch(WORKLOADS[workload], step, strict=workload in STRICT_WORKLOADS)
+    if workload in FILTER_WORKLOADS:
+        k, p = FILTER_WORKLOADS[workload]
+        b.top_k = np.full(b.batch, k, np.int32)
+        b.top_p = np.full(b.batch, p, np.float32)
+        b.name += f"; top-k {k} and top-p {p} on every sequence"
+    return b
 
 
 def row_bytes(batch) -> dict:
@@ -118,6 +125,8 @@ def to_device(batch, torch):
         temperature=torch.from_numpy(batch.temperature).to(dev),
         mode=torch.from_numpy(batch.mode).to(dev),
         seq_ids=torch.from_numpy(batch.seq_ids.view(np.int32)).to(dev),
+        top_k=None if batch.top_k is None else torch.from_numpy(batch.top_k).to(dev),
+        top_p=None if batch.top_p is None else torch.from_numpy(batch.top_p).to(dev),
     )
 
 
@@ -141,7 +150,9 @@ def cpu_baseline(workload: str, budget_s: float) -> dict:
             oracle.verify_batch(target=b.target[sl_t], draft=None if b.draft is None else b.draft[sl_d],
                                 dtype=b.dtype, vocab=b.vocab, num_draft=b.num_draft[s:s + 1],
                                 draft_tokens=b.draft_tokens[sl_d], temperature=b.temperature[s:s + 1],
-                                mode=b.mode[s:s + 1], seq_ids=b.seq_ids[s:s + 1], seed=passes)
+                                mode=b.mode[s:s + 1], seq_ids=b.seq_ids[s:s + 1], seed=passes,
+                                top_k=None if b.top_k is None else b.top_k[s:s + 1],
+                                top_p=None if b.top_p is None else b.top_p[s:s + 1])
             done_pos += K + 1
             nseq += 1
             if time.perf_counter() - t0 > budget_s:
@@ -198,7 +209,9 @@ def _oracle_worker(workload, budget_s, w, n):
             oracle.verify_batch(target=b.target[sl_t], draft=None if b.draft is None else b.draft[sl_d],
                                 dtype=b.dtype, vocab=b.vocab, num_draft=b.num_draft[s:s + 1],
                                 draft_tokens=b.draft_tokens[sl_d], temperature=b.temperature[s:s + 1],
-                                mode=b.mode[s:s + 1], seq_ids=b.seq_ids[s:s + 1], seed=passes)
+                                mode=b.mode[s:s + 1], seq_ids=b.seq_ids[s:s + 1], seed=passes,
+                                top_k=None if b.top_k is None else b.top_k[s:s + 1],
+                                top_p=None if b.top_p is None else b.top_p[s:s + 1])
             done += K + 1
             if time.perf_counter() - t0 > budget_s:
                 break
@@ -442,8 +455,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="C3", choices=sorted(WORKLOADS) + ["NG", "ST"],
-                    help="C0..C4: the verify step; C3S: C3 in strict sample-match mode; NG: the N-gram "
-                         "proposer; ST: acceptance statistics and the draft-length controller")
+                    help="C0..C4: the verify step; C3S: C3 in strict sample-match mode; C3F: C3 with top-k 50 "
+                         "and top-p 0.9; NG: the N-gram proposer; ST: acceptance statistics and the draft-length "
+                         "controller")
     ap.add_argument("--rotate", type=int, default=None, help="input sets kept resident and cycled")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -490,7 +504,8 @@ def main():
     v = sv.Verifier(max_batch=desc["batch"], max_k=maxk, max_vocab=desc["vocab"], device=0)
     outs = [v.make_outputs(b.batch, b.total_draft, want_pq=True, want_status=True) for b in batches]
     packed = [v.build_args(d["target"], d["draft"], d["draft_tokens"], d["num_draft"], d["temperature"],
-                           d["mode"], d["seq_ids"], seed=b.seed, out=o, vocab=b.vocab)
+                           d["mode"], d["seq_ids"], seed=b.seed, out=o, vocab=b.vocab, top_k=d["top_k"],
+                           top_p=d["top_p"])
               for b, d, o in zip(batches, dev_in, outs)]
 
     def step(i):
@@ -553,6 +568,15 @@ def main():
                     "kernel": "k_row_stats", "algorithmic_bytes_per_launch": int(ev_stats_bytes),
                     "mean_launch_ms": round(kern["row_stats"], 5)}
 
+    filter_roofline = None
+    if events and args.workload in FILTER_WORKLOADS and kern.get("filter", 0) > 0:
+        # the filter must see each filtered row once: the same bytes as the row statistics
+        ach = ev_stats_bytes / (kern["filter"] * 1e-3) / 1e9
+        filter_roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                           "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": "k_filter",
+                           "algorithmic_bytes_per_launch": int(ev_stats_bytes),
+                           "mean_launch_ms": round(kern["filter"], 5)}
+
     if args.copy_calibration:
         copy_calibration(torch)
 
@@ -577,6 +601,7 @@ def main():
         "step_traffic": step_traffic(args.workload, ms_step),
         "cpu_baseline_parallel": cpu_par,
         "kernel_ms": {k: round(x, 5) for k, x in kern.items()},
+        "filter_roofline": filter_roofline,
         "kernel_events_ms_per_step": None if ev_ms_step is None else round(ev_ms_step, 5),
         "input_generation_s": round(gen_s, 1),
     }

@@ -17,8 +17,10 @@
 //   2. a coarse histogram of d = M*c - x*c in steps of 1/8 (log2 units; the
 //      last of 256 bins also takes everything below 2^-32 of the maximum):
 //      counts and masses exp2(x*c - round(M*c)) in 2^-40 fixed point, in
-//      per-wave LDS copies with integer atomics (so every sum is exact and
-//      the result does not depend on the order of the atomics);
+//      LDS copies shared by pairs of waves with integer atomics (so every
+//      sum is exact and the result does not depend on the order of the
+//      atomics); the last bin, which at low temperature holds most of the
+//      row, is counted in registers;
 //   3. the bin holding the threshold (by count from the top for top-k, by
 //      mass for top-p), its elements compacted into LDS, and an exact radix
 //      select over their 32-bit order-preserving keys, 8 bits a pass (a bin
@@ -26,6 +28,7 @@
 //   4. the row's chunk partials rewritten as filtered sums against M (and,
 //      for strict-mode target rows, the filtered part below the proposal),
 //      and tau stored for the scan and the final draw.
+// Every pass over the row issues 16 loads per thread before using any.
 // Every decision on which tokens are kept is a comparison of stored values;
 // only the top-p crossing depends on sums (exact here, in fixed point).
 
@@ -44,10 +47,14 @@ using namespace wave;
 
 constexpr int kFThreads = 1024;
 constexpr int kFWaves = kFThreads / kWave;
+constexpr int kHist = 8;                       // histogram copies (one per pair of waves)
 constexpr int kBins = 256;
 constexpr float kBinScale = 8.f;               // bins per log2 unit below the row maximum
 constexpr float kBinSpan = kBins / kBinScale;  // 32: d beyond this falls into the last bin
-constexpr int kCap = 4096;                     // candidates held in LDS
+constexpr float kFineScale = 2048.f;           // fine bins per log2 unit inside one coarse bin
+constexpr int kCap = 2048;                     // candidates held in LDS
+constexpr int kUnroll = 16;                    // loads in flight per thread
+constexpr int kMaxChunks = kMaxTiles * kTileElems / (kChunkBytes / 4);   // 256
 constexpr double kMassOne = 1099511627776.0;   // 2^40
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr float kMinTemp = 1e-6f;
@@ -65,81 +72,211 @@ __device__ __forceinline__ float kval(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-__device__ __forceinline__ float load_x(const char* rowp, int e, int bf) {
-  return bf ? __uint_as_float((uint32_t)((const uint16_t*)rowp)[e] << 16) : ((const float*)rowp)[e];
+template <bool BF>
+__device__ __forceinline__ float load_x(const char* rowp, int e) {
+  return BF ? __uint_as_float((uint32_t)((const uint16_t*)rowp)[e] << 16) : ((const float*)rowp)[e];
 }
 
-// coarse bin: monotone non-increasing in x (d is the correctly rounded
-// M*c - x*c); NaN and -inf fall into the last bin
-__device__ __forceinline__ int coarse_bin(float x, float c, float mc) {
-  const float d = fmaf(-x, c, mc);
+// Every element e < V of the row once: thread t takes e = base + u*kFThreads + t,
+// all kUnroll loads of a round issued before f sees any.
+template <bool BF, typename F>
+__device__ __forceinline__ void for_row(const char* rowp, int V, F&& f) {
+  const int t = threadIdx.x;
+  for (int base = 0; base < V; base += kFThreads * kUnroll) {
+    float x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int e = base + u * kFThreads + t;
+      x[u] = e < V ? load_x<BF>(rowp, e) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int e = base + u * kFThreads + t;
+      if (e < V) f(x[u], e);
+    }
+  }
+}
+
+// coarse bin of d = M*c - x*c (correctly rounded, so monotone in x): 1/8
+// log2 unit per bin; d beyond 32 (and NaN, -inf) in the last bin
+__device__ __forceinline__ int coarse_bin(float d) {
   return (d < kBinSpan) ? min(kBins - 1, max(0, (int)(d * kBinScale))) : kBins - 1;
 }
+// fine bin inside coarse bin b: 1/2048 log2 unit per bin (monotone in d)
+__device__ __forceinline__ int fine_bin(float d, int b) {
+  const float f = (d - (float)b * (1.f / kBinScale)) * kFineScale;
+  return (f < (float)kBins) ? max(0, (int)f) : kBins - 1;
+}
 
-__device__ __forceinline__ uint64_t fixed_mass(float x, float c, float mc) {
-  const float e = fminf(fmaxf(fexp2(fmaf(x, c, -mc)), 0.f), 2.f);   // NaN -> 0
-  return (uint64_t)((double)e * kMassOne);
+// floor(e * 2^40) for e = exp2(-d) clamped to [0, 2], with integer operations only
+__device__ __forceinline__ uint64_t fixed_mass_d(float d) {
+  const float e = fminf(fmaxf(fexp2(-d), 0.f), 2.f);        // NaN -> 0
+  const uint32_t b = __float_as_uint(e);
+  const int E = (int)(b >> 23);
+  const uint64_t m = (uint64_t)((b & 0x7FFFFFu) | 0x800000u);
+  const int sh = E - 110;                                     // e = m * 2^(E-150); times 2^40
+  if (E == 0) return 0;
+  return sh >= 0 ? (m << sh) : (sh > -24 ? (m >> (-sh)) : 0);
 }
 
 struct FiltShared {
-  uint32_t wc[kFWaves][kBins];
-  uint64_t wm[kFWaves][kBins];
-  uint32_t hc[kBins];
+  uint32_t wc[kHist][kBins];   // per-pair histograms (coarse, then fine)
+  uint64_t wm[kHist][kBins];
+  uint32_t hc[kBins];          // merged coarse histogram
   uint64_t hm[kBins];
-  uint32_t ck[kCap];
+  uint32_t fc[kBins];          // merged fine histogram
+  uint64_t fm[kBins];
+  uint32_t ck[kCap];           // candidates: keys and masses
   uint64_t cm[kCap];
-  uint32_t rc[kBins];
+  uint32_t rc[kBins];          // radix byte histogram
   uint64_t rm[kBins];
-  float ra[kFWaves], rb[kFWaves];
-  uint32_t ncand;
-  uint32_t kcount;          // candidates of a bin at or above the top-k key
-  uint64_t kmass;
-  int sel_bin;
+  uint64_t cs[kMaxChunks];     // filtered chunk sums, fixed point
+  uint64_t cb[kMaxChunks];     // their parts below the proposal (strict target rows)
+  uint32_t ncand, kmin_c, kmax_c;
+  int last;                    // last non-empty bin of the latest crossing search
+  uint64_t amass;
+  int bin;
   uint32_t need;
   double rem;
-  int byte;
   int ok;
   int offd;
   float M;
 };
 
-// Candidates: elements of coarse bin `bin` whose key is >= kmin.
-struct Cand {
-  const char* rowp;
-  int bf, V;
-  float c, mc;
-  int bin;
-  uint32_t kmin;
-  bool in_lds;
-  uint32_t n;
-};
-
-__device__ __forceinline__ void compact(FiltShared& sh, Cand& cd) {
-  const int t = threadIdx.x;
-  if (t == 0) sh.ncand = 0;
-  __syncthreads();
-  for (int e = t; e < cd.V; e += kFThreads) {
-    const float x = load_x(cd.rowp, e, cd.bf);
-    const uint32_t k = fkey(x);
-    if (coarse_bin(x, cd.c, cd.mc) == cd.bin && k >= cd.kmin) {
-      const uint32_t i = atomicAdd(&sh.ncand, 1u);
-      if (i < (uint32_t)kCap) {
-        sh.ck[i] = k;
-        sh.cm[i] = fixed_mass(x, cd.c, cd.mc);
+// The crossing of a 256-bin histogram, run by wave 0: bins in order
+// i = 0..255 (bin i, or 255 - i when `desc`), empty bins skipped; the first
+// bin where the running count reaches `need` (or the running mass reaches
+// `target`).  Each lane sums 4 bins, then a walk over the 64 lane sums
+// (readlane, uniform) and over the 4 bins of the crossing lane.  Writes
+// sh.bin (-1 when never reached: rounding, mass mode only), sh.need or
+// sh.rem (what is left inside the bin) and sh.last (the last non-empty bin).
+template <bool BY_MASS>
+__device__ __forceinline__ void scan_bins(FiltShared& sh, const uint32_t* hc, const uint64_t* hm, bool desc,
+                                          uint32_t need, double target) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t lc = 0;
+  uint64_t lm = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = lane * 4 + j;
+    const int b = desc ? kBins - 1 - i : i;
+    lc += hc[b];
+    if (BY_MASS) lm += hm[b];
+  }
+  uint32_t acc_c = 0;
+  double acc_m = 0.0;
+  int cl = -1, last_l = -1;
+  for (int l = 0; l < kWave; ++l) {
+    const uint32_t c_l = (uint32_t)__builtin_amdgcn_readlane((int)lc, l);
+    if (c_l == 0) continue;
+    last_l = l;
+    double m_l = 0.0;
+    if (BY_MASS) {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lm, l);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(lm >> 32), l);
+      m_l = (double)(((uint64_t)hi << 32) | lo);
+      if (acc_m + m_l >= target) {
+        cl = l;
+        break;
+      }
+    } else if (acc_c + c_l >= need) {
+      cl = l;
+      break;
+    }
+    acc_c += c_l;
+    acc_m += m_l;
+  }
+  int bin = -1, last = -1;
+  const int ll = cl >= 0 ? cl : last_l;
+  if (ll >= 0) {
+    for (int j = 0; j < 4; ++j) {
+      const int i = ll * 4 + j;
+      const int b = desc ? kBins - 1 - i : i;
+      const uint32_t cb = hc[b];
+      if (cb == 0) continue;
+      last = b;
+      if (cl < 0) continue;
+      if (BY_MASS) {
+        const double mb = (double)hm[b];
+        if (acc_m + mb >= target) {
+          bin = b;
+          break;
+        }
+        acc_m += mb;
+      } else {
+        if (acc_c + cb >= need) {
+          bin = b;
+          break;
+        }
+        acc_c += cb;
       }
     }
   }
-  __syncthreads();
-  cd.n = sh.ncand;
-  cd.in_lds = cd.n <= (uint32_t)kCap;
+  if (lane == 0) {
+    sh.bin = bin;
+    sh.need = need - acc_c;
+    sh.rem = target - acc_m;
+    sh.last = last;
+  }
 }
 
-// Radix select over the candidates from the largest key down: by count
-// (the need-th largest key) or by mass (the key where the mass from the top
-// first reaches `target`; the smallest candidate key when it never does).
-template <bool BY_MASS>
-__device__ __forceinline__ uint32_t radix_select(FiltShared& sh, const Cand& cd, uint32_t need, double target) {
+// Elements of one region of the row: coarse bin `bin`, fine bin `fine`
+// (-1: any), key >= kmin.
+struct Region {
+  int bin, fine;
+  uint32_t kmin;
+};
+
+__device__ __forceinline__ bool in_region(const Region& rg, float d, uint32_t k) {
+  return coarse_bin(d) == rg.bin && (rg.fine < 0 || fine_bin(d, rg.bin) == rg.fine) && k >= rg.kmin;
+}
+
+// One slot per candidate: a ballot per wave and one LDS atomic by its first lane.
+__device__ __forceinline__ uint32_t claim_slot(FiltShared& sh, bool want) {
+  const unsigned long long m = __ballot(want);
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t base = 0;
+  if (m) {
+    const int leader = __ffsll((long long)m) - 1;
+    if (lane == leader) base = atomicAdd(&sh.ncand, (uint32_t)__popcll(m));
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
+  }
+  const unsigned long long below = (lane == 0) ? 0ull : (m & (~0ull >> (kWave - lane)));
+  return base + (uint32_t)__popcll(below);
+}
+
+// The key threshold inside a region, exactly: the need-th largest key
+// (by count) or the key where the mass from the top first reaches `target`
+// (the smallest key when it never does).  Candidates go to LDS when they
+// fit; otherwise the radix passes read the row.
+template <bool BF, bool BY_MASS, bool COLLECT>
+__device__ __forceinline__ uint32_t select_region(FiltShared& sh, const char* rowp, int V, float c, float mc,
+                                                  const Region& rg, uint32_t need, double target) {
   const int t = threadIdx.x;
+  if (t == 0) {
+    sh.ncand = 0;
+    sh.kmin_c = 0xFFFFFFFFu;
+    sh.kmax_c = 0u;
+  }
+  __syncthreads();
+  for_row<BF>(rowp, V, [&](float x, int) {
+    const float d = fmaf(-x, c, mc);
+    const uint32_t k = fkey(x);
+    const bool want = in_region(rg, d, k);
+    const uint32_t i = claim_slot(sh, want);
+    if (want) {
+      if (i < (uint32_t)kCap) {
+        sh.ck[i] = k;
+        if (COLLECT) sh.cm[i] = fixed_mass_d(d);
+      }
+      atomicMin(&sh.kmin_c, k);
+      atomicMax(&sh.kmax_c, k);
+    }
+  });
+  __syncthreads();
+  const uint32_t n = sh.ncand;
+  if (sh.kmin_c == sh.kmax_c) return sh.kmin_c;      // every candidate has the same key (or none)
+  const bool in_lds = n <= (uint32_t)kCap;
   uint32_t prefix = 0, pmask = 0;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
@@ -148,65 +285,246 @@ __device__ __forceinline__ uint32_t radix_select(FiltShared& sh, const Cand& cd,
       sh.rm[t] = 0;
     }
     __syncthreads();
-    if (cd.in_lds) {
-      for (uint32_t i = t; i < cd.n; i += kFThreads) {
+    if (in_lds) {
+      for (uint32_t i = t; i < n; i += kFThreads) {
         const uint32_t k = sh.ck[i];
-        if (k >= cd.kmin && (k & pmask) == prefix) {
+        if ((k & pmask) == prefix) {
           const int by = (k >> shift) & 0xFF;
           atomicAdd(&sh.rc[by], 1u);
           if (BY_MASS) atomicAdd(&sh.rm[by], (unsigned long long)sh.cm[i]);
         }
       }
     } else {
-      for (int e = t; e < cd.V; e += kFThreads) {
-        const float x = load_x(cd.rowp, e, cd.bf);
+      for_row<BF>(rowp, V, [&](float x, int) {
+        const float d = fmaf(-x, c, mc);
         const uint32_t k = fkey(x);
-        if (coarse_bin(x, cd.c, cd.mc) == cd.bin && k >= cd.kmin && (k & pmask) == prefix) {
+        if (in_region(rg, d, k) && (k & pmask) == prefix) {
           const int by = (k >> shift) & 0xFF;
           atomicAdd(&sh.rc[by], 1u);
-          if (BY_MASS) atomicAdd(&sh.rm[by], (unsigned long long)fixed_mass(x, cd.c, cd.mc));
+          if (BY_MASS) atomicAdd(&sh.rm[by], (unsigned long long)fixed_mass_d(d));
         }
-      }
+      });
     }
     __syncthreads();
-    if (t == 0) {
-      int chosen = -1, last = 0;
-      if (BY_MASS) {
-        double acc = 0.0;
-        for (int by = kBins - 1; by >= 0; --by) {
-          if (sh.rc[by] == 0) continue;
-          last = by;
-          const double m = (double)sh.rm[by];
-          if (acc + m >= target) {
-            chosen = by;
-            break;
-          }
-          acc += m;
-        }
-        sh.rem = target - acc;
-      } else {
-        uint32_t acc = 0;
-        for (int by = kBins - 1; by >= 0; --by) {
-          if (sh.rc[by] == 0) continue;
-          last = by;
-          if (acc + sh.rc[by] >= need) {
-            chosen = by;
-            break;
-          }
-          acc += sh.rc[by];
-        }
-        sh.need = need - acc;
-      }
-      sh.byte = chosen >= 0 ? chosen : last;
-    }
+    if (t < kWave) scan_bins<BY_MASS>(sh, sh.rc, sh.rm, true, need, target);
     __syncthreads();
-    prefix |= (uint32_t)sh.byte << shift;
+    const int by = sh.bin >= 0 ? sh.bin : sh.last;
+    prefix |= (uint32_t)by << shift;
     pmask |= 0xFFu << shift;
     if (BY_MASS) target = sh.rem;
     else need = sh.need;
     __syncthreads();
   }
   return prefix;
+}
+
+// Per-pair histograms of one region (coarse: fine = -2 means "bin every
+// element by its coarse bin"), merged into (hc, hm).
+template <bool BF, bool MASS>
+__device__ __forceinline__ void histogram(FiltShared& sh, const char* rowp, int V, float c, float mc, int coarse_b,
+                                          uint32_t kmin, uint32_t* hc, uint64_t* hm) {
+  const int t = threadIdx.x, h = (t / kWave) >> 1;
+  for (int j = t; j < kHist * kBins; j += kFThreads) {
+    (&sh.wc[0][0])[j] = 0;
+    (&sh.wm[0][0])[j] = 0;
+  }
+  __syncthreads();
+  uint32_t lc = 0;       // the coarse last bin, in registers
+  uint64_t lm = 0;
+  for_row<BF>(rowp, V, [&](float x, int) {
+    const float d = fmaf(-x, c, mc);
+    int b = coarse_bin(d);
+    if (coarse_b >= 0) {
+      if (b != coarse_b || fkey(x) < kmin) return;
+      b = fine_bin(d, coarse_b);
+    } else if (b == kBins - 1) {
+      ++lc;
+      if (MASS) lm += fixed_mass_d(d);
+      return;
+    }
+    atomicAdd(&sh.wc[h][b], 1u);
+    if (MASS) atomicAdd(&sh.wm[h][b], (unsigned long long)fixed_mass_d(d));
+  });
+  if (lc) {
+    atomicAdd(&sh.wc[h][kBins - 1], lc);
+    if (MASS) atomicAdd(&sh.wm[h][kBins - 1], (unsigned long long)lm);
+  }
+  __syncthreads();
+  if (t < kBins) {
+    uint32_t cs = 0;
+    uint64_t ms = 0;
+    for (int w = 0; w < kHist; ++w) {
+      cs += sh.wc[w][t];
+      if (MASS) ms += sh.wm[w][t];
+    }
+    hc[t] = cs;
+    hm[t] = ms;
+  }
+  __syncthreads();
+}
+
+// The threshold key inside coarse bin b (keys >= kmin): fine histogram, the
+// crossing fine bin, then the exact select among its elements.  With
+// `above` the mass at or above the returned key inside the bin is left in
+// sh.amass (by-count selections used before a top-p step need it).
+template <bool BF, bool BY_MASS, bool MASS>
+__device__ __forceinline__ uint32_t select_in_bin(FiltShared& sh, const char* rowp, int V, float c, float mc, int b,
+                                                  uint32_t kmin, uint32_t need, double target, bool above) {
+  const int t = threadIdx.x;
+  // a bin that fits the candidate buffer is selected in directly; a larger
+  // one is narrowed by a fine histogram first (one more pass over the row)
+  const bool fine = sh.hc[b] > (uint32_t)kCap;
+  int fb = -1;
+  uint32_t need2 = need;
+  double rem2 = target;
+  if (fine) {
+    histogram<BF, MASS>(sh, rowp, V, c, mc, b, kmin, sh.fc, sh.fm);
+    if (t < kWave) scan_bins<BY_MASS>(sh, sh.fc, sh.fm, false, need, target);
+    __syncthreads();
+    fb = sh.bin >= 0 ? sh.bin : sh.last;
+    need2 = sh.need;
+    rem2 = sh.rem;
+    __syncthreads();
+  }
+  const Region rg{b, fb, kmin};
+  const uint32_t key = select_region<BF, BY_MASS, MASS>(sh, rowp, V, c, mc, rg, need2, rem2);
+  if (above && MASS) {
+    // mass of the bin at or above the key: the fine bins before fb, plus fb's part at or above it
+    if (t == 0) sh.amass = 0;
+    __syncthreads();
+    uint64_t part = 0;
+    const uint32_t n = sh.ncand;
+    if (n <= (uint32_t)kCap) {
+      for (uint32_t i = t; i < n; i += kFThreads)
+        if (sh.ck[i] >= key) part += sh.cm[i];
+    } else {
+      for_row<BF>(rowp, V, [&](float x, int) {
+        const float d = fmaf(-x, c, mc);
+        const uint32_t k = fkey(x);
+        if (in_region(rg, d, k) && k >= key) part += fixed_mass_d(d);
+      });
+    }
+    if (fine && t < fb) part += sh.fm[t];
+    if (part) atomicAdd(&sh.amass, (unsigned long long)part);
+    __syncthreads();
+  }
+  return key;
+}
+
+// The filter of one row (template on the row's element type).
+template <bool BF>
+__device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Partial* pp, const char* rowp, int nch,
+                                           int ce, float c, float mc, float M, bool use_k, int topk, bool use_p,
+                                           float topp, int xs, float* tau_out) {
+  const int t = threadIdx.x, lane = t & (kWave - 1);
+  const int V = P.V;
+  for (int j = t; j < nch; j += kFThreads) {
+    sh.cs[j] = 0;
+    sh.cb[j] = 0;
+  }
+  // ---- coarse histogram (masses only when top-p needs them) ----
+  if (use_p) histogram<BF, true>(sh, rowp, V, c, mc, -1, 0u, sh.hc, sh.hm);
+  else histogram<BF, false>(sh, rowp, V, c, mc, -1, 0u, sh.hc, sh.hm);
+
+  float tau = -INFINITY;
+  uint32_t kkey = 0;
+  int bk = kBins;
+  uint64_t mass_bk = 0;          // mass of bin bk at or above the top-k key
+  // ---- top-k: the k-th largest logit ----
+  if (use_k) {
+    if (t < kWave) scan_bins<false>(sh, sh.hc, sh.hm, false, (uint32_t)topk, 0.0);
+    __syncthreads();
+    bk = sh.bin >= 0 ? sh.bin : kBins - 1;
+    const uint32_t need = sh.need;
+    __syncthreads();
+    if (use_p) {
+      kkey = select_in_bin<BF, false, true>(sh, rowp, V, c, mc, bk, 0u, need, 0.0, true);
+      mass_bk = sh.amass;
+    } else {
+      kkey = select_in_bin<BF, false, false>(sh, rowp, V, c, mc, bk, 0u, need, 0.0, false);
+    }
+    tau = kval(kkey);
+  }
+  // ---- top-p on the top-k distribution ----
+  if (use_p) {
+    // the top-k bin counts only its part at or above the top-k key
+    if (t == 0 && use_k) {
+      sh.hm[bk] = mass_bk;
+      for (int b = bk + 1; b < kBins; ++b) {
+        sh.hc[b] = 0;
+        sh.hm[b] = 0;
+      }
+    }
+    __syncthreads();
+    if (t < kWave) {
+      // Z = the mass of the kept (top-k) set, by a wave sum of lane totals
+      uint64_t z = 0;
+      for (int j = 0; j < 4; ++j) z += sh.hm[lane * 4 + j];
+      double zt = 0.0;
+      for (int l = 0; l < kWave; ++l) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)z, l);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(z >> 32), l);
+        zt += (double)(((uint64_t)hi << 32) | lo);
+      }
+      const double target = topp > 0.f ? (double)topp * zt : 0.0;
+      scan_bins<true>(sh, sh.hc, sh.hm, false, 0u, target);
+    }
+    __syncthreads();
+    const int bp = sh.bin;
+    const double rem = sh.rem;
+    __syncthreads();
+    if (bp >= 0) {               // -1: the crossing was never reached (rounding): keep the whole set
+      const uint32_t kmin = (use_k && bp == bk) ? kkey : 0u;
+      const uint32_t pkey = select_in_bin<BF, true, true>(sh, rowp, V, c, mc, bp, kmin, 0u, rem, false);
+      tau = fmaxf(tau, kval(pkey));
+    }
+  }
+
+  // ---- filtered chunk partials: per wave and chunk, float sums turned into fixed point ----
+  // (explicit rounds: every lane runs every step, so the wave sums see no
+  // inactive lanes; elements past V weigh 0, and the chunk of a step is the
+  // same for the whole block since chunks are whole rounds of kFThreads)
+  {
+    float a = 0.f, bl = 0.f;
+    int cur = 0;
+    for (int base = 0; base < V; base += kFThreads * kUnroll) {
+      float x[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int e = base + u * kFThreads + t;
+        x[u] = e < V ? load_x<BF>(rowp, e) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int e = base + u * kFThreads + t;
+        const int k = (base + u * kFThreads) / ce;
+        if (k != cur) {                        // block-uniform
+          const float wa = wave_sum(a), wb = wave_sum(bl);
+          if (lane == 0) {
+            if (wa != 0.f) atomicAdd(&sh.cs[cur], (unsigned long long)((double)wa * kMassOne));
+            if (wb != 0.f) atomicAdd(&sh.cb[cur], (unsigned long long)((double)wb * kMassOne));
+          }
+          a = 0.f;
+          bl = 0.f;
+          cur = k;
+        }
+        const float w = (e < V && x[u] >= tau) ? fexp2(fmaf(x[u], c, -mc)) : 0.f;
+        a += w;
+        bl += (e < xs) ? w : 0.f;
+      }
+    }
+    const float wa = wave_sum(a), wb = wave_sum(bl);
+    if (lane == 0) {
+      if (wa != 0.f) atomicAdd(&sh.cs[cur], (unsigned long long)((double)wa * kMassOne));
+      if (wb != 0.f) atomicAdd(&sh.cb[cur], (unsigned long long)((double)wb * kMassOne));
+    }
+  }
+  __syncthreads();
+  for (int k = t; k < nch; k += kFThreads) {
+    const Partial q = pp[k];
+    pp[k] = Partial{M, (float)((double)sh.cs[k] / kMassOne), q.idx, (float)((double)sh.cb[k] / kMassOne)};
+  }
+  if (t == 0) *tau_out = tau;
 }
 
 }  // namespace
@@ -260,169 +578,20 @@ __global__ void __launch_bounds__(kFThreads) k_filter(Params P) {
   if (!sh.ok) return;                        // the scan reports the layout
   const float M = sh.M;
   if (!(M > -INFINITY && M < INFINITY)) return;   // an all -inf or non-finite row: the scan reports it
+  if (nch > kMaxChunks) return;              // cannot happen within the context's vocabulary limit
 
   const int64_t row = draft ? (int64_t)sh.offd + (r - mk - 1) : (int64_t)sh.offd + s + r;
   const int bf = draft ? P.d_bf16 : P.t_bf16;
   const char* rowp = (const char*)(draft ? P.dft : P.tgt) + row * (draft ? P.ld_d : P.ld_t) * (bf ? 2 : 4);
-  const int V = P.V;
   const float c = kLog2eF / T;
   const float mc = M * c;
-
-  // ---- coarse histogram ----
-  for (int j = lane; j < kBins; j += kWave) {
-    sh.wc[wv][j] = 0;
-    sh.wm[wv][j] = 0;
-  }
-  __syncthreads();
-  for (int e = t; e < V; e += kFThreads) {
-    const float x = load_x(rowp, e, bf);
-    const int b = coarse_bin(x, c, mc);
-    atomicAdd(&sh.wc[wv][b], 1u);
-    atomicAdd(&sh.wm[wv][b], (unsigned long long)fixed_mass(x, c, mc));
-  }
-  __syncthreads();
-  if (t < kBins) {
-    uint32_t cs = 0;
-    uint64_t ms = 0;
-    for (int w = 0; w < kFWaves; ++w) {
-      cs += sh.wc[w][t];
-      ms += sh.wm[w][t];
-    }
-    sh.hc[t] = cs;
-    sh.hm[t] = ms;
-  }
-  __syncthreads();
-
-  Cand cd{rowp, bf, V, c, mc, 0, 0u, false, 0u};
-  float tau = -INFINITY;
-  uint32_t kkey = 0;
-  int bk = kBins;
-  // ---- top-k: the k-th largest logit ----
-  if (use_k) {
-    if (t == 0) {
-      uint32_t cum = 0;
-      int b = 0;
-      for (; b < kBins - 1; ++b) {
-        if (cum + sh.hc[b] >= (uint32_t)topk) break;
-        cum += sh.hc[b];
-      }
-      sh.sel_bin = b;
-      sh.need = (uint32_t)topk - cum;
-    }
-    __syncthreads();
-    bk = sh.sel_bin;
-    const uint32_t need = sh.need;
-    cd.bin = bk;
-    cd.kmin = 0u;
-    compact(sh, cd);
-    kkey = radix_select<false>(sh, cd, need, 0.0);
-    tau = kval(kkey);
-  }
-  // ---- top-p on the top-k distribution ----
-  if (use_p) {
-    uint64_t Z = 0, mass_bk = 0;
-    uint32_t cnt_bk = 0;
-    if (use_k) {
-      // mass and count of bin bk at or above the top-k key
-      if (t == 0) {
-        sh.kmass = 0;
-        sh.kcount = 0;
-      }
-      __syncthreads();
-      uint64_t mloc = 0;
-      uint32_t cloc = 0;
-      if (cd.in_lds) {
-        for (uint32_t i = t; i < cd.n; i += kFThreads)
-          if (sh.ck[i] >= kkey) {
-            mloc += sh.cm[i];
-            ++cloc;
-          }
-      } else {
-        for (int e = t; e < V; e += kFThreads) {
-          const float x = load_x(rowp, e, bf);
-          if (coarse_bin(x, c, mc) == bk && fkey(x) >= kkey) {
-            mloc += fixed_mass(x, c, mc);
-            ++cloc;
-          }
-        }
-      }
-      if (mloc) atomicAdd(&sh.kmass, (unsigned long long)mloc);
-      if (cloc) atomicAdd(&sh.kcount, cloc);
-      __syncthreads();
-      mass_bk = sh.kmass;
-      cnt_bk = sh.kcount;
-    }
-    if (t == 0) {
-      for (int b = 0; b < kBins; ++b) {
-        if (b > bk) break;
-        Z += (b == bk) ? mass_bk : sh.hm[b];
-      }
-      const double target = topp > 0.f ? (double)topp * (double)Z : 0.0;
-      double cum = 0.0;
-      int bp = -1;
-      for (int b = 0; b < kBins && b <= bk; ++b) {
-        const uint32_t nb = (b == bk) ? cnt_bk : sh.hc[b];
-        if (nb == 0) continue;
-        const double mb = (double)((b == bk) ? mass_bk : sh.hm[b]);
-        if (cum + mb >= target) {
-          bp = b;
-          break;
-        }
-        cum += mb;
-      }
-      sh.sel_bin = bp;                  // -1: the crossing was never reached (rounding): keep everything
-      sh.rem = target - cum;
-    }
-    __syncthreads();
-    const int bp = sh.sel_bin;
-    const double rem = sh.rem;
-    if (bp >= 0) {
-      // candidates of bin bp (at or above the top-k key when bp is the top-k bin, whose candidates
-      // may already be in LDS)
-      if (!(use_k && bp == bk && cd.in_lds)) {
-        cd.bin = bp;
-        cd.kmin = (use_k && bp == bk) ? kkey : 0u;
-        compact(sh, cd);
-      } else {
-        cd.kmin = kkey;
-      }
-      const Cand cp = cd;
-      const uint32_t pkey = radix_select<true>(sh, cp, 0u, rem);
-      tau = fmaxf(tau, kval(pkey));
-    }
-  }
-
-  // ---- filtered chunk partials ----
   const int ce = draft ? P.ce_d : P.ce_t;
   const int xs = (md == kModeStrict && !draft && r < K) ? P.ptok[(int64_t)s * mk + r] : -1;
-  for (int k = 0; k < nch; ++k) {
-    const int e0 = k * ce, e1 = min(V, e0 + ce);
-    float a = 0.f, bl = 0.f;
-    for (int e = e0 + t; e < e1; e += kFThreads) {
-      const float x = load_x(rowp, e, bf);
-      const float w = (x >= tau) ? fexp2(fmaf(x, c, -mc)) : 0.f;
-      a += w;
-      bl += (e < xs) ? w : 0.f;
-    }
-    a = wave_sum(a);
-    bl = wave_sum(bl);
-    if (lane == 0) {
-      sh.ra[wv] = a;
-      sh.rb[wv] = bl;
-    }
-    __syncthreads();
-    if (t == 0) {
-      float S = 0.f, Bs = 0.f;
-      for (int w = 0; w < kFWaves; ++w) {
-        S += sh.ra[w];
-        Bs += sh.rb[w];
-      }
-      const Partial q = pp[k];
-      pp[k] = Partial{M, S, q.idx, Bs};
-    }
-    __syncthreads();
-  }
-  if (t == 0) P.tau[(int64_t)s * P.slots + r] = tau;
+  float* tau_out = P.tau + (int64_t)s * P.slots + r;
+  if (bf)
+    filter_row<true>(P, sh, pp, rowp, nch, ce, c, mc, M, use_k, topk, use_p, topp, xs, tau_out);
+  else
+    filter_row<false>(P, sh, pp, rowp, nch, ce, c, mc, M, use_k, topk, use_p, topp, xs, tau_out);
 }
 
 hipError_t launch_filter(const Params& p, hipStream_t st) {
