@@ -59,7 +59,7 @@ def test_struct_layout_and_single_hip_runtime():
     _ensure_built()
     from rejection_sampling_verify_06_amd import _lib
     lib = _lib.load()                       # checks sizeof(spec_verify_args) against the binding
-    assert lib.spec_verify_args_size() == ctypes.sizeof(_lib.SpecVerifyArgs) == 152
+    assert lib.spec_verify_args_size() == ctypes.sizeof(_lib.SpecVerifyArgs) == 168   # with the two filter pointers
     assert b"gfx950" in lib.spec_verify_version()
     maps = open("/proc/self/maps").read()
     hip = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
