@@ -173,13 +173,14 @@ const char* spec_verify_last_error(void);
 
 /* ---- measurement hooks ---------------------------------------------------
  * spec_verify_timing_enable(ctx, n) makes the next n calls of
- * spec_verify_run record a HIP event before and after each of its kernel
- * slots on the call's stream (n = 0 turns it off; events are created here,
- * never inside run).  spec_verify_timing_read waits for those events and
+ * spec_verify_run time each of its kernel slots with a pair of HIP events
+ * that the dispatch itself records (hipExtLaunchKernel), so a slot's time is
+ * its kernel's execution, without event gaps (n = 0 turns it off; events are
+ * created here, never inside run).  spec_verify_timing_read waits for those events and
  * returns the number of recorded calls and, per slot, the summed elapsed
  * milliseconds (ms_per_kernel has SV_NUM_KERNELS entries: row statistics,
- * filter, final, select; a slot whose kernel was not launched reads about
- * 0), then resets the record. */
+ * filter, final, select; a slot whose kernel was not launched reads 0),
+ * then resets the record. */
 #define SV_NUM_KERNELS 4
 int spec_verify_timing_enable(spec_verify_ctx* ctx, int32_t max_calls);
 int spec_verify_timing_read(spec_verify_ctx* ctx, int32_t* calls, double* ms_per_kernel);

@@ -73,7 +73,8 @@ struct spec_verify_ctx {
   uint8_t* def_mode = nullptr;
   uint32_t* def_seq_ids = nullptr;
   // timing hooks
-  std::vector<hipEvent_t> events;   // SV_NUM_KERNELS + 1 per recorded call
+  std::vector<hipEvent_t> events;   // a start and a stop per kernel slot of every recorded call
+  std::vector<uint8_t> launched;    // per kernel slot of every recorded call: 1 when it launched
   int32_t timing_cap = 0;
   int32_t timing_used = 0;
 };
@@ -309,15 +310,16 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
   hipStream_t st = (hipStream_t)hip_stream;
 
   const bool timed = ctx->timing_used < ctx->timing_cap;
-  hipEvent_t* ev = timed ? &ctx->events[(size_t)ctx->timing_used * (SV_NUM_KERNELS + 1)] : nullptr;
-  typedef hipError_t (*Launch)(const sv::Params&, hipStream_t);
+  hipEvent_t* ev = timed ? &ctx->events[(size_t)ctx->timing_used * 2 * SV_NUM_KERNELS] : nullptr;
+  typedef hipError_t (*Launch)(const sv::Params&, hipStream_t, const sv::LaunchEvents*);
   static const Launch kLaunch[SV_NUM_KERNELS] = {sv::launch_row_stats, sv::launch_filter, sv::launch_final,
                                                  sv::launch_select};
   static const char* kName[SV_NUM_KERNELS] = {"row_stats", "filter", "final", "select"};
-  if (timed && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_fail("hipEventRecord", e);
+  uint8_t* launched = timed ? &ctx->launched[(size_t)ctx->timing_used * SV_NUM_KERNELS] : nullptr;
   for (int k = 0; k < SV_NUM_KERNELS; ++k) {
-    if ((e = kLaunch[k](p, st)) != hipSuccess) return hip_fail(kName[k], e);
-    if (timed && (e = hipEventRecord(ev[k + 1], st)) != hipSuccess) return hip_fail("hipEventRecord", e);
+    const sv::LaunchEvents le{timed ? ev[2 * k] : nullptr, timed ? ev[2 * k + 1] : nullptr,
+                              timed ? &launched[k] : nullptr};
+    if ((e = kLaunch[k](p, st, timed ? &le : nullptr)) != hipSuccess) return hip_fail(kName[k], e);
   }
   if (timed) ctx->timing_used++;
   return SV_OK;
@@ -491,7 +493,8 @@ int spec_verify_timing_enable(spec_verify_ctx* ctx, int32_t max_calls) {
   ctx->timing_cap = 0;
   ctx->timing_used = 0;
   if (max_calls == 0) return SV_OK;
-  ctx->events.resize((size_t)max_calls * (SV_NUM_KERNELS + 1));
+  ctx->events.resize((size_t)max_calls * 2 * SV_NUM_KERNELS);
+  ctx->launched.assign((size_t)max_calls * SV_NUM_KERNELS, 0);
   for (auto& ev : ctx->events) {
     if ((e = hipEventCreate(&ev)) != hipSuccess) {
       ctx->events.clear();
@@ -512,11 +515,13 @@ int spec_verify_timing_read(spec_verify_ctx* ctx, int32_t* calls, double* ms_per
   if (e != hipSuccess) return hip_fail("hipSetDevice", e);
   for (int k = 0; k < SV_NUM_KERNELS; ++k) ms_per_kernel[k] = 0.0;
   for (int32_t i = 0; i < ctx->timing_used; ++i) {
-    hipEvent_t* ev = &ctx->events[(size_t)i * (SV_NUM_KERNELS + 1)];
-    if ((e = hipEventSynchronize(ev[SV_NUM_KERNELS])) != hipSuccess) return hip_fail("hipEventSynchronize", e);
+    hipEvent_t* ev = &ctx->events[(size_t)i * 2 * SV_NUM_KERNELS];
+    const uint8_t* launched = &ctx->launched[(size_t)i * SV_NUM_KERNELS];
     for (int k = 0; k < SV_NUM_KERNELS; ++k) {
+      if (!launched[k]) continue;
+      if ((e = hipEventSynchronize(ev[2 * k + 1])) != hipSuccess) return hip_fail("hipEventSynchronize", e);
       float ms = 0.f;
-      if ((e = hipEventElapsedTime(&ms, ev[k], ev[k + 1])) != hipSuccess) return hip_fail("hipEventElapsedTime", e);
+      if ((e = hipEventElapsedTime(&ms, ev[2 * k], ev[2 * k + 1])) != hipSuccess) return hip_fail("hipEventElapsedTime", e);
       ms_per_kernel[k] += ms;
     }
   }

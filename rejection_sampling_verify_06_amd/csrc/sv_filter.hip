@@ -594,9 +594,9 @@ __global__ void __launch_bounds__(kFThreads) k_filter(Params P) {
     filter_row<false>(P, sh, pp, rowp, nch, ce, c, mc, M, use_k, topk, use_p, topp, xs, tau_out);
 }
 
-hipError_t launch_filter(const Params& p, hipStream_t st) {
-  if (p.B <= 0 || (!p.top_k && !p.top_p)) return hipSuccess;
-  hipLaunchKernelGGL(k_filter, dim3(p.slots, p.B), dim3(kFThreads), 0, st, p);
+hipError_t launch_filter(const Params& p, hipStream_t st, const LaunchEvents* ev) {
+  if (p.B <= 0 || (!p.top_k && !p.top_p)) return record_empty(st, ev);
+  launch_timed(k_filter, dim3(p.slots, p.B), dim3(kFThreads), st, ev, p);
   return hipGetLastError();
 }
 

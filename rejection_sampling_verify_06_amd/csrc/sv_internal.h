@@ -2,6 +2,7 @@
 // (sv_kernels.hip).  Not part of the public interface.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -119,6 +120,31 @@ struct NgramParams {
 
 hipError_t launch_ngram(const NgramParams& p, hipStream_t st);
 
+// Optional timing of one launch: the pair is recorded by the dispatch itself
+// (hipExtLaunchKernel), so the elapsed time is the kernel's, without the gap
+// that separately recorded events add.
+struct LaunchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+  uint8_t* launched;   // set to 1 when the pair was recorded by a launch
+};
+
+template <typename K, typename... A>
+inline void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t st, const LaunchEvents* ev, A... args) {
+  if (ev) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev->start, ev->stop, 0, args...);
+    *ev->launched = 1;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  }
+}
+
+// a slot with no work: nothing is recorded and the slot reads 0
+inline hipError_t record_empty(hipStream_t, const LaunchEvents* ev) {
+  if (ev) *ev->launched = 0;
+  return hipSuccess;
+}
+
 // acceptance statistics and draft-length controllers
 constexpr int kStatsMaxK = kMaxK;                       // positions tracked per round
 constexpr int kStatsMaxWords = 8 + 3 * kStatsMaxK;
@@ -154,9 +180,9 @@ hipError_t launch_adapt_reset(const AdaptParams& p, hipStream_t st);
 
 // The kernels of one verify step, in stream order (select only when
 // nsplit > 1).
-hipError_t launch_row_stats(const Params& p, hipStream_t st);
-hipError_t launch_filter(const Params& p, hipStream_t st);
-hipError_t launch_final(const Params& p, hipStream_t st);
-hipError_t launch_select(const Params& p, hipStream_t st);
+hipError_t launch_row_stats(const Params& p, hipStream_t st, const LaunchEvents* ev = nullptr);
+hipError_t launch_filter(const Params& p, hipStream_t st, const LaunchEvents* ev = nullptr);
+hipError_t launch_final(const Params& p, hipStream_t st, const LaunchEvents* ev = nullptr);
+hipError_t launch_select(const Params& p, hipStream_t st, const LaunchEvents* ev = nullptr);
 
 }  // namespace sv

@@ -1469,28 +1469,28 @@ __global__ void __launch_bounds__(kFinThreads) k_select(Params P) {
 // launchers
 // ---------------------------------------------------------------------------
 
-hipError_t launch_row_stats(const Params& p, hipStream_t st) {
+hipError_t launch_row_stats(const Params& p, hipStream_t st, const LaunchEvents* ev) {
   const int64_t blocks = (int64_t)p.n_t * p.nch_t + (int64_t)p.n_d * p.nch_d;
-  if (blocks <= 0) return hipSuccess;
+  if (blocks <= 0) return record_empty(st, ev);
   const dim3 g((unsigned)blocks), b(kThreads);
   if (p.t_bf16) {
-    if (p.d_bf16) hipLaunchKernelGGL((k_row_stats<true, true>), g, b, 0, st, p);
-    else hipLaunchKernelGGL((k_row_stats<true, false>), g, b, 0, st, p);
+    if (p.d_bf16) launch_timed(k_row_stats<true, true>, g, b, st, ev, p);
+    else launch_timed(k_row_stats<true, false>, g, b, st, ev, p);
   } else {
-    if (p.d_bf16) hipLaunchKernelGGL((k_row_stats<false, true>), g, b, 0, st, p);
-    else hipLaunchKernelGGL((k_row_stats<false, false>), g, b, 0, st, p);
+    if (p.d_bf16) launch_timed(k_row_stats<false, true>, g, b, st, ev, p);
+    else launch_timed(k_row_stats<false, false>, g, b, st, ev, p);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_final(const Params& p, hipStream_t st) {
-  hipLaunchKernelGGL(k_final, dim3(p.nsplit, p.B), dim3(kFinThreads), 0, st, p);
+hipError_t launch_final(const Params& p, hipStream_t st, const LaunchEvents* ev) {
+  launch_timed(k_final, dim3(p.nsplit, p.B), dim3(kFinThreads), st, ev, p);
   return hipGetLastError();
 }
 
-hipError_t launch_select(const Params& p, hipStream_t st) {
-  if (p.nsplit <= 1) return hipSuccess;
-  hipLaunchKernelGGL(k_select, dim3(p.B), dim3(kFinThreads), 0, st, p);
+hipError_t launch_select(const Params& p, hipStream_t st, const LaunchEvents* ev) {
+  if (p.nsplit <= 1) return record_empty(st, ev);
+  launch_timed(k_select, dim3(p.B), dim3(kFinThreads), st, ev, p);
   return hipGetLastError();
 }
 
