@@ -301,15 +301,16 @@ def bench_ngram(args):
     seqs = np.mean([batches[r].batch for r in sets])
     toks = np.mean([batches[r].total_len for r in sets])
     ms_step = elapsed * 1e3 / args.steps
-    # per-launch duration from HIP events on the stream the kernel runs on
+    # per-launch duration: K more launches back to back between two HIP events on the stream the
+    # kernel runs on (events between single launches would add their own gaps to each)
     st = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
     for i in range(args.steps):
-        ev[i][0].record(st)
         step(args.warmup + args.steps + i)
-        ev[i][1].record(st)
+    e1.record(st)
     torch.cuda.synchronize()
-    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    launch_ms = e0.elapsed_time(e1) / args.steps
     ev_sets = sorted(set((args.warmup + args.steps + i) % R for i in range(args.steps)))
     scan = {r: ngram_scan_bytes(batches[r], outs[r][2]["match_n"].cpu().numpy()) for r in ev_sets}
     scan_bytes = np.mean([scan[(args.warmup + args.steps + i) % R] for i in range(args.steps)])
