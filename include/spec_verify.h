@@ -67,6 +67,7 @@
  *   off_t[s] = off_d[s] + s             target rows / emitted_tokens
  *   target row off_t[s]+i judges draft token i; row off_t[s]+K_s is the bonus row.
  *   Logit rows are ld elements apart (ld >= vocab); columns >= vocab are never read.
+ *   Logits pointers are aligned to their element size (4 bytes fp32, 2 bf16).
  *
  * Arithmetic: float32 (logits are read as float32 or bfloat16 and widened
  * exactly); exp2-based online max/sum; fixed-order reductions, no float

@@ -224,6 +224,11 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
     set_err("spec_verify_run: draft_tokens is NULL with total_draft > 0");
     return SV_ERR_INVALID;
   }
+  if ((uintptr_t)a->target_logits % (a->target_dtype == SV_BF16 ? 2 : 4) ||
+      (a->draft_logits && (uintptr_t)a->draft_logits % (a->draft_dtype == SV_BF16 ? 2 : 4))) {
+    set_err("spec_verify_run: logits pointers must be aligned to their element size");
+    return SV_ERR_INVALID;
+  }
   if (a->ld_target < a->vocab) {
     set_err("spec_verify_run: ld_target %lld < vocab %lld", (long long)a->ld_target, (long long)a->vocab);
     return SV_ERR_INVALID;

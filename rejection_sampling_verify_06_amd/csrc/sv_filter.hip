@@ -63,9 +63,11 @@ constexpr int kLayoutKMax = 1 << 19;
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// order-preserving 32-bit key of a float (larger float, larger key; no NaN)
+// order-preserving 32-bit key of a float (larger float, larger key; no NaN);
+// -0 and +0 get the key of +0, so equal floats have equal keys
 __device__ __forceinline__ uint32_t fkey(float x) {
-  const uint32_t b = __float_as_uint(x);
+  uint32_t b = __float_as_uint(x);
+  b = (b == 0x80000000u) ? 0u : b;
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 __device__ __forceinline__ float kval(uint32_t k) {
@@ -119,9 +121,22 @@ __device__ __forceinline__ uint64_t fixed_mass_d(float d) {
   return sh >= 0 ? (m << sh) : (sh > -24 ? (m >> (-sh)) : 0);
 }
 
-struct FiltShared {
+struct HistBufs {
   uint32_t wc[kHist][kBins];   // per-pair histograms (coarse, then fine)
   uint64_t wm[kHist][kBins];
+};
+struct BoundBufs {
+  uint32_t tk[kFThreads];      // every thread's largest key
+  int32_t ci[kCap];            // candidates' token indices
+  uint64_t lsum[kWave];        // per-lane mass sums of a prefix walk
+  double zl[kWave];
+};
+
+struct FiltShared {
+  union {                      // the bounded selection runs before the histograms, never beside them
+    HistBufs hb;
+    BoundBufs bb;
+  };
   uint32_t hc[kBins];          // merged coarse histogram
   uint64_t hm[kBins];
   uint32_t fc[kBins];          // merged fine histogram
@@ -141,6 +156,8 @@ struct FiltShared {
   int ok;
   int offd;
   float M;
+  double zrow;                 // the row's mass against M, 2^-40 units, from the chunk partials
+  int nk, ne, ni;
 };
 
 // The crossing of a 256-bin histogram, run by wave 0: bins in order
@@ -325,8 +342,8 @@ __device__ __forceinline__ void histogram(FiltShared& sh, const char* rowp, int 
                                           uint32_t kmin, uint32_t* hc, uint64_t* hm) {
   const int t = threadIdx.x, h = (t / kWave) >> 1;
   for (int j = t; j < kHist * kBins; j += kFThreads) {
-    (&sh.wc[0][0])[j] = 0;
-    (&sh.wm[0][0])[j] = 0;
+    (&sh.hb.wc[0][0])[j] = 0;
+    (&sh.hb.wm[0][0])[j] = 0;
   }
   __syncthreads();
   uint32_t lc = 0;       // the coarse last bin, in registers
@@ -342,20 +359,20 @@ __device__ __forceinline__ void histogram(FiltShared& sh, const char* rowp, int 
       if (MASS) lm += fixed_mass_d(d);
       return;
     }
-    atomicAdd(&sh.wc[h][b], 1u);
-    if (MASS) atomicAdd(&sh.wm[h][b], (unsigned long long)fixed_mass_d(d));
+    atomicAdd(&sh.hb.wc[h][b], 1u);
+    if (MASS) atomicAdd(&sh.hb.wm[h][b], (unsigned long long)fixed_mass_d(d));
   });
   if (lc) {
-    atomicAdd(&sh.wc[h][kBins - 1], lc);
-    if (MASS) atomicAdd(&sh.wm[h][kBins - 1], (unsigned long long)lm);
+    atomicAdd(&sh.hb.wc[h][kBins - 1], lc);
+    if (MASS) atomicAdd(&sh.hb.wm[h][kBins - 1], (unsigned long long)lm);
   }
   __syncthreads();
   if (t < kBins) {
     uint32_t cs = 0;
     uint64_t ms = 0;
     for (int w = 0; w < kHist; ++w) {
-      cs += sh.wc[w][t];
-      if (MASS) ms += sh.wm[w][t];
+      cs += sh.hb.wc[w][t];
+      if (MASS) ms += sh.hb.wm[w][t];
     }
     hc[t] = cs;
     hm[t] = ms;
@@ -411,6 +428,268 @@ __device__ __forceinline__ uint32_t select_in_bin(FiltShared& sh, const char* ro
   return key;
 }
 
+// ---- bounded selection: two reads of the row, no per-element atomics ----
+//
+// Each thread's largest logit is an element of the row, so the k-th largest
+// of the 1024 thread maxima is at most the row's k-th largest logit: every
+// token that top-k keeps is at or above it.  For top-p alone, the maxima
+// taken from the top until their mass reaches the target give a bound with
+// the same property (everything below it has at least that much mass above
+// it).  The second read collects the tokens at or above the bound into LDS;
+// when they fit, the thresholds are selected exactly among them (a sort,
+// then counts and fixed-point mass prefixes) and the filtered chunk sums
+// are their masses.  When they do not (a bound that many tokens tie with,
+// or top-k above 1024), the histogram path takes over.
+
+constexpr int kVecPer = 4;                     // 16-byte loads in flight per thread
+
+// the row as whole 16-byte vectors plus a few single elements: `head`
+// elements before the first 16-byte boundary, `tail` after the last vector
+struct RowSplit {
+  int head, nvec, tail;
+};
+template <bool BF>
+__device__ __forceinline__ RowSplit split_row(const char* rowp, int V) {
+  constexpr int es = BF ? 2 : 4, epv = 16 / es;
+  const int mis = (int)((uintptr_t)rowp & 15);          // a multiple of es (pointers are element-aligned)
+  const int head = min(mis ? (16 - mis) / es : 0, V);
+  const int nvec = (V - head) / epv;
+  return {head, nvec, V - head - nvec * epv};
+}
+
+// the elements of one 16-byte vector (little-endian: element 2i in the low
+// half of word i for bf16); vectors past the row are filled with NaN, which
+// no comparison below accepts and fmaxf ignores
+template <bool BF>
+__device__ __forceinline__ float vec_elem(const uint4& w, int j) {
+  const uint32_t wd = (j / (BF ? 2 : 1)) == 0 ? w.x : (j / (BF ? 2 : 1)) == 1 ? w.y : (j / (BF ? 2 : 1)) == 2 ? w.z : w.w;
+  if (!BF) return __uint_as_float(wd);
+  return __uint_as_float((j & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+}
+constexpr uint32_t kNanFill = 0x7FC07FC0u;     // NaN as one fp32 word and as two bf16 halves
+
+// one pass over the row: f(x, e) for every element, kVecPer vectors per
+// thread issued before any is used; the single elements go to the first threads
+template <bool BF, typename F>
+__device__ __forceinline__ void for_row_vec(const char* rowp, const RowSplit& sp, F&& f) {
+  constexpr int es = BF ? 2 : 4, epv = 16 / es;
+  const int t = threadIdx.x;
+  const uint4* vp = (const uint4*)(rowp + (size_t)sp.head * es);
+  for (int v0 = 0; v0 < sp.nvec; v0 += kFThreads * kVecPer) {
+    uint4 w[kVecPer];
+#pragma unroll
+    for (int u = 0; u < kVecPer; ++u) {
+      const int vi = v0 + u * kFThreads + t;
+      w[u] = vi < sp.nvec ? vp[vi] : make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
+    }
+    f(w, v0);
+  }
+  if (t < sp.head + sp.tail) {
+    const int e = t < sp.head ? t : sp.head + sp.nvec * epv + (t - sp.head);
+    uint4 w[kVecPer];
+    w[0] = make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
+#pragma unroll
+    for (int u = 1; u < kVecPer; ++u) w[u] = w[0];
+    const float x = load_x<BF>(rowp, e);
+    if (BF) w[0].x = (__float_as_uint(x) >> 16) | 0x7FC00000u;   // element 0: x, element 1: NaN
+    else w[0].x = __float_as_uint(x);
+    f(w, -1 - e);                              // v0 < 0: element -1 - v0 is element 0 of w[0]
+  }
+}
+
+// index of element j of vector u of a round (v0 >= 0), or the single element
+template <bool BF>
+__device__ __forceinline__ int elem_index(const RowSplit& sp, int v0, int u, int j) {
+  constexpr int epv = BF ? 8 : 4;
+  return v0 >= 0 ? sp.head + (v0 + u * kFThreads + (int)threadIdx.x) * epv + j : -1 - v0;
+}
+
+// bitonic sort of k[0..n2) (n2 a power of two, at most 2 * kFThreads),
+// largest first, with an optional payload; every thread calls it
+__device__ __forceinline__ void sort_desc(uint32_t* k, int32_t* pay, int n2) {
+  const int t = threadIdx.x;
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int j = size >> 1; j > 0; j >>= 1) {
+      if (t < n2 / 2) {
+        const int i = ((t & ~(j - 1)) << 1) | (t & (j - 1));
+        const int l = i | j;
+        const uint32_t a = k[i], b = k[l];
+        const bool desc = (i & size) == 0;
+        if (desc ? a < b : a > b) {
+          k[i] = b;
+          k[l] = a;
+          if (pay) {
+            const int32_t pa = pay[i];
+            pay[i] = pay[l];
+            pay[l] = pa;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Wave 0: over keys[0..n) sorted largest first, the fixed-point masses
+// summed in order.  With Z = zuse (or the total of the n masses when zuse
+// < 0) and target = topp * Z (0 when topp <= 0), writes sh.ne = #{i: mass
+// strictly before i < target} and sh.ni = #{i: mass through i < target}.
+__device__ __forceinline__ void mass_prefix(FiltShared& sh, const uint32_t* keys, int n, float c, float mc,
+                                            float topp, double zuse) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int per = (n + kWave - 1) / kWave;
+  const int lo = min(lane * per, n), hi = min(lo + per, n);
+  uint64_t ls = 0;
+#pragma unroll 4
+  for (int i = lo; i < hi; ++i) ls += fixed_mass_d(fmaf(-kval(keys[i]), c, mc));
+  sh.bb.lsum[lane] = ls;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  uint64_t base = 0, tot = 0;
+#pragma unroll 8
+  for (int l = 0; l < kWave; ++l) {
+    const uint64_t v = sh.bb.lsum[l];
+    base += (l < lane) ? v : 0;
+    tot += v;
+  }
+  const double z = zuse < 0.0 ? (double)tot : zuse;
+  const double target = topp > 0.f ? (double)topp * z : 0.0;
+  uint32_t ne = 0, ni = 0;
+  uint64_t acc = base;
+#pragma unroll 4
+  for (int i = lo; i < hi; ++i) {
+    ne += (double)acc < target;
+    acc += fixed_mass_d(fmaf(-kval(keys[i]), c, mc));
+    ni += (double)acc < target;
+  }
+  ne = wave_sum_u32(ne);
+  ni = wave_sum_u32(ni);
+  if (lane == 0) {
+    sh.ne = (int)ne;
+    sh.ni = (int)ni;
+  }
+}
+
+// The bounded selection of one row; false (block-uniform) when the
+// histogram path must run instead.  On success the filtered chunk sums are
+// in sh.cs / sh.cb and the threshold key in *tau_key.
+template <bool BF>
+__device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp, int V, int ce, float c, float mc,
+                                               bool use_k, int topk, bool use_p, float topp, int xs,
+                                               uint32_t* tau_key) {
+  constexpr int epv = BF ? 8 : 4;
+  const int t = threadIdx.x;
+  if (use_k && topk > kFThreads) return false;
+  const RowSplit sp = split_row<BF>(rowp, V);
+
+  // ---- read 1: every thread's maximum ----
+  float mx = -INFINITY;
+  for_row_vec<BF>(rowp, sp, [&](const uint4(&w)[kVecPer], int) {
+#pragma unroll
+    for (int u = 0; u < kVecPer; ++u)
+#pragma unroll
+      for (int j = 0; j < epv; ++j) mx = fmaxf(mx, vec_elem<BF>(w[u], j));
+  });
+  sh.bb.tk[t] = fkey(mx);
+  if (t == 0) sh.ncand = 0;
+  __syncthreads();
+  sort_desc(sh.bb.tk, nullptr, kFThreads);
+
+  // ---- the bound ----
+  uint32_t bound;
+  if (use_k) {
+    bound = sh.bb.tk[topk - 1];
+  } else {
+    if (t < kWave) mass_prefix(sh, sh.bb.tk, kFThreads, c, mc, topp, sh.zrow);
+    __syncthreads();
+    const int j = sh.ni;                       // the first maximum whose running mass reaches the target
+    if (j >= kFThreads) {
+      __syncthreads();
+      return false;
+    }
+    bound = sh.bb.tk[j];
+  }
+  const float tf = kval(bound);
+
+  // ---- read 2: the tokens at or above the bound ----
+  // (one bit per element of a round; the rare hits are read again by index)
+  for_row_vec<BF>(rowp, sp, [&](const uint4(&w)[kVecPer], int v0) {
+    uint64_t hit = 0;
+#pragma unroll
+    for (int u = 0; u < kVecPer; ++u)
+#pragma unroll
+      for (int j = 0; j < epv; ++j) hit |= (uint64_t)(vec_elem<BF>(w[u], j) >= tf) << (u * epv + j);
+    if (__any(hit != 0)) {
+      uint32_t pos = hit ? atomicAdd(&sh.ncand, (uint32_t)__popcll(hit)) : 0u;
+      while (hit) {
+        const int b = __builtin_ctzll(hit);
+        hit &= hit - 1;
+        const int e = elem_index<BF>(sp, v0, b / epv, b % epv);
+        if (pos < (uint32_t)kCap) {
+          sh.ck[pos] = fkey(load_x<BF>(rowp, e));
+          sh.bb.ci[pos] = e;
+        }
+        ++pos;
+      }
+    }
+  });
+  __syncthreads();
+  const int n = (int)sh.ncand;
+  if (n > kCap || n < 1 || (use_k && n < topk)) {
+    __syncthreads();
+    return false;
+  }
+  int n2 = 2;
+  while (n2 < n) n2 <<= 1;
+  for (int i = n + t; i < n2; i += kFThreads) {
+    sh.ck[i] = 0u;
+    sh.bb.ci[i] = -1;
+  }
+  __syncthreads();
+  sort_desc(sh.ck, sh.bb.ci, n2);
+
+  // ---- exact thresholds among the candidates ----
+  uint32_t key = sh.ck[0];
+  int nk = n;                                  // candidates kept by top-k: keys >= the k-th largest
+  if (use_k) {
+    key = sh.ck[topk - 1];
+    if (t == 0) sh.nk = n;
+    __syncthreads();
+    for (int i = topk + t; i < n; i += kFThreads)
+      if (sh.ck[i] < key && sh.ck[i - 1] >= key) sh.nk = i;
+    __syncthreads();
+    nk = sh.nk;
+  }
+  if (use_p) {
+    if (t < kWave) mass_prefix(sh, sh.ck, nk, c, mc, topp, use_k ? -1.0 : sh.zrow);
+    __syncthreads();
+    key = sh.ck[max(sh.ne - 1, 0)];           // the last token whose mass above stays below the target
+  }
+
+  // ---- filtered chunk sums from the kept candidates ----
+  for (int i = t; i < n; i += kFThreads) {
+    const uint32_t k = sh.ck[i];
+    if (k >= key) {
+      const int e = sh.bb.ci[i];
+      const unsigned long long m = fixed_mass_d(fmaf(-kval(k), c, mc));
+      atomicAdd(&sh.cs[e / ce], m);
+      if (e < xs) atomicAdd(&sh.cb[e / ce], m);
+    }
+  }
+  __syncthreads();
+  *tau_key = key;
+  return true;
+}
+
+// the row's chunk partials as filtered sums against M, and its threshold
+__device__ __forceinline__ void write_partials(const FiltShared& sh, Partial* pp, int nch, float M, float tau,
+                                               float* tau_out) {
+  for (int k = threadIdx.x; k < nch; k += kFThreads) {
+    const Partial q = pp[k];
+    pp[k] = Partial{M, (float)((double)sh.cs[k] / kMassOne), q.idx, (float)((double)sh.cb[k] / kMassOne)};
+  }
+  if (threadIdx.x == 0) *tau_out = tau;
+}
+
 // The filter of one row (template on the row's element type).
 template <bool BF>
 __device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Partial* pp, const char* rowp, int nch,
@@ -421,6 +700,11 @@ __device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Part
   for (int j = t; j < nch; j += kFThreads) {
     sh.cs[j] = 0;
     sh.cb[j] = 0;
+  }
+  uint32_t bkey;
+  if (bounded_filter<BF>(sh, rowp, V, ce, c, mc, use_k, topk, use_p, topp, xs, &bkey)) {
+    write_partials(sh, pp, nch, M, kval(bkey), tau_out);
+    return;
   }
   // ---- coarse histogram (masses only when top-p needs them) ----
   if (use_p) histogram<BF, true>(sh, rowp, V, c, mc, -1, 0u, sh.hc, sh.hm);
@@ -520,16 +804,13 @@ __device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Part
     }
   }
   __syncthreads();
-  for (int k = t; k < nch; k += kFThreads) {
-    const Partial q = pp[k];
-    pp[k] = Partial{M, (float)((double)sh.cs[k] / kMassOne), q.idx, (float)((double)sh.cb[k] / kMassOne)};
-  }
-  if (t == 0) *tau_out = tau;
+  write_partials(sh, pp, nch, M, tau, tau_out);
 }
 
 }  // namespace
 
-__global__ void __launch_bounds__(kFThreads) k_filter(Params P) {
+// two blocks per CU (8 waves per SIMD): at most 64 VGPRs
+__global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) k_filter(Params P) {
   __shared__ FiltShared sh;
   const int r = blockIdx.x, s = blockIdx.y;
   const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
@@ -547,6 +828,7 @@ __global__ void __launch_bounds__(kFThreads) k_filter(Params P) {
   if (!use_k && !use_p) return;
   const float T = P.temperature[s];
   if (!(isfinite(T) && T >= kMinTemp)) return;
+  const float c = kLog2eF / T;
 
   const int nch = draft ? P.nch_d : P.nch_t;
   Partial* pp = P.partials + ((int64_t)s * P.slots + r) * P.nch_max;
@@ -568,10 +850,24 @@ __global__ void __launch_bounds__(kFThreads) k_filter(Params P) {
     float m = -INFINITY;
     for (int k = lane; k < nch; k += kWave) m = fmaxf(m, pp[k].m);
     m = wave_max(m);
+    // the row's mass against m from its partials (top-p without top-k
+    // measures against it), lane sums in chunk order, then lanes in order
+    double zl = 0.0;
+    if (use_p && !use_k) {
+      for (int k = lane; k < nch; k += kWave) {
+        const Partial q = pp[k];
+        if (q.m > -INFINITY) zl += (double)q.s * (double)fexp2(q.m * c - m * c);
+      }
+    }
+    sh.bb.zl[lane] = zl;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     if (lane == 0) {
+      double z = 0.0;
+      for (int l = 0; l < kWave; ++l) z += sh.bb.zl[l];
       sh.ok = !bad && tot == (uint32_t)P.total_draft;
       sh.offd = (int)bef;
       sh.M = m;
+      sh.zrow = z * kMassOne;
     }
   }
   __syncthreads();
@@ -583,7 +879,6 @@ __global__ void __launch_bounds__(kFThreads) k_filter(Params P) {
   const int64_t row = draft ? (int64_t)sh.offd + (r - mk - 1) : (int64_t)sh.offd + s + r;
   const int bf = draft ? P.d_bf16 : P.t_bf16;
   const char* rowp = (const char*)(draft ? P.dft : P.tgt) + row * (draft ? P.ld_d : P.ld_t) * (bf ? 2 : 4);
-  const float c = kLog2eF / T;
   const float mc = M * c;
   const int ce = draft ? P.ce_d : P.ce_t;
   const int xs = (md == kModeStrict && !draft && r < K) ? P.ptok[(int64_t)s * mk + r] : -1;
