@@ -63,6 +63,11 @@ constexpr int kLayoutKMax = 1 << 19;
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// a block-uniform value read from LDS, moved to a scalar register
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ float uni(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
+
 // order-preserving 32-bit key of a float (larger float, larger key; no NaN);
 // -0 and +0 get the key of +0, so equal floats have equal keys
 __device__ __forceinline__ uint32_t fkey(float x) {
@@ -141,13 +146,14 @@ struct FiltShared {
   uint64_t hm[kBins];
   uint32_t fc[kBins];          // merged fine histogram
   uint64_t fm[kBins];
-  uint32_t ck[kCap];           // candidates: keys and masses
+  alignas(16) uint32_t ck[kCap + 4];   // candidates: keys (4 spare entries for padding) and masses
   uint64_t cm[kCap];
   uint32_t rc[kBins];          // radix byte histogram
   uint64_t rm[kBins];
   uint64_t cs[kMaxChunks];     // filtered chunk sums, fixed point
   uint64_t cb[kMaxChunks];     // their parts below the proposal (strict target rows)
   uint32_t ncand, kmin_c, kmax_c;
+  uint32_t tmin, nkc;          // bounded selection: smallest kept key, kept-set counter
   int last;                    // last non-empty bin of the latest crossing search
   uint64_t amass;
   int bin;
@@ -249,13 +255,13 @@ __device__ __forceinline__ bool in_region(const Region& rg, float d, uint32_t k)
 }
 
 // One slot per candidate: a ballot per wave and one LDS atomic by its first lane.
-__device__ __forceinline__ uint32_t claim_slot(FiltShared& sh, bool want) {
+__device__ __forceinline__ uint32_t claim_slot(uint32_t* counter, bool want) {
   const unsigned long long m = __ballot(want);
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t base = 0;
   if (m) {
     const int leader = __ffsll((long long)m) - 1;
-    if (lane == leader) base = atomicAdd(&sh.ncand, (uint32_t)__popcll(m));
+    if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
     base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
   }
   const unsigned long long below = (lane == 0) ? 0ull : (m & (~0ull >> (kWave - lane)));
@@ -280,7 +286,7 @@ __device__ __forceinline__ uint32_t select_region(FiltShared& sh, const char* ro
     const float d = fmaf(-x, c, mc);
     const uint32_t k = fkey(x);
     const bool want = in_region(rg, d, k);
-    const uint32_t i = claim_slot(sh, want);
+    const uint32_t i = claim_slot(&sh.ncand, want);
     if (want) {
       if (i < (uint32_t)kCap) {
         sh.ck[i] = k;
@@ -431,8 +437,9 @@ __device__ __forceinline__ uint32_t select_in_bin(FiltShared& sh, const char* ro
 // ---- bounded selection: two reads of the row, no per-element atomics ----
 //
 // Each thread's largest logit is an element of the row, so the k-th largest
-// of the 1024 thread maxima is at most the row's k-th largest logit: every
-// token that top-k keeps is at or above it.  For top-p alone, the maxima
+// of the 1024 thread maxima (over the whole row or a prefix of it) is at
+// most the row's k-th largest logit: every token that top-k keeps is at or
+// above it.  For top-p alone, the maxima
 // taken from the top until their mass reaches the target give a bound with
 // the same property (everything below it has at least that much mass above
 // it).  The second read collects the tokens at or above the bound into LDS;
@@ -468,32 +475,37 @@ __device__ __forceinline__ float vec_elem(const uint4& w, int j) {
 }
 constexpr uint32_t kNanFill = 0x7FC07FC0u;     // NaN as one fp32 word and as two bf16 halves
 
-// one pass over the row: f(x, e) for every element, kVecPer vectors per
-// thread issued before any is used; the single elements go to the first threads
-template <bool BF, typename F>
-__device__ __forceinline__ void for_row_vec(const char* rowp, const RowSplit& sp, F&& f) {
-  constexpr int es = BF ? 2 : 4, epv = 16 / es;
+// rounds of 16-byte vectors [vb, ve) (vb a multiple of kFThreads * kVecPer):
+// f(w, v0) per round, vectors at or past ve filled with NaN
+template <typename F>
+__device__ __forceinline__ void for_rounds(const uint4* vp, int vb, int ve, F&& f) {
   const int t = threadIdx.x;
-  const uint4* vp = (const uint4*)(rowp + (size_t)sp.head * es);
-  for (int v0 = 0; v0 < sp.nvec; v0 += kFThreads * kVecPer) {
+  for (int v0 = vb; v0 < ve; v0 += kFThreads * kVecPer) {
     uint4 w[kVecPer];
 #pragma unroll
     for (int u = 0; u < kVecPer; ++u) {
       const int vi = v0 + u * kFThreads + t;
-      w[u] = vi < sp.nvec ? vp[vi] : make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
+      w[u] = vi < ve ? vp[vi] : make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
     }
     f(w, v0);
   }
+}
+
+// the head and tail elements of a row split: f(w, -1 - e) with element e as
+// element 0 of w[0] and NaN everywhere else, by the first head + tail threads
+template <bool BF, typename F>
+__device__ __forceinline__ void for_singles(const char* rowp, const RowSplit& sp, F&& f) {
+  constexpr int epv = BF ? 8 : 4;
+  const int t = threadIdx.x;
   if (t < sp.head + sp.tail) {
     const int e = t < sp.head ? t : sp.head + sp.nvec * epv + (t - sp.head);
     uint4 w[kVecPer];
-    w[0] = make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
 #pragma unroll
-    for (int u = 1; u < kVecPer; ++u) w[u] = w[0];
+    for (int u = 0; u < kVecPer; ++u) w[u] = make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
     const float x = load_x<BF>(rowp, e);
     if (BF) w[0].x = (__float_as_uint(x) >> 16) | 0x7FC00000u;   // element 0: x, element 1: NaN
     else w[0].x = __float_as_uint(x);
-    f(w, -1 - e);                              // v0 < 0: element -1 - v0 is element 0 of w[0]
+    f(w, -1 - e);
   }
 }
 
@@ -569,6 +581,126 @@ __device__ __forceinline__ void mass_prefix(FiltShared& sh, const uint32_t* keys
   }
 }
 
+// A lower bound of the key at a crossing among one key per thread: the
+// need-th largest (by count) or the key where the mass from the top first
+// reaches `target` (by mass), taken 8 bits a pass for `passes` passes; the
+// bits below are returned as zeros (so the result is at most the exact key,
+// which it equals after 4 passes).  Leaves sh.bin < 0 when the first pass
+// never reaches the target (mass only; the key returned is then
+// meaningless).  Every thread of the block calls it.
+template <bool BY_MASS>
+__device__ __forceinline__ uint32_t radix_select_regs(FiltShared& sh, uint32_t key, unsigned long long mass,
+                                                      uint32_t need, double target, int passes) {
+  const int t = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  for (int pass = 0; pass < passes; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (t < kBins) {
+      sh.rc[t] = 0;
+      sh.rm[t] = 0;
+    }
+    __syncthreads();
+    if ((key & pmask) == prefix) {
+      const int by = (key >> shift) & 0xFF;
+      atomicAdd(&sh.rc[by], 1u);
+      if (BY_MASS) atomicAdd(&sh.rm[by], mass);
+    }
+    __syncthreads();
+    if (t < kWave) scan_bins<BY_MASS>(sh, sh.rc, sh.rm, true, need, target);
+    __syncthreads();
+    const int bin = uni(sh.bin);
+    if (bin < 0) return 0u;                    // block-uniform
+    prefix |= (uint32_t)bin << shift;
+    pmask |= 0xFFu << shift;
+    if (BY_MASS) target = sh.rem;
+    else need = uni(sh.need);
+    __syncthreads();
+  }
+  return prefix;
+}
+
+constexpr int kRankP = 512;
+// 16 key bits (sign, exponent, 7 mantissa bits) of the bound: within 2^-7
+// of the exact maximum, for 8 barriers instead of 16
+constexpr int kBoundPasses = 2;
+constexpr uint32_t kKeyNegInf = 0x007FFFFFu;   // fkey(-inf)                    // top-p alone: the most candidates selected by ranks
+
+// Exact thresholds among the n candidates in sh.ck after sorting them
+// (largest first): the top-k key (the k-th), the kept set's end, then the
+// top-p key from fixed-point mass prefixes.  Returns the smallest kept key.
+__device__ __forceinline__ uint32_t sorted_thresholds(FiltShared& sh, int n, float c, float mc, bool use_k, int topk,
+                                                      bool use_p, float topp) {
+  const int t = threadIdx.x;
+  uint32_t key = sh.ck[0];
+  int nk = n;                                  // candidates kept by top-k: keys >= the k-th largest
+  if (use_k) {
+    key = sh.ck[topk - 1];
+    if (t == 0) sh.nk = n;
+    __syncthreads();
+    for (int i = topk + t; i < n; i += kFThreads)
+      if (sh.ck[i] < key && sh.ck[i - 1] >= key) sh.nk = i;
+    __syncthreads();
+    nk = sh.nk;
+  }
+  if (use_p) {
+    if (t < kWave) mass_prefix(sh, sh.ck, nk, c, mc, topp, use_k ? -1.0 : sh.zrow);
+    __syncthreads();
+    key = sh.ck[max(sh.ne - 1, 0)];           // the last token whose mass above stays below the target
+  }
+  return key;
+}
+
+// Exact thresholds among n <= kFThreads unsorted candidates, thread t
+// holding candidate t: top-k keeps a candidate with fewer than k larger
+// keys (counted over the candidates, four keys a read); top-p then runs over
+// the kept set, compacted, each member summing the masses above it and the
+// set's total (integers, so the order does not matter); the largest key is
+// always kept.  Returns the smallest kept key.
+__device__ __forceinline__ uint32_t select_by_rank(FiltShared& sh, int n, float c, float mc, bool use_k, int topk,
+                                                   bool use_p, float topp) {
+  const int t = threadIdx.x;
+  if (t < 4) sh.ck[n + t] = 0u;               // below every candidate: pads the last 4-wide read
+  __syncthreads();
+  const bool mine = t < n;
+  const uint32_t kt = mine ? sh.ck[t] : 0u;
+  bool kept = mine;
+  if (use_k && mine) {
+    int rank = 0;
+    for (int j = 0; j < n; j += 4) {
+      const uint4 q = *(const uint4*)&sh.ck[j];
+      rank += (int)(q.x > kt) + (int)(q.y > kt) + (int)(q.z > kt) + (int)(q.w > kt);
+    }
+    kept = rank < topk;
+  }
+  if (!use_p) {
+    if (kept) atomicMin(&sh.tmin, kt);
+    __syncthreads();
+    return sh.tmin;
+  }
+  // the kept set, compacted: keys in tk, masses in cm
+  const uint32_t pos = claim_slot(&sh.nkc, kept);
+  if (kept) {
+    sh.bb.tk[pos] = kt;
+    sh.cm[pos] = fixed_mass_d(fmaf(-kval(kt), c, mc));
+  }
+  __syncthreads();
+  const int nk = (int)sh.nkc;
+  if (t < nk) {
+    const uint32_t ku = sh.bb.tk[t];
+    uint64_t above = 0, tot = 0;
+    for (int j = 0; j < nk; ++j) {
+      const uint32_t kj = sh.bb.tk[j];
+      const uint64_t mj = sh.cm[j];
+      tot += mj;
+      above += (kj > ku) ? mj : 0;
+    }
+    const double target = topp > 0.f ? (double)topp * (use_k ? (double)tot : sh.zrow) : 0.0;
+    if (above == 0 || (double)above < target) atomicMin(&sh.tmin, ku);
+  }
+  __syncthreads();
+  return sh.tmin;
+}
+
 // The bounded selection of one row; false (block-uniform) when the
 // histogram path must run instead.  On success the filtered chunk sums are
 // in sh.cs / sh.cb and the threshold key in *tau_key.
@@ -580,39 +712,60 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
   const int t = threadIdx.x;
   if (use_k && topk > kFThreads) return false;
   const RowSplit sp = split_row<BF>(rowp, V);
+  const uint4* vp = (const uint4*)(rowp + (size_t)sp.head * (BF ? 2 : 4));
+  constexpr int kRound = kFThreads * kVecPer;  // vectors per round
+  // Top-k reads only a sample here, the first nva whole vectors: the k-th
+  // largest of any subset is at most the row's k-th largest, and a fraction
+  // 8k/kCap of the row leaves about kCap/8 tokens at or above the bound.
+  // Top-p alone reads every vector (a sample could miss the heaviest
+  // tokens).  Either way the head and tail elements are left to read 2.
+  const int nva = use_k ? (int)min((int64_t)sp.nvec, max((int64_t)kRound,
+                                                          ((int64_t)V * 8 * topk / kCap + epv - 1) / epv))
+                        : sp.nvec;
 
-  // ---- read 1: every thread's maximum ----
+  // ---- read 1: every thread's maximum over the sample ----
+  // (the first round stays in registers for read 2)
+  uint4 w0[kVecPer];
+#pragma unroll
+  for (int u = 0; u < kVecPer; ++u) {
+    const int vi = u * kFThreads + t;
+    w0[u] = vi < sp.nvec ? vp[vi] : make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
+  }
   float mx = -INFINITY;
-  for_row_vec<BF>(rowp, sp, [&](const uint4(&w)[kVecPer], int) {
+  auto take_max = [&](const uint4(&w)[kVecPer], int) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kVecPer; ++u)
 #pragma unroll
       for (int j = 0; j < epv; ++j) mx = fmaxf(mx, vec_elem<BF>(w[u], j));
-  });
-  sh.bb.tk[t] = fkey(mx);
-  if (t == 0) sh.ncand = 0;
-  __syncthreads();
-  sort_desc(sh.bb.tk, nullptr, kFThreads);
-
-  // ---- the bound ----
+  };
+  take_max(w0, 0);
+  for_rounds(vp, kRound, nva, take_max);
+  // ---- the bound: an exact radix select over the maxima's keys ----
+  // (by count for top-k: the k-th largest maximum; by mass for top-p alone:
+  // the maximum where their mass from the top reaches the target)
+  if (t == 0) {
+    sh.ncand = 0;
+    sh.tmin = 0xFFFFFFFFu;
+    sh.nkc = 0;
+  }
+  const uint32_t kmx = fkey(mx);               // a thread without elements: the key of -inf, mass 0
   uint32_t bound;
   if (use_k) {
-    bound = sh.bb.tk[topk - 1];
+    bound = radix_select_regs<false>(sh, kmx, 0ull, (uint32_t)topk, 0.0, kBoundPasses);
   } else {
-    if (t < kWave) mass_prefix(sh, sh.bb.tk, kFThreads, c, mc, topp, sh.zrow);
-    __syncthreads();
-    const int j = sh.ni;                       // the first maximum whose running mass reaches the target
-    if (j >= kFThreads) {
+    bound = radix_select_regs<true>(sh, kmx, fixed_mass_d(fmaf(-mx, c, mc)), 0u,
+                                    topp > 0.f ? (double)topp * sh.zrow : 0.0, kBoundPasses);
+    if (sh.bin < 0) {                          // the maxima do not reach the target mass
       __syncthreads();
       return false;
     }
-    bound = sh.bb.tk[j];
   }
+  bound = max(bound, kKeyNegInf);              // keys below that of -inf are NaN patterns
   const float tf = kval(bound);
 
   // ---- read 2: the tokens at or above the bound ----
   // (one bit per element of a round; the rare hits are read again by index)
-  for_row_vec<BF>(rowp, sp, [&](const uint4(&w)[kVecPer], int v0) {
+  auto collect = [&](const uint4(&w)[kVecPer], int v0) __attribute__((always_inline)) {
     uint64_t hit = 0;
 #pragma unroll
     for (int u = 0; u < kVecPer; ++u)
@@ -631,38 +784,29 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
         ++pos;
       }
     }
-  });
+  };
+  collect(w0, 0);
+  for_rounds(vp, kRound, sp.nvec, collect);
+  for_singles<BF>(rowp, sp, collect);
   __syncthreads();
-  const int n = (int)sh.ncand;
+  const int n = uni((int)sh.ncand);
   if (n > kCap || n < 1 || (use_k && n < topk)) {
     __syncthreads();
     return false;
   }
-  int n2 = 2;
-  while (n2 < n) n2 <<= 1;
-  for (int i = n + t; i < n2; i += kFThreads) {
-    sh.ck[i] = 0u;
-    sh.bb.ci[i] = -1;
-  }
-  __syncthreads();
-  sort_desc(sh.ck, sh.bb.ci, n2);
-
-  // ---- exact thresholds among the candidates ----
-  uint32_t key = sh.ck[0];
-  int nk = n;                                  // candidates kept by top-k: keys >= the k-th largest
-  if (use_k) {
-    key = sh.ck[topk - 1];
-    if (t == 0) sh.nk = n;
+  uint32_t key;
+  if (n <= kFThreads && (use_k || n <= kRankP)) {
+    key = select_by_rank(sh, n, c, mc, use_k, topk, use_p, topp);
+  } else {
+    int n2 = 2;
+    while (n2 < n) n2 <<= 1;
+    for (int i = n + t; i < n2; i += kFThreads) {
+      sh.ck[i] = 0u;
+      sh.bb.ci[i] = -1;
+    }
     __syncthreads();
-    for (int i = topk + t; i < n; i += kFThreads)
-      if (sh.ck[i] < key && sh.ck[i - 1] >= key) sh.nk = i;
-    __syncthreads();
-    nk = sh.nk;
-  }
-  if (use_p) {
-    if (t < kWave) mass_prefix(sh, sh.ck, nk, c, mc, topp, use_k ? -1.0 : sh.zrow);
-    __syncthreads();
-    key = sh.ck[max(sh.ne - 1, 0)];           // the last token whose mass above stays below the target
+    sort_desc(sh.ck, sh.bb.ci, n2);
+    key = sorted_thresholds(sh, n, c, mc, use_k, topk, use_p, topp);
   }
 
   // ---- filtered chunk sums from the kept candidates ----
@@ -871,12 +1015,13 @@ __global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(
     }
   }
   __syncthreads();
-  if (!sh.ok) return;                        // the scan reports the layout
-  const float M = sh.M;
+  if (!uni(sh.ok)) return;                   // the scan reports the layout
+  const float M = uni(sh.M);
   if (!(M > -INFINITY && M < INFINITY)) return;   // an all -inf or non-finite row: the scan reports it
   if (nch > kMaxChunks) return;              // cannot happen within the context's vocabulary limit
 
-  const int64_t row = draft ? (int64_t)sh.offd + (r - mk - 1) : (int64_t)sh.offd + s + r;
+  const int offd = uni(sh.offd);
+  const int64_t row = draft ? (int64_t)offd + (r - mk - 1) : (int64_t)offd + s + r;
   const int bf = draft ? P.d_bf16 : P.t_bf16;
   const char* rowp = (const char*)(draft ? P.dft : P.tgt) + row * (draft ? P.ld_d : P.ld_t) * (bf ? 2 : 4);
   const float mc = M * c;

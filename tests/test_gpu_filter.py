@@ -114,3 +114,20 @@ def test_c3_with_filters_bench_context(torch_mod):
             gu.check_batch(v, b, torch_mod, label=f"C3 step {step} top_k={k} top_p={p}, bench context")
     finally:
         v.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bounded_selection_edges(verifier, torch_mod, dtype):
+    """Top-k at the edges of the bounded selection (1, 1023, 1024; 1025 takes
+    the histogram path), with and without top-p, on rows that are not
+    16-byte aligned; a second call gives bitwise the same outputs."""
+    b = make_random_batch(540 + (dtype == "bf16"), B=16, V=40000, kmax=4, dtype=dtype, ld_pad=5,
+                          modes=ALL_MODES)
+    b.top_k = np.array([1, 1023, 1024, 1025, 300, 1024, 1, 1025] * 2, np.int32)
+    b.top_p = np.array([1.0] * 8 + [0.9, 0.5, 0.99, 0.9, 0.0, 0.7, 0.95, 0.8], np.float32)
+    _, out, _ = gu.check_batch(verifier, b, torch_mod, label=f"bounded selection edges {dtype}")
+    again = gu.run_gpu(verifier, b, torch_mod)
+    for k in ("accepted_len", "emitted", "status"):
+        assert np.array_equal(out[k], again[k]), k
+    assert np.array_equal(out["p_at"], again["p_at"], equal_nan=True)
+    assert np.array_equal(out["q_at"], again["q_at"], equal_nan=True)
