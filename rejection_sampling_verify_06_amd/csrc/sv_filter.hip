@@ -11,7 +11,7 @@
 // after top-k, keeps a token iff the mass of the strictly larger tokens is
 // below p (the largest logit always kept).
 //
-// One 1024-thread block per used slot of a filtered sequence, after the row
+// One 512-thread block per used slot of a filtered sequence, after the row
 // statistics:
 //   1. the row maximum M from the row's chunk partials;
 //   2. a coarse histogram of d = M*c - x*c in steps of 1/8 (log2 units; the
@@ -45,14 +45,14 @@ namespace {
 
 using namespace wave;
 
-constexpr int kFThreads = 1024;
+constexpr int kFThreads = 512;
 constexpr int kFWaves = kFThreads / kWave;
-constexpr int kHist = 8;                       // histogram copies (one per pair of waves)
+constexpr int kHist = kFWaves / 2;             // histogram copies (one per pair of waves)
 constexpr int kBins = 256;
 constexpr float kBinScale = 8.f;               // bins per log2 unit below the row maximum
 constexpr float kBinSpan = kBins / kBinScale;  // 32: d beyond this falls into the last bin
 constexpr float kFineScale = 2048.f;           // fine bins per log2 unit inside one coarse bin
-constexpr int kCap = 2048;                     // candidates held in LDS
+constexpr int kCap = 1024;                     // candidates held in LDS
 constexpr int kUnroll = 16;                    // loads in flight per thread
 constexpr int kMaxChunks = kMaxTiles * kTileElems / (kChunkBytes / 4);   // 256
 constexpr double kMassOne = 1099511627776.0;   // 2^40
@@ -131,7 +131,7 @@ struct HistBufs {
   uint64_t wm[kHist][kBins];
 };
 struct BoundBufs {
-  uint32_t tk[kFThreads];      // every thread's largest key
+  uint32_t tk[kFThreads];      // the compacted kept set's keys
   int32_t ci[kCap];            // candidates' token indices
   uint64_t lsum[kWave];        // per-lane mass sums of a prefix walk
   double zl[kWave];
@@ -436,8 +436,8 @@ __device__ __forceinline__ uint32_t select_in_bin(FiltShared& sh, const char* ro
 
 // ---- bounded selection: two reads of the row, no per-element atomics ----
 //
-// Each thread's largest logit is an element of the row, so the k-th largest
-// of the 1024 thread maxima (over the whole row or a prefix of it) is at
+// Each thread's largest logits are elements of the row, so the k-th largest
+// of the 1024 maxima (two per thread, over the whole row or a prefix of it) is at
 // most the row's k-th largest logit: every token that top-k keeps is at or
 // above it.  For top-p alone, the maxima
 // taken from the top until their mass reaches the target give a bound with
@@ -581,7 +581,7 @@ __device__ __forceinline__ void mass_prefix(FiltShared& sh, const uint32_t* keys
   }
 }
 
-// A lower bound of the key at a crossing among one key per thread: the
+// A lower bound of the key at a crossing among two keys per thread: the
 // need-th largest (by count) or the key where the mass from the top first
 // reaches `target` (by mass), taken 8 bits a pass for `passes` passes; the
 // bits below are returned as zeros (so the result is at most the exact key,
@@ -589,8 +589,9 @@ __device__ __forceinline__ void mass_prefix(FiltShared& sh, const uint32_t* keys
 // never reaches the target (mass only; the key returned is then
 // meaningless).  Every thread of the block calls it.
 template <bool BY_MASS>
-__device__ __forceinline__ uint32_t radix_select_regs(FiltShared& sh, uint32_t key, unsigned long long mass,
-                                                      uint32_t need, double target, int passes) {
+__device__ __forceinline__ uint32_t radix_select_regs(FiltShared& sh, uint32_t ka, unsigned long long ma,
+                                                      uint32_t kb, unsigned long long mb, uint32_t need,
+                                                      double target, int passes) {
   const int t = threadIdx.x;
   uint32_t prefix = 0, pmask = 0;
   for (int pass = 0; pass < passes; ++pass) {
@@ -600,10 +601,15 @@ __device__ __forceinline__ uint32_t radix_select_regs(FiltShared& sh, uint32_t k
       sh.rm[t] = 0;
     }
     __syncthreads();
-    if ((key & pmask) == prefix) {
-      const int by = (key >> shift) & 0xFF;
+    if ((ka & pmask) == prefix) {
+      const int by = (ka >> shift) & 0xFF;
       atomicAdd(&sh.rc[by], 1u);
-      if (BY_MASS) atomicAdd(&sh.rm[by], mass);
+      if (BY_MASS) atomicAdd(&sh.rm[by], ma);
+    }
+    if ((kb & pmask) == prefix) {
+      const int by = (kb >> shift) & 0xFF;
+      atomicAdd(&sh.rc[by], 1u);
+      if (BY_MASS) atomicAdd(&sh.rm[by], mb);
     }
     __syncthreads();
     if (t < kWave) scan_bins<BY_MASS>(sh, sh.rc, sh.rm, true, need, target);
@@ -619,11 +625,12 @@ __device__ __forceinline__ uint32_t radix_select_regs(FiltShared& sh, uint32_t k
   return prefix;
 }
 
-constexpr int kRankP = 512;
+constexpr int kRankP = 512;                    // top-p alone: the most candidates selected by ranks
+constexpr int kTargetCand = 256;               // top-k: tokens expected at or above the bound
 // 16 key bits (sign, exponent, 7 mantissa bits) of the bound: within 2^-7
 // of the exact maximum, for 8 barriers instead of 16
 constexpr int kBoundPasses = 2;
-constexpr uint32_t kKeyNegInf = 0x007FFFFFu;   // fkey(-inf)                    // top-p alone: the most candidates selected by ranks
+constexpr uint32_t kKeyNegInf = 0x007FFFFFu;   // fkey(-inf)
 
 // Exact thresholds among the n candidates in sh.ck after sorting them
 // (largest first): the top-k key (the k-th), the kept set's end, then the
@@ -710,17 +717,18 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
                                                uint32_t* tau_key) {
   constexpr int epv = BF ? 8 : 4;
   const int t = threadIdx.x;
-  if (use_k && topk > kFThreads) return false;
+  if (use_k && topk > 2 * kFThreads) return false;
   const RowSplit sp = split_row<BF>(rowp, V);
   const uint4* vp = (const uint4*)(rowp + (size_t)sp.head * (BF ? 2 : 4));
   constexpr int kRound = kFThreads * kVecPer;  // vectors per round
   // Top-k reads only a sample here, the first nva whole vectors: the k-th
   // largest of any subset is at most the row's k-th largest, and a fraction
-  // 8k/kCap of the row leaves about kCap/8 tokens at or above the bound.
-  // Top-p alone reads every vector (a sample could miss the heaviest
-  // tokens).  Either way the head and tail elements are left to read 2.
+  // k/kTargetCand of the row leaves about kTargetCand tokens at or above the
+  // bound.  Top-p alone reads every vector (a sample could miss the
+  // heaviest tokens).  Either way the head and tail elements are left to
+  // read 2.
   const int nva = use_k ? (int)min((int64_t)sp.nvec, max((int64_t)kRound,
-                                                          ((int64_t)V * 8 * topk / kCap + epv - 1) / epv))
+                                                          ((int64_t)V * topk / kTargetCand + epv - 1) / epv))
                         : sp.nvec;
 
   // ---- read 1: every thread's maximum over the sample ----
@@ -731,12 +739,16 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
     const int vi = u * kFThreads + t;
     w0[u] = vi < sp.nvec ? vp[vi] : make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
   }
-  float mx = -INFINITY;
+  // two maxima per thread, over its even and its odd vectors of each round
+  float mxa = -INFINITY, mxb = -INFINITY;
   auto take_max = [&](const uint4(&w)[kVecPer], int) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kVecPer; ++u)
 #pragma unroll
-      for (int j = 0; j < epv; ++j) mx = fmaxf(mx, vec_elem<BF>(w[u], j));
+      for (int j = 0; j < epv; ++j) {
+        if (u & 1) mxb = fmaxf(mxb, vec_elem<BF>(w[u], j));
+        else mxa = fmaxf(mxa, vec_elem<BF>(w[u], j));
+      }
   };
   take_max(w0, 0);
   for_rounds(vp, kRound, nva, take_max);
@@ -748,13 +760,13 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
     sh.tmin = 0xFFFFFFFFu;
     sh.nkc = 0;
   }
-  const uint32_t kmx = fkey(mx);               // a thread without elements: the key of -inf, mass 0
+  const uint32_t ka = fkey(mxa), kb = fkey(mxb);   // no elements: the key of -inf, mass 0
   uint32_t bound;
   if (use_k) {
-    bound = radix_select_regs<false>(sh, kmx, 0ull, (uint32_t)topk, 0.0, kBoundPasses);
+    bound = radix_select_regs<false>(sh, ka, 0ull, kb, 0ull, (uint32_t)topk, 0.0, kBoundPasses);
   } else {
-    bound = radix_select_regs<true>(sh, kmx, fixed_mass_d(fmaf(-mx, c, mc)), 0u,
-                                    topp > 0.f ? (double)topp * sh.zrow : 0.0, kBoundPasses);
+    bound = radix_select_regs<true>(sh, ka, fixed_mass_d(fmaf(-mxa, c, mc)), kb, fixed_mass_d(fmaf(-mxb, c, mc)),
+                                    0u, topp > 0.f ? (double)topp * sh.zrow : 0.0, kBoundPasses);
     if (sh.bin < 0) {                          // the maxima do not reach the target mass
       __syncthreads();
       return false;
