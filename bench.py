@@ -36,9 +36,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified positions/sec (B·(K+1) over V) + achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
-WORKLOADS = {"C0": 0, "C1": 1, "C2": 2, "C3": 3, "C4": 4, "C3S": 3, "C3F": 3}
+WORKLOADS = {"C0": 0, "C1": 1, "C2": 2, "C3": 3, "C4": 4, "C3S": 3, "C3F": 3, "C3P": 3}
 STRICT_WORKLOADS = {"C3S"}       # the same batches, every sequence in strict sample-match mode
-FILTER_WORKLOADS = {"C3F": (50, 0.9)}   # the same batches with top-k 50 and top-p 0.9 on every sequence
+# the same batches with top-k / top-p on every sequence (top-k 0: off)
+FILTER_WORKLOADS = {"C3F": (50, 0.9), "C3P": (0, 0.95)}
 NGRAM_ROTATE = 32          # 32 x ~8.6 MB of histories: more than the 256 MB last-level cache
 ROTATE = {0: 64, 1: 64, 2: 6, 3: 2, 4: 6}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "row_stats_counters.json")
@@ -64,7 +65,7 @@ def make_workload_batch(workload: str, step: int):
         k, p = FILTER_WORKLOADS[workload]
         b.top_k = np.full(b.batch, k, np.int32)
         b.top_p = np.full(b.batch, p, np.float32)
-        b.name += f"; top-k {k} and top-p {p} on every sequence"
+        b.name += (f"; top-k {k} and top-p {p} on every sequence" if k else f"; top-p {p} on every sequence")
     return b
 
 
@@ -457,7 +458,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="C3", choices=sorted(WORKLOADS) + ["NG", "ST"],
                     help="C0..C4: the verify step; C3S: C3 in strict sample-match mode; C3F: C3 with top-k 50 "
-                         "and top-p 0.9; NG: the N-gram proposer; ST: acceptance statistics and the draft-length "
+                         "and top-p 0.9; C3P: C3 with top-p 0.95; NG: the N-gram proposer; ST: acceptance statistics and the draft-length "
                          "controller")
     ap.add_argument("--rotate", type=int, default=None, help="input sets kept resident and cycled")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
