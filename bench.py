@@ -46,6 +46,8 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "row_stats_counters.json")
 NGRAM_COUNTERS_FILE = os.path.join(ROOT, "profiles", "ngram_counters.json")
 KERNEL_SOURCE = os.path.join(ROOT, "rejection_sampling_verify_06_amd", "csrc", "sv_kernels.hip")
 NGRAM_SOURCE = os.path.join(ROOT, "rejection_sampling_verify_06_amd", "csrc", "sv_ngram.hip")
+FILTER_COUNTERS_FILE = os.path.join(ROOT, "profiles", "filter_counters.json")
+FILTER_SOURCE = os.path.join(ROOT, "rejection_sampling_verify_06_amd", "csrc", "sv_filter.hip")
 
 
 def kernel_source_sha(path: str = KERNEL_SOURCE) -> str:
@@ -575,7 +577,9 @@ def main():
         # the filter must see each filtered row once: the same bytes as the row statistics
         ach = ev_stats_bytes / (kern["filter"] * 1e-3) / 1e9
         filter_roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                           "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": "k_filter",
+                           "frac": round(ach / PEAK_HBM_GBPS, 4),
+                           "traffic": load_traffic(args.workload, FILTER_COUNTERS_FILE, FILTER_SOURCE),
+                           "kernel": "k_filter",
                            "algorithmic_bytes_per_launch": int(ev_stats_bytes),
                            "mean_launch_ms": round(kern["filter"], 5)}
 

@@ -60,3 +60,23 @@ def test_max_vocab(torch_mod, dtype):
         gu.check_batch(v, b, torch_mod, label=f"V {V} {dtype} strict")
     finally:
         v.close()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_max_vocab_filtered(torch_mod, dtype):
+    """Top-k / top-p at a 2,097,152-token vocabulary: the bounded selection
+    (top-k 50 with top-p, top-k 1000), top-p alone on a peaked row and on a
+    flat one (the histogram path: its nucleus spans most of the row)."""
+    import numpy as np
+    import rejection_sampling_verify_06_amd as sv
+    V = 2097152
+    v = sv.Verifier(max_batch=4, max_k=2, max_vocab=V, device=0)
+    try:
+        b = make_random_batch(730 + (dtype == "bf16"), B=4, V=V, kmax=2, k_min=1, dtype=dtype,
+                              modes=(MODE_SAMPLE, MODE_ONEHOT, MODE_STRICT), scale=(0.3, 4.0))
+        b.top_k = np.array([50, 1000, 0, 0], np.int32)
+        b.top_p = np.array([0.9, 1.0, 0.95, 0.5], np.float32)
+        b.temperature = np.array([1.0, 0.7, 0.3, 2.0], np.float32)
+        gu.check_batch(v, b, torch_mod, label=f"V {V} {dtype} filtered")
+    finally:
+        v.close()
