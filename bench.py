@@ -36,8 +36,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified positions/sec (B·(K+1) over V) + achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
-WORKLOADS = {"C0": 0, "C1": 1, "C2": 2, "C3": 3, "C4": 4, "C3S": 3, "C3F": 3, "C3P": 3}
+WORKLOADS = {"C0": 0, "C1": 1, "C2": 2, "C3": 3, "C4": 4, "C3S": 3, "C3F": 3, "C3P": 3, "C3D8": 3}
 STRICT_WORKLOADS = {"C3S"}       # the same batches, every sequence in strict sample-match mode
+# one GPU's share when the batch is split across N GPUs by sequence: the
+# first B/N sequences, with their global seq_ids
+SHARD_WORKLOADS = {"C3D8": 8}
 # the same batches with top-k / top-p on every sequence (top-k 0: off)
 FILTER_WORKLOADS = {"C3F": (50, 0.9), "C3P": (0, 0.95)}
 NGRAM_ROTATE = 32          # 32 x ~8.6 MB of histories: more than the 256 MB last-level cache
@@ -63,6 +66,11 @@ def kernel_source_sha(path: str = KERNEL_SOURCE) -> str:
 def make_workload_batch(workload: str, step: int):
     from workloads import make_config_batch
     b = make_config_batch(WORKLOADS[workload], step, strict=workload in STRICT_WORKLOADS)
+    if workload in SHARD_WORKLOADS:
+        from workloads import sequence_slice
+        n = SHARD_WORKLOADS[workload]
+        b = sequence_slice(b, 0, b.batch // n,
+                           name=f"{b.name}; one GPU's share of {n}: sequences 0..{b.batch // n - 1}")
     if workload in FILTER_WORKLOADS:
         k, p = FILTER_WORKLOADS[workload]
         b.top_k = np.full(b.batch, k, np.int32)
@@ -460,7 +468,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="C3", choices=sorted(WORKLOADS) + ["NG", "ST"],
                     help="C0..C4: the verify step; C3S: C3 in strict sample-match mode; C3F: C3 with top-k 50 "
-                         "and top-p 0.9; C3P: C3 with top-p 0.95; NG: the N-gram proposer; ST: acceptance statistics and the draft-length "
+                         "and top-p 0.9; C3P: C3 with top-p 0.95; C3D8: one GPU's share of C3 split by sequence over 8 GPUs; "
+                         "NG: the N-gram proposer; ST: acceptance statistics and the draft-length "
                          "controller")
     ap.add_argument("--rotate", type=int, default=None, help="input sets kept resident and cycled")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
@@ -497,13 +506,16 @@ def main():
         sys.exit(1)
     sv.library_loaded_path()
     cfg = WORKLOADS[args.workload]
-    R = args.rotate or ROTATE[cfg]
+    # a GPU's share is an eighth of C3's bytes: enough input sets to exceed the 256 MB last-level cache
+    R = args.rotate or (12 if args.workload in SHARD_WORKLOADS else ROTATE[cfg])
 
     t_gen = time.perf_counter()
     batches = [make_workload_batch(args.workload, i) for i in range(R)]
     dev_in = [to_device(b, torch) for b in batches]
     gen_s = time.perf_counter() - t_gen
-    desc = config_description(cfg)
+    desc = dict(config_description(cfg))
+    if args.workload in SHARD_WORKLOADS:
+        desc["batch"] //= SHARD_WORKLOADS[args.workload]
     maxk = max(8, int(max(b.num_draft.max() for b in batches)))
     v = sv.Verifier(max_batch=desc["batch"], max_k=maxk, max_vocab=desc["vocab"], device=0)
     outs = [v.make_outputs(b.batch, b.total_draft, want_pq=True, want_status=True) for b in batches]

@@ -13,5 +13,5 @@ from .synth import (  # noqa: F401
     MODE_SAMPLE, MODE_GREEDY, MODE_ONEHOT, MODE_STRICT, Batch, CONFIG_NAMES, STRICT_SUFFIX,
     make_config_batch, make_random_batch, bf16_round, bf16_widen,
     config_description, NgramBatch, NGRAM_WORKLOAD, make_ngram_batch, make_ngram_workload,
-    ROUNDS_WORKLOAD, make_rounds_workload,
+    ROUNDS_WORKLOAD, make_rounds_workload, sequence_slice,
 )

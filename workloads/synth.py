@@ -93,6 +93,20 @@ class Batch:
 # row builders
 # ---------------------------------------------------------------------------
 
+def sequence_slice(b: "Batch", lo: int, hi: int, name: Optional[str] = None) -> "Batch":
+    """Sequences lo..hi-1 of a batch, as the packed layout of their own (their
+    target and draft rows, tokens and per-sequence values; seq_ids kept, so
+    the Philox draws are those of the whole batch).  Pure data slicing."""
+    K = b.num_draft.astype(np.int64)
+    d0, d1 = int(K[:lo].sum()), int(K[:hi].sum())
+    pick = lambda a: None if a is None else a[lo:hi].copy()
+    return Batch(name=name or f"{b.name} [sequences {lo}..{hi - 1}]", vocab=b.vocab, dtype=b.dtype,
+                 target=b.target[d0 + lo:d1 + hi].copy(), draft=None if b.draft is None else b.draft[d0:d1].copy(),
+                 num_draft=b.num_draft[lo:hi].copy(), draft_tokens=b.draft_tokens[d0:d1].copy(),
+                 temperature=b.temperature[lo:hi].copy(), mode=b.mode[lo:hi].copy(),
+                 seq_ids=b.seq_ids[lo:hi].copy(), seed=b.seed, top_k=pick(b.top_k), top_p=pick(b.top_p))
+
+
 def _zipf_base(V: int) -> np.ndarray:
     """Sorted Zipf-shaped base logits: -1.1 * ln(rank), rank = 1..V."""
     return (-1.1 * np.log(np.arange(1, V + 1, dtype=np.float64))).astype(np.float32)
