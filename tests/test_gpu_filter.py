@@ -131,3 +131,45 @@ def test_bounded_selection_edges(verifier, torch_mod, dtype):
         assert np.array_equal(out[k], again[k]), k
     assert np.array_equal(out["p_at"], again["p_at"], equal_nan=True)
     assert np.array_equal(out["q_at"], again["q_at"], equal_nan=True)
+
+
+def _mask_rows(b: Batch, rng, frac: float):
+    """-inf on a random fraction of every row's columns (a masked vocabulary),
+    never on the row's largest logit."""
+    from workloads import bf16_round
+    neg = bf16_round(np.array([-np.inf], np.float32))[0] if b.dtype == "bf16" else np.float32(-np.inf)
+    for arr in (b.target, b.draft):
+        if arr is None:
+            continue
+        vals = arr[:, :b.vocab].view(np.uint16).astype(np.uint32) << 16 if b.dtype == "bf16" else arr[:, :b.vocab]
+        vals = vals.view(np.float32) if b.dtype == "bf16" else vals
+        keep = np.argmax(vals, axis=1)
+        m = rng.random((arr.shape[0], b.vocab)) < frac
+        m[np.arange(arr.shape[0]), keep] = False
+        sub = arr[:, :b.vocab]
+        sub[m] = neg
+        arr[:, :b.vocab] = sub
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [5, 9, 4099, 50000])
+def test_filter_special_values(verifier, torch_mod, dtype, V):
+    """Filters on rows with a masked (-inf) part of the vocabulary, on
+    vocabularies too small for one 16-byte vector round, on rows whose
+    largest logit is tied, at temperatures from 0.05 to 5, on rows that are not
+    16-byte aligned."""
+    rng = np.random.default_rng(560 + V + (dtype == "bf16"))
+    b = make_random_batch(560 + V, B=20, V=V, kmax=3, dtype=dtype, ld_pad=1, modes=ALL_MODES)
+    _mask_rows(b, rng, 0.3)
+    # ties at the largest logit in some target rows
+    tgt = b.target if dtype == "f32" else None
+    if tgt is not None and V >= 9:
+        for r in range(0, b.target.shape[0], 4):
+            row = b.target[r, :V]
+            top = row.max()
+            row[rng.choice(V, 3, replace=False)] = top
+    b.temperature = rng.choice(np.array([0.05, 0.3, 1.0, 2.5, 5.0], np.float32), size=b.batch)
+    ks = [0, 1, 2, 3, 50, 1024, 1025, V - 1]
+    ps = [1.0, 0.95, 0.5, 0.0, 0.999]
+    _with_filters(b, 9 + V, ks, ps)
+    gu.check_batch(verifier, b, torch_mod, label=f"filter special values V={V} {dtype}")
