@@ -12,25 +12,29 @@
 // below p (the largest logit always kept).
 //
 // One 512-thread block per used slot of a filtered sequence, after the row
-// statistics:
-//   1. the row maximum M from the row's chunk partials;
-//   2. a coarse histogram of d = M*c - x*c in steps of 1/8 (log2 units; the
-//      last of 256 bins also takes everything below 2^-32 of the maximum):
-//      counts and masses exp2(x*c - round(M*c)) in 2^-40 fixed point, in
-//      LDS copies shared by pairs of waves with integer atomics (so every
-//      sum is exact and the result does not depend on the order of the
-//      atomics); the last bin, which at low temperature holds most of the
-//      row, is counted in registers;
-//   3. the bin holding the threshold (by count from the top for top-k, by
-//      mass for top-p), its elements compacted into LDS, and an exact radix
-//      select over their 32-bit order-preserving keys, 8 bits a pass (a bin
-//      larger than the LDS buffer is refined by passes over the row);
-//   4. the row's chunk partials rewritten as filtered sums against M (and,
-//      for strict-mode target rows, the filtered part below the proposal),
-//      and tau stored for the scan and the final draw.
-// Every pass over the row issues 16 loads per thread before using any.
-// Every decision on which tokens are kept is a comparison of stored values;
-// only the top-p crossing depends on sums (exact here, in fixed point).
+// statistics (four blocks per CU).  The row maximum M comes from the row's
+// chunk partials (for top-p alone, also the row's mass).  Then:
+//   A. the bounded selection (two reads of the row, no per-element atomics):
+//      every thread's two largest logits over a sample of the row (top-k)
+//      or the whole row (top-p alone); a 2-pass radix select over those
+//      1024 maxima gives a bound that every kept token is at or above; the
+//      second read collects the tokens at or above it into LDS; exact
+//      thresholds among them (ranks, or a sort when there are many); the
+//      filtered chunk sums are the kept tokens' masses;
+//   B. when the bound cannot hold (top-k above 1024, maxima short of the
+//      top-p mass, more tokens than the LDS buffer), the histogram path: a
+//      coarse histogram of d = M*c - x*c in steps of 1/8 (log2 units; the
+//      last of 256 bins also takes everything below 2^-32 of the maximum)
+//      with integer LDS atomics, the bin holding the threshold, its
+//      elements compacted into LDS (or refined by a fine histogram), an
+//      exact radix select over their keys, and a pass for the chunk sums.
+// Either way the row's chunk partials are rewritten as filtered sums against
+// M (and, for strict-mode target rows, the filtered part below the
+// proposal), and tau is stored for the scan and the final draw.  Masses are
+// exp2(x*c - M*c) in 2^-40 fixed point, summed as integers, so every result
+// is independent of the order of the atomics; every decision on which
+// tokens are kept is a comparison of stored values, and only the top-p
+// crossing depends on sums.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
