@@ -58,6 +58,7 @@ constexpr float kBinSpan = kBins / kBinScale;  // 32: d beyond this falls into t
 constexpr float kFineScale = 2048.f;           // fine bins per log2 unit inside one coarse bin
 constexpr int kCap = 1024;                     // candidates held in LDS
 constexpr int kUnroll = 16;                    // loads in flight per thread
+constexpr int kBJ = 4;                         // thresholds per bracket-search pass (8 or 16: slower, ALU-bound)
 constexpr int kMaxChunks = kMaxTiles * kTileElems / (kChunkBytes / 4);   // 256
 constexpr double kMassOne = 1099511627776.0;   // 2^40
 constexpr float kLog2eF = 1.4426950408889634f;
@@ -158,6 +159,14 @@ struct FiltShared {
   uint64_t cb[kMaxChunks];     // their parts below the proposal (strict target rows)
   uint32_t ncand, kmin_c, kmax_c;
   uint32_t tmin, nkc;          // bounded selection: smallest kept key, kept-set counter
+  double mtot;                 // mass above the candidates plus theirs (selection by ranks or prefixes)
+  // bracket search (top-p alone): per-wave, then block sums of the masses and
+  // counts at or below each threshold, and the bracket's key range
+  float wfm[kFWaves][kBJ];
+  uint32_t wfn[kFWaves][kBJ];
+  double bm[kBJ];
+  uint32_t bn[kBJ];
+  uint32_t bkmin, bkmax;
   int last;                    // last non-empty bin of the latest crossing search
   uint64_t amass;
   int bin;
@@ -547,11 +556,13 @@ __device__ __forceinline__ void sort_desc(uint32_t* k, int32_t* pay, int n2) {
 }
 
 // Wave 0: over keys[0..n) sorted largest first, the fixed-point masses
-// summed in order.  With Z = zuse (or the total of the n masses when zuse
-// < 0) and target = topp * Z (0 when topp <= 0), writes sh.ne = #{i: mass
-// strictly before i < target} and sh.ni = #{i: mass through i < target}.
+// summed in order, on top of mass0 (the mass of the row above keys[0]).
+// With Z = zuse (or the total of the n masses when zuse < 0) and target =
+// topp * Z (0 when topp <= 0), writes sh.ne = #{i: mass strictly before i <
+// target}, sh.ni = #{i: mass through i < target} and sh.mtot = mass0 + the
+// n masses.
 __device__ __forceinline__ void mass_prefix(FiltShared& sh, const uint32_t* keys, int n, float c, float mc,
-                                            float topp, double zuse) {
+                                            float topp, double zuse, double mass0 = 0.0) {
   const int lane = threadIdx.x & (kWave - 1);
   const int per = (n + kWave - 1) / kWave;
   const int lo = min(lane * per, n), hi = min(lo + per, n);
@@ -573,15 +584,16 @@ __device__ __forceinline__ void mass_prefix(FiltShared& sh, const uint32_t* keys
   uint64_t acc = base;
 #pragma unroll 4
   for (int i = lo; i < hi; ++i) {
-    ne += (double)acc < target;
+    ne += mass0 + (double)acc < target;
     acc += fixed_mass_d(fmaf(-kval(keys[i]), c, mc));
-    ni += (double)acc < target;
+    ni += mass0 + (double)acc < target;
   }
   ne = wave_sum_u32(ne);
   ni = wave_sum_u32(ni);
   if (lane == 0) {
     sh.ne = (int)ne;
     sh.ni = (int)ni;
+    sh.mtot = mass0 + (double)tot;
   }
 }
 
@@ -640,7 +652,7 @@ constexpr uint32_t kKeyNegInf = 0x007FFFFFu;   // fkey(-inf)
 // (largest first): the top-k key (the k-th), the kept set's end, then the
 // top-p key from fixed-point mass prefixes.  Returns the smallest kept key.
 __device__ __forceinline__ uint32_t sorted_thresholds(FiltShared& sh, int n, float c, float mc, bool use_k, int topk,
-                                                      bool use_p, float topp) {
+                                                      bool use_p, float topp, double mass0 = 0.0) {
   const int t = threadIdx.x;
   uint32_t key = sh.ck[0];
   int nk = n;                                  // candidates kept by top-k: keys >= the k-th largest
@@ -654,7 +666,7 @@ __device__ __forceinline__ uint32_t sorted_thresholds(FiltShared& sh, int n, flo
     nk = sh.nk;
   }
   if (use_p) {
-    if (t < kWave) mass_prefix(sh, sh.ck, nk, c, mc, topp, use_k ? -1.0 : sh.zrow);
+    if (t < kWave) mass_prefix(sh, sh.ck, nk, c, mc, topp, use_k ? -1.0 : sh.zrow, mass0);
     __syncthreads();
     key = sh.ck[max(sh.ne - 1, 0)];           // the last token whose mass above stays below the target
   }
@@ -668,7 +680,7 @@ __device__ __forceinline__ uint32_t sorted_thresholds(FiltShared& sh, int n, flo
 // set's total (integers, so the order does not matter); the largest key is
 // always kept.  Returns the smallest kept key.
 __device__ __forceinline__ uint32_t select_by_rank(FiltShared& sh, int n, float c, float mc, bool use_k, int topk,
-                                                   bool use_p, float topp) {
+                                                   bool use_p, float topp, double mass0 = 0.0) {
   const int t = threadIdx.x;
   if (t < 4) sh.ck[n + t] = 0u;               // below every candidate: pads the last 4-wide read
   __syncthreads();
@@ -706,7 +718,9 @@ __device__ __forceinline__ uint32_t select_by_rank(FiltShared& sh, int n, float 
       above += (kj > ku) ? mj : 0;
     }
     const double target = topp > 0.f ? (double)topp * (use_k ? (double)tot : sh.zrow) : 0.0;
-    if (above == 0 || (double)above < target) atomicMin(&sh.tmin, ku);
+    // (mass0 = 0: the set holds the row's largest logit, which is always kept)
+    if ((mass0 == 0.0 && above == 0) || mass0 + (double)above < target) atomicMin(&sh.tmin, ku);
+    if (t == 0) sh.mtot = mass0 + (double)tot;
   }
   __syncthreads();
   return sh.tmin;
@@ -850,22 +864,12 @@ __device__ __forceinline__ void write_partials(const FiltShared& sh, Partial* pp
   if (threadIdx.x == 0) *tau_out = tau;
 }
 
-// The filter of one row (template on the row's element type).
+// The threshold by histograms (any top-k / top-p): the coarse histogram, the
+// crossing bins, exact selects inside them.  Returns tau.
 template <bool BF>
-__device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Partial* pp, const char* rowp, int nch,
-                                           int ce, float c, float mc, float M, bool use_k, int topk, bool use_p,
-                                           float topp, int xs, float* tau_out) {
+__device__ __forceinline__ float histogram_threshold(FiltShared& sh, const char* rowp, int V, float c, float mc,
+                                                     bool use_k, int topk, bool use_p, float topp) {
   const int t = threadIdx.x, lane = t & (kWave - 1);
-  const int V = P.V;
-  for (int j = t; j < nch; j += kFThreads) {
-    sh.cs[j] = 0;
-    sh.cb[j] = 0;
-  }
-  uint32_t bkey;
-  if (bounded_filter<BF>(sh, rowp, V, ce, c, mc, use_k, topk, use_p, topp, xs, &bkey)) {
-    write_partials(sh, pp, nch, M, kval(bkey), tau_out);
-    return;
-  }
   // ---- coarse histogram (masses only when top-p needs them) ----
   if (use_p) histogram<BF, true>(sh, rowp, V, c, mc, -1, 0u, sh.hc, sh.hm);
   else histogram<BF, false>(sh, rowp, V, c, mc, -1, 0u, sh.hc, sh.hm);
@@ -924,6 +928,15 @@ __device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Part
     }
   }
 
+  return tau;
+}
+
+// The filtered chunk sums of a row whose threshold tau is known, into sh.cs /
+// sh.cb (zeroed by the caller).
+template <bool BF>
+__device__ __forceinline__ void chunk_pass(FiltShared& sh, const char* rowp, int V, int ce, float c, float mc,
+                                           float tau, int xs) {
+  const int t = threadIdx.x, lane = t & (kWave - 1);
   // ---- filtered chunk partials: per wave and chunk, float sums turned into fixed point ----
   // (explicit rounds: every lane runs every step, so the wave sums see no
   // inactive lanes; elements past V weigh 0, and the chunk of a step is the
@@ -964,12 +977,306 @@ __device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Part
     }
   }
   __syncthreads();
+}
+
+// ---- bracket search (top-p alone, nuclei the maxima cannot bound) ----
+//
+// The crossing lies in a bracket (dlo, dhi] of d = M*c - x*c.  A pass over
+// the row sums, per thread in registers, the masses and counts of the
+// bracket's tokens at or below kBJ thresholds dividing it evenly; the block
+// sums name the sub-bracket where the mass from the top reaches the target.
+// Once it holds at most kCap tokens (or after kBracketPasses passes), one
+// more pass collects them into LDS and sums the mass above the bracket; the
+// exact selection then runs on top of that mass.  A bracket of tokens that
+// all tie is decided without them.  false (block-uniform): the histogram
+// path must decide (a crossing past 2^-32 of the maximum, a bracket too
+// large, or a float sum that put the crossing outside the bracket).
+constexpr int kBracketPasses = 6;
+
+// a failed bracket search leaves the chunk sums zero for the histogram path
+__device__ __forceinline__ void bracket_clear(FiltShared& sh, bool chunk_sums) {
+  __syncthreads();
+  if (chunk_sums)
+    for (int k = threadIdx.x; k < kMaxChunks; k += kFThreads) {
+      sh.cs[k] = 0;
+      sh.cb[k] = 0;
+    }
+  __syncthreads();
+}
+
+template <bool BF>
+__device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, int V, int ce, float c, float mc,
+                                             float topp, int xs, uint32_t* tau_key, bool* sums) {
+  constexpr int epv = BF ? 8 : 4;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
+  if (!(topp > 0.f)) return false;
+  const RowSplit sp = split_row<BF>(rowp, V);
+  const uint4* vp = (const uint4*)(rowp + (size_t)sp.head * (BF ? 2 : 4));
+  const double target = (double)topp * sh.zrow / kMassOne;   // in units of the maximum's weight
+  float dlo = -1.f, dhi = kBinSpan;
+  double alo = 0.0;                            // mass of the tokens with d <= dlo
+  uint32_t cnt = 0xFFFFFFFFu;
+  for (int pass = 0; pass < kBracketPasses && cnt > (uint32_t)kCap; ++pass) {
+    const float base = fmaxf(dlo, 0.f), step = (dhi - base) / kBJ;
+    float D[kBJ];
+#pragma unroll
+    for (int q = 0; q < kBJ; ++q) D[q] = (q == kBJ - 1) ? dhi : base + (float)(q + 1) * step;
+    float m[kBJ];
+    uint32_t n[kBJ];
+#pragma unroll
+    for (int q = 0; q < kBJ; ++q) {
+      m[q] = 0.f;
+      n[q] = 0;
+    }
+    auto acc = [&](const uint4(&w)[kVecPer], int) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < kVecPer; ++u)
+#pragma unroll
+        for (int j = 0; j < epv; ++j) {
+          const float d = fmaf(-vec_elem<BF>(w[u], j), c, mc);
+          if (d > dlo && d <= dhi) {             // NaN and -inf logits never pass
+            const float e = fexp2(-d);
+#pragma unroll
+            for (int q = 0; q < kBJ; ++q) {
+              const bool in = d <= D[q];
+              m[q] += in ? e : 0.f;
+              n[q] += in ? 1u : 0u;
+            }
+          }
+        }
+    };
+    for_rounds(vp, 0, sp.nvec, acc);
+    for_singles<BF>(rowp, sp, acc);
+#pragma unroll
+    for (int q = 0; q < kBJ; ++q) {
+      const float ws = wave_sum(m[q]);
+      const uint32_t ns = wave_sum_u32(n[q]);
+      if (lane == 0) {
+        sh.wfm[wv][q] = ws;
+        sh.wfn[wv][q] = ns;
+      }
+    }
+    __syncthreads();
+    if (t < kBJ) {
+      double a = 0.0;
+      uint32_t b = 0;
+      for (int w = 0; w < kFWaves; ++w) {
+        a += (double)sh.wfm[w][t];
+        b += sh.wfn[w][t];
+      }
+      sh.bm[t] = a;
+      sh.bn[t] = b;
+    }
+    __syncthreads();
+    int jq = -1;
+    for (int q = kBJ - 1; q >= 0; --q)
+      if (alo + sh.bm[q] >= target) jq = q;     // the first threshold whose mass reaches the target
+    if (jq < 0) {                              // past dhi: beyond 2^-32 of the maximum, or rounding
+      __syncthreads();
+      return false;
+    }
+    const double aprev = jq > 0 ? sh.bm[jq - 1] : 0.0;
+    const uint32_t nprev = jq > 0 ? sh.bn[jq - 1] : 0u;
+    cnt = sh.bn[jq] - nprev;
+    alo += aprev;
+    dlo = jq > 0 ? D[jq - 1] : dlo;
+    dhi = D[jq];
+    __syncthreads();                           // wfm / bm are written again by the next pass
+  }
+
+  // ---- collect: the bracket's tokens, the mass above it, the bracket's key range ----
+  if (t == 0) {
+    sh.ncand = 0;
+    sh.bkmin = 0xFFFFFFFFu;
+    sh.bkmax = 0u;
+    sh.tmin = 0xFFFFFFFFu;                     // the selection's state
+    sh.nkc = 0;
+  }
+  __syncthreads();
+  // Without a proposal split (xs < 0) the pass also sums, per chunk, the
+  // mass above the bracket (into sh.cs: always kept) and inside it (into
+  // sh.cb, kept whole only when the bracket is one value).  A round of
+  // vectors spans exactly one chunk's length, so it touches chunks k0 and
+  // k0 + 1 only (k0 + 1 when the row does not start on 16 bytes).
+  static_assert(kFThreads * kVecPer * 16 == kChunkBytes, "a round of vectors is one chunk long");
+  const bool chunk_sums = xs < 0;
+  float above = 0.f, inside = 0.f;
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+  auto collect = [&](const uint4(&w)[kVecPer], int v0) __attribute__((always_inline)) {
+    uint64_t hit = 0;
+    float ra[2] = {0.f, 0.f}, ri[2] = {0.f, 0.f};   // this round's sums, chunks k0 and k0 + 1
+    const int eb = v0 >= 0 ? sp.head + v0 * epv : -1 - v0;
+    const int k0 = eb / ce;
+#pragma unroll
+    for (int u = 0; u < kVecPer; ++u)
+#pragma unroll
+      for (int j = 0; j < epv; ++j) {
+        const float x = vec_elem<BF>(w[u], j);
+        const float d = fmaf(-x, c, mc);
+        const bool up = elem_index<BF>(sp, v0, u, j) >= (k0 + 1) * ce;
+        if (d <= dlo) {
+          const float e = fexp2(-d);
+          above += e;
+          ra[up] += e;
+        } else if (d <= dhi) {
+          hit |= 1ull << (u * epv + j);
+          const float e = fexp2(-d);
+          inside += e;
+          ri[up] += e;
+          const uint32_t k = fkey(x);
+          kmn = min(kmn, k);
+          kmx = max(kmx, k);
+        }
+      }
+    if (chunk_sums) {
+      if (v0 >= 0) {                           // every lane of the wave is here: wave sums, one atomic each
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float wa = wave_sum(ra[h]), wi = wave_sum(ri[h]);
+          if (lane == 0 && k0 + h < kMaxChunks) {
+            if (wa != 0.f) atomicAdd(&sh.cs[k0 + h], (unsigned long long)((double)wa * kMassOne));
+            if (wi != 0.f) atomicAdd(&sh.cb[k0 + h], (unsigned long long)((double)wi * kMassOne));
+          }
+        }
+      } else {                                 // a single element (head or tail): its own atomics
+        if (ra[0] != 0.f) atomicAdd(&sh.cs[k0], (unsigned long long)((double)ra[0] * kMassOne));
+        if (ri[0] != 0.f) atomicAdd(&sh.cb[k0], (unsigned long long)((double)ri[0] * kMassOne));
+      }
+    }
+    if (__any(hit != 0)) {
+      uint32_t pos = hit ? atomicAdd(&sh.ncand, (uint32_t)__popcll(hit)) : 0u;
+      while (hit) {
+        const int b = __builtin_ctzll(hit);
+        hit &= hit - 1;
+        const int e = elem_index<BF>(sp, v0, b / epv, b % epv);
+        if (pos < (uint32_t)kCap) {
+          sh.ck[pos] = fkey(load_x<BF>(rowp, e));
+          sh.bb.ci[pos] = e;
+        }
+        ++pos;
+      }
+    }
+  };
+  for_rounds(vp, 0, sp.nvec, collect);
+  for_singles<BF>(rowp, sp, collect);
+  {
+    const float wa = wave_sum(above), wi = wave_sum(inside);
+    const uint32_t wmn = (uint32_t)wave_min_i((int)(kmn ^ 0x80000000u)) ^ 0x80000000u;   // unsigned min
+    const uint32_t wmx = (uint32_t)wave_max_i((int)(kmx ^ 0x80000000u)) ^ 0x80000000u;   // unsigned max
+    if (lane == 0) {
+      sh.wfm[wv][0] = wa;
+      sh.wfm[wv][1] = wi;
+      atomicMin(&sh.bkmin, wmn);
+      atomicMax(&sh.bkmax, wmx);
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    double a = 0.0, b = 0.0;
+    for (int w = 0; w < kFWaves; ++w) {
+      a += (double)sh.wfm[w][0];
+      b += (double)sh.wfm[w][1];
+    }
+    sh.bm[0] = a * kMassOne;                   // fixed-point units from here on
+    sh.bm[1] = b * kMassOne;
+  }
+  __syncthreads();
+  const double A = sh.bm[0], B = sh.bm[1], tgt = (double)topp * sh.zrow;
+  const int n = uni((int)sh.ncand);
+  if (n < 1 || A >= tgt || A + B < tgt) {      // the float sums moved the crossing out of the bracket
+    bracket_clear(sh, chunk_sums);
+    return false;
+  }
+  uint32_t key;
+  const bool single = sh.bkmin == sh.bkmax;
+  if (n > kCap) {
+    if (!single) {                             // too many distinct values to select among
+      bracket_clear(sh, chunk_sums);
+      return false;
+    }
+    key = sh.bkmin;                            // one value: kept, since the mass above it is below the target
+  } else {
+    if (n <= kFThreads && n <= kRankP) {
+      key = select_by_rank(sh, n, c, mc, false, 0, true, topp, A);
+    } else {
+      int n2 = 2;
+      while (n2 < n) n2 <<= 1;
+      for (int i = n + t; i < n2; i += kFThreads) {
+        sh.ck[i] = 0u;
+        sh.bb.ci[i] = -1;
+      }
+      __syncthreads();
+      sort_desc(sh.ck, sh.bb.ci, n2);
+      key = sorted_thresholds(sh, n, c, mc, false, 0, true, topp, A);
+    }
+    __syncthreads();
+    // the exact sums must agree: something kept, and the crossing inside
+    if (key == 0xFFFFFFFFu || !(sh.mtot >= tgt)) {
+      bracket_clear(sh, chunk_sums);
+      return false;
+    }
+  }
+  *sums = chunk_sums;
+  if (chunk_sums) {
+    // the kept part of the bracket joins the mass above it: all of it for a
+    // single value, else the kept candidates' own masses
+    if (single) {
+      for (int k = t; k < kMaxChunks; k += kFThreads) {
+        sh.cs[k] += sh.cb[k];
+        sh.cb[k] = 0;
+      }
+    } else {
+      for (int k = t; k < kMaxChunks; k += kFThreads) sh.cb[k] = 0;
+      __syncthreads();
+      for (int i = t; i < n; i += kFThreads) {
+        const uint32_t k = sh.ck[i];
+        if (k >= key) {
+          const int e = sh.bb.ci[i];
+          atomicAdd(&sh.cs[e / ce], (unsigned long long)fixed_mass_d(fmaf(-kval(k), c, mc)));
+        }
+      }
+    }
+    __syncthreads();
+  }
+  *tau_key = key;
+  return true;
+}
+
+// The filter of one row (template on the row's element type).
+template <bool BF>
+__device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Partial* pp, const char* rowp, int nch,
+                                           int ce, float c, float mc, float M, bool use_k, int topk, bool use_p,
+                                           float topp, int xs, float* tau_out) {
+  const int t = threadIdx.x;
+  const int V = P.V;
+  for (int j = t; j < nch; j += kFThreads) {
+    sh.cs[j] = 0;
+    sh.cb[j] = 0;
+  }
+  uint32_t bkey;
+  // top-p alone: the 1024 maxima weigh at most 1024 times the largest
+  // logit's weight, so a target above that rules the bounded selection out
+  const bool hopeless = use_p && !use_k && (double)topp * sh.zrow > 2.0 * kFThreads * kMassOne;
+  if (!hopeless && bounded_filter<BF>(sh, rowp, V, ce, c, mc, use_k, topk, use_p, topp, xs, &bkey)) {
+    write_partials(sh, pp, nch, M, kval(bkey), tau_out);
+    return;
+  }
+  if (use_p && !use_k) {
+    bool sums = false;
+    if (bracket_topp<BF>(sh, rowp, V, ce, c, mc, topp, xs, &bkey, &sums)) {
+      if (!sums) chunk_pass<BF>(sh, rowp, V, ce, c, mc, kval(bkey), xs);
+      write_partials(sh, pp, nch, M, kval(bkey), tau_out);
+      return;
+    }
+  }
+  const float tau = histogram_threshold<BF>(sh, rowp, V, c, mc, use_k, topk, use_p, topp);
+  chunk_pass<BF>(sh, rowp, V, ce, c, mc, tau, xs);
   write_partials(sh, pp, nch, M, tau, tau_out);
 }
 
 }  // namespace
 
-// two blocks per CU (8 waves per SIMD): at most 64 VGPRs
+// four blocks per CU (8 waves per SIMD): at most 64 VGPRs
 __global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) k_filter(Params P) {
   __shared__ FiltShared sh;
   const int r = blockIdx.x, s = blockIdx.y;
