@@ -642,7 +642,7 @@ __device__ __forceinline__ uint32_t radix_select_regs(FiltShared& sh, uint32_t k
 }
 
 constexpr int kRankP = 512;                    // top-p alone: the most candidates selected by ranks
-constexpr int kTargetCand = 256;               // top-k: tokens expected at or above the bound
+constexpr int kTargetCand = 160;               // top-k: tokens expected at or above the bound (C3F: 128..512 tried, 160 best)
 // 16 key bits (sign, exponent, 7 mantissa bits) of the bound: within 2^-7
 // of the exact maximum, for 8 barriers instead of 16
 constexpr int kBoundPasses = 2;
