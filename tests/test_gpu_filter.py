@@ -173,3 +173,24 @@ def test_filter_special_values(verifier, torch_mod, dtype, V):
     ps = [1.0, 0.95, 0.5, 0.0, 0.999]
     _with_filters(b, 9 + V, ks, ps)
     gu.check_batch(verifier, b, torch_mod, label=f"filter special values V={V} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_topp_crossing_past_bracket_range(verifier, torch_mod, dtype):
+    """Top-p alone whose crossing lies beyond 2^-32 of the largest weight (one
+    logit 25 above a N(0, 1) row, p = 0.9999999): neither the bounded
+    selection nor the bracket search can hold it, so the histogram path
+    decides."""
+    from workloads import bf16_round
+    b = make_random_batch(580 + (dtype == "bf16"), B=6, V=60000, kmax=2, dtype=dtype, modes=ALL_MODES,
+                          scale=(1.0, 1.0), noise=(0.0, 0.5), temp=(1.0, 1.0))
+    rng = np.random.default_rng(581)
+    for arr in (b.target, b.draft):
+        if arr is None:
+            continue
+        cols = rng.integers(0, b.vocab, size=arr.shape[0])
+        for r, col in enumerate(cols):
+            arr[r, col] = bf16_round(np.array([25.0], np.float32))[0] if dtype == "bf16" else np.float32(25.0)
+    b.top_k = np.zeros(b.batch, np.int32)
+    b.top_p = np.full(b.batch, 0.9999999, np.float32)
+    gu.check_batch(verifier, b, torch_mod, label=f"top-p past the bracket range {dtype}")
