@@ -65,6 +65,7 @@ struct spec_verify_ctx {
   sv::Partial* partials = nullptr;
   float* xval = nullptr;
   float* tau = nullptr;
+  int32_t* order = nullptr;   // the filter kernel's sequence order
   int32_t* ptok = nullptr;
   sv::SeqFinal* fin = nullptr;
   float* tilesum = nullptr;
@@ -140,6 +141,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
   const size_t o_dt = off;     off = align_up(off + sizeof(float) * (size_t)max_batch, 256);
   const size_t o_dm = off;     off = align_up(off + (size_t)max_batch, 256);
   const size_t o_ds = off;     off = align_up(off + sizeof(uint32_t) * (size_t)max_batch, 256);
+  const size_t o_ord = off;    off = align_up(off + sizeof(int32_t) * (size_t)max_batch, 256);
   c->bytes = off;
   e = hipMalloc(&c->mem, c->bytes);
   if (e != hipSuccess) {
@@ -163,6 +165,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
   c->def_temperature = (float*)(b + o_dt);
   c->def_mode = (uint8_t*)(b + o_dm);
   c->def_seq_ids = (uint32_t*)(b + o_ds);
+  c->order = (int32_t*)(b + o_ord);
   {
     std::vector<float> t((size_t)max_batch, 1.0f);
     std::vector<uint32_t> ids((size_t)max_batch);
@@ -284,6 +287,8 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
   p.partials = ctx->partials;
   p.xval = ctx->xval;
   p.tau = ctx->tau;
+  p.order = ctx->order;
+  p.order_block = (a->top_k || a->top_p) ? 1 : 0;
   p.top_k = a->top_k;
   p.top_p = a->top_p;
   p.ptok = ctx->ptok;

@@ -1279,7 +1279,7 @@ __device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Part
 // four blocks per CU (8 waves per SIMD): at most 64 VGPRs
 __global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) k_filter(Params P) {
   __shared__ FiltShared sh;
-  const int r = blockIdx.x, s = blockIdx.y;
+  const int r = blockIdx.x, s = P.order[blockIdx.y];   // the sequence order written by row_stats
   const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
   const int mk = P.max_k;
   const int K = P.num_draft[s];

@@ -100,6 +100,8 @@ struct Params {
   const int32_t* top_k;   // [B] or NULL: top-k filter (<= 0 or >= V: off)
   const float* top_p;     // [B] or NULL: top-p filter (>= 1 or NaN: off)
   float* tau;             // per slot: the filter threshold (written only for filtered sequences)
+  int32_t* order;         // [B]: the filter's sequence order (a permutation, costliest first)
+  int32_t order_block;    // 1: row_stats' block 0 writes `order` (filtered calls), its other blocks shift by one
 };
 
 // N-gram proposer (sv_ngram.hip).

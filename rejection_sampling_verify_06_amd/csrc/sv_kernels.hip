@@ -1074,8 +1074,7 @@ __device__ __forceinline__ void row_stats_seg(const Params& P, const char* rowp,
 }
 
 template <bool TB, bool DB>
-__device__ __forceinline__ void row_stats_body(const Params& P) {
-  const int b = blockIdx.x;
+__device__ __forceinline__ void row_stats_body(const Params& P, int b) {
   const int nblk_t = P.n_t * P.nch_t;
   const bool is_draft = b >= nblk_t;
   const int bb = is_draft ? b - nblk_t : b;
@@ -1091,6 +1090,45 @@ __device__ __forceinline__ void row_stats_body(const Params& P) {
   }
 }
 
+// The filter kernel's sequence order, written by one block of a filtered
+// call's row_stats launch: top-p sequences by decreasing temperature first
+// (a flatter row has a wider nucleus and takes more passes over the row), so
+// that the longest rows start early instead of trailing at the end of the
+// filter launch; top-k sequences next, unfiltered and greedy ones last.  A
+// counting sort over 64 buckets; the order inside a bucket is whatever the
+// atomics give, which changes no output (every row is filtered on its own).
+constexpr int kOrderBuckets = 64;
+
+__device__ __forceinline__ int order_bucket(const Params& P, int s) {
+  const int md = P.mode[s];
+  const float T = P.temperature[s];
+  const int topk = P.top_k ? P.top_k[s] : 0;
+  const float topp = P.top_p ? P.top_p[s] : 1.f;
+  const bool use_k = topk > 0 && topk < P.V, use_p = topp < 1.f;
+  if (md == kGreedy || !(use_k || use_p)) return kOrderBuckets - 1;
+  if (use_k || !(T > 0.f && T < 1e30f)) return kOrderBuckets - 2;
+  return max(0, kOrderBuckets - 3 - (int)fminf(T * 16.f, (float)(kOrderBuckets - 3)));
+}
+
+__device__ __forceinline__ void filter_order(const Params& P) {
+  __shared__ uint32_t cnt[kOrderBuckets];
+  const int t = threadIdx.x;
+  if (t < kOrderBuckets) cnt[t] = 0;
+  __syncthreads();
+  for (int s = t; s < P.B; s += kThreads) atomicAdd(&cnt[order_bucket(P, s)], 1u);
+  __syncthreads();
+  if (t == 0) {
+    uint32_t acc = 0;
+    for (int q = 0; q < kOrderBuckets; ++q) {
+      const uint32_t n = cnt[q];
+      cnt[q] = acc;
+      acc += n;
+    }
+  }
+  __syncthreads();
+  for (int s = t; s < P.B; s += kThreads) P.order[atomicAdd(&cnt[order_bucket(P, s)], 1u)] = s;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1099,7 +1137,15 @@ __device__ __forceinline__ void row_stats_body(const Params& P) {
 
 template <bool TB, bool DB>
 __global__ void __launch_bounds__(kThreads) k_row_stats(Params P) {
-  row_stats_body<TB, DB>(P);
+  int b = blockIdx.x;
+  if (P.order_block) {            // a filtered call: block 0 orders the filter's rows
+    if (b == 0) {
+      filter_order(P);
+      return;
+    }
+    --b;
+  }
+  row_stats_body<TB, DB>(P, b);
 }
 
 // ---------------------------------------------------------------------------
@@ -1470,7 +1516,7 @@ __global__ void __launch_bounds__(kFinThreads) k_select(Params P) {
 // ---------------------------------------------------------------------------
 
 hipError_t launch_row_stats(const Params& p, hipStream_t st, const LaunchEvents* ev) {
-  const int64_t blocks = (int64_t)p.n_t * p.nch_t + (int64_t)p.n_d * p.nch_d;
+  const int64_t blocks = (int64_t)p.n_t * p.nch_t + (int64_t)p.n_d * p.nch_d + p.order_block;
   if (blocks <= 0) return record_empty(st, ev);
   const dim3 g((unsigned)blocks), b(kThreads);
   if (p.t_bf16) {
