@@ -107,3 +107,28 @@ def test_random_batches_with_copies(torch_mod):
     for seed in (3, 4):
         b = make_ngram_batch(seed, B=100, min_len=1, max_len=5000, vocab=300, p_tail_hit=0.5)
         _check(torch_mod, b.history, b.offsets, 2, 6, 9, f"copies seed {seed}")
+
+
+def test_random_histories(torch_mod):
+    """200 seeded random batches: up to 256 histories of up to 60000 tokens
+    over vocabularies of 2 to 152064 ids (many ending in a copied span),
+    windows 1..16, 1..64 proposed tokens."""
+    for case in range(200):
+        rng = np.random.default_rng(700_000 + case)
+        B = int(rng.integers(1, 257))
+        maxlen = int(rng.choice([10, 100, 3000, 20000, 60000]))
+        lengths = rng.integers(0, maxlen + 1, B)
+        vocab = int(rng.choice([2, 5, 50, 1000, 152064]))
+        parts = []
+        for L in lengths:
+            h = rng.integers(0, vocab, L).astype(np.int32)
+            if L > 40 and rng.random() < 0.6:
+                span = int(rng.integers(2, 20))
+                src = int(rng.integers(0, L - span - 1))
+                h[L - span:] = h[src:src + span]
+            parts.append(h)
+        hist = np.concatenate(parts) if parts else np.zeros(0, np.int32)
+        off = np.concatenate(([0], np.cumsum(lengths))).astype(np.int64)
+        max_n = int(rng.choice([1, 2, 3, 4, 5, 8, 9, 16]))
+        min_n = int(rng.integers(1, max_n + 1))
+        _check(torch_mod, hist, off, min_n, max_n, int(rng.choice([1, 3, 5, 8, 64])), f"random {case}")

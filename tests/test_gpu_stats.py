@@ -183,3 +183,41 @@ def test_bad_arguments_enqueue_nothing(torch_mod):
         sv.DraftLengthController(4, 5, device="cuda")
     with pytest.raises(sv.VerifyError):
         sv.DraftLengthController(4, 0, target=1.5, device="cuda")
+
+
+def test_random_controller_parameters(torch_mod):
+    """40 seeded random controllers (kind, bounds, window, samples, target,
+    rate, batch, initial length) over random rounds, and random counter
+    batches: identical to the oracle."""
+    import rejection_sampling_verify_06_amd as sv
+    for case in range(40):
+        rng = np.random.default_rng(600_000 + case)
+        kind = int(rng.integers(0, 3))
+        max_k = int(rng.integers(1, 65))
+        kw = dict(min_k=int(rng.integers(1, max_k + 1)), max_k=max_k, target=float(rng.uniform(0.05, 0.95)))
+        if kind == 0:
+            kw.update(window=int(rng.integers(1, 257)), min_samples=int(rng.integers(1, 40)))
+        if kind == 1:
+            kw.update(rate=float(rng.uniform(0.01, 0.9)))
+        B, init_k = int(rng.integers(1, 600)), int(rng.integers(1, 65))
+        ctl = sv.DraftLengthController(B, kind, init_k=init_k, device="cuda", **kw)
+        states = [oracle.Controller(init_k) for _ in range(B)]
+        L = np.full(B, init_k, np.int32)
+        beta = rng.random(B)
+        for t in range(int(rng.integers(5, 60))):
+            K = np.minimum(L, 128).astype(np.int32)
+            K = np.where(rng.random(B) < 0.05, rng.integers(0, 130, B), K).astype(np.int32)
+            A = np.minimum(rng.geometric(np.clip(1 - beta, 1e-3, 1)) - 1, K).astype(np.int32)
+            A = np.where(rng.random(B) < 0.03, -1, A).astype(np.int32)
+            got = ctl.update(_dev(torch_mod, K), _dev(torch_mod, A)).cpu().numpy()
+            want = oracle.adapt_batch(states, K, A, kind, **kw)
+            assert np.array_equal(got, want), (case, t, np.nonzero(got != want)[0][:5])
+            L = want
+        mk, Bs = int(rng.integers(1, 129)), int(rng.integers(0, 5000))
+        K = rng.integers(0, mk + 3, Bs).astype(np.int32)
+        A = np.minimum(rng.integers(-1, mk + 1, Bs), K).astype(np.int32)
+        st = sv.AcceptanceStats(mk, "cuda")
+        st.add(_dev(torch_mod, K), _dev(torch_mod, A))
+        ref = oracle.acceptance_counters(K, A, mk)
+        assert np.array_equal(st.counters.cpu().numpy().astype(np.uint64), ref), case
+        assert _same_doubles(st.summary().cpu().numpy(), oracle.acceptance_summary(ref, mk)), case
