@@ -84,6 +84,28 @@ __device__ __forceinline__ float kval(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// bf16 values in the order of their 16-bit keys: one step up or down
+__device__ __forceinline__ float bf16_step(float v, int dir) {
+  const uint32_t h = __float_as_uint(v) >> 16;
+  uint32_t k = (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+  k = (k + (uint32_t)dir) & 0xFFFFu;
+  const uint32_t g = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+  return __uint_as_float(g << 16);
+}
+
+// true when at most one bf16 value x has dlo < fmaf(-x, c, mc) <= dhi (the
+// d of every element that value holds); false also when that is not sure
+__device__ __forceinline__ bool one_bf16_value(float dlo, float dhi, float c, float mc) {
+  // the smallest value with d <= dhi (d does not increase with x): from an
+  // estimate, a few steps each way
+  float v = __uint_as_float(__float_as_uint((mc - dhi) / c) & 0xFFFF0000u);
+  for (int i = 0; i < 4 && !(fmaf(-v, c, mc) <= dhi); ++i) v = bf16_step(v, 1);
+  for (int i = 0; i < 4 && fmaf(-bf16_step(v, -1), c, mc) <= dhi; ++i) v = bf16_step(v, -1);
+  if (!(fmaf(-v, c, mc) <= dhi) || fmaf(-bf16_step(v, -1), c, mc) <= dhi) return false;
+  // one value iff the next one up is above the bracket already
+  return fmaf(-bf16_step(v, 1), c, mc) <= dlo;
+}
+
 template <bool BF>
 __device__ __forceinline__ float load_x(const char* rowp, int e) {
   return BF ? __uint_as_float((uint32_t)((const uint16_t*)rowp)[e] << 16) : ((const float*)rowp)[e];
@@ -985,10 +1007,11 @@ __device__ __forceinline__ void chunk_pass(FiltShared& sh, const char* rowp, int
 // the row sums, per thread in registers, the masses and counts of the
 // bracket's tokens at or below kBJ thresholds dividing it evenly; the block
 // sums name the sub-bracket where the mass from the top reaches the target.
-// Once it holds at most kCap tokens (or after kBracketPasses passes), one
-// more pass collects them into LDS and sums the mass above the bracket; the
-// exact selection then runs on top of that mass.  A bracket of tokens that
-// all tie is decided without them.  false (block-uniform): the histogram
+// Once it holds at most kCap tokens (or after kBracketPasses passes, or,
+// for bf16 rows, once it can hold one value only), one more pass collects
+// them into LDS and sums the mass above the bracket; the exact selection
+// then runs on top of that mass.  A bracket of tokens that all tie is
+// decided without them.  false (block-uniform): the histogram
 // path must decide (a crossing past 2^-32 of the maximum, a bracket too
 // large, or a float sum that put the crossing outside the bracket).
 constexpr int kBracketPasses = 6;
@@ -1081,7 +1104,11 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
     alo += aprev;
     dlo = jq > 0 ? D[jq - 1] : dlo;
     dhi = D[jq];
+    // a bf16 bracket that can hold one value only is a tie group: narrower
+    // brackets would hold the same tokens
+    const bool tie = BF && cnt > (uint32_t)kCap && one_bf16_value(dlo, dhi, c, mc);
     __syncthreads();                           // wfm / bm are written again by the next pass
+    if (tie) break;
   }
 
   // ---- collect: the bracket's tokens, the mass above it, the bracket's key range ----
