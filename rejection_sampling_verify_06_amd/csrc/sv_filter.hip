@@ -58,7 +58,7 @@ constexpr float kBinSpan = kBins / kBinScale;  // 32: d beyond this falls into t
 constexpr float kFineScale = 2048.f;           // fine bins per log2 unit inside one coarse bin
 constexpr int kCap = 1024;                     // candidates held in LDS
 constexpr int kUnroll = 16;                    // loads in flight per thread
-constexpr int kBJ = 4;                         // thresholds per bracket-search pass (8 or 16: slower, ALU-bound)
+constexpr int kBJ = 4;                         // thresholds of a dense bracket-search pass (8 or 16: slower, ALU-bound)
 constexpr int kMaxChunks = kMaxTiles * kTileElems / (kChunkBytes / 4);   // 256
 constexpr double kMassOne = 1099511627776.0;   // 2^40
 constexpr float kLog2eF = 1.4426950408889634f;
@@ -1003,18 +1003,24 @@ __device__ __forceinline__ void chunk_pass(FiltShared& sh, const char* rowp, int
 
 // ---- bracket search (top-p alone, nuclei the maxima cannot bound) ----
 //
-// The crossing lies in a bracket (dlo, dhi] of d = M*c - x*c.  A pass over
-// the row sums, per thread in registers, the masses and counts of the
-// bracket's tokens at or below kBJ thresholds dividing it evenly; the block
-// sums name the sub-bracket where the mass from the top reaches the target.
-// Once it holds at most kCap tokens (or after kBracketPasses passes, or,
-// for bf16 rows, once it can hold one value only), one more pass collects
-// them into LDS and sums the mass above the bracket; the exact selection
-// then runs on top of that mass.  A bracket of tokens that all tie is
+// The crossing lies in a bracket (dlo, dhi] of d = M*c - x*c.  Each pass
+// over the row splits the bracket evenly and names the part where the mass
+// from the top reaches the target.  While the bracket holds more than half
+// the row, a pass sums per thread, in registers, the masses and counts at
+// or below kBJ thresholds; after that, the bracket's tokens are gathered
+// per wave and binned into kSB bins, so the cost per element is a test and
+// the binning is paid per token.  Once the bracket holds at most kCap
+// tokens (or after kBracketPasses passes, or, for bf16 rows, once it can
+// hold one value only), one more pass collects them into LDS and sums the
+// mass above the bracket; the exact selection then runs on top of that
+// mass.  A bracket of tokens that all tie is
 // decided without them.  false (block-uniform): the histogram
 // path must decide (a crossing past 2^-32 of the maximum, a bracket too
 // large, or a float sum that put the crossing outside the bracket).
 constexpr int kBracketPasses = 6;
+constexpr int kRing = 256;                     // per-wave ring of bracket tokens (in the idle candidate masses)
+constexpr int kSB = kBins;                     // bins per sparse pass (in the idle histogram buffers)
+static_assert(kFWaves * kRing * sizeof(float) <= kCap * sizeof(uint64_t), "the rings fit in sh.cm");
 
 // a failed bracket search leaves the chunk sums zero for the histogram path
 __device__ __forceinline__ void bracket_clear(FiltShared& sh, bool chunk_sums) {
@@ -1040,74 +1046,167 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
   double alo = 0.0;                            // mass of the tokens with d <= dlo
   uint32_t cnt = 0xFFFFFFFFu;
   for (int pass = 0; pass < kBracketPasses && cnt > (uint32_t)kCap; ++pass) {
-    const float base = fmaxf(dlo, 0.f), step = (dhi - base) / kBJ;
-    float D[kBJ];
+    const float base = fmaxf(dlo, 0.f);
+    int jq;                                    // the sub-bracket where the mass reaches the target
+    double aprev;                              // mass of the bracket's tokens below it
+    float nlo, nhi;                            // its bounds
+    if (cnt > (uint32_t)V / 2) {
+      // ---- dense pass (the first): kBJ thresholds, per-thread sums in registers ----
+      const float step = (dhi - base) / kBJ;
+      float D[kBJ];
 #pragma unroll
-    for (int q = 0; q < kBJ; ++q) D[q] = (q == kBJ - 1) ? dhi : base + (float)(q + 1) * step;
-    float m[kBJ];
-    uint32_t n[kBJ];
+      for (int q = 0; q < kBJ; ++q) D[q] = (q == kBJ - 1) ? dhi : base + (float)(q + 1) * step;
+      float m[kBJ];
+      uint32_t n[kBJ];
 #pragma unroll
-    for (int q = 0; q < kBJ; ++q) {
-      m[q] = 0.f;
-      n[q] = 0;
-    }
-    auto acc = [&](const uint4(&w)[kVecPer], int) __attribute__((always_inline)) {
+      for (int q = 0; q < kBJ; ++q) {
+        m[q] = 0.f;
+        n[q] = 0;
+      }
+      auto acc = [&](const uint4(&w)[kVecPer], int) __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = 0; u < kVecPer; ++u)
+        for (int u = 0; u < kVecPer; ++u)
 #pragma unroll
-        for (int j = 0; j < epv; ++j) {
-          const float d = fmaf(-vec_elem<BF>(w[u], j), c, mc);
-          if (d > dlo && d <= dhi) {             // NaN and -inf logits never pass
-            const float e = fexp2(-d);
+          for (int j = 0; j < epv; ++j) {
+            const float d = fmaf(-vec_elem<BF>(w[u], j), c, mc);
+            if (d > dlo && d <= dhi) {           // NaN and -inf logits never pass
+              const float e = fexp2(-d);
 #pragma unroll
-            for (int q = 0; q < kBJ; ++q) {
-              const bool in = d <= D[q];
-              m[q] += in ? e : 0.f;
-              n[q] += in ? 1u : 0u;
+              for (int q = 0; q < kBJ; ++q) {
+                const bool in = d <= D[q];
+                m[q] += in ? e : 0.f;
+                n[q] += in ? 1u : 0u;
+              }
             }
           }
-        }
-    };
-    for_rounds(vp, 0, sp.nvec, acc);
-    for_singles<BF>(rowp, sp, acc);
+      };
+      for_rounds(vp, 0, sp.nvec, acc);
+      for_singles<BF>(rowp, sp, acc);
 #pragma unroll
-    for (int q = 0; q < kBJ; ++q) {
-      const float ws = wave_sum(m[q]);
-      const uint32_t ns = wave_sum_u32(n[q]);
-      if (lane == 0) {
-        sh.wfm[wv][q] = ws;
-        sh.wfn[wv][q] = ns;
+      for (int q = 0; q < kBJ; ++q) {
+        const float ws = wave_sum(m[q]);
+        const uint32_t ns = wave_sum_u32(n[q]);
+        if (lane == 0) {
+          sh.wfm[wv][q] = ws;
+          sh.wfn[wv][q] = ns;
+        }
       }
-    }
-    __syncthreads();
-    if (t < kBJ) {
-      double a = 0.0;
-      uint32_t b = 0;
-      for (int w = 0; w < kFWaves; ++w) {
-        a += (double)sh.wfm[w][t];
-        b += sh.wfn[w][t];
+      __syncthreads();
+      if (t < kBJ) {
+        double a = 0.0;
+        uint32_t b = 0;
+        for (int w = 0; w < kFWaves; ++w) {
+          a += (double)sh.wfm[w][t];
+          b += sh.wfn[w][t];
+        }
+        sh.bm[t] = a;
+        sh.bn[t] = b;
       }
-      sh.bm[t] = a;
-      sh.bn[t] = b;
+      __syncthreads();
+      jq = -1;
+      for (int q = kBJ - 1; q >= 0; --q)
+        if (alo + sh.bm[q] >= target) jq = q;   // the first threshold whose mass reaches the target
+      aprev = jq > 0 ? sh.bm[jq - 1] : 0.0;
+      cnt = jq >= 0 ? sh.bn[jq] - (jq > 0 ? sh.bn[jq - 1] : 0u) : 0u;
+      nlo = jq > 0 ? D[jq - 1] : dlo;
+      nhi = jq >= 0 ? D[jq] : dhi;
+    } else {
+      // ---- sparse pass: kSB bins ----
+      // The wave gathers its bracket tokens' d in a ring in LDS and bins
+      // them 64 at a time, one per lane, into its wave pair's kSB bins
+      // (fixed-point masses and counts, LDS atomics: order-independent).
+      // The ring never holds more than 127 pending of its kRing entries;
+      // within a wave, LDS accesses complete in order.
+      const float step = (dhi - base) / kSB, inv = step > 0.f ? 1.f / step : 0.f;
+      auto thr = [&](int q) __attribute__((always_inline)) {
+        return q == kSB - 1 ? dhi : base + (float)(q + 1) * step;
+      };
+      for (int j = t; j < kHist * kBins; j += kFThreads) {
+        (&sh.hb.wc[0][0])[j] = 0;
+        (&sh.hb.wm[0][0])[j] = 0;
+      }
+      __syncthreads();
+      uint64_t* wbm = sh.hb.wm[wv >> 1];
+      uint32_t* wbn = sh.hb.wc[wv >> 1];
+      // one token (d = +inf: none) into the first bin q with d <= thr(q)
+      // (the estimate corrected by a step each way); its mass in units of
+      // 2^-31 of the weight at d = base (every token has d > base, or
+      // d >= 0 > dlo: below 2^32 units)
+      auto put = [&](float d) __attribute__((always_inline)) {
+        if (d <= dhi) {
+          int b = (int)ceilf(fminf(fmaxf((d - base) * inv, 0.f), (float)kSB)) - 1;
+          b = min(max(b, 0), kSB - 1);
+          if (b < kSB - 1 && d > thr(b)) ++b;
+          if (b > 0 && d <= thr(b - 1)) --b;
+          atomicAdd(&wbm[b], (unsigned long long)(uint32_t)fexp2(base - d + 31.f));
+          atomicAdd(&wbn[b], 1u);
+        }
+      };
+      float* ring = reinterpret_cast<float*>(sh.cm) + wv * kRing;
+      uint32_t wr = 0, rd = 0;                 // wave-uniform: tokens written, binned
+      auto gather = [&](const uint4(&w)[kVecPer], int) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kVecPer; ++u)
+#pragma unroll
+          for (int j = 0; j < epv; ++j) {
+            const float d = fmaf(-vec_elem<BF>(w[u], j), c, mc);
+            const bool in = d > dlo && d <= dhi;
+            const uint64_t mask = __ballot(in);
+            if (mask) {
+              if (in) {
+                const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                ring[(wr + below) & (kRing - 1)] = d;
+              }
+              wr += (uint32_t)__popcll(mask);
+              if (wr - rd >= (uint32_t)kWave) {
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                put(ring[(rd + lane) & (kRing - 1)]);
+                rd += kWave;
+              }
+            }
+          }
+      };
+      for_rounds(vp, 0, sp.nvec, gather);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      put(rd + lane < wr ? ring[(rd + lane) & (kRing - 1)] : INFINITY);
+      for_singles<BF>(rowp, sp, [&](const uint4(&w)[kVecPer], int) __attribute__((always_inline)) {
+        const float d = fmaf(-vec_elem<BF>(w[0], 0), c, mc);   // the single element
+        if (d > dlo) put(d);
+      });
+      __syncthreads();
+      if (t < kSB) {                           // block sums of the bins
+        uint64_t a = 0;
+        uint32_t k = 0;
+        for (int h = 0; h < kHist; ++h) {
+          a += sh.hb.wm[h][t];
+          k += sh.hb.wc[h][t];
+        }
+        sh.hm[t] = a;
+        sh.hc[t] = k;
+      }
+      __syncthreads();
+      const double unit = (double)fexp2(base) * 2147483648.0;   // bin mass units per maximum's weight
+      const double need = (target - alo) * unit;
+      if (wv == 0) scan_bins<true>(sh, sh.hc, sh.hm, false, 0u, need);
+      __syncthreads();
+      jq = uni(sh.bin);
+      aprev = (need - sh.rem) / unit;
+      cnt = jq >= 0 ? sh.hc[jq] : 0u;
+      nlo = jq > 0 ? thr(jq - 1) : dlo;
+      nhi = jq >= 0 ? thr(jq) : dhi;
     }
-    __syncthreads();
-    int jq = -1;
-    for (int q = kBJ - 1; q >= 0; --q)
-      if (alo + sh.bm[q] >= target) jq = q;     // the first threshold whose mass reaches the target
     if (jq < 0) {                              // past dhi: beyond 2^-32 of the maximum, or rounding
       __syncthreads();
       return false;
     }
-    const double aprev = jq > 0 ? sh.bm[jq - 1] : 0.0;
-    const uint32_t nprev = jq > 0 ? sh.bn[jq - 1] : 0u;
-    cnt = sh.bn[jq] - nprev;
     alo += aprev;
-    dlo = jq > 0 ? D[jq - 1] : dlo;
-    dhi = D[jq];
+    dlo = nlo;
+    dhi = nhi;
     // a bf16 bracket that can hold one value only is a tie group: narrower
     // brackets would hold the same tokens
     const bool tie = BF && cnt > (uint32_t)kCap && one_bf16_value(dlo, dhi, c, mc);
-    __syncthreads();                           // wfm / bm are written again by the next pass
+    __syncthreads();                           // the sums and bins are written again by the next pass
     if (tie) break;
   }
 
