@@ -1020,6 +1020,7 @@ __device__ __forceinline__ void chunk_pass(FiltShared& sh, const char* rowp, int
 constexpr int kBracketPasses = 6;
 constexpr int kRing = 256;                     // per-wave ring of bracket tokens (in the idle candidate masses)
 constexpr int kSB = kBins;                     // bins per sparse pass (in the idle histogram buffers)
+static_assert(kSB == 1 << 8, "the bracket search stops at kSB bins of 2^-21 * dhi = 2^-13 * dhi");
 static_assert(kFWaves * kRing * sizeof(float) <= kCap * sizeof(uint64_t), "the rings fit in sh.cm");
 
 // a failed bracket search leaves the chunk sums zero for the histogram path
@@ -1203,9 +1204,13 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
     alo += aprev;
     dlo = nlo;
     dhi = nhi;
-    // a bf16 bracket that can hold one value only is a tie group: narrower
-    // brackets would hold the same tokens
-    const bool tie = BF && cnt > (uint32_t)kCap && one_bf16_value(dlo, dhi, c, mc);
+    // A bf16 bracket that can hold one value only is a tie group: narrower
+    // brackets would hold the same tokens.  Nor is a bracket split further
+    // once the next pass's bins would be narrower than 2^-21 * dhi (4 to 8
+    // ulps of d; kSB such bins span 2^-13 * dhi): the thresholds would no
+    // longer separate tokens, and the bracket holds few distinct d values.
+    const bool tie = cnt > (uint32_t)kCap &&
+                     ((BF && one_bf16_value(dlo, dhi, c, mc)) || !(dhi - fmaxf(dlo, 0.f) >= dhi * 0x1p-13f));
     __syncthreads();                           // the sums and bins are written again by the next pass
     if (tie) break;
   }

@@ -4,7 +4,8 @@ near-ties; a top-p crossing within 1e-5 of a tie group may follow the
 neighbouring threshold).  Covers every mode with per-sequence filters,
 tie-heavy bf16 rows, thresholds on the largest and the smallest logits,
 boundary bins larger than the filter's LDS buffer (refined by passes over
-the row), filters that are off, and the C3 workload with filters."""
+the row), filters that are off, the C3 workload with filters, and top-p
+alone on flat rows that only the bracket search can decide."""
 import numpy as np
 import pytest
 
@@ -194,3 +195,53 @@ def test_topp_crossing_past_bracket_range(verifier, torch_mod, dtype):
     b.top_k = np.zeros(b.batch, np.int32)
     b.top_p = np.full(b.batch, 0.9999999, np.float32)
     gu.check_batch(verifier, b, torch_mod, label=f"top-p past the bracket range {dtype}")
+
+
+def _flat_batch(dtype: str, V: int, seed: int, grid: int) -> Batch:
+    """Rows of N(0, sigma) logits, sigma in {0.5, 1, 2}, at temperatures 0.7
+    to 3: with sigma / T <= 2 the 1024 largest of 100,000 weights carry at most
+    about 37% of a row's mass (the upper 1% of a normal holds P(Z > 2.33 -
+    sigma/T) of the exponential's mean), so every target row's top-p of 0.5 or
+    more is left to the bracket search (draft rows, target plus noise, take
+    either path).  With ``grid`` > 0 the logits sit on a grid of
+    1/grid, so the crossing falls inside a tie group of thousands of tokens.
+    Sample-mode sequences bring draft rows (filtered too); proposals are the
+    target row's argmax or a random token."""
+    rng = np.random.default_rng(seed)
+    B, K = 8, 2
+    sig_t = rng.choice(np.array([0.5, 1.0, 2.0], np.float32), size=(B * (K + 1), 1))
+    tgt = rng.standard_normal((B * (K + 1), V)).astype(np.float32) * sig_t
+    dft = (tgt.reshape(B, K + 1, V)[:, :K].reshape(B * K, V)
+           + 0.5 * rng.standard_normal((B * K, V)).astype(np.float32))
+    if grid:
+        tgt = np.round(tgt * grid) / grid
+        dft = np.round(dft * grid) / grid
+    temps = rng.choice(np.array([0.7, 1.0, 1.5, 3.0], np.float32), size=B)
+    # sigma / T <= 2 on every row: scale down the rows of low-temperature sequences
+    row_t = np.repeat(temps, K + 1)[:, None]
+    tgt = np.where(sig_t / row_t > 2.0, tgt * (2.0 * row_t / sig_t), tgt).astype(np.float32)
+    if grid:
+        tgt = np.round(tgt * grid) / grid
+    modes = rng.choice(np.asarray([MODE_SAMPLE, MODE_ONEHOT, MODE_STRICT], np.uint8), size=B)
+    am = tgt.reshape(B, K + 1, V)[:, :K].argmax(axis=2).reshape(-1)
+    toks = np.where(rng.random(B * K) < 0.5, am, rng.integers(0, V, size=B * K)).astype(np.int32)
+    store = (lambda a: bf16_round(a)) if dtype == "bf16" else (lambda a: a)
+    return Batch(name=f"flat rows V={V} {dtype} grid={grid}", vocab=V, dtype=dtype, target=store(tgt),
+                 draft=store(dft.astype(np.float32)), num_draft=np.full(B, K, np.int32), draft_tokens=toks,
+                 temperature=temps, mode=modes, seq_ids=np.arange(B, dtype=np.uint32), seed=seed,
+                 top_k=np.zeros(B, np.int32),
+                 top_p=rng.choice(np.array([0.5, 0.9, 0.95, 0.99, 0.999], np.float32), size=B))
+
+
+@pytest.mark.parametrize("dtype,grid", [("bf16", 0), ("f32", 0), ("bf16", 4), ("f32", 8)])
+def test_topp_bracket_search_flat_rows(verifier, torch_mod, dtype, grid):
+    """Top-p alone on rows whose nucleus the thread maxima cannot carry: the
+    bracket search's dense first pass, its binned passes, the end at one tied
+    bf16 value (grid 4) and the f32 tie group past the last pass (grid 8);
+    a second call gives bitwise the same outputs."""
+    b = _flat_batch(dtype, 100_000, 610 + grid + (dtype == "bf16"), grid)
+    _, out, _ = gu.check_batch(verifier, b, torch_mod, label=f"top-p bracket search, flat rows {dtype} grid={grid}")
+    again = gu.run_gpu(verifier, b, torch_mod)
+    for k in ("accepted_len", "emitted", "status"):
+        assert np.array_equal(out[k], again[k]), k
+    assert np.array_equal(out["p_at"], again["p_at"], equal_nan=True)
