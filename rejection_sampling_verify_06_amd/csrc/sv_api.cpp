@@ -63,6 +63,7 @@ struct spec_verify_ctx {
   void* mem = nullptr;
   size_t bytes = 0;
   sv::Partial* partials = nullptr;
+  float* segmax = nullptr;
   float* xval = nullptr;
   float* tau = nullptr;
   int32_t* order = nullptr;   // the filter kernel's sequence order
@@ -142,6 +143,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
   const size_t o_dm = off;     off = align_up(off + (size_t)max_batch, 256);
   const size_t o_ds = off;     off = align_up(off + sizeof(uint32_t) * (size_t)max_batch, 256);
   const size_t o_ord = off;    off = align_up(off + sizeof(int32_t) * (size_t)max_batch, 256);
+  const size_t o_seg = off;    off = align_up(off + sizeof(float) * sv::kSegPerChunk * c->max_rows * c->max_nch, 256);
   c->bytes = off;
   e = hipMalloc(&c->mem, c->bytes);
   if (e != hipSuccess) {
@@ -166,6 +168,7 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
   c->def_mode = (uint8_t*)(b + o_dm);
   c->def_seq_ids = (uint32_t*)(b + o_ds);
   c->order = (int32_t*)(b + o_ord);
+  c->segmax = (float*)(b + o_seg);
   {
     std::vector<float> t((size_t)max_batch, 1.0f);
     std::vector<uint32_t> ids((size_t)max_batch);
@@ -289,6 +292,7 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
   p.tau = ctx->tau;
   p.order = ctx->order;
   p.order_block = (a->top_k || a->top_p) ? 1 : 0;
+  p.segmax = a->top_k ? ctx->segmax : nullptr;   // top-k bounds from row_stats' segment maxima
   p.top_k = a->top_k;
   p.top_p = a->top_p;
   p.ptok = ctx->ptok;

@@ -182,6 +182,7 @@ struct FiltShared {
   uint32_t ncand, kmin_c, kmax_c;
   uint32_t tmin, nkc;          // bounded selection: smallest kept key, kept-set counter
   double mtot;                 // mass above the candidates plus theirs (selection by ranks or prefixes)
+  uint32_t segb;                // bounded selection: the top-k bound from the segment maxima
   // bracket search (top-p alone): per-wave, then block sums of the masses and
   // counts at or below each threshold, and the bracket's key range
   float wfm[kFWaves][kBJ];
@@ -754,7 +755,7 @@ __device__ __forceinline__ uint32_t select_by_rank(FiltShared& sh, int n, float 
 template <bool BF>
 __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp, int V, int ce, float c, float mc,
                                                bool use_k, int topk, bool use_p, float topp, int xs,
-                                               uint32_t* tau_key) {
+                                               const float* segp, int nseg, uint32_t* tau_key) {
   constexpr int epv = BF ? 8 : 4;
   const int t = threadIdx.x;
   if (use_k && topk > 2 * kFThreads) return false;
@@ -766,10 +767,14 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
   // k/kTargetCand of the row leaves about kTargetCand tokens at or above the
   // bound.  Top-p alone reads every vector (a sample could miss the
   // heaviest tokens).  Either way the head and tail elements are left to
-  // read 2.
-  const int nva = use_k ? (int)min((int64_t)sp.nvec, max((int64_t)kRound,
-                                                          ((int64_t)V * topk / kTargetCand + epv - 1) / epv))
-                        : sp.nvec;
+  // read 2.  With the row's segment maxima (segp: nseg maxima of disjoint
+  // parts of the row, from the row statistics) top-k reads nothing here:
+  // the k-th largest of maxima of k disjoint parts is at most the row's
+  // k-th largest too.
+  const int nva = segp ? 0
+                  : use_k ? (int)min((int64_t)sp.nvec, max((int64_t)kRound,
+                                                            ((int64_t)V * topk / kTargetCand + epv - 1) / epv))
+                          : sp.nvec;
 
   // ---- read 1: every thread's maximum over the sample ----
   // (the first round stays in registers for read 2)
@@ -790,8 +795,17 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
         else mxa = fmaxf(mxa, vec_elem<BF>(w[u], j));
       }
   };
-  take_max(w0, 0);
-  for_rounds(vp, kRound, nva, take_max);
+  if (segp) {
+    // more than kFThreads segments: every thread folds the segments t,
+    // t + 1024, ... and t + 512, t + 1536, ... (maxima of disjoint parts)
+    if (nseg > kFThreads) {
+      for (int i = t; i < nseg; i += 2 * kFThreads) mxa = fmaxf(mxa, segp[i]);
+      for (int i = t + kFThreads; i < nseg; i += 2 * kFThreads) mxb = fmaxf(mxb, segp[i]);
+    }
+  } else {
+    take_max(w0, 0);
+    for_rounds(vp, kRound, nva, take_max);
+  }
   // ---- the bound: an exact radix select over the maxima's keys ----
   // (by count for top-k: the k-th largest maximum; by mass for top-p alone:
   // the maximum where their mass from the top reaches the target)
@@ -802,7 +816,24 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
   }
   const uint32_t ka = fkey(mxa), kb = fkey(mxb);   // no elements: the key of -inf, mass 0
   uint32_t bound;
-  if (use_k) {
+  if (segp && nseg <= kFThreads) {
+    // few segment maxima: the topk-th largest by ranks (ties by position),
+    // one per thread, against all of them in LDS
+    const uint32_t my = t < nseg ? fkey(segp[t]) : 0u;
+    if (t < nseg) sh.ck[t] = my;
+    __syncthreads();
+    if (t < nseg) {
+      uint32_t above = 0;
+      for (int j = 0; j < nseg; ++j) {
+        const uint32_t kj = sh.ck[j];
+        above += (kj > my || (kj == my && j < t)) ? 1u : 0u;
+      }
+      if (above == (uint32_t)topk - 1) sh.segb = my;   // one thread: ranks are distinct
+    }
+    __syncthreads();
+    bound = sh.segb;
+    __syncthreads();                           // sh.ck is the candidates' buffer from here on
+  } else if (use_k) {
     bound = radix_select_regs<false>(sh, ka, 0ull, kb, 0ull, (uint32_t)topk, 0.0, kBoundPasses);
   } else {
     bound = radix_select_regs<true>(sh, ka, fixed_mass_d(fmaf(-mxa, c, mc)), kb, fixed_mass_d(fmaf(-mxb, c, mc)),
@@ -1377,7 +1408,7 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
 template <bool BF>
 __device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Partial* pp, const char* rowp, int nch,
                                            int ce, float c, float mc, float M, bool use_k, int topk, bool use_p,
-                                           float topp, int xs, float* tau_out) {
+                                           float topp, int xs, const float* segp, float* tau_out) {
   const int t = threadIdx.x;
   const int V = P.V;
   for (int j = t; j < nch; j += kFThreads) {
@@ -1388,7 +1419,8 @@ __device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Part
   // top-p alone: the 1024 maxima weigh at most 1024 times the largest
   // logit's weight, so a target above that rules the bounded selection out
   const bool hopeless = use_p && !use_k && (double)topp * sh.zrow > 2.0 * kFThreads * kMassOne;
-  if (!hopeless && bounded_filter<BF>(sh, rowp, V, ce, c, mc, use_k, topk, use_p, topp, xs, &bkey)) {
+  if (!hopeless &&
+      bounded_filter<BF>(sh, rowp, V, ce, c, mc, use_k, topk, use_p, topp, xs, segp, nch * kSegPerChunk, &bkey)) {
     write_partials(sh, pp, nch, M, kval(bkey), tau_out);
     return;
   }
@@ -1482,10 +1514,16 @@ __global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(
   const int ce = draft ? P.ce_d : P.ce_t;
   const int xs = (md == kModeStrict && !draft && r < K) ? P.ptok[(int64_t)s * mk + r] : -1;
   float* tau_out = P.tau + (int64_t)s * P.slots + r;
+  // the row's segment maxima: written by the row statistics' vector path
+  // (rows of this matrix 16-byte aligned, V of a vector or more); used for
+  // top-k of at most half their number, where they bound it closely
+  const bool vec_rows = (draft ? P.d_vec : P.t_vec) && P.V >= (bf ? 8 : 4);
+  const float* segp = (P.segmax && use_k && vec_rows && 2 * topk <= nch * kSegPerChunk)
+                          ? P.segmax + (pp - P.partials) * kSegPerChunk : nullptr;
   if (bf)
-    filter_row<true>(P, sh, pp, rowp, nch, ce, c, mc, M, use_k, topk, use_p, topp, xs, tau_out);
+    filter_row<true>(P, sh, pp, rowp, nch, ce, c, mc, M, use_k, topk, use_p, topp, xs, segp, tau_out);
   else
-    filter_row<false>(P, sh, pp, rowp, nch, ce, c, mc, M, use_k, topk, use_p, topp, xs, tau_out);
+    filter_row<false>(P, sh, pp, rowp, nch, ce, c, mc, M, use_k, topk, use_p, topp, xs, segp, tau_out);
 }
 
 hipError_t launch_filter(const Params& p, hipStream_t st, const LaunchEvents* ev) {

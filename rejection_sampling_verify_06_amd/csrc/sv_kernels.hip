@@ -45,6 +45,7 @@ namespace sv {
 namespace {
 
 using namespace wave;   // kWave and the DPP reductions and scans (sv_wave.h)
+static_assert(kSegPerChunk * 16 == kThreads, "one segment maximum per 16-lane group of a row-stats block");
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = kThreads / kWave;
@@ -966,7 +967,8 @@ __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp,
   float tmx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < N; ++k) tmx = fmaxf(tmx, f[k]);
-  const float mx = wave_max(tmx);
+  const float rmx = row16_max(tmx);        // the maximum of this thread's 16-lane group
+  const float mx = wave_max(rmx);
   if (lane == 0) sh.m[wv] = mx;
   __syncthreads();
   Owner own;                               // block-uniform: scalar registers
@@ -974,6 +976,11 @@ __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp,
   own.T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sh.own.T)));
   own.md = __builtin_amdgcn_readfirstlane(sh.own.md);
   if (own.s < 0) return;                   // the whole block: inconsistent layout
+  if (P.segmax) {                          // calls with top-k: the groups' maxima bound it (filter kernel)
+    const int sbs = __builtin_amdgcn_readfirstlane(sh.sb);
+    if (sbs >= 0 && (lane & 15) == 0)
+      P.segmax[((int64_t)sbs * P.nch_max + chunk) * kSegPerChunk + wv * (kWave / 16) + (lane >> 4)] = rmx;
+  }
   const float M = fmaxf(fmaxf(sh.m[0], sh.m[1]), fmaxf(sh.m[2], sh.m[3]));
   const float c = row_scale(own.md, own.T);
   const float mc = (M == -INFINITY) ? 0.f : M * c;
