@@ -146,9 +146,11 @@ typedef struct spec_verify_args {
 
 /* Create a context on HIP device `device` for batches of at most max_batch
  * sequences, K_s <= max_k (1..128) and vocab <= max_vocab.  Allocates the
- * context's device scratch (per-chunk partial row statistics, per-sequence
- * final-draw records and tile sums, defaults for NULL optional inputs); the
- * caller owns every input and output
+ * context's device scratch (per-chunk partial row statistics and, for the
+ * top-k filter, 16 segment maxima per chunk; per-sequence final-draw records
+ * and tile sums; defaults for NULL optional inputs): about 80 bytes per 8192
+ * vocabulary entries per row slot, max_batch * (2 * max_k + 1) slots, plus
+ * small per-sequence arrays.  The caller owns every input and output
  * buffer.  Returns SV_OK and sets *out, or an error code (then *out = NULL). */
 int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int32_t max_k, int64_t max_vocab);
 
