@@ -147,7 +147,7 @@ typedef struct spec_verify_args {
 /* Create a context on HIP device `device` for batches of at most max_batch
  * sequences, K_s <= max_k (1..128) and vocab <= max_vocab.  Allocates the
  * context's device scratch (per-chunk partial row statistics and, for the
- * top-k filter, 16 segment maxima per chunk; per-sequence final-draw records
+ * filters, 16 segment maxima per chunk; per-sequence final-draw records
  * and tile sums; defaults for NULL optional inputs): about 80 bytes per 8192
  * vocabulary entries per row slot, max_batch * (2 * max_k + 1) slots, plus
  * small per-sequence arrays.  The caller owns every input and output

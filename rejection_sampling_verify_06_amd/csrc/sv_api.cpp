@@ -292,7 +292,7 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
   p.tau = ctx->tau;
   p.order = ctx->order;
   p.order_block = (a->top_k || a->top_p) ? 1 : 0;
-  p.segmax = a->top_k ? ctx->segmax : nullptr;   // top-k bounds from row_stats' segment maxima
+  p.segmax = (a->top_k || a->top_p) ? ctx->segmax : nullptr;   // filter bounds from row_stats' segment maxima
   p.top_k = a->top_k;
   p.top_p = a->top_p;
   p.ptok = ctx->ptok;

@@ -796,9 +796,10 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
       }
   };
   if (segp) {
-    // more than kFThreads segments: every thread folds the segments t,
-    // t + 1024, ... and t + 512, t + 1536, ... (maxima of disjoint parts)
-    if (nseg > kFThreads) {
+    // top-p alone, or more than kFThreads segments: every thread folds the
+    // segments t, t + 1024, ... and t + 512, t + 1536, ... (maxima of
+    // disjoint parts)
+    if (nseg > kFThreads || !use_k) {
       for (int i = t; i < nseg; i += 2 * kFThreads) mxa = fmaxf(mxa, segp[i]);
       for (int i = t + kFThreads; i < nseg; i += 2 * kFThreads) mxb = fmaxf(mxb, segp[i]);
     }
@@ -816,7 +817,7 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
   }
   const uint32_t ka = fkey(mxa), kb = fkey(mxb);   // no elements: the key of -inf, mass 0
   uint32_t bound;
-  if (segp && nseg <= kFThreads) {
+  if (segp && use_k && nseg <= kFThreads) {
     // few segment maxima: the topk-th largest by ranks (ties by position),
     // one per thread, against all of them in LDS
     const uint32_t my = t < nseg ? fkey(segp[t]) : 0u;
@@ -1419,6 +1420,8 @@ __device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Part
   // top-p alone: the 1024 maxima weigh at most 1024 times the largest
   // logit's weight, so a target above that rules the bounded selection out
   const bool hopeless = use_p && !use_k && (double)topp * sh.zrow > 2.0 * kFThreads * kMassOne;
+  // With segment maxima, top-p alone bounds from them (no read for the
+  // bound); when they fall short of the mass, the bracket search decides.
   if (!hopeless &&
       bounded_filter<BF>(sh, rowp, V, ce, c, mc, use_k, topk, use_p, topp, xs, segp, nch * kSegPerChunk, &bkey)) {
     write_partials(sh, pp, nch, M, kval(bkey), tau_out);
@@ -1516,9 +1519,10 @@ __global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(
   float* tau_out = P.tau + (int64_t)s * P.slots + r;
   // the row's segment maxima: written by the row statistics' vector path
   // (rows of this matrix 16-byte aligned, V of a vector or more); used for
-  // top-k of at most half their number, where they bound it closely
+  // top-k of at most half their number, where they bound it closely, and
+  // for top-p alone
   const bool vec_rows = (draft ? P.d_vec : P.t_vec) && P.V >= (bf ? 8 : 4);
-  const float* segp = (P.segmax && use_k && vec_rows && 2 * topk <= nch * kSegPerChunk)
+  const float* segp = (P.segmax && vec_rows && (use_k ? 2 * topk <= nch * kSegPerChunk : use_p))
                           ? P.segmax + (pp - P.partials) * kSegPerChunk : nullptr;
   if (bf)
     filter_row<true>(P, sh, pp, rowp, nch, ce, c, mc, M, use_k, topk, use_p, topp, xs, segp, tau_out);

@@ -976,7 +976,7 @@ __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp,
   own.T = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sh.own.T)));
   own.md = __builtin_amdgcn_readfirstlane(sh.own.md);
   if (own.s < 0) return;                   // the whole block: inconsistent layout
-  if (P.segmax) {                          // calls with top-k: the groups' maxima bound it (filter kernel)
+  if (P.segmax) {                          // filtered calls: the groups' maxima bound the filter
     const int sbs = __builtin_amdgcn_readfirstlane(sh.sb);
     if (sbs >= 0 && (lane & 15) == 0)
       P.segmax[((int64_t)sbs * P.nch_max + chunk) * kSegPerChunk + wv * (kWave / 16) + (lane >> 4)] = rmx;
