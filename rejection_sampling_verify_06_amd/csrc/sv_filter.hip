@@ -768,9 +768,10 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
   // bound.  Top-p alone reads every vector (a sample could miss the
   // heaviest tokens).  Either way the head and tail elements are left to
   // read 2.  With the row's segment maxima (segp: nseg maxima of disjoint
-  // parts of the row, from the row statistics) top-k reads nothing here:
-  // the k-th largest of maxima of k disjoint parts is at most the row's
-  // k-th largest too.
+  // parts of the row, from the row statistics) nothing is read here: the
+  // k-th largest of maxima of k disjoint parts is at most the row's k-th
+  // largest too, and maxima whose masses reach the target bound top-p as
+  // the thread maxima do.
   const int nva = segp ? 0
                   : use_k ? (int)min((int64_t)sp.nvec, max((int64_t)kRound,
                                                             ((int64_t)V * topk / kTargetCand + epv - 1) / epv))
