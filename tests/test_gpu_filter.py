@@ -9,7 +9,7 @@ alone on flat rows that only the bracket search can decide."""
 import numpy as np
 import pytest
 
-from workloads import (MODE_GREEDY, MODE_ONEHOT, MODE_SAMPLE, MODE_STRICT, Batch, bf16_round,
+from workloads import (MODE_GREEDY, MODE_ONEHOT, MODE_SAMPLE, MODE_STRICT, Batch, bf16_round, bf16_widen,
                        make_config_batch, make_random_batch)
 
 from . import gpu_util as gu
@@ -245,3 +245,44 @@ def test_topp_bracket_search_flat_rows(verifier, torch_mod, dtype, grid):
     for k in ("accepted_len", "emitted", "status"):
         assert np.array_equal(out[k], again[k]), k
     assert np.array_equal(out["p_at"], again["p_at"], equal_nan=True)
+
+
+def _segment_elements(dtype: str, V: int, chunk: int, group: int) -> np.ndarray:
+    """Element indices of one row-statistics segment: the elements that the
+    16 lanes of `group` (of 16) load from 32 KB chunk `chunk`, 16-byte
+    vectors handed out to 256 threads in turn."""
+    vec = 8 if dtype == "bf16" else 4
+    ce = 32768 // (2 if dtype == "bf16" else 4)
+    e = np.arange(chunk * ce, min(V, (chunk + 1) * ce))
+    thread = ((e - chunk * ce) // vec) % 256
+    return e[thread // 16 == group]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_topk_heavy_tokens_in_one_segment(verifier, torch_mod, dtype):
+    """Top-k whose largest logits all sit in one segment of the row statistics:
+    the k-th largest segment maximum then lies far below the k-th largest
+    logit, so the bound from the segment maxima admits many tokens: about 130
+    for top-k 50, and on every other row, where 1500 tokens tie just below the
+    heavy ones, more than the candidate buffer holds (the histogram path then
+    decides)."""
+    rng = np.random.default_rng(640 + (dtype == "bf16"))
+    V, B, K = 100_000, 6, 2
+    b = make_random_batch(641, B=B, V=V, kmax=K, k_min=K, dtype=dtype, modes=ALL_MODES, scale=(0.5, 2.0))
+    for arr in (b.target, b.draft):
+        if arr is None:
+            continue
+        for r in range(arr.shape[0]):
+            row = bf16_widen(arr[r, :V]) if dtype == "bf16" else arr[r, :V]
+            top = float(row.max())
+            if r % 2:                            # 1500 tokens tied just below: more candidates than the buffer
+                tied = np.full(1500, top + 0.5, np.float32)
+                arr[r, rng.choice(np.arange(3 * 32768 // 4, V), size=tied.size, replace=False)] = (
+                    bf16_round(tied) if dtype == "bf16" else tied)
+            heavy = (top + np.linspace(2.0, 1.0, 64)).astype(np.float32)   # the row's 64 largest
+            seg = _segment_elements(dtype, V, int(rng.integers(0, 3)), int(rng.integers(0, 16)))
+            cols = rng.choice(seg, size=heavy.size, replace=False)
+            arr[r, cols] = bf16_round(heavy) if dtype == "bf16" else heavy
+    b.top_k = rng.choice(np.array([10, 50, 64], np.int32), size=B)
+    b.top_p = rng.choice(np.array([1.0, 0.9], np.float32), size=B)
+    gu.check_batch(verifier, b, torch_mod, label=f"top-k, heavy tokens in one segment {dtype}")
