@@ -282,38 +282,47 @@ int spec_verify_stats_summary(int32_t max_k, const uint64_t* stats, double* summ
 
 /* ---- draft-length controllers ---------------------------------------------
  * One controller per sequence slot, fed after each round with (K, A) and
- * giving the proposal length of the next round.  The ratio a controller sees
- * is A / max(K, 1) (accepted draft tokens only); a round with A < 0 changes
- * nothing.  Decisions are taken in float64.
+ * giving the proposal length of the next round; a round with A < 0 changes
+ * nothing.  The ratio a controller sees depends on `count`:
+ *   SV_ADAPT_COUNT_EMITTED (0, the pages' count)  min(A + 1, K) / K, and 0
+ *       when K = 0: the tutorial's verifier returns the accepted draft
+ *       tokens plus the token drawn after a rejection, without a bonus token
+ *       (gitcode.csdn.net tutorial, section 4.3 验证器实现), and its decoder
+ *       feeds len(accepted_tokens) / draft_len (section 4.4 完整的解码器);
+ *       "Speculative Decoding在分布式推理中的应用" (wmrh.cn), section 三,
+ *       counts the resampled token the same way.
+ *   SV_ADAPT_COUNT_DRAFT_ONLY (1)  A / max(K, 1): accepted draft tokens only.
+ * Decisions are taken in float64.
  *   SV_ADAPT_WINDOW          keep the last `window` ratios; once at least
  *       `min_samples` are held, their mean (summed oldest first) above
  *       target + 0.1 lengthens by one, below target - 0.1 shortens by one,
- *       within [min_k, max_k] (gitcode.csdn.net tutorial, section 5.2
- *       动态草稿长度策略; the page's defaults are window 100, min_samples 10,
- *       target 0.7, length 5 in 1..10).
+ *       within [min_k, max_k] (tutorial, section 5.2 动态草稿长度策略; the
+ *       page's defaults are window 100, min_samples 10, target 0.7,
+ *       length 5 in 1..10).
  *   SV_ADAPT_MULTIPLICATIVE  above target + 0.1 the length L becomes
  *       min(max_k, int(L (1 + rate))), below target - 0.1
- *       max(min_k, int(L (1 - rate))); int truncates (same tutorial,
- *       section 4.4; defaults target 0.7, rate 0.1, lengths 1..5).
+ *       max(min_k, int(L (1 - rate))); int truncates (tutorial, section
+ *       4.4; defaults target 0.7, rate 0.1, lengths 1..5).
  *   SV_ADAPT_OPTIMAL_K       a = max(ratio, 0.01), k* = floor(ln(1/(1-a))/a)
  *       (unbounded at a = 1), L becomes min(clamp(k*, 2, 16), max(L, 2));
- *       min_k, max_k, window and rate are not used ("Speculative Decoding
- *       在分布式推理中的应用", wmrh.cn, section 三, adapt_draft_length).
+ *       min_k, max_k, window and rate are not used (wmrh.cn, section 三,
+ *       adapt_draft_length).
  *
  * state: device memory owned by the caller, SV_ADAPT_STATE_BYTES(batch,
  * window) bytes, 16-byte aligned: int32 [batch][4] {length, count, head, 0},
  * then float64 [batch][window] ratio rings.  spec_verify_adapt_reset sets
  * every length to init_k and empties the rings (call it first, and again
- * after changing kind or window); spec_verify_adapt reads num_draft and
+ * after changing kind, window or count); spec_verify_adapt reads num_draft and
  * accepted_len (device int32 [batch]), updates the state and writes next_k
  * (device int32 [batch]; also for unchanged lengths).  Sequence b always
  * uses slot b.  Each call enqueues one kernel on `hip_stream`, allocates
  * nothing and does not synchronise; SV_ERR_INVALID (nothing enqueued) for a
- * bad kind, bounds outside 1 <= min_k <= max_k <= SV_ADAPT_MAX_LENGTH,
+ * bad kind or count, bounds outside 1 <= min_k <= max_k <= SV_ADAPT_MAX_LENGTH,
  * window outside 1..SV_ADAPT_MAX_WINDOW or min_samples < 1 (window kind),
  * target or rate outside [0, 1], init_k outside 1..SV_ADAPT_MAX_LENGTH, or a
  * missing or misaligned buffer. */
 enum { SV_ADAPT_WINDOW = 0, SV_ADAPT_MULTIPLICATIVE = 1, SV_ADAPT_OPTIMAL_K = 2 };
+enum { SV_ADAPT_COUNT_EMITTED = 0, SV_ADAPT_COUNT_DRAFT_ONLY = 1 };
 #define SV_ADAPT_MAX_WINDOW 256
 #define SV_ADAPT_MAX_LENGTH 4096
 #define SV_ADAPT_STATE_BYTES(batch, window) ((int64_t)(batch) * (16 + 8 * (int64_t)(window)))
@@ -324,6 +333,7 @@ typedef struct spec_verify_adapt_args {
   int32_t max_k;
   int32_t window;
   int32_t min_samples;
+  int32_t count;               /* SV_ADAPT_COUNT_EMITTED or SV_ADAPT_COUNT_DRAFT_ONLY */
   double target;
   double rate;
   const int32_t* num_draft;

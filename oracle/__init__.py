@@ -25,6 +25,7 @@ from .verify import (  # noqa: F401
 from .compare import CompareReport, compare  # noqa: F401
 from .ngram import ngram_propose, ngram_propose_batch, valid_starts  # noqa: F401
 from .stats import (  # noqa: F401
-    WINDOW, MULTIPLICATIVE, OPTIMAL_K, Controller, acceptance_counters, acceptance_summary, adapt_step, adapt_batch,
+    WINDOW, MULTIPLICATIVE, OPTIMAL_K, COUNT_EMITTED, COUNT_DRAFT_ONLY, Controller, acceptance_counters,
+    acceptance_summary, adapt_step, adapt_batch, controller_ratio,
 )
 from .filter import filter_threshold, filtered_softmax, kept_by_definition, topk_threshold  # noqa: F401

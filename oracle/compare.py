@@ -10,10 +10,14 @@ Test infrastructure.  The rule:
 * accepted_len and emitted tokens identical, except where the oracle flags a
   near-tie: a uniform within 1e-5 of an acceptance ratio (then the other
   branch of that decision is followed in the oracle and compared again), or
-  a uniform within 1e-5 of a boundary of the inverse-CDF interval (then the
-  emitted token must lie in the oracle's candidate set), or a top-p crossing
-  within 1e-5 of a tie group's mass (then the sequence may match the
-  oracle run with the neighbouring filter threshold instead).
+  a uniform within 1e-5 of a boundary of the emitted token's interval of the
+  normalised CDF (then the emitted token must lie in the oracle's candidate
+  set), or a top-p crossing within 1e-5 of a tie group's mass (then the
+  sequence may match the oracle run with the neighbouring filter threshold
+  instead).  Such matches are counted in ``n_exempt``.
+* inputs float32 cannot resolve (q(x) < 1e-30 at a SAMPLE position, a
+  residual with less than 1e-6 of mass) are followed the same way but counted
+  in ``n_degenerate``, so that a caller can require none.
 """
 from __future__ import annotations
 
@@ -30,7 +34,7 @@ class CompareReport:
     n_seq: int = 0
     n_exact: int = 0
     n_exempt: int = 0             # matched only thanks to a 1e-5 near-tie flag
-    n_cond_exempt: int = 0        # matched only thanks to the float32-conditioning band
+    n_degenerate: int = 0         # matched only thanks to a degenerate-input flag (q underflow, empty residual)
     n_mismatch: int = 0
     n_oracle_flagged: int = 0     # sequences the oracle flagged at all
     max_pq_err: float = 0.0
@@ -42,7 +46,7 @@ class CompareReport:
 
     def summary(self) -> str:
         return (f"seqs={self.n_seq} exact={self.n_exact} exempt={self.n_exempt} "
-                f"cond_exempt={self.n_cond_exempt} mismatch={self.n_mismatch} "
+                f"degenerate={self.n_degenerate} mismatch={self.n_mismatch} "
                 f"oracle_flagged={self.n_oracle_flagged} max|dp,dq|={self.max_pq_err:.3g}")
 
 
@@ -53,7 +57,7 @@ def _fail(rep: CompareReport, msg: str):
 
 
 def compare(res: BatchResult, accepted_len, emitted, p_at=None, q_at=None, status=None,
-            pq_tol: float = 1e-5, strict_band: bool = False) -> CompareReport:
+            pq_tol: float = 1e-5) -> CompareReport:
     accepted_len = np.asarray(accepted_len)
     emitted = np.asarray(emitted)
     B = accepted_len.shape[0]
@@ -80,32 +84,31 @@ def compare(res: BatchResult, accepted_len, emitted, p_at=None, q_at=None, statu
             rep.n_oracle_flagged += 1
         g_p = None if p_at is None else np.asarray(p_at, np.float64)[od:od + K]
         g_q = None if q_at is None else np.asarray(q_at, np.float64)[od:od + K]
-        verdict, msg, pq_err = _compare_seq(res, s, r, K, gA, g_emit, gst, g_p, g_q, pq_tol, strict_band)
+        verdict, msg, pq_err = _compare_seq(res, s, r, K, gA, g_emit, gst, g_p, g_q, pq_tol)
         if verdict is None and r.filter_alts:
             # a top-p near-tie: the filter threshold on one side of it is as valid as on the other
             for key, alt in r.filter_alts:
                 r2 = res.rerun(s, {}, {key: alt})
-                v2, _, e2 = _compare_seq(res, s, r2, K, gA, g_emit, gst, g_p, g_q, pq_tol, strict_band)
+                v2, _, e2 = _compare_seq(res, s, r2, K, gA, g_emit, gst, g_p, g_q, pq_tol)
                 if v2 is not None:
-                    verdict, pq_err = ("cond" if v2 == "cond" else "exempt"), e2
+                    verdict, pq_err = ("degenerate" if v2 == "degenerate" else "exempt"), e2
                     break
         rep.max_pq_err = max(rep.max_pq_err, pq_err)
         if verdict is None:
             _fail(rep, msg)
         elif verdict == "exact":
             rep.n_exact += 1
-        elif verdict == "cond":
-            rep.n_cond_exempt += 1
+        elif verdict == "degenerate":
+            rep.n_degenerate += 1
         else:
             rep.n_exempt += 1
     return rep
 
 
-def _compare_seq(res: BatchResult, s: int, r, K: int, gA: int, g_emit, gst, g_p, g_q, pq_tol: float,
-                 strict_band: bool):
+def _compare_seq(res: BatchResult, s: int, r, K: int, gA: int, g_emit, gst, g_p, g_q, pq_tol: float):
     """One sequence against one oracle result: (verdict, message, max |dp,dq|)
     with verdict "exact", "exempt" (matched through a 1e-5 near-tie),
-    "cond" (through the float32-conditioning band only) or None."""
+    "degenerate" (through a degenerate-input flag) or None."""
     if r.status & ST_ERROR_MASK:
         bad = (gA != -1) or (g_emit != -1).any() or (gst is not None and gst != r.status)
         for arr in (g_p, g_q):
@@ -123,16 +126,19 @@ def _compare_seq(res: BatchResult, s: int, r, K: int, gA: int, g_emit, gst, g_p,
             pq_err = max(pq_err, float(d.max()))
     if pq_err > pq_tol:
         return None, f"seq {s}: p/q at proposal differ by {pq_err:.3g} > {pq_tol}", pq_err
-    # follow near-tie branches of the acceptance scan
+    # follow flagged branches of the acceptance scan
     cur = r
-    exempt = False
+    exempt = degenerate = False
     for _ in range(K + 1):
         if gA == cur.A:
             break
         i = min(gA, cur.A)
-        if 0 <= i < K and i in cur.accept_flags:
+        if 0 <= i < K and (i in cur.accept_flags or i in cur.underflow_flags):
+            if i in cur.accept_flags:
+                exempt = True
+            else:
+                degenerate = True
             cur = res.rerun(s, {**cur.forced, i: gA > i}, cur.forced_tau)
-            exempt = True
             continue
         return None, (f"seq {s}: accepted_len gpu={gA} oracle={cur.A} (no near-tie at {i}; "
                       f"u={cur.u_acc[i] if i < len(cur.u_acc) else None} "
@@ -144,20 +150,20 @@ def _compare_seq(res: BatchResult, s: int, r, K: int, gA: int, g_emit, gst, g_p,
         return None, f"seq {s}: emitted prefix/suffix differ: gpu={g_emit.tolist()} oracle={cur.emitted.tolist()}", pq_err
     gy = int(g_emit[A])
     f = cur.final
-    cond_only = False
     if gy != f.y:
-        allowed = f.candidates is not None and gy in f.candidates
-        if allowed and strict_band and not (f.cdf_flag or f.z_flag):
-            allowed = False
-        if not allowed:
+        if f.candidates is not None and gy in f.candidates:
+            exempt = True
+        elif f.z_candidates is not None and gy in f.z_candidates:
+            degenerate = True
+        else:
             return None, (f"seq {s}: final token gpu={gy} oracle={f.y} ({f.kind}, u={f.u:.9f}, Z={f.Z:.6g}, "
-                          f"flags cdf={f.cdf_flag} cond={f.cdf_cond_flag} z={f.z_flag})"), pq_err
-        exempt = True
-        cond_only = f.cdf_cond_flag and not (f.cdf_flag or f.z_flag)
+                          f"flags cdf={f.cdf_flag} z={f.z_flag})"), pq_err
     if gst is not None:
         mask = ~ST_ZERO_RESIDUAL if f.z_flag else ~0
         if (gst & mask) != (cur.status & mask):
             return None, f"seq {s}: status gpu={gst} oracle={cur.status}", pq_err
-    if cond_only:
-        return "cond", "", pq_err
+        if f.z_flag and (gst != cur.status):
+            degenerate = True
+    if degenerate:
+        return "degenerate", "", pq_err
     return ("exempt" if exempt else "exact"), "", pq_err

@@ -31,27 +31,33 @@ Summary (float64; NaN where a denominator is 0):
   [4 + max_k + i]  accepted through i      accepted_i / proposed_i
 
 Controllers, one per sequence, fed after every round with (K, A); a round
-with A < 0 leaves the state alone.  Readings where the pages leave a point
-open: the ratio a controller sees is A / max(K, 1), accepted DRAFT tokens
-only (the section 7 C); the tutorial's decoder counts the corrected token
-too, which makes a round with a rejection look fully accepted.
-  window          (gitcode.csdn.net tutorial, section 5.2 动态草稿长度策略):
-                  keep the last `window` ratios; once at least `min_samples`
-                  are held, compare their mean (summed oldest first) with
-                  target +- 0.1 and move the length by one within
-                  [min_k, max_k].
-  multiplicative  (same tutorial, section 4.4 完整的解码器): above target + 0.1
-                  the length becomes min(max_k, int(L * (1 + rate))), below
-                  target - 0.1 max(min_k, int(L * (1 - rate))); int truncates.
-  optimal_k       (wmrh.cn, "Speculative Decoding在分布式推理中的应用",
-                  section 三, adapt_draft_length): with a = max(ratio, 0.01),
-                  k* = floor(ln(1 / (1 - a)) / a) (infinite at a = 1), and
-                  L becomes min(clamp(k*, 2, 16), max(L, 2)).
-All arithmetic in float64, in the order written above.
+with A < 0 leaves the state alone.  The ratio a controller sees, by default,
+is the tutorial's own: its verifier (gitcode.csdn.net tutorial, section 4.3
+验证器实现) returns the accepted draft tokens plus the token drawn after a
+rejection (no bonus token), and its decoder (section 4.4 完整的解码器) feeds
+len(accepted_tokens) / draft_len, 0 when nothing was proposed; so the count
+is min(A + 1, K).  "Speculative Decoding在分布式推理中的应用" (wmrh.cn),
+section 三, counts the same way (the resampled token still counts as
+produced).  COUNT_DRAFT_ONLY gives A / max(K, 1) instead (the section 7 C).
+  window          (tutorial, section 5.2 动态草稿长度策略): the mean of the
+                  most recent `window` ratios, once at least `min_samples`
+                  are held, moves the length one step up above target + 0.1
+                  and one step down below target - 0.1, within [min_k, max_k].
+  multiplicative  (tutorial, section 4.4): the ratio of the round itself moves
+                  the length to int(L * (1 + rate)) (at most max_k) above
+                  target + 0.1, to int(L * (1 - rate)) (at least min_k) below
+                  target - 0.1; int truncates.
+  optimal_k       (wmrh.cn, section 三, adapt_draft_length): with
+                  a = max(ratio, 0.01), k* = floor(ln(1 / (1 - a)) / a)
+                  (infinite at a = 1), and L becomes min(clamp(k*, 2, 16),
+                  max(L, 2)).
+All arithmetic in float64; a mean is summed oldest first, as a plain sum
+over a list of the window's ratios is.
 """
 from __future__ import annotations
 
 import math
+from collections import deque
 from dataclasses import dataclass, field
 from typing import List
 
@@ -101,45 +107,64 @@ def acceptance_summary(c, max_k: int) -> np.ndarray:
     return out
 
 
+COUNT_EMITTED, COUNT_DRAFT_ONLY = 0, 1
+
+
+def controller_ratio(K: int, A: int, count: int = COUNT_EMITTED) -> float:
+    """The acceptance ratio of one round as a controller sees it."""
+    if count == COUNT_EMITTED:
+        return min(A + 1, K) / K if K > 0 else 0.0
+    if count == COUNT_DRAFT_ONLY:
+        return A / max(K, 1)
+    raise ValueError(f"unknown count {count}")
+
+
 @dataclass
 class Controller:
-    """One sequence's controller state."""
+    """One sequence's controller state: its length and, for the window rule,
+    the most recent ratios (oldest first)."""
     length: int
-    window: List[float] = field(default_factory=list)
+    recent: deque = field(default_factory=deque)
+
+
+def _band(v: float, target: float) -> int:
+    """+1 above the dead band around the target, -1 below it, 0 inside."""
+    return 1 if v > target + BAND else (-1 if v < target - BAND else 0)
+
+
+def _move(L: int, direction: int, up: int, down: int, min_k: int, max_k: int) -> int:
+    """The new length: `up` capped at max_k, `down` floored at min_k, or L."""
+    if direction > 0:
+        return min(max_k, up)
+    if direction < 0:
+        return max(min_k, down)
+    return L
 
 
 def adapt_step(st: Controller, K: int, A: int, kind: int, *, min_k: int, max_k: int, window: int = 100,
-               min_samples: int = 10, target: float = 0.7, rate: float = 0.1) -> int:
+               min_samples: int = 10, target: float = 0.7, rate: float = 0.1, count: int = COUNT_EMITTED) -> int:
     """Feed one round (K proposed, A accepted) and return the next length."""
     if A < 0:
         return st.length
-    ratio = A / max(K, 1)
+    ratio = controller_ratio(K, A, count)
+    L = st.length
     if kind == WINDOW:
-        st.window.append(ratio)
-        if len(st.window) > window:
-            st.window.pop(0)
-        if len(st.window) >= min_samples:
-            acc = 0.0
-            for r in st.window:
-                acc += r
-            avg = acc / len(st.window)
-            if avg > target + BAND:
-                st.length = min(max_k, st.length + 1)
-            elif avg < target - BAND:
-                st.length = max(min_k, st.length - 1)
+        st.recent.append(ratio)
+        while len(st.recent) > window:
+            st.recent.popleft()
+        if len(st.recent) >= min_samples:
+            mean = sum(st.recent) / len(st.recent)
+            L = _move(L, _band(mean, target), L + 1, L - 1, min_k, max_k)
     elif kind == MULTIPLICATIVE:
-        if ratio > target + BAND:
-            st.length = min(max_k, int(st.length * (1 + rate)))
-        elif ratio < target - BAND:
-            st.length = max(min_k, int(st.length * (1 - rate)))
+        L = _move(L, _band(ratio, target), int(L * (1 + rate)), int(L * (1 - rate)), min_k, max_k)
     elif kind == OPTIMAL_K:
         a = max(ratio, 0.01)
         x = math.log(1.0 / (1.0 - a)) / a if a < 1.0 else math.inf
-        k = 16 if x >= 16 else max(2, int(x))
-        st.length = min(k, max(st.length, 2))
+        L = min(16 if x >= 16 else max(2, int(x)), max(L, 2))
     else:
         raise ValueError(f"unknown controller kind {kind}")
-    return st.length
+    st.length = L
+    return L
 
 
 def adapt_batch(states: List[Controller], num_draft, accepted_len, kind: int, **kw) -> np.ndarray:

@@ -44,10 +44,18 @@ notes):
   0); purpose 0 for the acceptance test at positions 0..K-1, purpose 1 for
   the final draw at position A; u = (word0 >> 8) * 2^-24;
 * strict mode: the target's own sample at position i is the inverse-CDF
-  draw from p_i with the acceptance uniform u_i; x_i is accepted iff that
-  draw is x_i; at a mismatch the draw itself is emitted (so the correction
-  uses u_A, purpose 0); all K accepted: the bonus from p_K with purpose 1.
-  No draft logits are used; reported q is 1.
+  draw y_i = inverse_cdf(p_i, u_i) with the acceptance uniform u_i; x_i is
+  accepted iff y_i = x_i; at the first mismatch y_A itself is emitted (so
+  the correction uses u_A, purpose 0); all K accepted: the bonus from p_K
+  with purpose 1.  No draft logits are used; reported q is 1.
+
+Near-ties.  A decision is flagged when its uniform lies within 1e-5 of the
+acceptance ratio, or within 1e-5 of a boundary of the emitted token's
+interval of the normalised CDF; the comparison then also admits the other
+branch or a neighbouring token.  Two further flags mark inputs that float32
+cannot resolve at all and are counted apart: q(x) below 1e-30 (float32
+underflow of the ratio's denominator) and a residual with less than 1e-6 of
+mass (cancellation leaves no correct digit of max(0, p - q)).
 """
 from __future__ import annotations
 
@@ -75,7 +83,6 @@ ST_ERROR_MASK = 127
 
 # tolerance bands
 BAND = 1e-5               # a uniform this close to a ratio or CDF boundary is a near-tie
-CDF_ABS_BAND = 4e-7       # float32 conditioning of a residual CDF (absolute, in units of mass)
 Q_UNDERFLOW = 1e-30       # q(x) below this is in float32's underflow zone
 Z_DEGENERATE = 1e-6       # a residual with less mass than this is numerically empty in float32
 MIN_TEMPERATURE = float(np.float32(1e-6))   # smallest valid SAMPLE/ONEHOT temperature (float32 value)
@@ -138,13 +145,11 @@ def cdf_interval(p: np.ndarray, x: int):
 
 
 def strict_correction(p: np.ndarray, x: int, u: float):
-    """Strict mode, after a mismatch at a position with proposal x: the
-    target's own draw y = inverse_cdf(p, u), written as a draw from p with x
-    removed (weights w) at the point t' = t below x's interval and t - p(x)
-    above it, so that y != x by construction.  Returns (w, u') with
-    u' = t' / sum(w).  When u itself lies in x's interval (only when a
-    near-tie is followed down its other branch) t' is the boundary where
-    x's interval was, so that the tokens on both sides of x are candidates."""
+    """Strict mode, only where a near-tie is followed down its rejecting
+    branch although u lies inside x's own interval: the correction is then
+    drawn from p with x removed (weights w) at the boundary where x's
+    interval was, so that the tokens on both sides of x are candidates.
+    Returns (w, u') with u' = t' / sum(w)."""
     w = p.copy()
     w[x] = 0.0
     lo, hi = cdf_interval(p, x)
@@ -165,10 +170,10 @@ class FinalDraw:
     y: int
     u: float = float("nan")
     Z: float = float("nan")
-    cdf_flag: bool = False          # u within BAND of a boundary of y's interval
-    cdf_cond_flag: bool = False     # only the float32-conditioning band reaches a boundary
-    z_flag: bool = False            # residual numerically empty
-    candidates: Optional[set] = None
+    cdf_flag: bool = False          # u within BAND of a boundary of y's interval (normalised CDF)
+    z_flag: bool = False            # residual numerically empty (degenerate, counted apart)
+    candidates: Optional[set] = None        # tokens within the 1e-5 band (cdf_flag)
+    z_candidates: Optional[set] = None      # every token with mass, when the residual is degenerate
 
 
 @dataclass
@@ -178,7 +183,8 @@ class SeqResult:
     emitted: np.ndarray                      # int32 [K+1]
     p_at: np.ndarray                         # float64 [K]
     q_at: np.ndarray                         # float64 [K]
-    accept_flags: List[int] = field(default_factory=list)   # near-tie positions evaluated
+    accept_flags: List[int] = field(default_factory=list)   # positions whose |u - r| < BAND
+    underflow_flags: List[int] = field(default_factory=list)   # SAMPLE positions with q(x) < Q_UNDERFLOW
     u_acc: List[float] = field(default_factory=list)
     ratios: List[float] = field(default_factory=list)
     final: Optional[FinalDraw] = None
@@ -190,7 +196,7 @@ class SeqResult:
     @property
     def flagged(self) -> bool:
         f = self.final
-        return bool(self.accept_flags) or (f is not None and (f.cdf_flag or f.cdf_cond_flag or f.z_flag))
+        return bool(self.accept_flags or self.underflow_flags) or (f is not None and (f.cdf_flag or f.z_flag))
 
 
 def _error_result(K: int, status: int) -> SeqResult:
@@ -216,23 +222,39 @@ def _final_from_weights(w: np.ndarray, u: float, z_check: bool, fallback_p: Opti
     lo = C[y - 1] if y > 0 else 0.0
     hi = C[y]
     t = u * Z
-    band_rel = BAND * Z
-    band = max(band_rel, CDF_ABS_BAND)
-    cdf_flag = (t - lo < band_rel) or (hi - t < band_rel)
-    cdf_cond = (not cdf_flag) and ((t - lo < band) or (hi - t < band))
+    band = BAND * Z          # 1e-5 of the normalised CDF
+    cdf_flag = (t - lo < band) or (hi - t < band)
     cands = None
-    if cdf_flag or cdf_cond:
+    if cdf_flag:
         Cm = np.concatenate(([0.0], C[:-1]))
         ok = (w > 0) & (Cm <= t + band) & (C >= t - band)
         cands = set(int(k) for k in np.nonzero(ok)[0])
         cands.add(y)
+    zc = None
     if z_flag:
-        extra = set(int(k) for k in np.nonzero(w0 > 0)[0])
+        zc = set(int(k) for k in np.nonzero(w0 > 0)[0])
         if fallback_p is not None:
-            extra |= set(int(k) for k in np.nonzero(fallback_p > 0)[0])
-        cands = (cands or set()) | extra
-    return FinalDraw(kind=kind, y=y, u=u, Z=Z, cdf_flag=bool(cdf_flag), cdf_cond_flag=bool(cdf_cond),
-                     z_flag=z_flag, candidates=cands), status
+            zc |= set(int(k) for k in np.nonzero(fallback_p > 0)[0])
+    return FinalDraw(kind=kind, y=y, u=u, Z=Z, cdf_flag=bool(cdf_flag), z_flag=z_flag, candidates=cands,
+                     z_candidates=zc), status
+
+
+def strict_emit(p: np.ndarray, x: int, u: float):
+    """Strict mode, at the first position A whose proposal x was not the
+    target's own sample: the emitted token is that sample itself,
+    y_A = inverse_cdf(p_A, u_A) ([DIST] §二, §三).  Returns (FinalDraw, status)."""
+    y = int(inverse_cdf(p, u))
+    if y != x:
+        f, st = _final_from_weights(p, u, False, None)
+        if f.candidates is not None:
+            f.candidates.discard(x)          # this branch rejected x
+    else:
+        # only when a near-tie at A is followed down its rejecting branch: u lies in x's own
+        # interval, so the correction sits on the boundary where that interval was
+        w, ur = strict_correction(p, x, u)
+        f, st = _final_from_weights(w, ur, True, p)
+    f.kind = "strict"
+    return f, st
 
 
 def verify_sequence(xt: np.ndarray, xd: Optional[np.ndarray], tokens: np.ndarray, T: float, mode: int,
@@ -312,8 +334,10 @@ def verify_sequence(xt: np.ndarray, xd: Optional[np.ndarray], tokens: np.ndarray
             res.u_acc.append(u)
             res.ratios.append(r)
             acc = u < r
-            if abs(u - r) < BAND or (mode == SAMPLE and q_at[i] < Q_UNDERFLOW):
+            if abs(u - r) < BAND:
                 res.accept_flags.append(i)
+            elif mode == SAMPLE and q_at[i] < Q_UNDERFLOW:
+                res.underflow_flags.append(i)
         if i in force:
             acc = bool(force[i])
         if not acc:
@@ -327,10 +351,7 @@ def verify_sequence(xt: np.ndarray, xd: Optional[np.ndarray], tokens: np.ndarray
         y = int(np.argmax(xt[A]))
         res.final = FinalDraw(kind="greedy", y=y)
     elif mode == STRICT and A < K:
-        u = verify_uniform(seed, seq_id, A, PURPOSE_ACCEPT)
-        w, ur = strict_correction(p[A], tok[A], u)
-        res.final, st = _final_from_weights(w, ur, True, p[A])
-        res.final.kind = "strict"
+        res.final, st = strict_emit(p[A], tok[A], verify_uniform(seed, seq_id, A, PURPOSE_ACCEPT))
         res.status |= st
     else:
         u = verify_uniform(seed, seq_id, A, PURPOSE_SAMPLE)

@@ -23,7 +23,7 @@ from ._lib import (  # noqa: F401
     SV_ST_BAD_LAYOUT, SV_ST_K_TOO_LARGE, SV_ST_BAD_MODE, SV_ST_BAD_TEMPERATURE,
     SV_ST_NO_DRAFT_LOGITS, SV_ST_BAD_TOKEN, SV_ST_NONFINITE, SV_ST_ZERO_RESIDUAL,
     KERNEL_NAMES, LibraryMissing,
-    SV_ADAPT_WINDOW, SV_ADAPT_MULTIPLICATIVE, SV_ADAPT_OPTIMAL_K,
+    SV_ADAPT_WINDOW, SV_ADAPT_MULTIPLICATIVE, SV_ADAPT_OPTIMAL_K, SV_ADAPT_COUNT_EMITTED, SV_ADAPT_COUNT_DRAFT_ONLY,
 )
 
 __all__ = ["Verifier", "VerifyError", "verify", "propose_ngram", "NgramProposer", "AcceptanceStats",
@@ -194,22 +194,45 @@ class Verifier:
         return int(calls.value), dict(zip(KERNEL_NAMES, list(ms)))
 
 
-_CACHE: dict = {}
+_SHARED: dict = {}
+
+
+def _shared_verifier(dev: int, B: int, kmax: int, V: int) -> Verifier:
+    """The one context per device that ``verify`` uses.  It only grows: a
+    call beyond its sizes replaces it by one sized for the larger of the old
+    and the new maxima (the batch rounded up to a power of two), so a serving
+    loop with varying batch sizes holds one context, not one per size."""
+    v = _SHARED.get(dev)
+    if v is not None and B <= v.max_batch and kmax <= v.max_k and V <= v.max_vocab:
+        return v
+    nb = 1
+    while nb < B:
+        nb *= 2
+    if v is not None:
+        nb, kmax, V = max(nb, v.max_batch), max(kmax, v.max_k), max(V, v.max_vocab)
+        import torch
+        torch.cuda.synchronize(dev)      # work queued on the old context finishes before its scratch is freed
+        v.close()
+        del _SHARED[dev]
+    v = _SHARED[dev] = Verifier(min(nb, 4096), kmax, V, dev)
+    return v
 
 
 def verify(target, draft, draft_tokens, num_draft, temperature=None, mode=None, seed: int = 0,
-           want_pq: bool = False, seq_ids=None) -> dict:
-    """One-shot verify step with a cached context sized for the call."""
+           want_pq: bool = False, seq_ids=None, top_k=None, top_p=None, want_status: bool = True) -> dict:
+    """One-shot verify step on torch's current stream: allocates the outputs
+    (``p_at``/``q_at`` only with ``want_pq``, ``status`` only with
+    ``want_status``) and runs the library on a per-device context that is
+    reused across calls.  ``top_k`` / ``top_p`` are optional per-sequence
+    filters (int32 / float32 [B])."""
     import torch
     dev = target.device.index if target.device.index is not None else torch.cuda.current_device()
     B = int(num_draft.numel())
     T = int(draft_tokens.numel())
-    kmax = 128 if B == 0 else max(1, min(128, T))
-    key = (dev, B, kmax, int(target.shape[1]))
-    v = _CACHE.get(key)
-    if v is None:
-        v = _CACHE[key] = Verifier(max(B, 1), kmax, int(target.shape[1]), dev)
-    return v.run(target, draft, draft_tokens, num_draft, temperature, mode, seq_ids, seed, want_pq=want_pq)
+    kmax = max(1, min(128, T))          # K_s <= total_draft: the context holds any split of it
+    v = _shared_verifier(dev, max(B, 1), kmax, int(target.shape[1]))
+    return v.run(target, draft, draft_tokens, num_draft, temperature, mode, seq_ids, seed, want_pq=want_pq,
+                 want_status=want_status, top_k=top_k, top_p=top_p)
 
 
 class NgramProposer:
@@ -316,11 +339,13 @@ class AcceptanceStats:
 class DraftLengthController:
     """Per-sequence draft-length controllers on the device
     (spec_verify_adapt_reset / spec_verify_adapt).  `update` takes a round's
-    num_draft and accepted_len and returns the next lengths (int32 [batch])."""
+    num_draft and accepted_len and returns the next lengths (int32 [batch]).
+    `count` picks the ratio: SV_ADAPT_COUNT_EMITTED (the pages' count,
+    min(A + 1, K) / K) or SV_ADAPT_COUNT_DRAFT_ONLY (A / max(K, 1))."""
 
     def __init__(self, batch: int, kind: int = SV_ADAPT_WINDOW, *, min_k: int = 1, max_k: int = 10,
                  window: int = 100, min_samples: int = 10, target: float = 0.7, rate: float = 0.1,
-                 init_k: int = 5, device=None):
+                 init_k: int = 5, device=None, count: int = SV_ADAPT_COUNT_EMITTED):
         import torch
         self._lib = _lib.load()
         dev = torch.device("cuda", 0) if device is None else torch.device(device)
@@ -331,6 +356,7 @@ class DraftLengthController:
         a = _lib.SpecVerifyAdaptArgs()
         a.batch, a.kind, a.min_k, a.max_k = self.batch, int(kind), int(min_k), int(max_k)
         a.window, a.min_samples, a.target, a.rate = int(window), int(min_samples), float(target), float(rate)
+        a.count = int(count)
         a.state, a.next_k = _ptr(self.state), _ptr(self.next_k)
         self._args = a
         self.reset(init_k)

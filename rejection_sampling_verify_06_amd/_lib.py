@@ -26,6 +26,7 @@ SV_NGRAM_MAX_TOKENS = 128
 
 SV_STATS_MAX_K = 128
 SV_ADAPT_WINDOW, SV_ADAPT_MULTIPLICATIVE, SV_ADAPT_OPTIMAL_K = 0, 1, 2
+SV_ADAPT_COUNT_EMITTED, SV_ADAPT_COUNT_DRAFT_ONLY = 0, 1
 SV_ADAPT_MAX_WINDOW = 256
 SV_ADAPT_MAX_LENGTH = 4096
 
@@ -100,6 +101,7 @@ class SpecVerifyAdaptArgs(ctypes.Structure):
         ("max_k", ctypes.c_int32),
         ("window", ctypes.c_int32),
         ("min_samples", ctypes.c_int32),
+        ("count", ctypes.c_int32),
         ("target", ctypes.c_double),
         ("rate", ctypes.c_double),
         ("num_draft", ctypes.c_void_p),

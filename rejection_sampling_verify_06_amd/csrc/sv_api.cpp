@@ -428,8 +428,9 @@ static int adapt_params(const spec_verify_adapt_args* a, const char* who, sv::Ad
     set_err("%s: args is NULL", who);
     return SV_ERR_INVALID;
   }
-  if (a->batch < 0 || a->kind < SV_ADAPT_WINDOW || a->kind > SV_ADAPT_OPTIMAL_K) {
-    set_err("%s: batch %d < 0 or unknown kind %d", who, a->batch, a->kind);
+  if (a->batch < 0 || a->kind < SV_ADAPT_WINDOW || a->kind > SV_ADAPT_OPTIMAL_K ||
+      (a->count != SV_ADAPT_COUNT_EMITTED && a->count != SV_ADAPT_COUNT_DRAFT_ONLY)) {
+    set_err("%s: batch %d < 0, unknown kind %d or unknown count %d", who, a->batch, a->kind, a->count);
     return SV_ERR_INVALID;
   }
   if (a->kind != SV_ADAPT_OPTIMAL_K && (a->min_k < 1 || a->max_k < a->min_k || a->max_k > SV_ADAPT_MAX_LENGTH)) {
@@ -457,6 +458,7 @@ static int adapt_params(const spec_verify_adapt_args* a, const char* who, sv::Ad
   p->max_k = a->max_k;
   p->window = a->kind == SV_ADAPT_WINDOW ? a->window : 1;
   p->min_samples = a->min_samples;
+  p->count = a->count;
   p->target = a->target;
   p->rate = a->rate;
   p->num_draft = a->num_draft;

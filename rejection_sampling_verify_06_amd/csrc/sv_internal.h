@@ -169,6 +169,7 @@ struct AdaptParams {
   int kind;                    // 0 window, 1 multiplicative, 2 optimal-k
   int min_k, max_k;
   int window, min_samples;
+  int count;                   // 0: min(A + 1, K) / K (0 for K = 0); 1: A / max(K, 1)
   double target, rate;
   const int32_t* num_draft;
   const int32_t* accepted_len;

@@ -51,6 +51,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kNV = 8;   // 16-byte vectors per thread per 32 KB chunk
 constexpr int kSample = 0, kGreedy = 1, kOnehot = 2, kStrict = 3;
+constexpr int64_t kMaxGridX = 65535;   // blocks per grid dimension of the row-statistics launch
 constexpr int kStBadLayout = 1, kStKTooLarge = 2, kStBadMode = 4, kStBadTemp = 8, kStNoDraft = 16,
               kStBadToken = 32, kStNonfinite = 64, kStZeroResidual = 128;
 constexpr float kMinTemperature = 1e-6f;
@@ -1142,9 +1143,15 @@ __device__ __forceinline__ void filter_order(const Params& P) {
 // kernels
 // ---------------------------------------------------------------------------
 
+// One block per (row, 32 KB chunk), numbered row-major; a grid of more than
+// 65535 blocks is laid out in several rows of the y dimension (dispatch order
+// is still the block number), and the few blocks past the end return at once.
 template <bool TB, bool DB>
 __global__ void __launch_bounds__(kThreads) k_row_stats(Params P) {
-  int b = blockIdx.x;
+  const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t nblocks = (int64_t)P.n_t * P.nch_t + (int64_t)P.n_d * P.nch_d + P.order_block;
+  if (lin >= nblocks) return;
+  int b = (int)lin;
   if (P.order_block) {            // a filtered call: block 0 orders the filter's rows
     if (b == 0) {
       filter_order(P);
@@ -1525,7 +1532,10 @@ __global__ void __launch_bounds__(kFinThreads) k_select(Params P) {
 hipError_t launch_row_stats(const Params& p, hipStream_t st, const LaunchEvents* ev) {
   const int64_t blocks = (int64_t)p.n_t * p.nch_t + (int64_t)p.n_d * p.nch_d + p.order_block;
   if (blocks <= 0) return record_empty(st, ev);
-  const dim3 g((unsigned)blocks), b(kThreads);
+  // at most 65535 blocks per grid dimension; gy rows of gx blocks leave fewer than gy unused
+  const int64_t gy = (blocks + kMaxGridX - 1) / kMaxGridX;
+  const int64_t gx = (blocks + gy - 1) / gy;
+  const dim3 g((unsigned)gx, (unsigned)gy), b(kThreads);
   if (p.t_bf16) {
     if (p.d_bf16) launch_timed(k_row_stats<true, true>, g, b, st, ev, p);
     else launch_timed(k_row_stats<true, false>, g, b, st, ev, p);

@@ -14,8 +14,11 @@
 //   multiplicative  the rule of that tutorial's decoder, section 4.4;
 //   optimal-k       the rule of "Speculative Decoding在分布式推理中的应用"
 //                   (wmrh.cn), section 三.
-// The ratio each one sees is A / max(K, 1); rounds with A < 0 were not
-// verified and change nothing.  Decisions are taken in float64 in the rules'
+// The ratio each one sees is, by default, the tutorial's count of the tokens
+// its verifier returns (accepted draft tokens plus the token drawn after a
+// rejection, no bonus) over the proposed length, min(A + 1, K) / K (0 when
+// K = 0; tutorial sections 4.3 and 4.4); or, on request, A / max(K, 1).
+// Rounds with A < 0 were not verified and change nothing.  Decisions are taken in float64 in the rules'
 // own order (the window mean sums its entries oldest first), so the lengths
 // are exact.
 //
@@ -169,7 +172,8 @@ __global__ void __launch_bounds__(kAdWaves * kWave) k_adapt(AdaptParams P) {
   }
   int L = h.x;
   if (A >= 0) {
-    const double ratio = (double)A / (double)max(K, 1);
+    const double ratio = P.count == 0 ? (K > 0 ? (double)min(A + 1, K) / (double)K : 0.0)
+                                      : (double)A / (double)max(K, 1);
     if (P.kind == 0) {
       int count = h.y, head = h.z, slot;
       if (count < W) {                               // append

@@ -72,16 +72,36 @@ def oracle_for(batch, max_k, draft=None, dtype=None, total_draft=None):
                                total_draft=total_draft, top_k=batch.top_k, top_p=batch.top_p)
 
 
-def compare(ref, out, strict_band=False):
+def compare(ref, out):
     return oracle.compare(ref, out["accepted_len"], out["emitted"], out.get("p_at"), out.get("q_at"),
-                          out.get("status"), strict_band=strict_band)
+                          out.get("status"))
 
 
-def check_batch(verifier, batch, torch, label="", **kw):
+def assert_parity(rep, allow_degenerate=False):
+    """The parity bar: every sequence identical to the oracle, or matched
+    through a flagged 1e-5 near-tie; matches through a degenerate-input flag
+    (q(x) < 1e-30, residual mass < 1e-6) only where a test asks for them."""
+    assert rep.ok, "\n".join(rep.messages)
+    if not allow_degenerate:
+        assert rep.n_degenerate == 0, f"{rep.n_degenerate} sequences matched only through a degenerate-input flag"
+
+
+def add_reports(tot, rep):
+    """Accumulate compare reports (tot None: start from rep)."""
+    if tot is None:
+        return rep
+    for f in ("n_seq", "n_exact", "n_exempt", "n_degenerate", "n_mismatch", "n_oracle_flagged"):
+        setattr(tot, f, getattr(tot, f) + getattr(rep, f))
+    tot.max_pq_err = max(tot.max_pq_err, rep.max_pq_err)
+    tot.messages.extend(rep.messages[:max(0, 20 - len(tot.messages))])
+    return tot
+
+
+def check_batch(verifier, batch, torch, label="", allow_degenerate=False, **kw):
     log(f"[gpu] {label} {batch.name}")
     out = run_gpu(verifier, batch, torch, **kw)
     ref = oracle_for(batch, verifier.max_k)
     rep = compare(ref, out)
     log(f"      {rep.summary()}")
-    assert rep.ok, "\n".join(rep.messages)
+    assert_parity(rep, allow_degenerate)
     return rep, out, ref

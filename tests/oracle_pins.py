@@ -343,7 +343,9 @@ def _page_sample(p, u):
 def check_grid_strict(seed=5, V=6):
     """Over all 2^24 uniforms: the proposal x is accepted exactly on x's
     interval (probability p(x) to the grid), and for a sample of rejected
-    uniforms the emitted correction is the target's own sample."""
+    uniforms the emitted correction is the target's own sample; so is the
+    draw from p without x at the shifted point t (t - p(x) above x's
+    interval), the form the forced-branch helper uses."""
     rng = np.random.default_rng(seed)
     p = special.softmax(rng.standard_normal(V) * 1.4)
     ys = _page_sample(p, GRID)
@@ -353,9 +355,11 @@ def check_grid_strict(seed=5, V=6):
         rej = np.nonzero(~acc)[0]
         for j in rng.choice(rej, size=min(3000, len(rej)), replace=False):
             u = float(GRID[j])
+            f, st = ov.strict_emit(p, x, u)
+            assert f.y == ys[j] and f.y != x and st == 0, (x, u, f.y, ys[j])
             w, ur = ov.strict_correction(p, x, u)
             y = int(ov.inverse_cdf(w, ur))
-            assert y == ys[j] and y != x, (x, u, y, ys[j])
+            assert y == ys[j], (x, u, y, ys[j])
 
 
 def check_strict_acceptance_rate(n=40000, V=8, seed=6):

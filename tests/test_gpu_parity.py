@@ -88,7 +88,7 @@ def test_unaligned_base_pointer(verifier, torch_mod):
     out = gu.run_gpu(verifier, b, torch_mod, d=d)
     rep = gu.compare(gu.oracle_for(b, MAX_K), out)
     gu.log(f"[gpu] unaligned base: {rep.summary()}")
-    assert rep.ok, rep.messages
+    gu.assert_parity(rep)
 
 
 @pytest.mark.parametrize("tdtype,ddtype", [("bf16", "f32"), ("f32", "bf16")])
@@ -107,7 +107,7 @@ def test_mixed_target_draft_dtypes(verifier, torch_mod, tdtype, ddtype):
                                  seq_ids=b.seq_ids, seed=b.seed, max_k=MAX_K)
     rep = gu.compare(ref, out)
     gu.log(f"[gpu] mixed dtypes {tdtype}/{ddtype}: {rep.summary()}")
-    assert rep.ok, rep.messages
+    gu.assert_parity(rep)
 
 
 # ---------------------------------------------------------------------------
@@ -170,7 +170,7 @@ def test_bad_layout(verifier, torch_mod, nd):
     ref = gu.oracle_for(b, MAX_K, total_draft=4)
     assert not ref.layout_ok
     rep = gu.compare(ref, out)
-    assert rep.ok, rep.messages
+    gu.assert_parity(rep)
 
 
 # ---------------------------------------------------------------------------
@@ -256,38 +256,16 @@ def test_workload_parity(verifier, torch_mod, cfg, steps):
         b = make_config_batch(cfg, step)
         rep, _, _ = gu.check_batch(verifier, b, torch_mod, label=f"C{cfg} step {step}") if steps <= 20 or step % 50 == 0 \
             else _quiet(verifier, b, torch_mod)
-        if tot is None:
-            tot = rep
-        else:
-            for f in ("n_seq", "n_exact", "n_exempt", "n_cond_exempt", "n_mismatch", "n_oracle_flagged"):
-                setattr(tot, f, getattr(tot, f) + getattr(rep, f))
-            tot.max_pq_err = max(tot.max_pq_err, rep.max_pq_err)
+        tot = gu.add_reports(tot, rep)
     gu.log(f"[gpu] C{cfg} x{steps}: {tot.summary()}")
+    gu.assert_parity(tot)
 
 
 def _quiet(verifier, b, torch_mod):
     out = gu.run_gpu(verifier, b, torch_mod)
     rep = gu.compare(gu.oracle_for(b, verifier.max_k), out)
-    assert rep.ok, rep.messages
+    gu.assert_parity(rep)
     return rep, out, None
-
-
-@pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_workload_bench_context(torch_mod, cfg):
-    """The full-size workloads through a context sized the way bench.py sizes
-    it (max_k = 8 here): the scan's one-round path, with two lanes per slot
-    where a row has 9..16 chunks, and the launch shapes bench.py times."""
-    import rejection_sampling_verify_06_amd as sv
-    from workloads import config_description
-    desc = config_description(cfg)
-    batches = [make_config_batch(cfg, step) for step in (0, 1)]
-    maxk = max(8, int(max(b.num_draft.max() for b in batches)))
-    v = sv.Verifier(max_batch=desc["batch"], max_k=maxk, max_vocab=desc["vocab"], device=0)
-    try:
-        for step, b in enumerate(batches):
-            gu.check_batch(v, b, torch_mod, label=f"C{cfg} step {step}, bench context")
-    finally:
-        v.close()
 
 
 def test_small_max_k_mixed(torch_mod):

@@ -99,6 +99,9 @@ CTRL_CASES = [
     ("multiplicative", 1, dict(min_k=1, max_k=5, target=0.7, rate=0.1), 5),
     ("multiplicative wide", 1, dict(min_k=1, max_k=40, target=0.5, rate=0.35), 12),
     ("optimal-k", 2, dict(min_k=1, max_k=16, target=0.7), 16),
+    ("window draft-only", 0, dict(min_k=1, max_k=10, window=100, min_samples=10, target=0.7, count=1), 5),
+    ("multiplicative draft-only", 1, dict(min_k=1, max_k=40, target=0.5, rate=0.35, count=1), 12),
+    ("optimal-k draft-only", 2, dict(min_k=1, max_k=16, target=0.7, count=1), 16),
 ]
 
 
@@ -183,6 +186,8 @@ def test_bad_arguments_enqueue_nothing(torch_mod):
         sv.DraftLengthController(4, 5, device="cuda")
     with pytest.raises(sv.VerifyError):
         sv.DraftLengthController(4, 0, target=1.5, device="cuda")
+    with pytest.raises(sv.VerifyError):
+        sv.DraftLengthController(4, 0, count=2, device="cuda")
 
 
 def test_random_controller_parameters(torch_mod):
@@ -194,7 +199,8 @@ def test_random_controller_parameters(torch_mod):
         rng = np.random.default_rng(600_000 + case)
         kind = int(rng.integers(0, 3))
         max_k = int(rng.integers(1, 65))
-        kw = dict(min_k=int(rng.integers(1, max_k + 1)), max_k=max_k, target=float(rng.uniform(0.05, 0.95)))
+        kw = dict(min_k=int(rng.integers(1, max_k + 1)), max_k=max_k, target=float(rng.uniform(0.05, 0.95)),
+                  count=int(case % 3 == 2))
         if kind == 0:
             kw.update(window=int(rng.integers(1, 257)), min_samples=int(rng.integers(1, 40)))
         if kind == 1:

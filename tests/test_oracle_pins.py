@@ -198,8 +198,8 @@ def test_plant_strict_without_remap(monkeypatch):
 
 def test_plant_strict_other_uniform(monkeypatch):
     """The correction drawn with another uniform than the position's own."""
-    real = ov.strict_correction
-    monkeypatch.setattr(ov, "strict_correction", lambda p, x, u: real(p, x, (u + 0.37) % 1.0))
+    real = ov.strict_emit
+    monkeypatch.setattr(ov, "strict_emit", lambda p, x, u: real(p, x, (u + 0.37) % 1.0))
     with pytest.raises(AssertionError):
         pins.check_strict_wiring()
 

@@ -125,20 +125,39 @@ def test_accumulation_over_calls():
 
 
 # ---- controllers -------------------------------------------------------------
+#
+# The ratio a controller sees, by default, is the tutorial's (section 4.3
+# verifier, section 4.4 decoder): len(accepted_tokens) / draft_len, where the
+# verifier returns the accepted draft tokens and, after a rejection, the token
+# drawn in its place (no bonus).  Traced by hand: K = 4 with A = 1 gives
+# accepted_tokens = [x0, y1], ratio 2/4; A = 4 gives [x0..x3], ratio 1; K = 0
+# gives an empty list, ratio 0 (the decoder's `else 0`).
+
+EMIT, DRAFT = os_.COUNT_EMITTED, os_.COUNT_DRAFT_ONLY
+
 
 def _run(kind, rounds, length, **kw):
     st = os_.Controller(length)
     return [os_.adapt_step(st, K, A, kind, **kw) for K, A in rounds]
 
 
-def _check_window(step_fn):
-    kw = dict(min_k=1, max_k=7, window=12, min_samples=10, target=0.7)
+def test_controller_ratio_traced():
+    assert [os_.controller_ratio(4, a) for a in range(5)] == [1 / 4, 2 / 4, 3 / 4, 4 / 4, 4 / 4]
+    assert os_.controller_ratio(0, 0) == 0.0 and os_.controller_ratio(1, 0) == 1.0
+    assert [os_.controller_ratio(4, a, DRAFT) for a in range(5)] == [0.0, 0.25, 0.5, 0.75, 1.0]
+    assert os_.controller_ratio(0, 0, DRAFT) == 0.0
+
+
+def _check_window(step_fn, count=EMIT):
+    kw = dict(min_k=1, max_k=7, window=12, min_samples=10, target=0.7, count=count)
     st = os_.Controller(5)
     full = [step_fn(st, 4, 4, os_.WINDOW, **kw) for _ in range(14)]
     # nine rounds: too few samples; from the tenth on the mean (1.0) is above 0.8
     assert full == [5] * 9 + [6, 7, 7, 7, 7]
-    # now rounds at 0.25: the 12-entry window's mean drops as full rounds leave it
-    low = [step_fn(st, 4, 1, os_.WINDOW, **kw) for _ in range(12)]
+    # now rounds of ratio 1/4: (4, 0) as the tutorial counts (one token returned),
+    # (4, 1) counted by draft tokens; the 12-entry window's mean drops as the full
+    # rounds leave it
+    low = [step_fn(st, 4, 0 if count == EMIT else 1, os_.WINDOW, **kw) for _ in range(12)]
     means = [(12 - j - 1 + 0.25 * (j + 1)) / 12 for j in range(12)]
     want, L = [], 7
     for m in means:
@@ -148,10 +167,12 @@ def _check_window(step_fn):
             L = max(1, L - 1)
         want.append(L)
     assert low == want and want[-1] == 1 and want[0] == 7
-    # a mean inside the band changes nothing; K = 0 counts as ratio 0
+    # a mean inside the band changes nothing: (10, 6) is 7/10 counted the tutorial's way,
+    # (10, 7) is 7/10 counted by draft tokens
     st = os_.Controller(3)
-    mid = [step_fn(st, 10, 7, os_.WINDOW, **kw) for _ in range(15)]
+    mid = [step_fn(st, 10, 6 if count == EMIT else 7, os_.WINDOW, **kw) for _ in range(15)]
     assert mid == [3] * 15
+    # K = 0 counts as ratio 0
     st = os_.Controller(3)
     assert [step_fn(st, 0, 0, os_.WINDOW, **kw) for _ in range(11)][-1] == 1
     # a round that was not verified is no sample
@@ -159,27 +180,36 @@ def _check_window(step_fn):
     assert [step_fn(st, 4, -1, os_.WINDOW, **kw) for _ in range(20)] == [5] * 20
 
 
-def test_window_controller_traced():
-    _check_window(os_.adapt_step)
+@pytest.mark.parametrize("count", [EMIT, DRAFT])
+def test_window_controller_traced(count):
+    _check_window(os_.adapt_step, count)
 
 
-def _check_multiplicative(step_fn):
-    kw = dict(min_k=1, max_k=20, target=0.7, rate=0.1)
+def _check_multiplicative(step_fn, count=EMIT):
+    kw = dict(min_k=1, max_k=20, target=0.7, rate=0.1, count=count)
     st = os_.Controller(10)
     assert step_fn(st, 4, 4, os_.MULTIPLICATIVE, **kw) == 11          # int(11.0)
     assert step_fn(st, 4, 4, os_.MULTIPLICATIVE, **kw) == 12          # int(12.100000000000001)
-    assert step_fn(st, 4, 3, os_.MULTIPLICATIVE, **kw) == 12          # 0.75 is inside 0.6..0.8
-    assert step_fn(st, 4, 2, os_.MULTIPLICATIVE, **kw) == 10          # int(10.8)
+    if count == EMIT:
+        # (4, 3): the rejected round still returns 4 tokens, ratio 1.0 -> int(13.200000000000001)
+        assert step_fn(st, 4, 3, os_.MULTIPLICATIVE, **kw) == 13
+        assert step_fn(st, 4, 2, os_.MULTIPLICATIVE, **kw) == 13      # 3/4 is inside 0.6..0.8
+        assert step_fn(st, 4, 1, os_.MULTIPLICATIVE, **kw) == 11      # 2/4: int(11.700000000000001)
+    else:
+        assert step_fn(st, 4, 3, os_.MULTIPLICATIVE, **kw) == 12      # 0.75 is inside 0.6..0.8
+        assert step_fn(st, 4, 2, os_.MULTIPLICATIVE, **kw) == 10      # int(10.8)
     st = os_.Controller(5)                                             # int(5.5) = 5: stuck, as written
     assert [step_fn(st, 5, 5, os_.MULTIPLICATIVE, **kw) for _ in range(3)] == [5, 5, 5]
-    st = os_.Controller(2)
-    assert [step_fn(st, 2, 0, os_.MULTIPLICATIVE, **kw) for _ in range(2)] == [1, 1]   # floor min_k
+    st = os_.Controller(2)                                             # (3, 0): 1/3 or 0, both below 0.6
+    assert [step_fn(st, 3, 0, os_.MULTIPLICATIVE, **kw) for _ in range(2)] == [1, 1]   # floor min_k
     st = os_.Controller(19)
-    assert step_fn(st, 3, 3, os_.MULTIPLICATIVE, min_k=1, max_k=20, target=0.7, rate=0.5) == 20   # int(28.5) capped
+    assert step_fn(st, 3, 3, os_.MULTIPLICATIVE, min_k=1, max_k=20, target=0.7, rate=0.5,
+                   count=count) == 20                                  # int(28.5) capped
 
 
-def test_multiplicative_controller_traced():
-    _check_multiplicative(os_.adapt_step)
+@pytest.mark.parametrize("count", [EMIT, DRAFT])
+def test_multiplicative_controller_traced(count):
+    _check_multiplicative(os_.adapt_step, count)
 
 
 def _series_x(a, terms=4000):
@@ -187,22 +217,26 @@ def _series_x(a, terms=4000):
     return sum(a ** j / (j + 1) for j in range(terms))
 
 
-def _check_optimal_k(step_fn):
+def _check_optimal_k(step_fn, count=EMIT):
+    kw = dict(min_k=1, max_k=16, count=count)
     st = os_.Controller(8)
-    assert step_fn(st, 4, 4, os_.OPTIMAL_K, min_k=1, max_k=16) == 8      # a = 1: k* infinite -> 16, min with L
+    assert step_fn(st, 4, 4, os_.OPTIMAL_K, **kw) == 8      # a = 1: k* infinite -> 16, min with L
     st = os_.Controller(40)
-    assert step_fn(st, 4, 4, os_.OPTIMAL_K, min_k=1, max_k=16) == 16
+    assert step_fn(st, 4, 4, os_.OPTIMAL_K, **kw) == 16
     st = os_.Controller(1)
-    assert step_fn(st, 4, 4, os_.OPTIMAL_K, min_k=1, max_k=16) == 2      # max(L, 2)
-    for K, A in [(2, 1), (100, 99), (1000, 999), (4, 0), (128, 127), (128, 120)]:
-        a = max(A / K, 0.01)
+    assert step_fn(st, 4, 4, os_.OPTIMAL_K, **kw) == 2      # max(L, 2)
+    # (K, A) with the accepted count as each reading has it: the correction counted, or not
+    for K, A, n_emit in [(2, 0, 1), (100, 98, 99), (1000, 998, 999), (5, 0, 1), (128, 126, 127), (128, 119, 120)]:
+        n = n_emit if count == EMIT else A
+        a = max(n / K, 0.01)
         want = min(16, max(2, math.floor(_series_x(a, 20000))))
         st = os_.Controller(16)
-        assert step_fn(st, K, A, os_.OPTIMAL_K, min_k=1, max_k=16) == want, (K, A)
+        assert step_fn(st, K, A, os_.OPTIMAL_K, **kw) == want, (K, A)
 
 
-def test_optimal_k_controller_against_series():
-    _check_optimal_k(os_.adapt_step)
+@pytest.mark.parametrize("count", [EMIT, DRAFT])
+def test_optimal_k_controller_against_series(count):
+    _check_optimal_k(os_.adapt_step, count)
 
 
 def test_optimal_k_has_no_near_integer_case():
@@ -272,10 +306,10 @@ def _mut_window_ge(st, K, A, kind, **kw):
     """>= instead of > against target + 0.1, and no sample gate."""
     if A < 0:
         return st.length
-    st.window.append(A / max(K, 1))
-    if len(st.window) > kw["window"]:
-        st.window.pop(0)
-    avg = sum(st.window) / len(st.window)
+    st.recent.append(os_.controller_ratio(K, A, kw["count"]))
+    while len(st.recent) > kw["window"]:
+        st.recent.popleft()
+    avg = sum(st.recent) / len(st.recent)
     if avg >= kw["target"] + os_.BAND:
         st.length = min(kw["max_k"], st.length + 1)
     elif avg < kw["target"] - os_.BAND:
@@ -283,15 +317,27 @@ def _mut_window_ge(st, K, A, kind, **kw):
     return st.length
 
 
-def _mut_ratio_with_correction(st, K, A, kind, **kw):
-    """Counting the corrected token as accepted."""
-    return os_.adapt_step(st, K, min(A + 1, K) if A >= 0 else A, kind, **kw)
+def _mut_ratio_without_correction(st, K, A, kind, **kw):
+    """The tutorial's count without the token drawn after a rejection."""
+    return os_.adapt_step(st, K, A, kind, **{**kw, "count": DRAFT})
+
+
+def _mut_ratio_with_bonus(st, K, A, kind, **kw):
+    """The bonus token counted as well: (A + 1) / K after a fully accepted round."""
+    if A < 0:
+        return st.length
+    if A == K and K > 0 and kind == os_.MULTIPLICATIVE:
+        r = (A + 1) / K
+        if r > kw["target"] + os_.BAND:
+            st.length = min(kw["max_k"], int(st.length * (1 + kw["rate"]) * r))
+        return st.length
+    return os_.adapt_step(st, K, A, kind, **kw)
 
 
 def _mut_round_not_trunc(st, K, A, kind, **kw):
     if A < 0:
         return st.length
-    r = A / max(K, 1)
+    r = os_.controller_ratio(K, A, kw["count"])
     if r > kw["target"] + os_.BAND:
         st.length = min(kw["max_k"], round(st.length * (1 + kw["rate"])))
     elif r < kw["target"] - os_.BAND:
@@ -300,13 +346,17 @@ def _mut_round_not_trunc(st, K, A, kind, **kw):
 
 
 def _mut_optimal_no_floor_two(st, K, A, kind, **kw):
-    a = max(A / max(K, 1), 0.01)
+    a = max(os_.controller_ratio(K, A, kw["count"]), 0.01)
     x = math.log(1.0 / (1.0 - a)) / a if a < 1 else math.inf
     st.length = min(16 if x >= 16 else int(x), max(st.length, 2))
     return st.length
 
 
-@pytest.mark.parametrize("mut,check", [(_mut_window_ge, _check_window), (_mut_ratio_with_correction, _check_window),
+@pytest.mark.parametrize("mut,check", [(_mut_window_ge, _check_window),
+                                       (_mut_ratio_without_correction, _check_window),
+                                       (_mut_ratio_without_correction, _check_multiplicative),
+                                       (_mut_ratio_without_correction, _check_optimal_k),
+                                       (_mut_ratio_with_bonus, _check_multiplicative),
                                        (_mut_round_not_trunc, _check_multiplicative),
                                        (_mut_optimal_no_floor_two, _check_optimal_k)])
 def test_pins_catch_controller_mistakes(mut, check):

@@ -132,3 +132,41 @@ def test_comparator_final_token_candidates():
         w = np.array([0.5, 0.5])
         f, _ = ov._final_from_weights(w, 0.5 - 1e-6, False, None)
         assert f.cdf_flag and f.candidates == {0, 1}
+
+
+def test_no_absolute_band_in_the_final_draw():
+    """The only final-draw band is 1e-5 of the normalised CDF: on a residual of
+    mass 1e-3, a uniform 2e-7 of mass (2e-4 of the CDF) from a boundary is
+    no near-tie, so no other token is admitted."""
+    w = np.array([5e-4, 5e-4])
+    f, _ = ov._final_from_weights(w, (5e-4 - 2e-7) / 1e-3, False, None)
+    assert f.y == 0 and not f.cdf_flag and f.candidates is None
+    f, _ = ov._final_from_weights(w, (5e-4 - 4e-9) / 1e-3, False, None)     # 4e-6 of the CDF: flagged
+    assert f.cdf_flag and f.candidates == {0, 1}
+
+
+def test_strict_near_tie_followed_to_rejection():
+    """STRICT, K = 1: u_0 lies 4e-6 inside the proposal's interval, so the
+    oracle accepts and flags the decision; a device that rejected there must
+    emit a neighbour of the proposal (the correction lands on the boundary
+    where its interval was), and is counted as a near-tie match."""
+    for seed in range(50):
+        u0 = verify_uniform(seed, 0, 0, PURPOSE_ACCEPT)
+        if 0.1 < u0 < 0.6:
+            break
+    p0 = np.array([u0 - 4e-6, 0.3, 0.0])
+    p0[2] = 1.0 - p0[0] - p0[1]
+    t = np.log(np.stack([p0, [0.2, 0.3, 0.5]]))
+    res = oracle.verify_batch(target=t.astype(np.float32), draft=None, dtype="f32", vocab=3, num_draft=[1],
+                              draft_tokens=np.array([1], np.int32), temperature=[1.0], mode=[ov.STRICT], seed=seed,
+                              max_k=4)
+    s = res.seqs[0]
+    assert s.A == 1 and s.accept_flags == [0]
+    alt = res.rerun(0, {0: False})
+    assert alt.A == 0 and alt.final.cdf_flag and alt.final.candidates == {0, 2}
+    for y in (0, 2):
+        em = np.array([y, -1], np.int32)
+        rep = oracle.compare(res, [0], em, res.p_at, res.q_at, [0])
+        assert rep.ok and rep.n_exempt == 1, rep.messages
+    rep = oracle.compare(res, [0], np.array([1, -1], np.int32), res.p_at, res.q_at, [0])
+    assert not rep.ok                                   # the proposal itself is never the correction
