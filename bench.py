@@ -18,6 +18,9 @@ last-level cache cannot serve repeated reads.  Prints one JSON line:
               kernel source is committed
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same
               workload, single process
+  configs     the other target workloads (C2 and C4 after the default C3),
+              each measured the same way: its own step time, positions per
+              second, row-statistics roofline and step bytes
 """
 from __future__ import annotations
 
@@ -461,61 +464,23 @@ def load_traffic(workload: str, path: str = COUNTERS_FILE, source: str = KERNEL_
     return None if w is None else w.get("hbm_bytes_per_launch")
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="C3", choices=sorted(WORKLOADS) + ["NG", "ST"],
-                    help="C0..C4: the verify step; C3S: C3 in strict sample-match mode; C3F: C3 with top-k 50 "
-                         "and top-p 0.9; C3P: C3 with top-p 0.95; C3D8: one GPU's share of C3 split by sequence over 8 GPUs; "
-                         "NG: the N-gram proposer; ST: acceptance statistics and the draft-length "
-                         "controller")
-    ap.add_argument("--rotate", type=int, default=None, help="input sets kept resident and cycled")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1),
-                    help="processes for the parallel oracle baseline (0: skip it)")
-    ap.add_argument("--cpu-parallel-child", default=None, help=argparse.SUPPRESS)
-    ap.add_argument("--no-kernel-events", action="store_true", help="time without per-kernel HIP events")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run 5 plain device copies of 1 GiB (the reference kernel for counter scaling)")
-    args = ap.parse_args()
-    if args.cpu_parallel_child is not None:      # child interpreter: CPU only
-        print(json.dumps(cpu_baseline_parallel(args.cpu_parallel_child, args.cpu_budget, args.cpu_workers)))
-        return
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world} requested): the verify "
-              f"step of a sequence-sharded batch needs no communication, so a multi-GPU run would just repeat "
-              f"this line per device.", file=sys.stderr)
-        sys.exit(2)
-
-    if args.workload == "NG":
-        return bench_ngram(args)
-    if args.workload == "ST":
-        return bench_stats(args)
-
-    import torch
-    import rejection_sampling_verify_06_amd as sv
+def measure_verify(workload: str, args, torch, sv) -> dict:
+    """Run one verify-step workload: warm up, time K steps without per-kernel
+    events (five repetitions for the median), then K more steps with each
+    kernel timed by the events its own dispatch records.  Returns the
+    measurement fields of the JSON line and frees the workload's memory."""
     from workloads import config_description
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    sv.library_loaded_path()
-    cfg = WORKLOADS[args.workload]
+    cfg = WORKLOADS[workload]
     # a GPU's share is an eighth of C3's bytes: enough input sets to exceed the 256 MB last-level cache
-    R = args.rotate or (12 if args.workload in SHARD_WORKLOADS else ROTATE[cfg])
+    R = args.rotate or (12 if workload in SHARD_WORKLOADS else ROTATE[cfg])
 
     t_gen = time.perf_counter()
-    batches = [make_workload_batch(args.workload, i) for i in range(R)]
+    batches = [make_workload_batch(workload, i) for i in range(R)]
     dev_in = [to_device(b, torch) for b in batches]
     gen_s = time.perf_counter() - t_gen
     desc = dict(config_description(cfg))
-    if args.workload in SHARD_WORKLOADS:
-        desc["batch"] //= SHARD_WORKLOADS[args.workload]
+    if workload in SHARD_WORKLOADS:
+        desc["batch"] //= SHARD_WORKLOADS[workload]
     maxk = max(8, int(max(b.num_draft.max() for b in batches)))
     v = sv.Verifier(max_batch=desc["batch"], max_k=maxk, max_vocab=desc["vocab"], device=0)
     outs = [v.make_outputs(b.batch, b.total_draft, want_pq=True, want_status=True) for b in batches]
@@ -538,7 +503,7 @@ def main():
         fin_b.append(final_bytes(batches[r], outs[r]["accepted_len"].cpu().numpy()))
         st = outs[r]["status"].cpu().numpy()
         if (st & 127).any():
-            raise RuntimeError(f"input set {r}: unexpected status bits {np.unique(st)}")
+            raise RuntimeError(f"{workload} input set {r}: unexpected status bits {np.unique(st)}")
 
     def timed(k0):
         torch.cuda.synchronize()
@@ -578,22 +543,105 @@ def main():
     roofline = None
     if events and kern.get("row_stats", 0) > 0:
         ach = ev_stats_bytes / (kern["row_stats"] * 1e-3) / 1e9
-        traffic = load_traffic(args.workload)
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                    "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                    "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": load_traffic(workload),
                     "kernel": "k_row_stats", "algorithmic_bytes_per_launch": int(ev_stats_bytes),
                     "mean_launch_ms": round(kern["row_stats"], 5)}
 
     filter_roofline = None
-    if events and args.workload in FILTER_WORKLOADS and kern.get("filter", 0) > 0:
+    if events and workload in FILTER_WORKLOADS and kern.get("filter", 0) > 0:
         # the filter must see each filtered row once: the same bytes as the row statistics
         ach = ev_stats_bytes / (kern["filter"] * 1e-3) / 1e9
         filter_roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                            "frac": round(ach / PEAK_HBM_GBPS, 4),
-                           "traffic": load_traffic(args.workload, FILTER_COUNTERS_FILE, FILTER_SOURCE),
+                           "traffic": load_traffic(workload, FILTER_COUNTERS_FILE, FILTER_SOURCE),
                            "kernel": "k_filter",
                            "algorithmic_bytes_per_launch": int(ev_stats_bytes),
                            "mean_launch_ms": round(kern["filter"], 5)}
+    step_gbps = (stats_bytes + fin_bytes) / (ms_step * 1e-3) / 1e9
+    res = {
+        "workload": batches[0].name, "value": round(float(value), 1), "ms_per_step": round(ms_step, 5),
+        "ms_per_step_median_of_5": round(float(np.median(reps)), 5),
+        "config": {"workload": batches[0].name, "batch": desc["batch"], "k": desc["k"],
+                   "vocab": desc["vocab"], "logits": desc["dtype"], "rotating_input_sets": R,
+                   "positions_per_step": round(float(pos), 2)},
+        "roofline": roofline,
+        "step_bytes": {"row_stats": int(stats_bytes), "final_draw": int(fin_bytes),
+                       "final_draw_formula": int(fin_formula), "early_exit_lower_bound": int(early_bytes),
+                       "step_GBps": round(step_gbps, 1), "step_frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4)},
+        "step_traffic": step_traffic(workload, ms_step),
+        "kernel_ms": {k: round(x, 5) for k, x in kern.items()},
+        "filter_roofline": filter_roofline,
+        "kernel_events_ms_per_step": None if ev_ms_step is None else round(ev_ms_step, 5),
+        "input_generation_s": round(gen_s, 1),
+    }
+    v.close()
+    del packed, outs, dev_in, batches
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="C3", choices=sorted(WORKLOADS) + ["NG", "ST"],
+                    help="C0..C4: the verify step; C3S: C3 in strict sample-match mode; C3F: C3 with top-k 50 "
+                         "and top-p 0.9; C3P: C3 with top-p 0.95; C3D8: one GPU's share of C3 split by sequence over 8 GPUs; "
+                         "NG: the N-gram proposer; ST: acceptance statistics and the draft-length "
+                         "controller")
+    ap.add_argument("--also", default=None,
+                    help="comma-separated verify workloads measured after the main one and reported under "
+                         "'configs' (default: C2,C4 with the default C3 workload, none otherwise; '' for none)")
+    ap.add_argument("--rotate", type=int, default=None, help="input sets kept resident and cycled")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=min(16, os.cpu_count() or 1),
+                    help="processes for the parallel oracle baseline (0: skip it)")
+    ap.add_argument("--cpu-parallel-child", default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--no-kernel-events", action="store_true", help="time without per-kernel HIP events")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run 5 plain device copies of 1 GiB (the reference kernel for counter scaling)")
+    args = ap.parse_args()
+    if args.cpu_parallel_child is not None:      # child interpreter: CPU only
+        print(json.dumps(cpu_baseline_parallel(args.cpu_parallel_child, args.cpu_budget, args.cpu_workers)))
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world} requested): the verify "
+              f"step of a sequence-sharded batch needs no communication, so a multi-GPU run would just repeat "
+              f"this line per device.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.workload == "NG":
+        return bench_ngram(args)
+    if args.workload == "ST":
+        return bench_stats(args)
+
+    import torch
+    import rejection_sampling_verify_06_amd as sv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    sv.library_loaded_path()
+    also = (["C2", "C4"] if args.workload == "C3" else []) if args.also is None else \
+        [w for w in args.also.split(",") if w]
+    for w in also:
+        if w not in WORKLOADS:
+            raise SystemExit(f"--also: unknown workload {w}")
+
+    main_res = measure_verify(args.workload, args, torch, sv)
+    sub = {}
+    for w in also:
+        r = measure_verify(w, args, torch, sv)
+        sub[w] = {k: r[k] for k in ("workload", "value", "ms_per_step", "ms_per_step_median_of_5", "roofline",
+                                    "step_bytes", "kernel_ms")}
+        sub[w]["unit"] = "positions/s"
+        sub[w]["positions_per_step"] = r["config"]["positions_per_step"]
 
     if args.copy_calibration:
         copy_calibration(torch)
@@ -602,29 +650,24 @@ def main():
     cpu_par = None if (args.no_cpu_baseline or args.cpu_workers < 1) else \
         run_parallel_baseline_child(args.workload, args.cpu_budget, args.cpu_workers)
     line = {
-        "metric": METRIC, "value": round(float(value), 1), "unit": "positions/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "metric": METRIC, "value": main_res["value"], "unit": "positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": batches[0].name, "batch": desc["batch"], "k": desc["k"],
-                   "vocab": desc["vocab"], "logits": desc["dtype"], "rotating_input_sets": R,
-                   "positions_per_step": round(float(pos), 2)},
-        "roofline": roofline,
+        "config": main_res["config"],
+        "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
-        "ms_per_step_median_of_5": round(float(np.median(reps)), 5),
-        "step_bytes": {"row_stats": int(stats_bytes), "final_draw": int(fin_bytes),
-                       "final_draw_formula": int(fin_formula), "early_exit_lower_bound": int(early_bytes),
-                       "step_GBps": round((stats_bytes + fin_bytes) / (ms_step * 1e-3) / 1e9, 1),
-                       "step_frac_of_peak": round((stats_bytes + fin_bytes) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
-        "step_traffic": step_traffic(args.workload, ms_step),
+        "ms_per_step_median_of_5": main_res["ms_per_step_median_of_5"],
+        "step_bytes": main_res["step_bytes"],
+        "step_traffic": main_res["step_traffic"],
         "cpu_baseline_parallel": cpu_par,
-        "kernel_ms": {k: round(x, 5) for k, x in kern.items()},
-        "filter_roofline": filter_roofline,
-        "kernel_events_ms_per_step": None if ev_ms_step is None else round(ev_ms_step, 5),
-        "input_generation_s": round(gen_s, 1),
+        "kernel_ms": main_res["kernel_ms"],
+        "filter_roofline": main_res["filter_roofline"],
+        "kernel_events_ms_per_step": main_res["kernel_events_ms_per_step"],
+        "input_generation_s": main_res["input_generation_s"],
+        "configs": sub,
     }
     print(json.dumps(line), flush=True)
-    v.close()
 
 
 if __name__ == "__main__":

@@ -17,7 +17,9 @@ Test infrastructure.  The rule:
   instead).  Such matches are counted in ``n_exempt``.
 * inputs float32 cannot resolve (q(x) < 1e-30 at a SAMPLE position, a
   residual with less than 1e-6 of mass) are followed the same way but counted
-  in ``n_degenerate``, so that a caller can require none.
+  in ``n_degenerate``, so that a caller can require none; where the tokens
+  are identical and only the informational status bit 128 differs on such a
+  residual, the sequence counts as exact and is tallied in ``n_status_z``.
 """
 from __future__ import annotations
 
@@ -36,6 +38,7 @@ class CompareReport:
     n_exempt: int = 0             # matched only thanks to a 1e-5 near-tie flag
     n_degenerate: int = 0         # matched only thanks to a degenerate-input flag (q underflow, empty residual)
     n_mismatch: int = 0
+    n_status_z: int = 0           # tokens identical, only the informational bit 128 differs (empty residual)
     n_oracle_flagged: int = 0     # sequences the oracle flagged at all
     max_pq_err: float = 0.0
     messages: List[str] = field(default_factory=list)
@@ -46,7 +49,7 @@ class CompareReport:
 
     def summary(self) -> str:
         return (f"seqs={self.n_seq} exact={self.n_exact} exempt={self.n_exempt} "
-                f"degenerate={self.n_degenerate} mismatch={self.n_mismatch} "
+                f"degenerate={self.n_degenerate} mismatch={self.n_mismatch} status128_only={self.n_status_z} "
                 f"oracle_flagged={self.n_oracle_flagged} max|dp,dq|={self.max_pq_err:.3g}")
 
 
@@ -84,16 +87,17 @@ def compare(res: BatchResult, accepted_len, emitted, p_at=None, q_at=None, statu
             rep.n_oracle_flagged += 1
         g_p = None if p_at is None else np.asarray(p_at, np.float64)[od:od + K]
         g_q = None if q_at is None else np.asarray(q_at, np.float64)[od:od + K]
-        verdict, msg, pq_err = _compare_seq(res, s, r, K, gA, g_emit, gst, g_p, g_q, pq_tol)
+        verdict, msg, pq_err, znote = _compare_seq(res, s, r, K, gA, g_emit, gst, g_p, g_q, pq_tol)
         if verdict is None and r.filter_alts:
             # a top-p near-tie: the filter threshold on one side of it is as valid as on the other
             for key, alt in r.filter_alts:
                 r2 = res.rerun(s, {}, {key: alt})
-                v2, _, e2 = _compare_seq(res, s, r2, K, gA, g_emit, gst, g_p, g_q, pq_tol)
+                v2, _, e2, z2 = _compare_seq(res, s, r2, K, gA, g_emit, gst, g_p, g_q, pq_tol)
                 if v2 is not None:
-                    verdict, pq_err = ("degenerate" if v2 == "degenerate" else "exempt"), e2
+                    verdict, pq_err, znote = ("degenerate" if v2 == "degenerate" else "exempt"), e2, z2
                     break
         rep.max_pq_err = max(rep.max_pq_err, pq_err)
+        rep.n_status_z += int(bool(znote) and verdict is not None)
         if verdict is None:
             _fail(rep, msg)
         elif verdict == "exact":
@@ -106,26 +110,28 @@ def compare(res: BatchResult, accepted_len, emitted, p_at=None, q_at=None, statu
 
 
 def _compare_seq(res: BatchResult, s: int, r, K: int, gA: int, g_emit, gst, g_p, g_q, pq_tol: float):
-    """One sequence against one oracle result: (verdict, message, max |dp,dq|)
-    with verdict "exact", "exempt" (matched through a 1e-5 near-tie),
-    "degenerate" (through a degenerate-input flag) or None."""
+    """One sequence against one oracle result: (verdict, message, max |dp,dq|,
+    status note) with verdict "exact", "exempt" (matched through a 1e-5
+    near-tie), "degenerate" (through a degenerate-input flag) or None; the
+    note is True when only status bit 128 differs on a numerically empty
+    residual (the tokens themselves are compared as usual)."""
     if r.status & ST_ERROR_MASK:
         bad = (gA != -1) or (g_emit != -1).any() or (gst is not None and gst != r.status)
         for arr in (g_p, g_q):
             if arr is not None and K and not np.isnan(arr).all():
                 bad = True
         if bad:
-            return None, f"seq {s}: error status {r.status}: got A={gA} status={gst} emit={g_emit.tolist()}", 0.0
-        return "exact", "", 0.0
+            return None, f"seq {s}: error status {r.status}: got A={gA} status={gst} emit={g_emit.tolist()}", 0.0, False
+        return "exact", "", 0.0, False
     pq_err = 0.0
     for arr, ref in ((g_p, r.p_at), (g_q, r.q_at)):
         if arr is not None and K:
             d = np.abs(arr - ref)
             if not np.isfinite(d).all():
-                return None, f"seq {s}: p/q at proposal not finite", float("inf")
+                return None, f"seq {s}: p/q at proposal not finite", float("inf"), False
             pq_err = max(pq_err, float(d.max()))
     if pq_err > pq_tol:
-        return None, f"seq {s}: p/q at proposal differ by {pq_err:.3g} > {pq_tol}", pq_err
+        return None, f"seq {s}: p/q at proposal differ by {pq_err:.3g} > {pq_tol}", pq_err, False
     # follow flagged branches of the acceptance scan
     cur = r
     exempt = degenerate = False
@@ -142,12 +148,12 @@ def _compare_seq(res: BatchResult, s: int, r, K: int, gA: int, g_emit, gst, g_p,
             continue
         return None, (f"seq {s}: accepted_len gpu={gA} oracle={cur.A} (no near-tie at {i}; "
                       f"u={cur.u_acc[i] if i < len(cur.u_acc) else None} "
-                      f"r={cur.ratios[i] if i < len(cur.ratios) else None})"), pq_err
+                      f"r={cur.ratios[i] if i < len(cur.ratios) else None})"), pq_err, False
     if gA != cur.A:
-        return None, f"seq {s}: accepted_len gpu={gA} oracle={cur.A}", pq_err
+        return None, f"seq {s}: accepted_len gpu={gA} oracle={cur.A}", pq_err, False
     A = cur.A
     if (g_emit[:A] != cur.emitted[:A]).any() or (g_emit[A + 1:] != -1).any():
-        return None, f"seq {s}: emitted prefix/suffix differ: gpu={g_emit.tolist()} oracle={cur.emitted.tolist()}", pq_err
+        return None, f"seq {s}: emitted prefix/suffix differ: gpu={g_emit.tolist()} oracle={cur.emitted.tolist()}", pq_err, False
     gy = int(g_emit[A])
     f = cur.final
     if gy != f.y:
@@ -157,13 +163,13 @@ def _compare_seq(res: BatchResult, s: int, r, K: int, gA: int, g_emit, gst, g_p,
             degenerate = True
         else:
             return None, (f"seq {s}: final token gpu={gy} oracle={f.y} ({f.kind}, u={f.u:.9f}, Z={f.Z:.6g}, "
-                          f"flags cdf={f.cdf_flag} z={f.z_flag})"), pq_err
+                          f"flags cdf={f.cdf_flag} z={f.z_flag})"), pq_err, False
+    znote = False
     if gst is not None:
         mask = ~ST_ZERO_RESIDUAL if f.z_flag else ~0
         if (gst & mask) != (cur.status & mask):
-            return None, f"seq {s}: status gpu={gst} oracle={cur.status}", pq_err
-        if f.z_flag and (gst != cur.status):
-            degenerate = True
+            return None, f"seq {s}: status gpu={gst} oracle={cur.status}", pq_err, False
+        znote = gst != cur.status
     if degenerate:
-        return "degenerate", "", pq_err
-    return ("exempt" if exempt else "exact"), "", pq_err
+        return "degenerate", "", pq_err, znote
+    return ("exempt" if exempt else "exact"), "", pq_err, znote

@@ -90,7 +90,7 @@ def add_reports(tot, rep):
     """Accumulate compare reports (tot None: start from rep)."""
     if tot is None:
         return rep
-    for f in ("n_seq", "n_exact", "n_exempt", "n_degenerate", "n_mismatch", "n_oracle_flagged"):
+    for f in ("n_seq", "n_exact", "n_exempt", "n_degenerate", "n_mismatch", "n_oracle_flagged", "n_status_z"):
         setattr(tot, f, getattr(tot, f) + getattr(rep, f))
     tot.max_pq_err = max(tot.max_pq_err, rep.max_pq_err)
     tot.messages.extend(rep.messages[:max(0, 20 - len(tot.messages))])

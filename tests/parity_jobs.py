@@ -19,6 +19,6 @@ def compare(job):
     ref = oracle.verify_batch_from(b, max_k=max_k)
     rep = oracle.compare(ref, out["accepted_len"], out["emitted"], out["p_at"], out["q_at"], out["status"])
     return {"step": step, "n_seq": rep.n_seq, "n_exact": rep.n_exact, "n_exempt": rep.n_exempt,
-            "n_degenerate": rep.n_degenerate, "n_mismatch": rep.n_mismatch,
+            "n_degenerate": rep.n_degenerate, "n_mismatch": rep.n_mismatch, "n_status_z": rep.n_status_z,
             "n_oracle_flagged": rep.n_oracle_flagged, "max_pq_err": rep.max_pq_err,
             "messages": [f"step {step}: {m}" for m in rep.messages[:5]]}

@@ -170,3 +170,22 @@ def test_strict_near_tie_followed_to_rejection():
         assert rep.ok and rep.n_exempt == 1, rep.messages
     rep = oracle.compare(res, [0], np.array([1, -1], np.int32), res.p_at, res.q_at, [0])
     assert not rep.ok                                   # the proposal itself is never the correction
+
+
+def test_empty_residual_status_bit_only():
+    """top-k 1 with the same kept token in p and q and a proposal outside it:
+    rejected, the residual is exactly empty, so the oracle draws from p and
+    sets bit 128.  A device whose rounding left a residual on the same token
+    emits the same token without the bit: identical tokens, counted as exact
+    and tallied apart; a different token is a mismatch."""
+    t = np.array([[2.0, 0.0, 0.0], [0.0, 1.0, 0.5]], np.float32)
+    d = np.array([[2.0, 0.1, 0.0]], np.float32)
+    res = oracle.verify_batch(target=t, draft=d, dtype="f32", vocab=3, num_draft=[1],
+                              draft_tokens=np.array([1], np.int32), temperature=[1.0], mode=[ov.SAMPLE],
+                              top_k=np.array([1], np.int32), max_k=4)
+    s = res.seqs[0]
+    assert s.A == 0 and s.status == ov.ST_ZERO_RESIDUAL and s.final.z_flag and s.emitted[0] == 0
+    rep = oracle.compare(res, [0], np.array([0, -1], np.int32), res.p_at, res.q_at, [0])
+    assert rep.ok and rep.n_exact == 1 and rep.n_status_z == 1 and rep.n_degenerate == 0
+    rep = oracle.compare(res, [0], np.array([0, -1], np.int32), res.p_at, res.q_at, [ov.ST_ZERO_RESIDUAL])
+    assert rep.ok and rep.n_exact == 1 and rep.n_status_z == 0
