@@ -168,6 +168,28 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
  * search. */
 int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* args, void* hip_stream);
 
+/* ---- allocation-free call --------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as spec_verify_run, without a context.  Its scratch is one array of
+ * SV_NOALLOC_SCRATCH_BYTES bytes in the library's device data, which every
+ * GPU the library runs on holds until the process ends; it is laid out per
+ * call for exactly the call's sizes (about 16 bytes per 32 KB chunk of each
+ * of batch * (2 * max_k + 1) row slots, four times that more with top_k /
+ * top_p, plus small per-sequence arrays).  max_k (1..128) plays the part of
+ * the context's max_k (K_s > max_k: status SV_ST_K_TOO_LARGE); batch <= 4096.
+ * A call that would need more scratch returns SV_ERR_CAPACITY with the
+ * needed size in the message; other checks and errors as spec_verify_run.
+ * Runs on the calling thread's current device (hip_stream must belong to
+ * it).  Allocates nothing; the first call on a device looks up the array's
+ * address and writes the defaults for NULL temperature / mode / seq_ids with
+ * synchronous copies, so make one call on each device before capturing a
+ * graph.  All calls on one GPU share its array and it keeps the last call's
+ * contents: calls that overlap on one GPU (concurrent streams or threads)
+ * race and give undefined results.  No timing hooks. */
+#define SV_NOALLOC_SCRATCH_BYTES 67108864
+int spec_verify_run_noalloc(const spec_verify_args* args, int32_t max_k, void* hip_stream);
+
 /* Free the context and its device memory.  NULL is accepted. */
 void spec_verify_destroy(spec_verify_ctx* ctx);
 

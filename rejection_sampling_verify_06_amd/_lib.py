@@ -47,8 +47,9 @@ EXPORTED = (
     "spec_verify_timing_enable", "spec_verify_timing_read", "spec_verify_version",
     "spec_verify_args_size", "spec_verify_ngram_propose", "spec_verify_ngram_args_size",
     "spec_verify_stats_accumulate", "spec_verify_stats_summary", "spec_verify_adapt_reset", "spec_verify_adapt",
-    "spec_verify_adapt_args_size",
+    "spec_verify_adapt_args_size", "spec_verify_run_noalloc",
 )
+SV_NOALLOC_SCRATCH_BYTES = 67108864
 
 
 class SpecVerifyArgs(ctypes.Structure):
@@ -135,6 +136,8 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_create.restype = ctypes.c_int
     lib.spec_verify_run.argtypes = [P, ctypes.POINTER(SpecVerifyArgs), P]
     lib.spec_verify_run.restype = ctypes.c_int
+    lib.spec_verify_run_noalloc.argtypes = [ctypes.POINTER(SpecVerifyArgs), ctypes.c_int32, P]
+    lib.spec_verify_run_noalloc.restype = ctypes.c_int
     lib.spec_verify_destroy.argtypes = [P]
     lib.spec_verify_destroy.restype = None
     lib.spec_verify_last_error.argtypes = []

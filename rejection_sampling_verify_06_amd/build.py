@@ -8,7 +8,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libspec_verify.so"
-SOURCES = ["csrc/sv_kernels.hip", "csrc/sv_ngram.hip", "csrc/sv_stats.hip", "csrc/sv_filter.hip", "csrc/sv_api.cpp"]
+SOURCES = ["csrc/sv_kernels.hip", "csrc/sv_ngram.hip", "csrc/sv_stats.hip", "csrc/sv_filter.hip", "csrc/sv_noalloc.hip",
+           "csrc/sv_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -13,7 +13,7 @@
 #include "spec_verify.h"
 #include "sv_internal.h"
 
-namespace {
+namespace sv {
 
 thread_local char g_err[512] = "";
 
@@ -30,6 +30,26 @@ int hip_fail(const char* what, hipError_t e) {
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// 1.0, SV_SAMPLE (0) and s for the first n sequences (synchronous copies).
+hipError_t fill_defaults(const Scratch& v, int32_t n) {
+  std::vector<float> t((size_t)n, 1.0f);
+  std::vector<uint8_t> m((size_t)n, 0);
+  std::vector<uint32_t> ids((size_t)n);
+  for (int32_t i = 0; i < n; ++i) ids[i] = (uint32_t)i;
+  hipError_t e = hipMemcpy(v.def_temperature, t.data(), t.size() * sizeof(float), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(v.def_mode, m.data(), m.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(v.def_seq_ids, ids.data(), ids.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
+  return e;
+}
+
+}  // namespace sv
+
+using sv::align_up;
+using sv::hip_fail;
+using sv::set_err;
+
+namespace {
 
 // Restores the caller's current device on scope exit.
 struct DeviceGuard {
@@ -54,26 +74,9 @@ struct DeviceGuard {
 
 struct spec_verify_ctx {
   int device = 0;
-  int32_t max_batch = 0;
-  int32_t max_k = 0;
-  int64_t max_vocab = 0;
-  int64_t max_rows = 0;     // sequence slots: max_batch * (2 * max_k + 1)
-  int32_t max_nch = 0;      // chunks per row at the smallest chunk (8192 elements)
-  int32_t max_tiles = 0;
+  sv::Caps caps;
   void* mem = nullptr;
-  size_t bytes = 0;
-  sv::Partial* partials = nullptr;
-  float* segmax = nullptr;
-  float* xval = nullptr;
-  float* tau = nullptr;
-  int32_t* order = nullptr;   // the filter kernel's sequence order
-  int32_t* ptok = nullptr;
-  sv::SeqFinal* fin = nullptr;
-  float* tilesum = nullptr;
-  // defaults for NULL temperature / mode / seq_ids: 1.0, SV_SAMPLE, s
-  float* def_temperature = nullptr;
-  uint8_t* def_mode = nullptr;
-  uint32_t* def_seq_ids = nullptr;
+  sv::Scratch scratch;
   // timing hooks
   std::vector<hipEvent_t> events;   // a start and a stop per kernel slot of every recorded call
   std::vector<uint8_t> launched;    // per kernel slot of every recorded call: 1 when it launched
@@ -81,9 +84,197 @@ struct spec_verify_ctx {
   int32_t timing_used = 0;
 };
 
+namespace sv {
+
+ScratchLayout scratch_layout(int32_t max_batch, int32_t max_k, int64_t max_rows, int32_t max_nch, int32_t max_tiles,
+                             bool with_segmax) {
+  ScratchLayout L;
+  size_t off = 0;
+  L.o_part = off;  off = align_up(off + sizeof(Partial) * max_rows * max_nch, 256);
+  L.o_xval = off;  off = align_up(off + sizeof(float) * max_rows, 256);
+  L.o_tau = off;   off = align_up(off + sizeof(float) * max_rows, 256);
+  L.o_ptok = off;  off = align_up(off + sizeof(int32_t) * (size_t)max_batch * max_k, 256);
+  L.o_fin = off;   off = align_up(off + sizeof(SeqFinal) * max_batch, 256);
+  L.o_tile = off;  off = align_up(off + sizeof(float) * (size_t)max_batch * max_tiles, 256);
+  L.o_ord = off;   off = align_up(off + sizeof(int32_t) * (size_t)max_batch, 256);
+  L.o_seg = off;
+  if (with_segmax) off = align_up(off + sizeof(float) * kSegPerChunk * max_rows * max_nch, 256);
+  L.bytes = off;
+  return L;
+}
+
+Scratch scratch_at(void* base, const ScratchLayout& L, bool with_segmax) {
+  char* b = (char*)base;
+  Scratch v;
+  v.partials = (Partial*)(b + L.o_part);
+  v.xval = (float*)(b + L.o_xval);
+  v.tau = (float*)(b + L.o_tau);
+  v.ptok = (int32_t*)(b + L.o_ptok);
+  v.fin = (SeqFinal*)(b + L.o_fin);
+  v.tilesum = (float*)(b + L.o_tile);
+  v.order = (int32_t*)(b + L.o_ord);
+  v.segmax = with_segmax ? (float*)(b + L.o_seg) : nullptr;
+  return v;
+}
+
+Caps caps_for(int32_t max_batch, int32_t max_k, int64_t max_vocab) {
+  Caps c;
+  c.max_batch = max_batch;
+  c.max_k = max_k;
+  c.max_vocab = max_vocab;
+  c.max_rows = (int64_t)max_batch * (2 * (int64_t)max_k + 1);
+  const int min_ce = kChunkBytes / 4;
+  c.max_nch = (int32_t)((max_vocab + min_ce - 1) / min_ce);
+  c.max_tiles = (int32_t)((max_vocab + kTileElems - 1) / kTileElems);
+  return c;
+}
+
+// Host-side checks of one call against the capacity `c` and the launch
+// parameters; SV_OK, or an error code with the message set (nothing enqueued).
+int prepare_call(const char* who, const spec_verify_args* a, const Caps& c, const Scratch& v, Params* out) {
+  if (!a) {
+    set_err("%s: args is NULL", who);
+    return SV_ERR_INVALID;
+  }
+  if (a->batch < 0) {
+    set_err("%s: batch %d < 0", who, a->batch);
+    return SV_ERR_INVALID;
+  }
+  if (a->vocab < 1 || a->vocab > 0x7FFFFFFF) {
+    set_err("%s: vocab %lld out of range", who, (long long)a->vocab);
+    return SV_ERR_INVALID;
+  }
+  if (a->total_draft < 0) {
+    set_err("%s: total_draft %lld < 0", who, (long long)a->total_draft);
+    return SV_ERR_INVALID;
+  }
+  if (a->target_dtype != SV_F32 && a->target_dtype != SV_BF16) {
+    set_err("%s: target_dtype %d is not SV_F32 or SV_BF16", who, a->target_dtype);
+    return SV_ERR_INVALID;
+  }
+  if (a->draft_logits && a->draft_dtype != SV_F32 && a->draft_dtype != SV_BF16) {
+    set_err("%s: draft_dtype %d is not SV_F32 or SV_BF16", who, a->draft_dtype);
+    return SV_ERR_INVALID;
+  }
+  if (!a->target_logits || !a->num_draft || !a->accepted_len || !a->emitted_tokens) {
+    set_err("%s: target_logits, num_draft, accepted_len and emitted_tokens are required", who);
+    return SV_ERR_INVALID;
+  }
+  if (a->total_draft > 0 && !a->draft_tokens) {
+    set_err("%s: draft_tokens is NULL with total_draft > 0", who);
+    return SV_ERR_INVALID;
+  }
+  if ((uintptr_t)a->target_logits % (a->target_dtype == SV_BF16 ? 2 : 4) ||
+      (a->draft_logits && (uintptr_t)a->draft_logits % (a->draft_dtype == SV_BF16 ? 2 : 4))) {
+    set_err("%s: logits pointers must be aligned to their element size", who);
+    return SV_ERR_INVALID;
+  }
+  if (a->ld_target < a->vocab) {
+    set_err("%s: ld_target %lld < vocab %lld", who, (long long)a->ld_target, (long long)a->vocab);
+    return SV_ERR_INVALID;
+  }
+  if (a->draft_logits && a->ld_draft < a->vocab) {
+    set_err("%s: ld_draft %lld < vocab %lld", who, (long long)a->ld_draft, (long long)a->vocab);
+    return SV_ERR_INVALID;
+  }
+  if (a->batch > c.max_batch) {
+    set_err("%s: batch %d > max_batch %d", who, a->batch, c.max_batch);
+    return SV_ERR_CAPACITY;
+  }
+  if (a->vocab > c.max_vocab) {
+    set_err("%s: vocab %lld > max_vocab %lld", who, (long long)a->vocab, (long long)c.max_vocab);
+    return SV_ERR_CAPACITY;
+  }
+  if (a->total_draft > (int64_t)c.max_batch * c.max_k) {
+    set_err("%s: total_draft %lld > max_batch * max_k = %lld", who, (long long)a->total_draft,
+            (long long)c.max_batch * c.max_k);
+    return SV_ERR_CAPACITY;
+  }
+
+  Params& p = *out;
+  memset(&p, 0, sizeof(p));
+  p.B = a->batch;
+  p.V = (int32_t)a->vocab;
+  p.total_draft = (int32_t)a->total_draft;
+  p.max_k = c.max_k;
+  p.n_t = p.total_draft + p.B;
+  p.n_d = a->draft_logits ? p.total_draft : 0;
+  p.tgt = a->target_logits;
+  p.ld_t = a->ld_target;
+  p.t_bf16 = a->target_dtype == SV_BF16;
+  const int es_t = p.t_bf16 ? 2 : 4;
+  p.t_vec = ((uintptr_t)a->target_logits % 16 == 0) && ((a->ld_target * es_t) % 16 == 0);
+  p.dft = a->draft_logits;
+  p.ld_d = a->draft_logits ? a->ld_draft : 0;
+  p.d_bf16 = a->draft_logits ? (a->draft_dtype == SV_BF16) : p.t_bf16;
+  const int es_d = p.d_bf16 ? 2 : 4;
+  p.d_vec = a->draft_logits && ((uintptr_t)a->draft_logits % 16 == 0) && ((a->ld_draft * es_d) % 16 == 0);
+  p.tokens = a->draft_tokens;
+  p.num_draft = a->num_draft;
+  p.temperature = a->temperature ? a->temperature : v.def_temperature;
+  p.mode = a->mode ? a->mode : v.def_mode;
+  p.seq_ids = a->seq_ids ? a->seq_ids : v.def_seq_ids;
+  p.seed_lo = (uint32_t)(a->seed & 0xFFFFFFFFu);
+  p.seed_hi = (uint32_t)(a->seed >> 32);
+  p.accepted_len = a->accepted_len;
+  p.emitted = a->emitted_tokens;
+  p.p_at = a->p_at_proposal;
+  p.q_at = a->q_at_proposal;
+  p.status = a->status;
+  p.partials = v.partials;
+  p.xval = v.xval;
+  p.tau = v.tau;
+  p.order = v.order;
+  const bool filtered = a->top_k || a->top_p;
+  p.order_block = filtered ? 1 : 0;
+  p.segmax = filtered ? v.segmax : nullptr;   // filter bounds from row_stats' segment maxima
+  p.top_k = a->top_k;
+  p.top_p = a->top_p;
+  p.ptok = v.ptok;
+  p.fin = v.fin;
+  p.tilesum = v.tilesum;
+  // one row-stats block streams 32 KB of a row
+  p.ce_t = kChunkBytes / es_t;
+  p.ce_d = kChunkBytes / es_d;
+  p.nch_t = (p.V + p.ce_t - 1) / p.ce_t;
+  p.nch_d = (p.V + p.ce_d - 1) / p.ce_d;
+  p.ntiles = (p.V + kTileElems - 1) / kTileElems;
+  p.slots = 2 * c.max_k + 1;
+  p.nch_max = p.nch_t > p.nch_d ? p.nch_t : p.nch_d;
+  p.nsplit = 1;
+  if (p.B < kFuseMinBatch) {
+    const int want = (kSplitTargetBlocks + p.B - 1) / p.B;
+    p.nsplit = want < p.ntiles ? want : p.ntiles;
+    if (p.nsplit < 1) p.nsplit = 1;
+  }
+  if ((int64_t)(p.n_t + p.n_d) > c.max_rows || p.nch_t > c.max_nch || p.nch_d > c.max_nch ||
+      p.ntiles > c.max_tiles || (filtered && !v.segmax)) {
+    set_err("%s: scratch capacity exceeded", who);
+    return SV_ERR_CAPACITY;
+  }
+  return SV_OK;
+}
+
+// Enqueue the kernels of one step (timed when `events` is not NULL: a start
+// and a stop event per kernel slot).
+int launch_call(const Params& p, hipStream_t st, hipEvent_t* events, uint8_t* launched) {
+  typedef hipError_t (*Launch)(const Params&, hipStream_t, const LaunchEvents*);
+  static const Launch kLaunch[SV_NUM_KERNELS] = {launch_row_stats, launch_filter, launch_final, launch_select};
+  static const char* kName[SV_NUM_KERNELS] = {"row_stats", "filter", "final", "select"};
+  for (int k = 0; k < SV_NUM_KERNELS; ++k) {
+    const LaunchEvents le{events ? events[2 * k] : nullptr, events ? events[2 * k + 1] : nullptr,
+                          events ? &launched[k] : nullptr};
+    hipError_t e = kLaunch[k](p, st, events ? &le : nullptr);
+    if (e != hipSuccess) return hip_fail(kName[k], e);
+  }
+  return SV_OK;
+}
+
+}  // namespace sv
+
 extern "C" {
 
-const char* spec_verify_last_error(void) { return g_err; }
+const char* spec_verify_last_error(void) { return sv::g_err; }
 
 const char* spec_verify_version(void) { return "spec_verify 0.1 (gfx950)"; }
 
@@ -124,64 +315,35 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
     return SV_ERR_NOMEM;
   }
   c->device = device;
-  c->max_batch = max_batch;
-  c->max_k = max_k;
-  c->max_vocab = max_vocab;
-  c->max_rows = (int64_t)max_batch * (2 * (int64_t)max_k + 1);
-  const int min_ce = sv::kChunkBytes / 4;
-  c->max_nch = (int32_t)((max_vocab + min_ce - 1) / min_ce);
-  c->max_tiles = (int32_t)((max_vocab + sv::kTileElems - 1) / sv::kTileElems);
-
-  size_t off = 0;
-  const size_t o_part = off;   off = align_up(off + sizeof(sv::Partial) * c->max_rows * c->max_nch, 256);
-  const size_t o_xval = off;   off = align_up(off + sizeof(float) * c->max_rows, 256);
-  const size_t o_tau = off;    off = align_up(off + sizeof(float) * c->max_rows, 256);
-  const size_t o_ptok = off;   off = align_up(off + sizeof(int32_t) * (size_t)max_batch * max_k, 256);
-  const size_t o_fin = off;    off = align_up(off + sizeof(sv::SeqFinal) * max_batch, 256);
-  const size_t o_tile = off;   off = align_up(off + sizeof(float) * (size_t)max_batch * c->max_tiles, 256);
-  const size_t o_dt = off;     off = align_up(off + sizeof(float) * (size_t)max_batch, 256);
-  const size_t o_dm = off;     off = align_up(off + (size_t)max_batch, 256);
-  const size_t o_ds = off;     off = align_up(off + sizeof(uint32_t) * (size_t)max_batch, 256);
-  const size_t o_ord = off;    off = align_up(off + sizeof(int32_t) * (size_t)max_batch, 256);
-  const size_t o_seg = off;    off = align_up(off + sizeof(float) * sv::kSegPerChunk * c->max_rows * c->max_nch, 256);
-  c->bytes = off;
-  e = hipMalloc(&c->mem, c->bytes);
+  c->caps = sv::caps_for(max_batch, max_k, max_vocab);
+  const sv::ScratchLayout L = sv::scratch_layout(max_batch, max_k, c->caps.max_rows, c->caps.max_nch,
+                                                 c->caps.max_tiles, true);
+  // defaults for NULL temperature / mode / seq_ids (1.0, SV_SAMPLE, s) after the call's scratch
+  const size_t o_dt = L.bytes;
+  const size_t o_dm = align_up(o_dt + sizeof(float) * (size_t)max_batch, 256);
+  const size_t o_ds = align_up(o_dm + (size_t)max_batch, 256);
+  const size_t bytes = align_up(o_ds + sizeof(uint32_t) * (size_t)max_batch, 256);
+  e = hipMalloc(&c->mem, bytes);
   if (e != hipSuccess) {
     delete c;
-    set_err("spec_verify_create: hipMalloc of %zu bytes: %s", off, hipGetErrorString(e));
+    set_err("spec_verify_create: hipMalloc of %zu bytes: %s", bytes, hipGetErrorString(e));
     return SV_ERR_NOMEM;
   }
-  e = hipMemset(c->mem, 0, c->bytes);
+  e = hipMemset(c->mem, 0, bytes);
   if (e != hipSuccess) {
     (void)hipFree(c->mem);
     delete c;
     return hip_fail("hipMemset", e);
   }
+  c->scratch = sv::scratch_at(c->mem, L, true);
   char* b = (char*)c->mem;
-  c->partials = (sv::Partial*)(b + o_part);
-  c->xval = (float*)(b + o_xval);
-  c->tau = (float*)(b + o_tau);
-  c->ptok = (int32_t*)(b + o_ptok);
-  c->fin = (sv::SeqFinal*)(b + o_fin);
-  c->tilesum = (float*)(b + o_tile);
-  c->def_temperature = (float*)(b + o_dt);
-  c->def_mode = (uint8_t*)(b + o_dm);
-  c->def_seq_ids = (uint32_t*)(b + o_ds);
-  c->order = (int32_t*)(b + o_ord);
-  c->segmax = (float*)(b + o_seg);
-  {
-    std::vector<float> t((size_t)max_batch, 1.0f);
-    std::vector<uint32_t> ids((size_t)max_batch);
-    for (int32_t i = 0; i < max_batch; ++i) ids[i] = (uint32_t)i;
-    // mode: the scratch is zeroed above, and 0 is SV_SAMPLE
-    e = hipMemcpy(c->def_temperature, t.data(), t.size() * sizeof(float), hipMemcpyHostToDevice);
-    if (e == hipSuccess)
-      e = hipMemcpy(c->def_seq_ids, ids.data(), ids.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-      (void)hipFree(c->mem);
-      delete c;
-      return hip_fail("hipMemcpy", e);
-    }
+  c->scratch.def_temperature = (float*)(b + o_dt);
+  c->scratch.def_mode = (uint8_t*)(b + o_dm);
+  c->scratch.def_seq_ids = (uint32_t*)(b + o_ds);
+  if ((e = sv::fill_defaults(c->scratch, max_batch)) != hipSuccess) {
+    (void)hipFree(c->mem);
+    delete c;
+    return hip_fail("hipMemcpy", e);
   }
   *out = c;
   return SV_OK;
@@ -201,140 +363,19 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* a, void* hip_s
     set_err("spec_verify_run: ctx or args is NULL");
     return SV_ERR_INVALID;
   }
-  if (a->batch < 0) {
-    set_err("spec_verify_run: batch %d < 0", a->batch);
-    return SV_ERR_INVALID;
-  }
   if (a->batch == 0) return SV_OK;
-  if (a->vocab < 1 || a->vocab > 0x7FFFFFFF) {
-    set_err("spec_verify_run: vocab %lld out of range", (long long)a->vocab);
-    return SV_ERR_INVALID;
-  }
-  if (a->total_draft < 0) {
-    set_err("spec_verify_run: total_draft %lld < 0", (long long)a->total_draft);
-    return SV_ERR_INVALID;
-  }
-  if (a->target_dtype != SV_F32 && a->target_dtype != SV_BF16) {
-    set_err("spec_verify_run: target_dtype %d is not SV_F32 or SV_BF16", a->target_dtype);
-    return SV_ERR_INVALID;
-  }
-  if (a->draft_logits && a->draft_dtype != SV_F32 && a->draft_dtype != SV_BF16) {
-    set_err("spec_verify_run: draft_dtype %d is not SV_F32 or SV_BF16", a->draft_dtype);
-    return SV_ERR_INVALID;
-  }
-  if (!a->target_logits || !a->num_draft || !a->accepted_len || !a->emitted_tokens) {
-    set_err("spec_verify_run: target_logits, num_draft, accepted_len and emitted_tokens are required");
-    return SV_ERR_INVALID;
-  }
-  if (a->total_draft > 0 && !a->draft_tokens) {
-    set_err("spec_verify_run: draft_tokens is NULL with total_draft > 0");
-    return SV_ERR_INVALID;
-  }
-  if ((uintptr_t)a->target_logits % (a->target_dtype == SV_BF16 ? 2 : 4) ||
-      (a->draft_logits && (uintptr_t)a->draft_logits % (a->draft_dtype == SV_BF16 ? 2 : 4))) {
-    set_err("spec_verify_run: logits pointers must be aligned to their element size");
-    return SV_ERR_INVALID;
-  }
-  if (a->ld_target < a->vocab) {
-    set_err("spec_verify_run: ld_target %lld < vocab %lld", (long long)a->ld_target, (long long)a->vocab);
-    return SV_ERR_INVALID;
-  }
-  if (a->draft_logits && a->ld_draft < a->vocab) {
-    set_err("spec_verify_run: ld_draft %lld < vocab %lld", (long long)a->ld_draft, (long long)a->vocab);
-    return SV_ERR_INVALID;
-  }
-  if (a->batch > ctx->max_batch) {
-    set_err("spec_verify_run: batch %d > max_batch %d", a->batch, ctx->max_batch);
-    return SV_ERR_CAPACITY;
-  }
-  if (a->vocab > ctx->max_vocab) {
-    set_err("spec_verify_run: vocab %lld > max_vocab %lld", (long long)a->vocab, (long long)ctx->max_vocab);
-    return SV_ERR_CAPACITY;
-  }
-  if (a->total_draft > (int64_t)ctx->max_batch * ctx->max_k) {
-    set_err("spec_verify_run: total_draft %lld > max_batch * max_k = %lld", (long long)a->total_draft,
-            (long long)ctx->max_batch * ctx->max_k);
-    return SV_ERR_CAPACITY;
-  }
-
   sv::Params p;
-  memset(&p, 0, sizeof(p));
-  p.B = a->batch;
-  p.V = (int32_t)a->vocab;
-  p.total_draft = (int32_t)a->total_draft;
-  p.max_k = ctx->max_k;
-  p.n_t = p.total_draft + p.B;
-  p.n_d = a->draft_logits ? p.total_draft : 0;
-  p.tgt = a->target_logits;
-  p.ld_t = a->ld_target;
-  p.t_bf16 = a->target_dtype == SV_BF16;
-  const int es_t = p.t_bf16 ? 2 : 4;
-  p.t_vec = ((uintptr_t)a->target_logits % 16 == 0) && ((a->ld_target * es_t) % 16 == 0);
-  p.dft = a->draft_logits;
-  p.ld_d = a->draft_logits ? a->ld_draft : 0;
-  p.d_bf16 = a->draft_logits ? (a->draft_dtype == SV_BF16) : p.t_bf16;
-  const int es_d = p.d_bf16 ? 2 : 4;
-  p.d_vec = a->draft_logits && ((uintptr_t)a->draft_logits % 16 == 0) && ((a->ld_draft * es_d) % 16 == 0);
-  p.tokens = a->draft_tokens;
-  p.num_draft = a->num_draft;
-  p.temperature = a->temperature ? a->temperature : ctx->def_temperature;
-  p.mode = a->mode ? a->mode : ctx->def_mode;
-  p.seq_ids = a->seq_ids ? a->seq_ids : ctx->def_seq_ids;
-  p.seed_lo = (uint32_t)(a->seed & 0xFFFFFFFFu);
-  p.seed_hi = (uint32_t)(a->seed >> 32);
-  p.accepted_len = a->accepted_len;
-  p.emitted = a->emitted_tokens;
-  p.p_at = a->p_at_proposal;
-  p.q_at = a->q_at_proposal;
-  p.status = a->status;
-  p.partials = ctx->partials;
-  p.xval = ctx->xval;
-  p.tau = ctx->tau;
-  p.order = ctx->order;
-  p.order_block = (a->top_k || a->top_p) ? 1 : 0;
-  p.segmax = (a->top_k || a->top_p) ? ctx->segmax : nullptr;   // filter bounds from row_stats' segment maxima
-  p.top_k = a->top_k;
-  p.top_p = a->top_p;
-  p.ptok = ctx->ptok;
-  p.fin = ctx->fin;
-  p.tilesum = ctx->tilesum;
-  // one row-stats block streams 32 KB of a row
-  p.ce_t = sv::kChunkBytes / es_t;
-  p.ce_d = sv::kChunkBytes / es_d;
-  p.nch_t = (p.V + p.ce_t - 1) / p.ce_t;
-  p.nch_d = (p.V + p.ce_d - 1) / p.ce_d;
-  p.ntiles = (p.V + sv::kTileElems - 1) / sv::kTileElems;
-  p.slots = 2 * ctx->max_k + 1;
-  p.nch_max = p.nch_t > p.nch_d ? p.nch_t : p.nch_d;
-  p.nsplit = 1;
-  if (p.B < sv::kFuseMinBatch) {
-    const int want = (sv::kSplitTargetBlocks + p.B - 1) / p.B;
-    p.nsplit = want < p.ntiles ? want : p.ntiles;
-    if (p.nsplit < 1) p.nsplit = 1;
-  }
-  if ((int64_t)(p.n_t + p.n_d) > ctx->max_rows || p.nch_t > ctx->max_nch || p.nch_d > ctx->max_nch ||
-      p.ntiles > ctx->max_tiles) {
-    set_err("spec_verify_run: scratch capacity exceeded");
-    return SV_ERR_CAPACITY;
-  }
+  int rc = sv::prepare_call("spec_verify_run", a, ctx->caps, ctx->scratch, &p);
+  if (rc != SV_OK) return rc;
 
   DeviceGuard g;
   hipError_t e = g.enter(ctx->device);
   if (e != hipSuccess) return hip_fail("hipSetDevice", e);
-  hipStream_t st = (hipStream_t)hip_stream;
-
   const bool timed = ctx->timing_used < ctx->timing_cap;
   hipEvent_t* ev = timed ? &ctx->events[(size_t)ctx->timing_used * 2 * SV_NUM_KERNELS] : nullptr;
-  typedef hipError_t (*Launch)(const sv::Params&, hipStream_t, const sv::LaunchEvents*);
-  static const Launch kLaunch[SV_NUM_KERNELS] = {sv::launch_row_stats, sv::launch_filter, sv::launch_final,
-                                                 sv::launch_select};
-  static const char* kName[SV_NUM_KERNELS] = {"row_stats", "filter", "final", "select"};
   uint8_t* launched = timed ? &ctx->launched[(size_t)ctx->timing_used * SV_NUM_KERNELS] : nullptr;
-  for (int k = 0; k < SV_NUM_KERNELS; ++k) {
-    const sv::LaunchEvents le{timed ? ev[2 * k] : nullptr, timed ? ev[2 * k + 1] : nullptr,
-                              timed ? &launched[k] : nullptr};
-    if ((e = kLaunch[k](p, st, timed ? &le : nullptr)) != hipSuccess) return hip_fail(kName[k], e);
-  }
+  rc = sv::launch_call(p, (hipStream_t)hip_stream, ev, launched);
+  if (rc != SV_OK) return rc;
   if (timed) ctx->timing_used++;
   return SV_OK;
 }

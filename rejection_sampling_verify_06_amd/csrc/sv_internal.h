@@ -4,7 +4,10 @@
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
+
+#include "spec_verify.h"
 
 namespace sv {
 
@@ -183,6 +186,49 @@ hipError_t launch_stats_accumulate(const StatsParams& p, hipStream_t st);
 hipError_t launch_stats_summary(const StatsParams& p, hipStream_t st);
 hipError_t launch_adapt(const AdaptParams& p, hipStream_t st);
 hipError_t launch_adapt_reset(const AdaptParams& p, hipStream_t st);
+
+// ---- host side shared by the entry points (sv_api.cpp) ----------------------
+
+// Sizes a verify call may use: those of a context, or of one allocation-free call.
+struct Caps {
+  int32_t max_batch;
+  int32_t max_k;
+  int64_t max_vocab;
+  int64_t max_rows;    // sequence slots: max_batch * (2 * max_k + 1)
+  int32_t max_nch;     // chunks per row at the smallest chunk (8192 elements)
+  int32_t max_tiles;
+};
+
+// Where one call's scratch lives.
+struct Scratch {
+  Partial* partials;
+  float* segmax;       // NULL: no room for the filters' segment maxima
+  float* xval;
+  float* tau;
+  int32_t* order;
+  int32_t* ptok;
+  SeqFinal* fin;
+  float* tilesum;
+  float* def_temperature;   // defaults for NULL temperature / mode / seq_ids: 1.0, SV_SAMPLE, s
+  uint8_t* def_mode;
+  uint32_t* def_seq_ids;
+};
+
+// Byte offsets of the scratch arrays for the given sizes (256-byte aligned).
+struct ScratchLayout {
+  size_t o_part, o_xval, o_tau, o_ptok, o_fin, o_tile, o_ord, o_seg, bytes;
+};
+
+Caps caps_for(int32_t max_batch, int32_t max_k, int64_t max_vocab);
+ScratchLayout scratch_layout(int32_t max_batch, int32_t max_k, int64_t max_rows, int32_t max_nch, int32_t max_tiles,
+                             bool with_segmax);
+Scratch scratch_at(void* base, const ScratchLayout& L, bool with_segmax);
+hipError_t fill_defaults(const Scratch& v, int32_t n);
+int prepare_call(const char* who, const spec_verify_args* a, const Caps& c, const Scratch& v, struct Params* out);
+int launch_call(const struct Params& p, hipStream_t st, hipEvent_t* events, uint8_t* launched);
+void set_err(const char* fmt, ...);
+int hip_fail(const char* what, hipError_t e);
+size_t align_up(size_t x, size_t a);
 
 // The kernels of one verify step, in stream order (select only when
 // nsplit > 1).
