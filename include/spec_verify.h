@@ -159,13 +159,13 @@ int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int
  * SV_ERR_CAPACITY: nothing is enqueued); problems that only the device can
  * see are reported per sequence through `status`.  Does not allocate, does
  * not synchronise; outputs are valid once the stream has reached this point.
- * Launches two or three kernels: row statistics (one block per 32 KB of
- * every logit row); final (per sequence: the acceptance test, then the sums
- * of the final weights over 8192-element tiles of the row(s) at the stop
- * position and, when one block holds the whole sequence, the inverse-CDF
- * search); for batches below 128 the tiles of a sequence are spread over
- * several blocks and a select kernel (one block per sequence) does the
- * search. */
+ * Launches two kernels (three with top_k / top_p): row statistics (one
+ * block per 32 KB of every logit row); final (per sequence: the acceptance
+ * test, then the sums of the final weights over 8192-element tiles of the
+ * row(s) at the stop position and the inverse-CDF search; for batches below
+ * 128 a sequence's tiles are spread over several blocks, and the last of
+ * them to store its tile sums does the search).  The timing slot "select"
+ * is kept for the interface and reads 0. */
 int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* args, void* hip_stream);
 
 /* ---- allocation-free call --------------------------------------------------

@@ -96,6 +96,7 @@ ScratchLayout scratch_layout(int32_t max_batch, int32_t max_k, int64_t max_rows,
   L.o_ptok = off;  off = align_up(off + sizeof(int32_t) * (size_t)max_batch * max_k, 256);
   L.o_fin = off;   off = align_up(off + sizeof(SeqFinal) * max_batch, 256);
   L.o_tile = off;  off = align_up(off + sizeof(float) * (size_t)max_batch * max_tiles, 256);
+  L.o_cnt = off;   off = align_up(off + sizeof(uint32_t) * (size_t)max_batch, 256);
   L.o_ord = off;   off = align_up(off + sizeof(int32_t) * (size_t)max_batch, 256);
   L.o_seg = off;
   if (with_segmax) off = align_up(off + sizeof(float) * kSegPerChunk * max_rows * max_nch, 256);
@@ -112,6 +113,7 @@ Scratch scratch_at(void* base, const ScratchLayout& L, bool with_segmax) {
   v.ptok = (int32_t*)(b + L.o_ptok);
   v.fin = (SeqFinal*)(b + L.o_fin);
   v.tilesum = (float*)(b + L.o_tile);
+  v.fincnt = (uint32_t*)(b + L.o_cnt);
   v.order = (int32_t*)(b + L.o_ord);
   v.segmax = with_segmax ? (float*)(b + L.o_seg) : nullptr;
   return v;
@@ -233,6 +235,7 @@ int prepare_call(const char* who, const spec_verify_args* a, const Caps& c, cons
   p.ptok = v.ptok;
   p.fin = v.fin;
   p.tilesum = v.tilesum;
+  p.fincnt = v.fincnt;
   // one row-stats block streams 32 KB of a row
   p.ce_t = kChunkBytes / es_t;
   p.ce_d = kChunkBytes / es_d;

@@ -19,7 +19,8 @@ constexpr int kMaxK = 128;
 constexpr int kMaxTiles = 256;          // => vocab <= 2,097,152
 // The final kernel runs one 1024-thread block per sequence when the batch
 // alone fills the chip; smaller batches split each sequence's tiles over
-// about kSplitTargetBlocks / B blocks and finish in a select kernel.
+// about kSplitTargetBlocks / B blocks, and the last of them to store its tile
+// sums draws the token.
 constexpr int kFuseMinBatch = 128;
 constexpr int kSplitTargetBlocks = 256;
 
@@ -94,7 +95,8 @@ struct Params {
   float* xval;        // per slot: the row's logit at its proposed token
   int32_t* ptok;      // [B * max_k]: the proposed tokens, copied by row statistics
   SeqFinal* fin;      // [B]
-  float* tilesum;     // [B * ntiles]
+  float* tilesum;     // [B * ntiles]: tile sums of a split final draw
+  uint32_t* fincnt;   // [B]: split final blocks of the sequence that have stored their tile sums
   int32_t nch_t;      // chunks per target row
   int32_t nch_d;      // chunks per draft row
   int32_t ce_t;       // elements per target chunk (32 KB)
@@ -209,6 +211,7 @@ struct Scratch {
   int32_t* ptok;
   SeqFinal* fin;
   float* tilesum;
+  uint32_t* fincnt;
   float* def_temperature;   // defaults for NULL temperature / mode / seq_ids: 1.0, SV_SAMPLE, s
   uint8_t* def_mode;
   uint32_t* def_seq_ids;
@@ -216,7 +219,7 @@ struct Scratch {
 
 // Byte offsets of the scratch arrays for the given sizes (256-byte aligned).
 struct ScratchLayout {
-  size_t o_part, o_xval, o_tau, o_ptok, o_fin, o_tile, o_ord, o_seg, bytes;
+  size_t o_part, o_xval, o_tau, o_ptok, o_fin, o_tile, o_cnt, o_ord, o_seg, bytes;
 };
 
 Caps caps_for(int32_t max_batch, int32_t max_k, int64_t max_vocab);
@@ -230,8 +233,8 @@ void set_err(const char* fmt, ...);
 int hip_fail(const char* what, hipError_t e);
 size_t align_up(size_t x, size_t a);
 
-// The kernels of one verify step, in stream order (select only when
-// nsplit > 1).
+// The kernels of one verify step, in stream order (the select slot launches
+// nothing: a split final draw finishes in its last block).
 hipError_t launch_row_stats(const Params& p, hipStream_t st, const LaunchEvents* ev = nullptr);
 hipError_t launch_filter(const Params& p, hipStream_t st, const LaunchEvents* ev = nullptr);
 hipError_t launch_final(const Params& p, hipStream_t st, const LaunchEvents* ev = nullptr);

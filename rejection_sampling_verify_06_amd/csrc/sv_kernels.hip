@@ -19,8 +19,10 @@
 //             sequence (batches of 128 and more) the same block picks the
 //             tile holding t = u * Z, re-reads it and emits the first token
 //             whose inclusive prefix exceeds t.
-// select      (batches below 128 only) one block per sequence: the tile sums
-//             written by the split final blocks, then the same search.
+//             Smaller batches spread a sequence's tiles over several
+//             blocks; each stores its tile sums with device-coherent stores
+//             and counts itself in, and the one that arrives last reads them
+//             back and runs the same search.
 //
 // The method (accept with probability min(1, p/q), stop at the first
 // rejection, redraw from norm(max(0, p - q)) or take a bonus token from the
@@ -29,9 +31,11 @@
 // proposal follows "5.2 Draft 模型与无模型方案" (AIInfraGuide) section 4.3;
 // temperature on both rows follows the gitcode.csdn.net tutorial section 4.3.
 // The path is a memory-bound streaming reduction: no matrix cores are used.
-// Blocks never wait on one another: ordering comes only from kernel
-// boundaries, so there are no device-scope fences (each one writes back a
-// whole L2 on this chip) and no spin loops.
+// Blocks never wait on one another and there are no device-scope fences (each
+// one writes back a whole L2 on this chip) and no spin loops: row statistics
+// reach the final kernel across a kernel boundary, and the split final draw
+// hands its tile sums to its last-arriving block through device-coherent
+// stores and loads and one counter per sequence.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -385,6 +389,7 @@ struct FinShared {
   float tp;                         // remainder of u * Z inside tile jj
   int jj;
   int fallback;
+  int arrived_last;                 // a split draw: this block arrived last and draws the token
 };
 
 // The final weights of the VEC elements e.. of one 16-byte vector (target
@@ -1151,6 +1156,9 @@ __global__ void __launch_bounds__(kThreads) k_row_stats(Params P) {
   const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
   const int64_t nblocks = (int64_t)P.n_t * P.nch_t + (int64_t)P.n_d * P.nch_d + P.order_block;
   if (lin >= nblocks) return;
+  if (lin == 0 && P.nsplit > 1) {   // the split final blocks' arrival counters start at zero
+    for (int i = threadIdx.x; i < P.B; i += kThreads) P.fincnt[i] = 0u;
+  }
   int b = (int)lin;
   if (P.order_block) {            // a filtered call: block 0 orders the filter's rows
     if (b == 0) {
@@ -1479,7 +1487,8 @@ __device__ __forceinline__ SeqFinal scan_sequence(const Params& P, int s, ScanSh
 // scan of sequence s (split 0 writes its outputs and the record); then the
 // block sums the final weights of its tiles (j = split mod nsplit) of the
 // row(s) at the stop position.  With one block per sequence the same block
-// picks the token; otherwise the tile sums go to HBM for k_select.
+// picks the token; otherwise the tile sums go to HBM and the last of the
+// sequence's blocks to store its share picks it.
 __global__ void __launch_bounds__(kFinThreads) k_final(Params P) {
   __shared__ ScanShared ssh;
   __shared__ FinShared sh;
@@ -1502,27 +1511,33 @@ __global__ void __launch_bounds__(kFinThreads) k_final(Params P) {
   }
   tile_sums_pass(P, f, f.kind, split, P.nsplit, sh);
   __syncthreads();
-  if (t < P.ntiles && t % P.nsplit == split) {
-    const float z = tile_total(sh, t);
-    if (P.nsplit == 1) sh.tile[t] = z;
-    else P.tilesum[(int64_t)s * P.ntiles + t] = z;
+  if (P.nsplit == 1) {
+    if (t < P.ntiles) sh.tile[t] = tile_total(sh, t);
+    __syncthreads();
+    finish_draw(P, f, sh);
+    return;
   }
-  if (P.nsplit > 1) return;
+  // Split draw: wave 0 stores this block's tile sums (tiles split, split +
+  // nsplit, ...) with device-coherent stores and waits until they are done,
+  // then counts the block in.  The block that brings the count to nsplit
+  // reads every tile sum back with device-coherent loads and draws the token.
+  // No block waits for another; the counter was zeroed by row_stats.
+  if (t < kWave) {
+    const int64_t tb = (int64_t)s * P.ntiles;
+    for (int j = split + t * P.nsplit; j < P.ntiles; j += kWave * P.nsplit)
+      __hip_atomic_store(&P.tilesum[tb + j], tile_total(sh, j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stores are done before the count
+    uint32_t old = 0;
+    if (t == 0) old = __hip_atomic_fetch_add(&P.fincnt[s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = __builtin_amdgcn_readfirstlane((int)old) == P.nsplit - 1;
+    if (last) {
+      for (int j = t; j < P.ntiles; j += kWave)
+        sh.tile[j] = __hip_atomic_load(&P.tilesum[tb + j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (t == 0) sh.arrived_last = last;
+  }
   __syncthreads();
-  finish_draw(P, f, sh);
-}
-
-// One block per sequence when the final kernel was split: the tile sums from
-// HBM, then the tile and the token.
-__global__ void __launch_bounds__(kFinThreads) k_select(Params P) {
-  __shared__ FinShared sh;
-  const int s = blockIdx.x;
-  const int t = threadIdx.x;
-  const SeqFinal f = P.fin[s];
-  if (f.kind != kFinalResidual) return;   // drawn by the final kernel (or nothing to draw)
-  if (t < P.ntiles) sh.tile[t] = P.tilesum[(int64_t)s * P.ntiles + t];
-  __syncthreads();
-  finish_draw(P, f, sh);
+  if (sh.arrived_last) finish_draw(P, f, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1552,9 +1567,8 @@ hipError_t launch_final(const Params& p, hipStream_t st, const LaunchEvents* ev)
 }
 
 hipError_t launch_select(const Params& p, hipStream_t st, const LaunchEvents* ev) {
-  if (p.nsplit <= 1) return record_empty(st, ev);
-  launch_timed(k_select, dim3(p.B), dim3(kFinThreads), st, ev, p);
-  return hipGetLastError();
+  (void)p;
+  return record_empty(st, ev);   // the last split final block draws the token
 }
 
 }  // namespace sv
