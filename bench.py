@@ -39,13 +39,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified positions/sec (B·(K+1) over V) + achieved HBM GB/s vs peak"
 PEAK_HBM_GBPS = 8000.0
-WORKLOADS = {"C0": 0, "C1": 1, "C2": 2, "C3": 3, "C4": 4, "C3S": 3, "C3F": 3, "C3P": 3, "C3D8": 3}
+WORKLOADS = {"C0": 0, "C1": 1, "C2": 2, "C3": 3, "C4": 4, "C3S": 3, "C3F": 3, "C3P": 3, "C3K": 3, "C3D8": 3}
 STRICT_WORKLOADS = {"C3S"}       # the same batches, every sequence in strict sample-match mode
 # one GPU's share when the batch is split across N GPUs by sequence: the
 # first B/N sequences, with their global seq_ids
 SHARD_WORKLOADS = {"C3D8": 8}
 # the same batches with top-k / top-p on every sequence (top-k 0: off)
-FILTER_WORKLOADS = {"C3F": (50, 0.9), "C3P": (0, 0.95)}
+FILTER_WORKLOADS = {"C3F": (50, 0.9), "C3P": (0, 0.95), "C3K": (2000, 1.0)}
 NGRAM_ROTATE = 32          # 32 x ~8.6 MB of histories: more than the 256 MB last-level cache
 ROTATE = {0: 64, 1: 64, 2: 6, 3: 2, 4: 6}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "row_stats_counters.json")
@@ -78,7 +78,8 @@ def make_workload_batch(workload: str, step: int):
         k, p = FILTER_WORKLOADS[workload]
         b.top_k = np.full(b.batch, k, np.int32)
         b.top_p = np.full(b.batch, p, np.float32)
-        b.name += (f"; top-k {k} and top-p {p} on every sequence" if k else f"; top-p {p} on every sequence")
+        b.name += (f"; top-p {p} on every sequence" if not k else
+                   (f"; top-k {k} on every sequence" if p >= 1.0 else f"; top-k {k} and top-p {p} on every sequence"))
     return b
 
 
@@ -589,7 +590,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="C3", choices=sorted(WORKLOADS) + ["NG", "ST"],
                     help="C0..C4: the verify step; C3S: C3 in strict sample-match mode; C3F: C3 with top-k 50 "
-                         "and top-p 0.9; C3P: C3 with top-p 0.95; C3D8: one GPU's share of C3 split by sequence over 8 GPUs; "
+                         "and top-p 0.9; C3P: C3 with top-p 0.95; C3K: C3 with top-k 2000; C3D8: one GPU's share of C3 split by sequence over 8 GPUs; "
                          "NG: the N-gram proposer; ST: acceptance statistics and the draft-length "
                          "controller")
     ap.add_argument("--also", default=None,

@@ -1051,6 +1051,7 @@ __device__ __forceinline__ void chunk_pass(FiltShared& sh, const char* rowp, int
 // path must decide (a crossing past 2^-32 of the maximum, a bracket too
 // large, or a float sum that put the crossing outside the bracket).
 constexpr int kBracketPasses = 6;
+constexpr float kCountSpan = 1024.f;           // a count bracket starts at (-1, kCountSpan] of d
 constexpr int kRing = 256;                     // per-wave ring of bracket tokens (in the idle candidate masses)
 constexpr int kSB = kBins;                     // bins per sparse pass (in the idle histogram buffers)
 static_assert(kSB == 1 << 8, "the bracket search stops at kSB bins of 2^-21 * dhi = 2^-13 * dhi");
@@ -1067,17 +1068,24 @@ __device__ __forceinline__ void bracket_clear(FiltShared& sh, bool chunk_sums) {
   __syncthreads();
 }
 
-template <bool BF>
-__device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, int V, int ce, float c, float mc,
-                                             float topp, int xs, uint32_t* tau_key, bool* sums) {
+// BY_MASS: top-p alone, the crossing is where the mass from the top reaches
+// p * Z.  Otherwise top-k alone (k beyond the bounded selection): the
+// crossing is where the count from the top reaches k; the bracket starts at
+// (-1, 1024] and the first pass splits it at 8, 32, 128 (the k-th token can
+// lie far below the maximum), later passes evenly; no masses are summed
+// until the collect pass.
+template <bool BF, bool BY_MASS>
+__device__ __forceinline__ bool bracket_search(FiltShared& sh, const char* rowp, int V, int ce, float c, float mc,
+                                               int topk, float topp, int xs, uint32_t* tau_key, bool* sums) {
   constexpr int epv = BF ? 8 : 4;
   const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
-  if (!(topp > 0.f)) return false;
+  if (BY_MASS ? !(topp > 0.f) : topk < 1) return false;
   const RowSplit sp = split_row<BF>(rowp, V);
   const uint4* vp = (const uint4*)(rowp + (size_t)sp.head * (BF ? 2 : 4));
-  const double target = (double)topp * sh.zrow / kMassOne;   // in units of the maximum's weight
-  float dlo = -1.f, dhi = kBinSpan;
-  double alo = 0.0;                            // mass of the tokens with d <= dlo
+  // mass in units of the maximum's weight, or the count k
+  const double target = BY_MASS ? (double)topp * sh.zrow / kMassOne : (double)topk;
+  float dlo = -1.f, dhi = BY_MASS ? kBinSpan : kCountSpan;
+  double alo = 0.0;                            // mass (count) of the tokens with d <= dlo
   uint32_t cnt = 0xFFFFFFFFu;
   for (int pass = 0; pass < kBracketPasses && cnt > (uint32_t)kCap; ++pass) {
     const float base = fmaxf(dlo, 0.f);
@@ -1090,6 +1098,12 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
       float D[kBJ];
 #pragma unroll
       for (int q = 0; q < kBJ; ++q) D[q] = (q == kBJ - 1) ? dhi : base + (float)(q + 1) * step;
+      if (!BY_MASS && pass == 0) {
+        static_assert(kBJ == 4, "the first count pass's thresholds");
+        D[0] = 8.f;
+        D[1] = 32.f;
+        D[2] = 128.f;
+      }
       float m[kBJ];
       uint32_t n[kBJ];
 #pragma unroll
@@ -1104,11 +1118,11 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
           for (int j = 0; j < epv; ++j) {
             const float d = fmaf(-vec_elem<BF>(w[u], j), c, mc);
             if (d > dlo && d <= dhi) {           // NaN and -inf logits never pass
-              const float e = fexp2(-d);
+              const float e = BY_MASS ? fexp2(-d) : 0.f;
 #pragma unroll
               for (int q = 0; q < kBJ; ++q) {
                 const bool in = d <= D[q];
-                m[q] += in ? e : 0.f;
+                if (BY_MASS) m[q] += in ? e : 0.f;
                 n[q] += in ? 1u : 0u;
               }
             }
@@ -1138,9 +1152,9 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
       }
       __syncthreads();
       jq = -1;
-      for (int q = kBJ - 1; q >= 0; --q)
-        if (alo + sh.bm[q] >= target) jq = q;   // the first threshold whose mass reaches the target
-      aprev = jq > 0 ? sh.bm[jq - 1] : 0.0;
+      for (int q = kBJ - 1; q >= 0; --q)         // the first threshold whose mass (count) reaches the target
+        if (alo + (BY_MASS ? sh.bm[q] : (double)sh.bn[q]) >= target) jq = q;
+      aprev = jq > 0 ? (BY_MASS ? sh.bm[jq - 1] : (double)sh.bn[jq - 1]) : 0.0;
       cnt = jq >= 0 ? sh.bn[jq] - (jq > 0 ? sh.bn[jq - 1] : 0u) : 0u;
       nlo = jq > 0 ? D[jq - 1] : dlo;
       nhi = jq >= 0 ? D[jq] : dhi;
@@ -1172,7 +1186,7 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
           b = min(max(b, 0), kSB - 1);
           if (b < kSB - 1 && d > thr(b)) ++b;
           if (b > 0 && d <= thr(b - 1)) --b;
-          atomicAdd(&wbm[b], (unsigned long long)(uint32_t)fexp2(base - d + 31.f));
+          if (BY_MASS) atomicAdd(&wbm[b], (unsigned long long)(uint32_t)fexp2(base - d + 31.f));
           atomicAdd(&wbn[b], 1u);
         }
       };
@@ -1220,17 +1234,24 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
         sh.hc[t] = k;
       }
       __syncthreads();
-      const double unit = (double)fexp2(base) * 2147483648.0;   // bin mass units per maximum's weight
-      const double need = (target - alo) * unit;
-      if (wv == 0) scan_bins<true>(sh, sh.hc, sh.hm, false, 0u, need);
-      __syncthreads();
+      if (BY_MASS) {
+        const double unit = (double)fexp2(base) * 2147483648.0;   // bin mass units per maximum's weight
+        const double need = (target - alo) * unit;
+        if (wv == 0) scan_bins<true>(sh, sh.hc, sh.hm, false, 0u, need);
+        __syncthreads();
+        aprev = (need - sh.rem) / unit;
+      } else {
+        const uint32_t needc = (uint32_t)(target - alo);         // tokens still to pass, >= 1
+        if (wv == 0) scan_bins<false>(sh, sh.hc, sh.hm, false, needc, 0.0);
+        __syncthreads();
+        aprev = (double)(needc - uni(sh.need));
+      }
       jq = uni(sh.bin);
-      aprev = (need - sh.rem) / unit;
       cnt = jq >= 0 ? sh.hc[jq] : 0u;
       nlo = jq > 0 ? thr(jq - 1) : dlo;
       nhi = jq >= 0 ? thr(jq) : dhi;
     }
-    if (jq < 0) {                              // past dhi: beyond 2^-32 of the maximum, or rounding
+    if (jq < 0) {                              // past dhi: beyond 2^-32 of the maximum (1024 log2 units for a count), or rounding
       __syncthreads();
       return false;
     }
@@ -1265,6 +1286,7 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
   static_assert(kFThreads * kVecPer * 16 == kChunkBytes, "a round of vectors is one chunk long");
   const bool chunk_sums = xs < 0;
   float above = 0.f, inside = 0.f;
+  uint32_t nabove = 0;                         // tokens above the bracket (d <= dlo)
   uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
   auto collect = [&](const uint4(&w)[kVecPer], int v0) __attribute__((always_inline)) {
     uint64_t hit = 0;
@@ -1282,6 +1304,7 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
           const float e = fexp2(-d);
           above += e;
           ra[up] += e;
+          ++nabove;
         } else if (d <= dhi) {
           hit |= 1ull << (u * epv + j);
           const float e = fexp2(-d);
@@ -1325,11 +1348,13 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
   for_singles<BF>(rowp, sp, collect);
   {
     const float wa = wave_sum(above), wi = wave_sum(inside);
+    const uint32_t wn = wave_sum_u32(nabove);
     const uint32_t wmn = (uint32_t)wave_min_i((int)(kmn ^ 0x80000000u)) ^ 0x80000000u;   // unsigned min
     const uint32_t wmx = (uint32_t)wave_max_i((int)(kmx ^ 0x80000000u)) ^ 0x80000000u;   // unsigned max
     if (lane == 0) {
       sh.wfm[wv][0] = wa;
       sh.wfm[wv][1] = wi;
+      sh.wfn[wv][0] = wn;
       atomicMin(&sh.bkmin, wmn);
       atomicMax(&sh.bkmax, wmx);
     }
@@ -1337,17 +1362,22 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
   __syncthreads();
   if (t == 0) {
     double a = 0.0, b = 0.0;
+    uint32_t na = 0;
     for (int w = 0; w < kFWaves; ++w) {
       a += (double)sh.wfm[w][0];
       b += (double)sh.wfm[w][1];
+      na += sh.wfn[w][0];
     }
     sh.bm[0] = a * kMassOne;                   // fixed-point units from here on
     sh.bm[1] = b * kMassOne;
+    sh.bn[0] = na;
   }
   __syncthreads();
-  const double A = sh.bm[0], B = sh.bm[1], tgt = (double)topp * sh.zrow;
+  const double A = sh.bm[0], B = sh.bm[1], tgt = BY_MASS ? (double)topp * sh.zrow : 0.0;
   const int n = uni((int)sh.ncand);
-  if (n < 1 || A >= tgt || A + B < tgt) {      // the float sums moved the crossing out of the bracket
+  const int nab = uni((int)sh.bn[0]);
+  // the float sums (the counts) must put the crossing inside the bracket
+  if (n < 1 || (BY_MASS ? (A >= tgt || A + B < tgt) : (nab >= topk || nab + n < topk))) {
     bracket_clear(sh, chunk_sums);
     return false;
   }
@@ -1360,8 +1390,9 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
     }
     key = sh.bkmin;                            // one value: kept, since the mass above it is below the target
   } else {
-    if (n <= kFThreads && n <= kRankP) {
-      key = select_by_rank(sh, n, c, mc, false, 0, true, topp, A);
+    if (n <= kFThreads && (!BY_MASS || n <= kRankP)) {
+      key = BY_MASS ? select_by_rank(sh, n, c, mc, false, 0, true, topp, A)
+                    : select_by_rank(sh, n, c, mc, true, topk - nab, false, 0.f);
     } else {
       int n2 = 2;
       while (n2 < n) n2 <<= 1;
@@ -1371,11 +1402,12 @@ __device__ __forceinline__ bool bracket_topp(FiltShared& sh, const char* rowp, i
       }
       __syncthreads();
       sort_desc(sh.ck, sh.bb.ci, n2);
-      key = sorted_thresholds(sh, n, c, mc, false, 0, true, topp, A);
+      key = BY_MASS ? sorted_thresholds(sh, n, c, mc, false, 0, true, topp, A)
+                    : sorted_thresholds(sh, n, c, mc, true, topk - nab, false, 0.f);
     }
     __syncthreads();
     // the exact sums must agree: something kept, and the crossing inside
-    if (key == 0xFFFFFFFFu || !(sh.mtot >= tgt)) {
+    if (key == 0xFFFFFFFFu || (BY_MASS && !(sh.mtot >= tgt))) {
       bracket_clear(sh, chunk_sums);
       return false;
     }
@@ -1428,9 +1460,11 @@ __device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Part
     write_partials(sh, pp, nch, M, kval(bkey), tau_out);
     return;
   }
-  if (use_p && !use_k) {
+  if (use_p != use_k) {
     bool sums = false;
-    if (bracket_topp<BF>(sh, rowp, V, ce, c, mc, topp, xs, &bkey, &sums)) {
+    const bool found = use_p ? bracket_search<BF, true>(sh, rowp, V, ce, c, mc, 0, topp, xs, &bkey, &sums)
+                             : bracket_search<BF, false>(sh, rowp, V, ce, c, mc, topk, 1.f, xs, &bkey, &sums);
+    if (found) {
       if (!sums) chunk_pass<BF>(sh, rowp, V, ce, c, mc, kval(bkey), xs);
       write_partials(sh, pp, nch, M, kval(bkey), tau_out);
       return;

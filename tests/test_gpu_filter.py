@@ -286,3 +286,30 @@ def test_topk_heavy_tokens_in_one_segment(verifier, torch_mod, dtype):
     b.top_k = rng.choice(np.array([10, 50, 64], np.int32), size=B)
     b.top_p = rng.choice(np.array([1.0, 0.9], np.float32), size=B)
     gu.check_batch(verifier, b, torch_mod, label=f"top-k, heavy tokens in one segment {dtype}")
+
+
+@pytest.mark.parametrize("dtype,V,ks", [("bf16", 152064, (1025, 2000, 5000)), ("f32", 40000, (1100, 3000, 30000)),
+                                        ("bf16", 20000, (1500, 19999))])
+def test_large_top_k_count_bracket(verifier, torch_mod, dtype, V, ks):
+    """top-k above the bounded selection's 1024 tokens, alone: the count
+    bracket search (a first pass split at 8, 32, 128 log2 units below the
+    maximum, then even or binned passes) finds the k-th largest logit; every
+    mode, temperatures 0.3..1.5 (the k-th token far below the maximum at low
+    temperature)."""
+    b = make_random_batch(560 + V % 97, B=12, V=V, kmax=3, dtype=dtype, modes=ALL_MODES, temp=(0.3, 1.5))
+    b.top_k = np.resize(np.asarray(ks, np.int32), b.batch).astype(np.int32)
+    b.top_p = None
+    gu.check_batch(verifier, b, torch_mod, label=f"large top-k {ks} {dtype}")
+
+
+def test_large_top_k_on_tie_rows(verifier, torch_mod):
+    """top-k 1500 and 3000 on bf16 rows on a coarse grid: the k-th value is
+    shared by many tokens (the bracket ends as one value and keeps them all)."""
+    b = _tie_batch("bf16", 30000, 571, flat=False)
+    b.top_k = np.resize(np.asarray([1500, 3000, 1100], np.int32), b.batch).astype(np.int32)
+    b.top_p = None
+    gu.check_batch(verifier, b, torch_mod, label="large top-k on tie rows")
+    b = _tie_batch("bf16", 30000, 572, flat=True)
+    b.top_k = np.resize(np.asarray([2000, 1030], np.int32), b.batch).astype(np.int32)
+    b.top_p = None
+    gu.check_batch(verifier, b, torch_mod, label="large top-k on flat tie rows")
