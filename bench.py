@@ -1,14 +1,18 @@
 """Throughput of the batched speculative-decoding verify step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--workload C3]
 
 A step is one call of the library's verify step (row statistics, then the
 acceptance scan and final draw) over one batch of a synthetic workload whose
 inputs are already resident in HBM.  R distinct input sets rotate so that the 256 MB
 last-level cache cannot serve repeated reads.  Prints one JSON line:
 
-  value       verified positions per second, sum_s (K_s + 1) per step
-  value       from the K timed steps, run without per-kernel events
+  value       verified positions per second, sum_s (K_s + 1) per step, from
+              the K timed steps, run without per-kernel events after the W
+              warm-up steps and an untimed settle of --settle-ms (the chip's
+              clocks rise over tens of milliseconds of sustained load);
+              ``warmup_ms_per_step`` is the W warm-up steps' own rate, on a
+              cold chip and with the first calls' costs
   roofline    the row-statistics kernel (the dominant one): algorithmic
               bytes per launch (every streamed logit row read once) over its
               mean duration from HIP events recorded around each kernel on
@@ -48,6 +52,7 @@ SHARD_WORKLOADS = {"C3D8": 8}
 FILTER_WORKLOADS = {"C3F": (50, 0.9), "C3P": (0, 0.95), "C3K": (2000, 1.0)}
 NGRAM_ROTATE = 32          # 32 x ~8.6 MB of histories: more than the 256 MB last-level cache
 ROTATE = {0: 64, 1: 64, 2: 6, 3: 2, 4: 6}
+SETTLE_SEED0 = 1 << 30     # seeds of the untimed settle steps: apart from the warm-up's and the timed steps'
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "row_stats_counters.json")
 NGRAM_COUNTERS_FILE = os.path.join(ROOT, "profiles", "ngram_counters.json")
 KERNEL_SOURCE = os.path.join(ROOT, "rejection_sampling_verify_06_amd", "csrc", "sv_kernels.hip")
@@ -64,6 +69,36 @@ def kernel_source_sha(path: str = KERNEL_SOURCE) -> str:
     lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
     code = "\n".join(ln for ln in lines if ln)
     return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
+def settle(step, k0: int, torch, min_ms: float, chunk: int = 10):
+    """Untimed steps after the warm-up until at least ``min_ms`` of wall time
+    has passed, synchronised every ``chunk`` steps so the queue stays short.
+    The GPU's clocks rise over some tens of milliseconds of sustained load and
+    fall again after a few milliseconds idle; a handful of warm-up steps
+    leaves a short timed region on a chip that is still ramping up, which a
+    serving loop running steps back to back never sees.  Returns (steps run,
+    wall ms)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(chunk):
+            step(k0 + n)
+            n += 1
+        torch.cuda.synchronize()
+    return n, round((time.perf_counter() - t0) * 1e3, 2)
+
+
+def timed_warmup(step, w: int, torch):
+    """The W warm-up steps, timed on their own (first calls and a cold chip
+    included): ms per step, or None for W = 0."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(w):
+        step(i)
+    torch.cuda.synchronize()
+    return round((time.perf_counter() - t0) * 1e3 / w, 5) if w else None
 
 
 def make_workload_batch(workload: str, step: int):
@@ -304,8 +339,8 @@ def bench_ngram(args):
     def step(i):
         prop.run_args(packed[i % R])
 
-    for i in range(args.warmup):
-        step(i)
+    warm_ms = timed_warmup(step, args.warmup, torch)
+    settled = settle(step, SETTLE_SEED0, torch, args.settle_ms)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -350,7 +385,8 @@ def bench_ngram(args):
         "metric": "N-gram proposals/sec (histories searched per second)", "value": round(float(seqs / (ms_step * 1e-3)), 1),
         "unit": "histories/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int32", "data": "synthetic",
+        "dtype": "int32", "data": "synthetic", "warmup_ms_per_step": warm_ms,
+        "settle": {"steps": settled[0], "ms": settled[1]},
         "config": {"workload": NGRAM_WORKLOAD, "histories": int(seqs), "tokens_per_step": int(toks),
                    "rotating_input_sets": R},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -392,8 +428,10 @@ def bench_stats(args):
         add()
         update()
 
-    for i in range(window + args.warmup):            # fill the windows, then warm up
+    for i in range(window):                          # fill the windows, then warm up
         step(i)
+    warm_ms = timed_warmup(lambda i: step(window + i), args.warmup, torch)
+    settled = settle(step, 0, torch, args.settle_ms)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -439,7 +477,8 @@ def bench_stats(args):
         "metric": "verify rounds/sec through acceptance statistics + draft-length controller",
         "value": round(B / (ms_step * 1e-3), 1), "unit": "rounds/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic", "warmup_ms_per_step": warm_ms,
+        "settle": {"steps": settled[0], "ms": settled[1]},
         "config": {"workload": ROUNDS_WORKLOAD, "rounds_per_call": B, "rotating_input_sets": R},
         "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(ach / PEAK_HBM_GBPS, 6), "traffic": None, "kernel": "k_adapt",
@@ -494,17 +533,8 @@ def measure_verify(workload: str, args, torch, sv) -> dict:
         packed[i % R].seed = i
         v.run_args(packed[i % R])
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # final-draw bytes depend on the outcome; measure them on the rotating sets
-    fin_b = []
-    for r in range(R):
-        fin_b.append(final_bytes(batches[r], outs[r]["accepted_len"].cpu().numpy()))
-        st = outs[r]["status"].cpu().numpy()
-        if (st & 127).any():
-            raise RuntimeError(f"{workload} input set {r}: unexpected status bits {np.unique(st)}")
+    warm_ms = timed_warmup(step, args.warmup, torch)
+    settled = settle(step, SETTLE_SEED0, torch, args.settle_ms)
 
     def timed(k0):
         torch.cuda.synchronize()
@@ -514,8 +544,19 @@ def measure_verify(workload: str, args, torch, sv) -> dict:
         torch.cuda.synchronize()
         return time.perf_counter() - t0
 
-    # the timed region: K steps, no per-kernel events (they add gaps)
+    # the timed region: K steps right after the warm-up and the settle, no per-kernel events (they add gaps)
     elapsed = timed(args.warmup)
+    # four more repetitions of the same K steps, for the median
+    reps_ms = [timed(args.warmup + args.steps * (r + 1)) * 1e3 / args.steps for r in range(4)]
+
+    # final-draw bytes depend on the outcome; measured on each rotating set's latest outputs (read back only
+    # now, so that no host work sits between the warm-up and the timed steps)
+    fin_b = []
+    for r in range(R):
+        fin_b.append(final_bytes(batches[r], outs[r]["accepted_len"].cpu().numpy()))
+        st = outs[r]["status"].cpu().numpy()
+        if (st & 127).any():
+            raise RuntimeError(f"{workload} input set {r}: unexpected status bits {np.unique(st)}")
     sets_used = [(args.warmup + i) % R for i in range(args.steps)]
     pos = np.mean([batches[r].positions for r in sets_used])
     stats_bytes = np.mean([row_bytes(batches[r])["row_stats"] for r in sets_used])
@@ -524,8 +565,7 @@ def measure_verify(workload: str, args, torch, sv) -> dict:
     early_bytes = np.mean([fin_b[r]["early_exit"] for r in sets_used])
     ms_step = elapsed * 1e3 / args.steps
     value = pos * args.steps / elapsed
-    # four more repetitions of the same K steps, for the median
-    reps = [ms_step] + [timed(args.warmup + args.steps * (r + 1)) * 1e3 / args.steps for r in range(4)]
+    reps = [ms_step] + reps_ms
 
     # per-kernel HIP events on the library's stream, K more steps
     events = not args.no_kernel_events
@@ -563,6 +603,8 @@ def measure_verify(workload: str, args, torch, sv) -> dict:
     res = {
         "workload": batches[0].name, "value": round(float(value), 1), "ms_per_step": round(ms_step, 5),
         "ms_per_step_median_of_5": round(float(np.median(reps)), 5),
+        "warmup_ms_per_step": warm_ms,
+        "settle": {"steps": settled[0], "ms": settled[1]},
         "config": {"workload": batches[0].name, "batch": desc["batch"], "k": desc["k"],
                    "vocab": desc["vocab"], "logits": desc["dtype"], "rotating_input_sets": R,
                    "positions_per_step": round(float(pos), 2)},
@@ -588,6 +630,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed steps after the W warm-up steps for at least this many ms, so the timed "
+                         "steps run at the clocks of sustained load (0: none)")
     ap.add_argument("--workload", default="C3", choices=sorted(WORKLOADS) + ["NG", "ST"],
                     help="C0..C4: the verify step; C3S: C3 in strict sample-match mode; C3F: C3 with top-k 50 "
                          "and top-p 0.9; C3P: C3 with top-p 0.95; C3K: C3 with top-k 2000; C3D8: one GPU's share of C3 split by sequence over 8 GPUs; "
@@ -639,8 +684,8 @@ def main():
     sub = {}
     for w in also:
         r = measure_verify(w, args, torch, sv)
-        sub[w] = {k: r[k] for k in ("workload", "value", "ms_per_step", "ms_per_step_median_of_5", "roofline",
-                                    "step_bytes", "kernel_ms")}
+        sub[w] = {k: r[k] for k in ("workload", "value", "ms_per_step", "ms_per_step_median_of_5",
+                                    "warmup_ms_per_step", "settle", "roofline", "step_bytes", "kernel_ms")}
         sub[w]["unit"] = "positions/s"
         sub[w]["positions_per_step"] = r["config"]["positions_per_step"]
 
@@ -659,6 +704,8 @@ def main():
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
         "ms_per_step_median_of_5": main_res["ms_per_step_median_of_5"],
+        "warmup_ms_per_step": main_res["warmup_ms_per_step"],
+        "settle": main_res["settle"],
         "step_bytes": main_res["step_bytes"],
         "step_traffic": main_res["step_traffic"],
         "cpu_baseline_parallel": cpu_par,
