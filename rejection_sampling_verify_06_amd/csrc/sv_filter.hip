@@ -164,10 +164,17 @@ struct BoundBufs {
   double zl[kWave];
 };
 
+// the value table of a bf16 row: keys of S slots, then per slot the token
+// counts of its chunks, 16 bits a chunk, two chunks a word
+struct ValueBufs {
+  uint32_t w[sizeof(HistBufs) / sizeof(uint32_t)];
+};
+
 struct FiltShared {
-  union {                      // the bounded selection runs before the histograms, never beside them
+  union {                      // the bounded selection, the value table and the histograms run one after another
     HistBufs hb;
     BoundBufs bb;
+    ValueBufs vt;
   };
   uint32_t hc[kBins];          // merged coarse histogram
   uint64_t hm[kBins];
@@ -200,6 +207,11 @@ struct FiltShared {
   float M;
   double zrow;                 // the row's mass against M, 2^-40 units, from the chunk partials
   int nk, ne, ni;
+  int vt_over;                 // value table: more distinct values than it takes
+  uint32_t vt_n;               // value table: distinct values inserted
+  uint32_t vt_tau;             // value table: the threshold key (0: none)
+  uint32_t vt_na;              // value table: tokens above the band
+  uint32_t vt_u16, vt_l16;     // value table: the band's keys
 };
 
 // The crossing of a 256-bin histogram, run by wave 0: bins in order
@@ -1438,6 +1450,409 @@ __device__ __forceinline__ bool bracket_search(FiltShared& sh, const char* rowp,
   return true;
 }
 
+// ---- value table and band (bf16 rows of at most kVTMaxChunks chunks) ----
+//
+// A bf16 row takes few distinct values where the thresholds can fall (128
+// per binade), and every token of one value weighs the same: a value's
+// fixed-point mass is its count times one token's, exactly.  The counts
+// live in an LDS hash table keyed by the 16-bit pattern (Fibonacci hashing
+// with a 24-bit multiply, linear probing, a slot claimed by
+// compare-and-swap; per slot 16-bit counts per chunk, two chunks a word,
+// laid out [chunk pair][slot]).  Every counted token costs LDS atomics, so
+// only a band of values around the crossing is counted in full:
+//   1. a sample read (the first 128 bytes of every 2 KB: 1/kVTSample of the
+//      row, whole cache lines) counts each value's tokens;
+//      a weighted radix select over the sample's values (counts for top-k,
+//      masses for top-p) names a band [l, u] of 16-bit keys that should
+//      hold the crossing: top-k ranks k/kVTSample +- 4 sqrt(k/kVTSample) + 2;
+//      top-p the values where the tail below holds (1 - p) Z +- a quarter of
+//      it (the tail: Z is known exactly, and the tail is the smaller mass to
+//      estimate);
+//   2. the full read sums, per chunk, the mass of the tokens above the band
+//      (float, per wave, then fixed point, as the bracket search's last pass
+//      does) and counts those above it; tokens in the band are counted per
+//      value and chunk; tokens below are dropped;
+//   3. the crossing must lie inside the band (mass or count above it below
+//      the target, with the band's reaching it); the band's values, sorted,
+//      then give the threshold exactly by the rules above -- top-k keeps a
+//      value with fewer than k tokens strictly above it, top-p alone one
+//      whose mass strictly above is below p * Z, the largest always -- and
+//      its kept values join the chunk sums as counts times masses.
+// -0 and +0 are two patterns with one key: for a single filter the
+// threshold key is the same whichever of the two entries a crossing falls
+// on, and the key comparison keeps or drops both together.  Top-p counts
+// the tokens with d <= kBinSpan only (a crossing past 2^-32 of the maximum's
+// weight is left to the other paths), top-k every finite token.  Rows that
+// start on 16 bytes only (then a round of vectors is exactly one chunk).
+// false (block-uniform), with the chunk sums zero: a table over seven
+// eighths full (its read stops at the next round), or the crossing outside
+// the band.
+constexpr int kVTWords = (int)(sizeof(ValueBufs) / sizeof(uint32_t));
+constexpr int kVTMaxChunks = 16;
+constexpr int kVTMinSlots = 256;
+constexpr int kVTSample = 16;                  // the sample read takes the first 128 bytes of every 2 KB
+constexpr uint32_t kVTEmpty = 0xFFFFFFFFu;     // not a 16-bit pattern
+constexpr uint32_t kVTGolden = 40503u;         // 2^16 / golden ratio
+static_assert(kChunkBytes / 2 == 1 << 14, "a bf16 token's chunk is its index >> 14");
+static_assert(kFThreads * kVecPer * 8 == 1 << 14, "a round of bf16 vectors is one chunk long");
+
+// the slot of pattern r whose home slot h held cur != r: probe on, claiming
+// an empty slot; kVTEmpty (and the overflow flag set) when the table is full
+__device__ __forceinline__ uint32_t vt_probe(FiltShared& sh, uint32_t* keys, uint32_t r, uint32_t h, uint32_t cur,
+                                             uint32_t smask, uint32_t limit) {
+  for (uint32_t steps = 0; cur != r;) {
+    if (cur == kVTEmpty) {
+      const uint32_t old = atomicCAS(&keys[h], kVTEmpty, r);
+      if (old == kVTEmpty) {                   // this lane claimed the slot
+        if (atomicAdd(&sh.vt_n, 1u) >= limit)
+          __hip_atomic_store(&sh.vt_over, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return h;
+      }
+      cur = old;                               // taken meanwhile: by this pattern, or another one
+      continue;
+    }
+    if (++steps > smask) {                     // every slot taken by other patterns
+      __hip_atomic_store(&sh.vt_over, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return kVTEmpty;
+    }
+    h = (h + 1u) & smask;
+    cur = __hip_atomic_load(&keys[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  return h;
+}
+
+// the 16-bit order-preserving key of a bf16 value (-0 and +0 alike)
+__device__ __forceinline__ uint32_t key16(float x) { return fkey(x) >> 16; }
+
+// the bf16 value whose 16-bit order-preserving key is k
+__device__ __forceinline__ float val16(uint32_t k) {
+  return __uint_as_float(((k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu)) << 16);
+}
+
+// the smallest bf16 value x with fmaf(-x, c, mc) <= dhi (d does not increase
+// with x), from an estimate and a few steps each way; NaN when not found
+__device__ __forceinline__ float bf16_floor_of(float dhi, float c, float mc) {
+  float v = __uint_as_float(__float_as_uint((mc - dhi) / c) & 0xFFFF0000u);
+  for (int i = 0; i < 4 && !(fmaf(-v, c, mc) <= dhi); ++i) v = bf16_step(v, 1);
+  for (int i = 0; i < 4 && fmaf(-bf16_step(v, -1), c, mc) <= dhi; ++i) v = bf16_step(v, -1);
+  if (!(fmaf(-v, c, mc) <= dhi) || fmaf(-bf16_step(v, -1), c, mc) <= dhi) return NAN;
+  return v;
+}
+
+template <bool BY_P>
+__device__ __forceinline__ bool value_filter(FiltShared& sh, const char* rowp, int V, int nch, float c, float mc,
+                                             int topk, float topp, uint32_t* tau_key) {
+  const int t = threadIdx.x, lane = t & (kWave - 1);
+  const int W = (nch + 1) >> 1;                // count words per slot
+  int S = 1024, lg = 10;                       // slots: the most that fit with their counts
+  while (S * (1 + W) > kVTWords) {
+    S >>= 1;
+    --lg;
+  }
+  const RowSplit sp = split_row<true>(rowp, V);
+  if (nch > kVTMaxChunks || S < kVTMinSlots || sp.head != 0 || sp.nvec < kFThreads ||
+      (BY_P ? !(topp > 0.f) : topk < 1))
+    return false;
+  // top-p counts the tokens at or above xw (d <= kBinSpan), top-k the finite ones
+  const float xw = BY_P ? bf16_floor_of(kBinSpan, c, mc) : -__FLT_MAX__;
+  if (!(xw == xw)) return false;               // (NaN: not found)
+  const uint32_t smask = (uint32_t)S - 1u, limit = (uint32_t)(S * 7 / 8);
+  uint32_t* keys = sh.vt.w;
+  uint32_t* cnts = sh.vt.w + S;                // word q of slot h at cnts[q * S + h]
+  const uint4* vp = (const uint4*)(rowp + (size_t)sp.head * 2);
+
+  auto clear_table = [&]() __attribute__((always_inline)) {
+    for (int i = t; i < S; i += kFThreads) keys[i] = kVTEmpty;
+    for (int i = t; i < S * W; i += kFThreads) cnts[i] = 0u;
+    if (t == 0) {
+      sh.vt_over = 0;
+      sh.vt_n = 0;
+      sh.vt_na = 0;
+      sh.ncand = 0;
+    }
+    __syncthreads();
+  };
+  // the slot of pattern r, inserted when new (kVTEmpty: the table is full)
+  auto slot = [&](uint32_t r) __attribute__((always_inline)) {
+    const uint32_t h = __builtin_amdgcn_ubfe(__umul24(r, kVTGolden), 16 - lg, lg);
+    const uint32_t cur = __hip_atomic_load(&keys[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return cur == r ? h : vt_probe(sh, keys, r, h, cur, smask, limit);
+  };
+  auto over = [&]() __attribute__((always_inline)) {
+    return uni(__hip_atomic_load(&sh.vt_over, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0;
+  };
+
+  // ---- 1. the sample: the first 128 bytes (8 vectors) of every 2 KB of the row, counts per value ----
+  clear_table();
+  const int ns = (sp.nvec >> 7) * 8 + min(sp.nvec & 127, 8);
+  for (int s0 = 0; s0 < ns; s0 += kFThreads * kVecPer) {
+    if (over()) break;
+    uint4 w[kVecPer];
+#pragma unroll
+    for (int u = 0; u < kVecPer; ++u) {
+      const int si = s0 + u * kFThreads + t;
+      w[u] = si < ns ? vp[(si >> 3) * 128 + (si & 7)] : make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
+    }
+#pragma unroll
+    for (int u = 0; u < kVecPer; ++u) {
+      const uint32_t q[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t r = (i & 1) ? (q[i >> 1] >> 16) : (q[i >> 1] & 0xFFFFu);
+        if (!(__uint_as_float(r << 16) >= xw)) continue;   // NaN and -inf too
+        const uint32_t h = slot(r);
+        if (h != kVTEmpty) atomicAdd(&cnts[h], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  if (uni(sh.vt_over)) {
+    __syncthreads();
+    return false;
+  }
+
+  // ---- 2. the band [l16, u16] from the sample: wave 0, a binary search over the keys ----
+  // (per slot its key and its weight -- count, or mass against the maximum -- in LDS first)
+  float* wf = reinterpret_cast<float*>(sh.cm);
+  for (int i = t; i < S; i += kFThreads) {
+    const uint32_t r = keys[i];
+    const float x = __uint_as_float(r << 16);
+    sh.ck[i] = r == kVTEmpty ? 0u : key16(x);
+    wf[i] = r == kVTEmpty ? 0.f : (float)cnts[i] * (BY_P ? fexp2(fmaf(x, c, -mc)) : 1.f);
+  }
+  __syncthreads();
+  if (t < kWave) {
+    // this lane's slots lane, lane + 64, ... in registers (S <= 1024: at most 16)
+    constexpr int kPer = 1024 / kWave;
+    uint32_t kr[kPer];
+    float wr[kPer];
+    float tot = 0.f;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = lane + j * kWave;
+      kr[j] = i < S ? sh.ck[i] : 0u;
+      wr[j] = i < S ? wf[i] : 0.f;
+      tot += wr[j];
+    }
+    tot = wave_sum(tot);
+    float tu, tl;                              // weights from the top where u and l are reached
+    if (BY_P) {
+      // the tail below the crossing holds (1 - p) Z; the band: a quarter of it either way
+      const float zt = (float)(sh.zrow / kMassOne), tail = (1.f - topp) * zt, m = 0.25f * tail;
+      tu = tot - (tail + m) / kVTSample;
+      tl = (tail - m) > 0.f ? tot - (tail - m) / kVTSample : tot * 2.f + 1.f;
+    } else {
+      const float ks = (float)topk / kVTSample, mk = 4.f * sqrtf(ks) + 2.f;
+      tu = ks - mk;
+      tl = ks + mk;
+    }
+    // the largest key k with (weight at or above k) >= the target, for both targets
+    uint32_t lu = 0, hu = 0xFFFFu, ll = 0, hl = 0xFFFFu;
+    for (int it = 0; it < 16; ++it) {
+      const uint32_t mu = (lu + hu + 1) >> 1, ml = (ll + hl + 1) >> 1;
+      float su = 0.f, sl = 0.f;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        su += kr[j] >= mu ? wr[j] : 0.f;
+        sl += kr[j] >= ml ? wr[j] : 0.f;
+      }
+      su = wave_sum(su);
+      sl = wave_sum(sl);
+      if (su >= tu) lu = mu; else hu = mu - 1;
+      if (sl >= tl) ll = ml; else hl = ml - 1;
+    }
+    if (lane == 0) {
+      sh.vt_u16 = (tu > 0.f && tu <= tot) ? lu : 0xFFFFu;   // reached at once (or never): from the top
+      sh.vt_l16 = tl <= tot ? ll : 0u;         // never reached: the band runs to the bottom
+    }
+  }
+  __syncthreads();
+  const uint32_t u16 = uni(sh.vt_u16), l16 = uni(sh.vt_l16);
+  const float xu = u16 >= 0xFFFFu ? INFINITY : val16(u16);   // above the band: x > xu
+  const float xl = fmaxf(l16 == 0u ? -__FLT_MAX__ : val16(l16), xw);   // in it: xl <= x <= xu
+
+  // ---- 3. the full read: mass (and count) above the band per chunk, the band's values per chunk ----
+  clear_table();
+  uint32_t na = 0;
+  auto band = [&](uint32_t r, int ch) __attribute__((always_inline)) {
+    const uint32_t h = slot(r);
+    if (h != kVTEmpty) atomicAdd(&cnts[(ch >> 1) * S + h], 1u << ((ch & 1) << 4));
+  };
+  for (int v0 = 0; v0 < sp.nvec; v0 += kFThreads * kVecPer) {
+    if (over()) break;
+    uint4 w[kVecPer];
+#pragma unroll
+    for (int u = 0; u < kVecPer; ++u) {
+      const int vi = v0 + u * kFThreads + t;
+      w[u] = vi < sp.nvec ? vp[vi] : make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
+    }
+    const int k0 = (v0 * 8) >> 14;             // (the row starts on 16 bytes: the round is chunk k0 exactly)
+    float ra = 0.f;
+#pragma unroll
+    for (int u = 0; u < kVecPer; ++u) {
+      const uint32_t q[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+      uint32_t bits = 0;                       // the vector's tokens in the band
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = __uint_as_float((i & 1) ? (q[i >> 1] & 0xFFFF0000u) : (q[i >> 1] << 16));
+        const bool above = x > xu;
+        ra += above ? fexp2(fmaf(x, c, -mc)) : 0.f;
+        if (!BY_P) na += above ? 1u : 0u;
+        bits |= (!above && x >= xl) ? (1u << i) : 0u;
+      }
+      // the sums are formed here, before the band's branch (else each test's mask is kept across it)
+      asm volatile("" : "+v"(ra), "+v"(na));
+      if (bits) {
+        const int e = (v0 + u * kFThreads + t) * 8;
+        const uint16_t* rp = (const uint16_t*)rowp;
+        while (bits) {
+          const int i = __builtin_ctz(bits);
+          bits &= bits - 1u;
+          band(rp[e + i], k0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);       // one vector's tests live at a time (no spilled masks)
+    }
+    const float wa = wave_sum(ra);               // every lane of the wave is here: a wave sum, one atomic
+    if (lane == 0 && wa != 0.f) atomicAdd(&sh.cs[k0], (unsigned long long)((double)wa * kMassOne));
+  }
+  for_singles<true>(rowp, sp, [&](const uint4(&w)[kVecPer], int v0) __attribute__((always_inline)) {
+    const int e = -1 - v0, ch = e >> 14;
+    const float x = vec_elem<true>(w[0], 0);
+    if (x > xu) {
+      atomicAdd(&sh.cs[ch], (unsigned long long)((double)fexp2(fmaf(x, c, -mc)) * kMassOne));
+      if (!BY_P) ++na;
+    } else if (x >= xl) {
+      band(__float_as_uint(x) >> 16, ch);
+    }
+  });
+  if (!BY_P) {
+    const uint32_t wn = wave_sum_u32(na);
+    if (lane == 0 && wn) atomicAdd(&sh.vt_na, wn);
+  }
+  __syncthreads();
+  auto fail = [&]() __attribute__((always_inline)) {
+    for (int k = t; k < kMaxChunks; k += kFThreads) sh.cs[k] = 0;
+    __syncthreads();
+    return false;
+  };
+  if (uni(sh.vt_over)) return fail();
+
+  // ---- 4. the band's values: exact weights from the top, the threshold ----
+  int32_t* pay = reinterpret_cast<int32_t*>(sh.cm);
+  for (int i = t; i < S; i += kFThreads) {     // whole waves: S is a multiple of 64
+    const uint32_t r = keys[i];
+    const uint32_t pos = claim_slot(&sh.ncand, r != kVTEmpty);
+    if (r != kVTEmpty) {
+      sh.ck[pos] = fkey(__uint_as_float(r << 16));
+      pay[pos] = i;
+    }
+  }
+  __syncthreads();
+  const int n = uni((int)sh.ncand);
+  if (n < 1) return fail();
+  auto cnt_of = [&](int i) __attribute__((always_inline)) {
+    const int h = pay[i];
+    uint32_t a = 0;
+    for (int q = 0; q < W; ++q) {
+      const uint32_t v = cnts[q * S + h];
+      a += (v & 0xFFFFu) + (v >> 16);
+    }
+    return a;
+  };
+  auto wgt_of = [&](int i) __attribute__((always_inline)) {
+    return BY_P ? (uint64_t)cnt_of(i) * fixed_mass_d(fmaf(-kval(sh.ck[i]), c, mc)) : (uint64_t)cnt_of(i);
+  };
+  const double target = BY_P ? (double)topp * sh.zrow : (double)topk;
+  if (n <= kWave) {
+    // few values (the usual band): lane i holds value i and sums the weights of the larger ones
+    if (t < kWave) {
+      uint64_t a0 = 0;                         // above the band: its mass (the chunk sums so far) or its count
+      if (BY_P) {
+        for (int k = 0; k < nch; ++k) a0 += sh.cs[k];
+      } else {
+        a0 = sh.vt_na;
+      }
+      const bool mine = lane < n;
+      const uint32_t ki = mine ? sh.ck[lane] : 0u;
+      const uint64_t wi = mine ? wgt_of(lane) : 0ull;
+      uint64_t before = 0, tot = 0;
+      for (int l = 0; l < kWave; ++l) {
+        const uint32_t kl = (uint32_t)__builtin_amdgcn_readlane((int)ki, l);
+        const uint32_t vl = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)wi, l);
+        const uint32_t vh = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(wi >> 32), l);
+        const uint64_t v = ((uint64_t)vh << 32) | vl;
+        before += kl > ki ? v : 0ull;
+        tot += v;
+      }
+      const double above = (double)a0;
+      const bool ok = above < target && above + (double)tot >= target;
+      const bool kept = ok && mine && ((BY_P && a0 == 0 && before == 0) || above + (double)before < target);
+      const uint32_t kmin = (uint32_t)wave_min_i((int)((kept ? ki : 0xFFFFFFFFu) ^ 0x80000000u)) ^ 0x80000000u;
+      if (lane == 0) sh.vt_tau = kmin == 0xFFFFFFFFu ? 0u : kmin;
+    }
+  } else {
+    int n2 = 2;
+    while (n2 < n) n2 <<= 1;
+    for (int i = n + t; i < n2; i += kFThreads) {
+      sh.ck[i] = 0u;
+      pay[i] = -1;
+    }
+    __syncthreads();
+    sort_desc(sh.ck, pay, n2);
+    if (t < kWave) {
+      const int per = (n + kWave - 1) / kWave;
+      const int lo = min(lane * per, n), hi = min(lo + per, n);
+      uint64_t a0 = 0;
+      if (BY_P) {
+        for (int k = 0; k < nch; ++k) a0 += sh.cs[k];
+      } else {
+        a0 = sh.vt_na;
+      }
+      uint64_t lw = 0;
+      for (int i = lo; i < hi; ++i) lw += wgt_of(i);
+      uint64_t before = 0, tot = 0;
+      for (int l = 0; l < kWave; ++l) {
+        const uint32_t vl = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lw, l);
+        const uint32_t vh = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(lw >> 32), l);
+        const uint64_t v = ((uint64_t)vh << 32) | vl;
+        before += (l < lane) ? v : 0ull;
+        tot += v;
+      }
+      const double above = (double)a0;
+      uint32_t kept = 0;
+      if (above < target && above + (double)tot >= target) {
+        for (int i = lo; i < hi; ++i) {
+          kept += ((BY_P && a0 == 0 && i == 0) || above + (double)before < target) ? 1u : 0u;
+          before += wgt_of(i);
+        }
+      }
+      const int nk = (int)wave_sum_u32(kept);
+      if (lane == 0) sh.vt_tau = nk >= 1 ? sh.ck[nk - 1] : 0u;
+    }
+  }
+  __syncthreads();
+  const uint32_t tk = uni(sh.vt_tau);
+  if (tk == 0u) return fail();
+
+  // ---- the band's kept values join the chunk sums: counts times masses ----
+  for (int i = t; i < S; i += kFThreads) {
+    const uint32_t r = keys[i];
+    if (r == kVTEmpty) continue;
+    const float x = __uint_as_float(r << 16);
+    if (fkey(x) < tk) continue;
+    const uint64_t f = fixed_mass_d(fmaf(-x, c, mc));
+    for (int q = 0; q < W; ++q) {
+      const uint32_t v = cnts[q * S + i];
+      if (v & 0xFFFFu) atomicAdd(&sh.cs[2 * q], (unsigned long long)((uint64_t)(v & 0xFFFFu) * f));
+      if (v >> 16) atomicAdd(&sh.cs[2 * q + 1], (unsigned long long)((uint64_t)(v >> 16) * f));
+    }
+  }
+  __syncthreads();
+  *tau_key = tk;
+  return true;
+}
+
 // The filter of one row (template on the row's element type).
 template <bool BF>
 __device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Partial* pp, const char* rowp, int nch,
@@ -1459,6 +1874,14 @@ __device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Part
       bounded_filter<BF>(sh, rowp, V, ce, c, mc, use_k, topk, use_p, topp, xs, segp, nch * kSegPerChunk, &bkey)) {
     write_partials(sh, pp, nch, M, kval(bkey), tau_out);
     return;
+  }
+  if constexpr (BF) {
+    if (xs < 0 && use_p != use_k &&
+        (use_p ? value_filter<true>(sh, rowp, V, nch, c, mc, 0, topp, &bkey)
+               : value_filter<false>(sh, rowp, V, nch, c, mc, topk, 1.f, &bkey))) {
+      write_partials(sh, pp, nch, M, kval(bkey), tau_out);
+      return;
+    }
   }
   if (use_p != use_k) {
     bool sums = false;

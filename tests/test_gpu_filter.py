@@ -236,9 +236,12 @@ def _flat_batch(dtype: str, V: int, seed: int, grid: int) -> Batch:
 @pytest.mark.parametrize("dtype,grid", [("bf16", 0), ("f32", 0), ("bf16", 4), ("f32", 8)])
 def test_topp_bracket_search_flat_rows(verifier, torch_mod, dtype, grid):
     """Top-p alone on rows whose nucleus the thread maxima cannot carry: the
-    bracket search's dense first pass, its binned passes, the end at one tied
-    bf16 value (grid 4) and the f32 tie group past the last pass (grid 8);
-    a second call gives bitwise the same outputs."""
+    bracket search's dense first pass, its binned passes and the f32 tie
+    group past the last pass (grid 8); bf16 rows of N(0, sigma) take more
+    distinct values than the value table holds and fall back to the bracket
+    search, bf16 rows on a grid of 1/4 take the value table (strict-mode
+    target rows take the bracket search either way); a second call gives
+    bitwise the same outputs."""
     b = _flat_batch(dtype, 100_000, 610 + grid + (dtype == "bf16"), grid)
     _, out, _ = gu.check_batch(verifier, b, torch_mod, label=f"top-p bracket search, flat rows {dtype} grid={grid}")
     again = gu.run_gpu(verifier, b, torch_mod)
@@ -291,11 +294,13 @@ def test_topk_heavy_tokens_in_one_segment(verifier, torch_mod, dtype):
 @pytest.mark.parametrize("dtype,V,ks", [("bf16", 152064, (1025, 2000, 5000)), ("f32", 40000, (1100, 3000, 30000)),
                                         ("bf16", 20000, (1500, 19999))])
 def test_large_top_k_count_bracket(verifier, torch_mod, dtype, V, ks):
-    """top-k above the bounded selection's 1024 tokens, alone: the count
-    bracket search (a first pass split at 8, 32, 128 log2 units below the
-    maximum, then even or binned passes) finds the k-th largest logit; every
-    mode, temperatures 0.3..1.5 (the k-th token far below the maximum at low
-    temperature)."""
+    """top-k above the bounded selection's 1024 tokens, alone: the value table
+    (bf16 rows, its band around the k-th largest from a sample) or the count
+    bracket search (f32 rows, strict-mode target rows, and bf16 rows with
+    more distinct values than the table holds: a first pass split at 8, 32,
+    128 log2 units below the maximum, then even or binned passes) finds the
+    k-th largest logit; every mode, temperatures 0.3..1.5 (the k-th token far
+    below the maximum at low temperature)."""
     b = make_random_batch(560 + V % 97, B=12, V=V, kmax=3, dtype=dtype, modes=ALL_MODES, temp=(0.3, 1.5))
     b.top_k = np.resize(np.asarray(ks, np.int32), b.batch).astype(np.int32)
     b.top_p = None
@@ -313,3 +318,60 @@ def test_large_top_k_on_tie_rows(verifier, torch_mod):
     b.top_k = np.resize(np.asarray([2000, 1030], np.int32), b.batch).astype(np.int32)
     b.top_p = None
     gu.check_batch(verifier, b, torch_mod, label="large top-k on flat tie rows")
+
+
+def _zipf_bf16_batch(seed: int, V: int, ld: int, B: int = 10) -> Batch:
+    """Zipf-shaped bf16 rows as in the benchmark workloads: -1.1 ln(rank) +
+    N(0, 1), randomly relabelled per row, draft = target + N(0, 0.7^2).  In
+    bf16 such a row takes a few hundred distinct values, the ones near a
+    top-p crossing shared by thousands of tokens.  K ~ U{1..3}, modes SAMPLE,
+    ONEHOT, GREEDY and STRICT, T ~ U[0.3, 1.5]; SAMPLE proposals are the draft
+    row's argmax or one of its 2000 largest tokens, the others the target
+    row's argmax or a random token."""
+    rng = np.random.default_rng(seed)
+    K = rng.integers(1, 4, size=B).astype(np.int32)
+    modes = rng.choice(np.asarray([MODE_SAMPLE, MODE_ONEHOT, MODE_GREEDY, MODE_STRICT], np.uint8), size=B)
+    temps = rng.uniform(0.3, 1.5, size=B).astype(np.float32)
+    base = (-1.1 * np.log(np.arange(1, V + 1, dtype=np.float64))).astype(np.float32)
+    n_t, n_d = int(K.sum()) + B, int(K.sum())
+    tgt = np.zeros((n_t, ld), np.float32)
+    dft = np.zeros((n_d, ld), np.float32)
+    toks = np.empty(n_d, np.int32)
+    rt = rd = 0
+    for s in range(B):
+        for i in range(int(K[s]) + 1):
+            t32 = bf16_widen(bf16_round(base[rng.permutation(V)] + rng.standard_normal(V).astype(np.float32)))
+            tgt[rt, :V] = t32
+            if i < K[s]:
+                d32 = bf16_widen(bf16_round(t32 + 0.7 * rng.standard_normal(V).astype(np.float32)))
+                dft[rd, :V] = d32
+                src = d32 if modes[s] == MODE_SAMPLE else t32
+                top = np.argpartition(-src, 2000)[:2000]
+                toks[rd] = int(src.argmax()) if rng.random() < 0.5 else int(rng.choice(top))
+                rd += 1
+            rt += 1
+    return Batch(name=f"zipf bf16 rows V={V} ld={ld}", vocab=V, dtype="bf16", target=bf16_round(tgt),
+                 draft=bf16_round(dft), num_draft=K, draft_tokens=toks, temperature=temps, mode=modes,
+                 seq_ids=np.arange(B, dtype=np.uint32), seed=seed, top_k=np.zeros(B, np.int32),
+                 top_p=np.ones(B, np.float32))
+
+
+@pytest.mark.parametrize("V,ld", [(152064, 152064), (100003, 100008)])
+@pytest.mark.parametrize("which", ["top_p", "top_k"])
+def test_value_table_zipf_rows(verifier, torch_mod, V, ld, which):
+    """bf16 rows with few distinct values and large tie groups, one filter per
+    sequence: the value table's sample, its band around the crossing, the
+    full read's counts and the exact threshold (top-p 0.5 .. 0.99, top-k
+    1025 .. 40000), the row tail past the last whole vector (V = 100003),
+    strict-mode target rows on the other paths; a second call gives bitwise
+    the same outputs."""
+    b = _zipf_bf16_batch(700 + V % 7 + (which == "top_k"), V, ld)
+    rng = np.random.default_rng(710 + V % 7)
+    if which == "top_p":
+        b.top_p = rng.choice(np.array([0.5, 0.9, 0.95, 0.99], np.float32), size=b.batch)
+    else:
+        b.top_k = rng.choice(np.array([1025, 2000, 5000, 40000], np.int32), size=b.batch)
+    _, out, _ = gu.check_batch(verifier, b, torch_mod, label=f"value table, zipf bf16 V={V} {which}")
+    again = gu.run_gpu(verifier, b, torch_mod)
+    for k in ("accepted_len", "emitted", "status"):
+        assert np.array_equal(out[k], again[k]), k
