@@ -1692,13 +1692,32 @@ __device__ __forceinline__ bool value_filter(FiltShared& sh, const char* rowp, i
     for (int u = 0; u < kVecPer; ++u) {
       const uint32_t q[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
       uint32_t bits = 0;                       // the vector's tokens in the band
+      if (BY_P) {
+        // top-p: about a third of a flat row lies above its band, so every token's weight is formed
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = __uint_as_float((i & 1) ? (q[i >> 1] & 0xFFFF0000u) : (q[i >> 1] << 16));
-        const bool above = x > xu;
-        ra += above ? fexp2(fmaf(x, c, -mc)) : 0.f;
-        if (!BY_P) na += above ? 1u : 0u;
-        bits |= (!above && x >= xl) ? (1u << i) : 0u;
+        for (int i = 0; i < 8; ++i) {
+          const float x = __uint_as_float((i & 1) ? (q[i >> 1] & 0xFFFF0000u) : (q[i >> 1] << 16));
+          const bool above = x > xu;
+          ra += above ? fexp2(fmaf(x, c, -mc)) : 0.f;
+          bits |= (!above && x >= xl) ? (1u << i) : 0u;
+        }
+      } else {
+        // top-k: few tokens lie above the band; their weights only, by their bits
+        uint32_t abits = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = __uint_as_float((i & 1) ? (q[i >> 1] & 0xFFFF0000u) : (q[i >> 1] << 16));
+          const bool above = x > xu;
+          abits |= above ? (1u << i) : 0u;
+          bits |= (!above && x >= xl) ? (1u << i) : 0u;
+        }
+        na += (uint32_t)__builtin_popcount(abits);
+        while (abits) {
+          const int i = __builtin_ctz(abits);
+          abits &= abits - 1u;
+          const uint32_t qq = (i >> 1) == 0 ? q[0] : (i >> 1) == 1 ? q[1] : (i >> 1) == 2 ? q[2] : q[3];
+          ra += fexp2(fmaf(__uint_as_float((i & 1) ? (qq & 0xFFFF0000u) : (qq << 16)), c, -mc));
+        }
       }
       // the sums are formed here, before the band's branch (else each test's mask is kept across it)
       asm volatile("" : "+v"(ra), "+v"(na));
