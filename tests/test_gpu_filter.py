@@ -375,3 +375,40 @@ def test_value_table_zipf_rows(verifier, torch_mod, V, ld, which):
     again = gu.run_gpu(verifier, b, torch_mod)
     for k in ("accepted_len", "emitted", "status"):
         assert np.array_equal(out[k], again[k]), k
+
+
+@pytest.mark.parametrize("V", [4104, 30000])
+@pytest.mark.parametrize("which", ["top_p", "top_k"])
+def test_value_table_signed_zero_and_masked_rows(verifier, torch_mod, V, which):
+    """bf16 rows (16-byte aligned) built so that the crossing falls in a tie
+    group of exact zeros stored half as +0 and half as -0 (two bit patterns,
+    one value: the value table must keep or drop both together): a few
+    positive tokens, about 40% zeros, the rest negative; a third of the rows
+    also masked to -inf over 30% of the vocabulary; temperatures 0.05 to 5;
+    V just above the table's smallest row and 30000."""
+    rng = np.random.default_rng(730 + V % 11 + (which == "top_k"))
+    b = make_random_batch(731 + V % 11, B=16, V=V, kmax=3, k_min=1, dtype="bf16", modes=ALL_MODES)
+    n_pos = max(8, V // 50)
+    for arr in (b.target, b.draft):
+        if arr is None:
+            continue
+        for r in range(arr.shape[0]):
+            row = np.empty(V, np.float32)
+            perm = rng.permutation(V)
+            n_zero = int(0.4 * V)
+            row[perm[:n_pos]] = rng.uniform(0.5, 3.0, size=n_pos)
+            zeros = perm[n_pos:n_pos + n_zero]
+            row[zeros] = np.where(rng.random(n_zero) < 0.5, np.float32(0.0), np.float32(-0.0))
+            rest = perm[n_pos + n_zero:]
+            row[rest] = rng.uniform(-5.0, -1.0, size=rest.size)
+            if r % 3 == 2:
+                row[rng.choice(V, int(0.3 * V), replace=False)] = -np.inf
+            arr[r, :V] = bf16_round(row)
+    b.temperature = rng.choice(np.array([0.05, 0.3, 1.0, 2.5, 5.0], np.float32), size=b.batch)
+    if which == "top_p":
+        b.top_p = rng.choice(np.array([0.3, 0.5, 0.9, 0.999], np.float32), size=b.batch)
+    else:
+        b.top_k = rng.choice(np.array([n_pos + 10, n_pos + V // 8, V // 2, V - 1], np.int32), size=b.batch)
+    neg_zero = int((b.target[:, :V] == 0x8000).sum())
+    assert neg_zero > 0, "the rows must hold -0 patterns"
+    gu.check_batch(verifier, b, torch_mod, label=f"value table, signed zeros and masked rows V={V} {which}")
