@@ -22,13 +22,20 @@
 //      thresholds among them (ranks, or a sort when there are many); the
 //      filtered chunk sums are the kept tokens' masses;
 //   B. when the bound cannot hold (top-k above 1024, maxima short of the
-//      top-p mass, more tokens than the LDS buffer), the histogram path: a
-//      coarse histogram of d = M*c - x*c in steps of 1/8 (log2 units; the
-//      last of 256 bins also takes everything below 2^-32 of the maximum)
-//      with integer LDS atomics, the bin holding the threshold, its
-//      elements compacted into LDS (or refined by a fine histogram), an
-//      exact radix select over their keys, and a pass for the chunk sums.
-// Either way the row's chunk partials are rewritten as filtered sums against
+//      top-p mass, more tokens than the LDS buffer) and one filter acts
+//      alone: on 16-byte aligned bf16 rows the value table (a sample picks a
+//      band of values around the crossing; one read counts the band's
+//      tokens per value and chunk in LDS and sums the mass above it; the
+//      threshold is exact among the band's values), else, or when the
+//      table cannot decide, the bracket search (passes that narrow a
+//      bracket of d holding the crossing, then one that collects it);
+//   C. the histogram path, for what the others leave: a coarse histogram
+//      of d = M*c - x*c in steps of 1/8 (log2 units; the last of 256 bins
+//      also takes everything below 2^-32 of the maximum) with integer LDS
+//      atomics, the bin holding the threshold, its elements compacted into
+//      LDS (or refined by a fine histogram), an exact radix select over
+//      their keys, and a pass for the chunk sums.
+// Every path rewrites the row's chunk partials as filtered sums against
 // M (and, for strict-mode target rows, the filtered part below the
 // proposal), and tau is stored for the scan and the final draw.  Masses are
 // exp2(x*c - M*c) in 2^-40 fixed point, summed as integers, so every result
