@@ -1618,7 +1618,7 @@ __device__ __forceinline__ bool value_filter(FiltShared& sh, const char* rowp, i
     return false;
   }
 
-  // ---- 2. the band [l16, u16] from the sample: wave 0, a binary search over the keys ----
+  // ---- 2. the band [l16, u16] from the sample: waves 0 and 1, a binary search over the keys each ----
   // (per slot its key and its weight -- count, or mass against the maximum -- in LDS first)
   float* wf = reinterpret_cast<float*>(sh.cm);
   for (int i = t; i < S; i += kFThreads) {
@@ -1628,8 +1628,9 @@ __device__ __forceinline__ bool value_filter(FiltShared& sh, const char* rowp, i
     wf[i] = r == kVTEmpty ? 0.f : (float)cnts[i] * (BY_P ? fexp2(fmaf(x, c, -mc)) : 1.f);
   }
   __syncthreads();
-  if (t < kWave) {
-    // this lane's slots lane, lane + 64, ... in registers (S <= 1024: at most 16)
+  if (t < 2 * kWave) {
+    // waves 0 and 1 search for u and l, each with this lane's slots lane, lane + 64, ... in registers
+    // (S <= 1024: at most 16)
     constexpr int kPer = 1024 / kWave;
     uint32_t kr[kPer];
     float wr[kPer];
@@ -1653,25 +1654,19 @@ __device__ __forceinline__ bool value_filter(FiltShared& sh, const char* rowp, i
       tu = ks - mk;
       tl = ks + mk;
     }
-    // the largest key k with (weight at or above k) >= the target, for both targets
-    uint32_t lu = 0, hu = 0xFFFFu, ll = 0, hl = 0xFFFFu;
+    // the largest key k with (weight at or above k) >= the wave's target
+    const float tt = t < kWave ? tu : tl;
+    uint32_t lo = 0, hi = 0xFFFFu;
     for (int it = 0; it < 16; ++it) {
-      const uint32_t mu = (lu + hu + 1) >> 1, ml = (ll + hl + 1) >> 1;
-      float su = 0.f, sl = 0.f;
+      const uint32_t mid = (lo + hi + 1) >> 1;
+      float sm = 0.f;
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        su += kr[j] >= mu ? wr[j] : 0.f;
-        sl += kr[j] >= ml ? wr[j] : 0.f;
-      }
-      su = wave_sum(su);
-      sl = wave_sum(sl);
-      if (su >= tu) lu = mu; else hu = mu - 1;
-      if (sl >= tl) ll = ml; else hl = ml - 1;
+      for (int j = 0; j < kPer; ++j) sm += kr[j] >= mid ? wr[j] : 0.f;
+      sm = wave_sum(sm);
+      if (sm >= tt) lo = mid; else hi = mid - 1;
     }
-    if (lane == 0) {
-      sh.vt_u16 = (tu > 0.f && tu <= tot) ? lu : 0xFFFFu;   // reached at once (or never): from the top
-      sh.vt_l16 = tl <= tot ? ll : 0u;         // never reached: the band runs to the bottom
-    }
+    if (t == 0) sh.vt_u16 = (tu > 0.f && tu <= tot) ? lo : 0xFFFFu;   // reached at once (or never): from the top
+    if (t == kWave) sh.vt_l16 = tl <= tot ? lo : 0u;                 // never reached: the band runs to the bottom
   }
   __syncthreads();
   const uint32_t u16 = uni(sh.vt_u16), l16 = uni(sh.vt_l16);
