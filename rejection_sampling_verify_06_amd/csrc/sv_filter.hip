@@ -1468,10 +1468,11 @@ __device__ __forceinline__ bool bracket_search(FiltShared& sh, const char* rowp,
 // laid out [chunk pair][slot]).  Every counted token costs LDS atomics, so
 // only a band of values around the crossing is counted in full:
 //   1. a sample read (the first 128 bytes of every 2 KB: 1/kVTSample of the
-//      row, whole cache lines) counts each value's tokens;
-//      a weighted radix select over the sample's values (counts for top-k,
-//      masses for top-p) names a band [l, u] of 16-bit keys that should
-//      hold the crossing: top-k ranks k/kVTSample +- 4 sqrt(k/kVTSample) + 2;
+//      row, whole cache lines) counts each value's tokens; two binary
+//      searches over the 16-bit keys, one a wave, weigh the sample's values
+//      (counts for top-k, masses for top-p) and name a band [l, u] of keys
+//      that should hold the crossing: top-k ranks k/kVTSample +-
+//      (4 sqrt(k/kVTSample) + 2);
 //      top-p the values where the tail below holds (1 - p) Z +- a quarter of
 //      it (the tail: Z is known exactly, and the tail is the smaller mass to
 //      estimate);
@@ -1480,8 +1481,9 @@ __device__ __forceinline__ bool bracket_search(FiltShared& sh, const char* rowp,
 //      does) and counts those above it; tokens in the band are counted per
 //      value and chunk; tokens below are dropped;
 //   3. the crossing must lie inside the band (mass or count above it below
-//      the target, with the band's reaching it); the band's values, sorted,
-//      then give the threshold exactly by the rules above -- top-k keeps a
+//      the target, with the band's reaching it); the band's values, ranked
+//      by wave 0 (up to 64 of them; sorted beyond), then give the threshold
+//      exactly by the rules above -- top-k keeps a
 //      value with fewer than k tokens strictly above it, top-p alone one
 //      whose mass strictly above is below p * Z, the largest always -- and
 //      its kept values join the chunk sums as counts times masses.
