@@ -108,7 +108,7 @@ def test_c3_with_filters_bench_context(torch_mod):
     import rejection_sampling_verify_06_amd as sv
     v = sv.Verifier(max_batch=256, max_k=8, max_vocab=152064, device=0)
     try:
-        for step, (k, p) in enumerate([(50, 0.9), (0, 0.95)]):
+        for step, (k, p) in enumerate([(50, 0.9), (0, 0.95), (2000, 1.0)]):
             b = make_config_batch(3, step)
             b.top_k = np.full(b.batch, k, np.int32)
             b.top_p = np.full(b.batch, p, np.float32)
