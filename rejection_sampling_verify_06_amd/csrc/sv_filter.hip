@@ -546,6 +546,55 @@ __device__ __forceinline__ void for_rounds(const uint4* vp, int vb, int ve, F&& 
   }
 }
 
+// Rounds of 16-byte vectors [vb, ve) (vb a multiple of kFThreads * kVecPer,
+// vb < ve), the first round's vectors already in w: f(w, v0) per round.
+// Each round's loads are issued before the previous round is passed to f,
+// and every load is issued (indices clamped into [0, ve), so the last
+// round's loads are issued twice): the wait before f then covers that
+// round's loads only.  f sees vectors at or past ve as NaN, and must load
+// nothing from global memory itself (such a load would wait for the next
+// round's too).
+template <typename F>
+__device__ __forceinline__ void for_rounds_pipe(const uint4* vp, uint4 (&w)[kVecPer], int vb, int ve, F&& f) {
+  constexpr int kRound = kFThreads * kVecPer;
+  const int t = threadIdx.x;
+  const int last = ((ve - 1) / kRound) * kRound;
+  for (int v0 = vb; v0 < ve; v0 += kRound) {
+    uint4 nx[kVecPer];
+    const int vn = min(v0 + kRound, last);
+#pragma unroll
+    for (int u = 0; u < kVecPer; ++u) nx[u] = vp[min(vn + u * kFThreads + t, ve - 1)];
+    if (v0 == last) {
+#pragma unroll
+      for (int u = 0; u < kVecPer; ++u)
+        if (v0 + u * kFThreads + t >= ve) w[u] = make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
+    }
+    f(w, v0);
+#pragma unroll
+    for (int u = 0; u < kVecPer; ++u) w[u] = nx[u];
+  }
+}
+
+// element b of a round (vector b / epv, element b % epv), from the
+// registers: a tree of selects over the round's 16 words held as separate
+// scalars (selects between elements of one array would be folded into a
+// run-time index, which places the array in memory)
+template <bool BF>
+__device__ __forceinline__ float round_elem(const uint4 (&w)[kVecPer], int b) {
+  static_assert(kVecPer == 4, "16 words a round");
+  const int wi = BF ? (b >> 1) : b;
+  const bool b0 = wi & 1, b1 = wi & 2, b2 = wi & 4, b3 = wi & 8;
+  const uint32_t p0 = b0 ? w[0].y : w[0].x, p1 = b0 ? w[0].w : w[0].z;
+  const uint32_t p2 = b0 ? w[1].y : w[1].x, p3 = b0 ? w[1].w : w[1].z;
+  const uint32_t p4 = b0 ? w[2].y : w[2].x, p5 = b0 ? w[2].w : w[2].z;
+  const uint32_t p6 = b0 ? w[3].y : w[3].x, p7 = b0 ? w[3].w : w[3].z;
+  const uint32_t q0 = b1 ? p1 : p0, q1 = b1 ? p3 : p2, q2 = b1 ? p5 : p4, q3 = b1 ? p7 : p6;
+  const uint32_t r0 = b2 ? q1 : q0, r1 = b2 ? q3 : q2;
+  const uint32_t wd = b3 ? r1 : r0;
+  if (!BF) return __uint_as_float(wd);
+  return __uint_as_float((b & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+}
+
 // the head and tail elements of a row split: f(w, -1 - e) with element e as
 // element 0 of w[0] and NaN everywhere else, by the first head + tail threads
 template <bool BF, typename F>
@@ -882,15 +931,14 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
         hit &= hit - 1;
         const int e = elem_index<BF>(sp, v0, b / epv, b % epv);
         if (pos < (uint32_t)kCap) {
-          sh.ck[pos] = fkey(load_x<BF>(rowp, e));
+          sh.ck[pos] = fkey(round_elem<BF>(w, b));
           sh.bb.ci[pos] = e;
         }
         ++pos;
       }
     }
   };
-  collect(w0, 0);
-  for_rounds(vp, kRound, sp.nvec, collect);
+  if (sp.nvec > 0) for_rounds_pipe(vp, w0, 0, sp.nvec, collect);
   for_singles<BF>(rowp, sp, collect);
   __syncthreads();
   const int n = uni((int)sh.ncand);
@@ -1356,7 +1404,7 @@ __device__ __forceinline__ bool bracket_search(FiltShared& sh, const char* rowp,
         hit &= hit - 1;
         const int e = elem_index<BF>(sp, v0, b / epv, b % epv);
         if (pos < (uint32_t)kCap) {
-          sh.ck[pos] = fkey(load_x<BF>(rowp, e));
+          sh.ck[pos] = fkey(round_elem<BF>(w, b));
           sh.bb.ci[pos] = e;
         }
         ++pos;
@@ -1682,13 +1730,25 @@ __device__ __forceinline__ bool value_filter(FiltShared& sh, const char* rowp, i
     const uint32_t h = slot(r);
     if (h != kVTEmpty) atomicAdd(&cnts[(ch >> 1) * S + h], 1u << ((ch & 1) << 4));
   };
-  for (int v0 = 0; v0 < sp.nvec; v0 += kFThreads * kVecPer) {
-    if (over()) break;
-    uint4 w[kVecPer];
+  // A round's vectors.  The next round's loads are issued before this round
+  // is counted; every load is issued (indices clamped into the row, so the
+  // last round's is issued again), which lets the wait before the counting
+  // cover this round's loads only; vectors past the row become NaN when used.
+  constexpr int kRound = kFThreads * kVecPer;
+  const int last_v0 = ((sp.nvec - 1) / kRound) * kRound;
+  auto load_round = [&](int v0, uint4(&dst)[kVecPer]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < kVecPer; ++u) {
-      const int vi = v0 + u * kFThreads + t;
-      w[u] = vi < sp.nvec ? vp[vi] : make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
+    for (int u = 0; u < kVecPer; ++u) dst[u] = vp[min(v0 + u * kFThreads + t, sp.nvec - 1)];
+  };
+  uint4 w[kVecPer], nx[kVecPer];
+  load_round(0, w);
+  for (int v0 = 0; v0 < sp.nvec; v0 += kRound) {
+    if (over()) break;
+    load_round(min(v0 + kRound, last_v0), nx);
+    if (v0 == last_v0) {
+#pragma unroll
+      for (int u = 0; u < kVecPer; ++u)
+        if (v0 + u * kFThreads + t >= sp.nvec) w[u] = make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
     }
     const int k0 = (v0 * 8) >> 14;             // (the row starts on 16 bytes: the round is chunk k0 exactly)
     float ra = 0.f;
@@ -1725,19 +1785,19 @@ __device__ __forceinline__ bool value_filter(FiltShared& sh, const char* rowp, i
       }
       // the sums are formed here, before the band's branch (else each test's mask is kept across it)
       asm volatile("" : "+v"(ra), "+v"(na));
-      if (bits) {
-        const int e = (v0 + u * kFThreads + t) * 8;
-        const uint16_t* rp = (const uint16_t*)rowp;
-        while (bits) {
-          const int i = __builtin_ctz(bits);
-          bits &= bits - 1u;
-          band(rp[e + i], k0);
-        }
+      // a band token's pattern comes from the registers (a load here would wait for the next round's)
+      while (bits) {
+        const int i = __builtin_ctz(bits);
+        bits &= bits - 1u;
+        const uint32_t qq = (i >> 1) == 0 ? q[0] : (i >> 1) == 1 ? q[1] : (i >> 1) == 2 ? q[2] : q[3];
+        band((i & 1) ? (qq >> 16) : (qq & 0xFFFFu), k0);
       }
       __builtin_amdgcn_sched_barrier(0);       // one vector's tests live at a time (no spilled masks)
     }
     const float wa = wave_sum(ra);               // every lane of the wave is here: a wave sum, one atomic
     if (lane == 0 && wa != 0.f) atomicAdd(&sh.cs[k0], (unsigned long long)((double)wa * kMassOne));
+#pragma unroll
+    for (int u = 0; u < kVecPer; ++u) w[u] = nx[u];
   }
   for_singles<true>(rowp, sp, [&](const uint4(&w)[kVecPer], int v0) __attribute__((always_inline)) {
     const int e = -1 - v0, ch = e >> 14;
