@@ -98,6 +98,7 @@ ScratchLayout scratch_layout(int32_t max_batch, int32_t max_k, int64_t max_rows,
   L.o_tile = off;  off = align_up(off + sizeof(float) * (size_t)max_batch * max_tiles, 256);
   L.o_cnt = off;   off = align_up(off + sizeof(uint32_t) * (size_t)max_batch, 256);
   L.o_ord = off;   off = align_up(off + sizeof(int32_t) * (size_t)max_batch, 256);
+  L.o_flist = off; off = align_up(off + sizeof(int32_t) * ((size_t)max_rows + 1), 256);
   L.o_seg = off;
   if (with_segmax) off = align_up(off + sizeof(float) * kSegPerChunk * max_rows * max_nch, 256);
   L.bytes = off;
@@ -115,6 +116,7 @@ Scratch scratch_at(void* base, const ScratchLayout& L, bool with_segmax) {
   v.tilesum = (float*)(b + L.o_tile);
   v.fincnt = (uint32_t*)(b + L.o_cnt);
   v.order = (int32_t*)(b + L.o_ord);
+  v.flist = (int32_t*)(b + L.o_flist);
   v.segmax = with_segmax ? (float*)(b + L.o_seg) : nullptr;
   return v;
 }
@@ -227,6 +229,7 @@ int prepare_call(const char* who, const spec_verify_args* a, const Caps& c, cons
   p.xval = v.xval;
   p.tau = v.tau;
   p.order = v.order;
+  p.flist = v.flist;
   const bool filtered = a->top_k || a->top_p;
   p.order_block = filtered ? 1 : 0;
   p.segmax = filtered ? v.segmax : nullptr;   // filter bounds from row_stats' segment maxima

@@ -1983,10 +1983,8 @@ __device__ __forceinline__ void filter_row(const Params& P, FiltShared& sh, Part
 
 }  // namespace
 
-// four blocks per CU (8 waves per SIMD): at most 64 VGPRs
-__global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) k_filter(Params P) {
-  __shared__ FiltShared sh;
-  const int r = blockIdx.x, s = P.order[blockIdx.y];   // the sequence order written by row_stats
+// The filter of sequence slot (s, r); every return is block-uniform.
+__device__ __forceinline__ void filter_slot(const Params& P, FiltShared& sh, int s, int r) {
   const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
   const int mk = P.max_k;
   const int K = P.num_draft[s];
@@ -2071,9 +2069,22 @@ __global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(
     filter_row<false>(P, sh, pp, rowp, nch, ce, c, mc, M, use_k, topk, use_p, topp, xs, segp, tau_out);
 }
 
+// One block per row of the list row_stats wrote (the filter's rows, costliest
+// first; blocks past its count return at once); four blocks per CU (8 waves
+// per SIMD: at most 64 VGPRs).
+__global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) k_filter(Params P) {
+  __shared__ FiltShared sh;
+  const int i = blockIdx.x;
+  if (i >= P.flist[P.n_t + P.n_d]) return;
+  const int sl = P.flist[i];
+  const int s = sl / P.slots;
+  filter_slot(P, sh, s, sl - s * P.slots);
+}
+
 hipError_t launch_filter(const Params& p, hipStream_t st, const LaunchEvents* ev) {
-  if (p.B <= 0 || (!p.top_k && !p.top_p)) return record_empty(st, ev);
-  launch_timed(k_filter, dim3(p.slots, p.B), dim3(kFThreads), st, ev, p);
+  const int rows = p.n_t + p.n_d;
+  if (p.B <= 0 || (!p.top_k && !p.top_p) || rows <= 0) return record_empty(st, ev);
+  launch_timed(k_filter, dim3(rows), dim3(kFThreads), st, ev, p);
   return hipGetLastError();
 }
 

@@ -109,6 +109,8 @@ struct Params {
   const float* top_p;     // [B] or NULL: top-p filter (>= 1 or NaN: off)
   float* tau;             // per slot: the filter threshold (written only for filtered sequences)
   int32_t* order;         // [B]: the filter's sequence order (a permutation, costliest first)
+  int32_t* flist;         // [n_t + n_d + 1]: the filter's rows in that order (slot s * slots + r), their
+                          // number in the last entry (written by row_stats' order block)
   int32_t order_block;    // 1: row_stats' block 0 writes `order` (filtered calls), its other blocks shift by one
 };
 
@@ -208,6 +210,7 @@ struct Scratch {
   float* xval;
   float* tau;
   int32_t* order;
+  int32_t* flist;
   int32_t* ptok;
   SeqFinal* fin;
   float* tilesum;
@@ -219,7 +222,7 @@ struct Scratch {
 
 // Byte offsets of the scratch arrays for the given sizes (256-byte aligned).
 struct ScratchLayout {
-  size_t o_part, o_xval, o_tau, o_ptok, o_fin, o_tile, o_cnt, o_ord, o_seg, bytes;
+  size_t o_part, o_xval, o_tau, o_ptok, o_fin, o_tile, o_cnt, o_ord, o_flist, o_seg, bytes;
 };
 
 Caps caps_for(int32_t max_batch, int32_t max_k, int64_t max_vocab);

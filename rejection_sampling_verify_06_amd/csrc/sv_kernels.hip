@@ -1140,6 +1140,51 @@ __device__ __forceinline__ void filter_order(const Params& P) {
   }
   __syncthreads();
   for (int s = t; s < P.B; s += kThreads) P.order[atomicAdd(&cnt[order_bucket(P, s)], 1u)] = s;
+  __syncthreads();
+  // The filter's rows in this order, as sequence slots s * slots + r: the
+  // rows the filter kernel takes (target rows 0..K, then draft rows of a
+  // SAMPLE sequence), none of a sequence it would skip; the count follows the
+  // list (n_t + n_d entries at most: a num_draft that does not add up to
+  // total_draft, which the scan reports, could ask for more).  Thread t lists
+  // the sequences at order positions [i0, i1).
+  __shared__ uint32_t part[kThreads];
+  auto nrows = [&](int s) __attribute__((always_inline)) {
+    const int K = P.num_draft[s];
+    const int md = P.mode[s];
+    const int topk = P.top_k ? P.top_k[s] : 0;
+    const float topp = P.top_p ? P.top_p[s] : 1.f;
+    const float T = P.temperature[s];
+    if (K < 0 || K > P.max_k || md == kGreedy || !((topk > 0 && topk < P.V) || topp < 1.f) ||
+        !(isfinite(T) && T >= kMinTemperature))
+      return 0;
+    return K + 1 + ((md == kSample && P.dft) ? K : 0);
+  };
+  const int per = (P.B + kThreads - 1) / kThreads;
+  const int i0 = min(t * per, P.B), i1 = min(i0 + per, P.B);
+  uint32_t n = 0;
+  for (int i = i0; i < i1; ++i) n += (uint32_t)nrows(P.order[i]);
+  part[t] = n;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t acc = 0;
+    for (int q = 0; q < kThreads; ++q) {
+      const uint32_t m = part[q];
+      part[q] = acc;
+      acc += m;
+    }
+    const uint32_t cap = (uint32_t)(P.n_t + P.n_d);
+    P.flist[cap] = (int32_t)(acc < cap ? acc : cap);
+  }
+  __syncthreads();
+  uint32_t at = part[t];
+  for (int i = i0; i < i1; ++i) {
+    const int s = P.order[i];
+    const int k = nrows(s), K = P.num_draft[s];
+    for (int j = 0; j < k; ++j)
+      if (at + (uint32_t)j < (uint32_t)(P.n_t + P.n_d))
+        P.flist[at + j] = s * P.slots + (j <= K ? j : P.max_k + 1 + (j - K - 1));
+    at += (uint32_t)k;
+  }
 }
 
 }  // namespace
