@@ -150,7 +150,8 @@ typedef struct spec_verify_args {
  * filters, 16 segment maxima per chunk; per-sequence final-draw records
  * and tile sums; defaults for NULL optional inputs): about 80 bytes per 8192
  * vocabulary entries per row slot, max_batch * (2 * max_k + 1) slots, plus
- * small per-sequence arrays.  The caller owns every input and output
+ * small per-slot and per-sequence arrays (among them the filter's list of
+ * rows).  The caller owns every input and output
  * buffer.  Returns SV_OK and sets *out, or an error code (then *out = NULL). */
 int spec_verify_create(spec_verify_ctx** out, int device, int32_t max_batch, int32_t max_k, int64_t max_vocab);
 
