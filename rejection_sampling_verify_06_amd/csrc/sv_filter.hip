@@ -1679,6 +1679,9 @@ __device__ __forceinline__ bool value_filter(FiltShared& sh, const char* rowp, i
   }
   __syncthreads();
   if (t < 2 * kWave) {
+    // (at raised issue priority: the block's other waves wait, while the
+    // CU's other blocks stream)
+    __builtin_amdgcn_s_setprio(3);
     // waves 0 and 1 search for u and l, each with this lane's slots lane, lane + 64, ... in registers
     // (S <= 1024: at most 16)
     constexpr int kPer = 1024 / kWave;
@@ -1717,6 +1720,7 @@ __device__ __forceinline__ bool value_filter(FiltShared& sh, const char* rowp, i
     }
     if (t == 0) sh.vt_u16 = (tu > 0.f && tu <= tot) ? lo : 0xFFFFu;   // reached at once (or never): from the top
     if (t == kWave) sh.vt_l16 = tl <= tot ? lo : 0u;                 // never reached: the band runs to the bottom
+    __builtin_amdgcn_s_setprio(0);
   }
   __syncthreads();
   const uint32_t u16 = uni(sh.vt_u16), l16 = uni(sh.vt_l16);
@@ -2005,6 +2009,7 @@ __device__ __forceinline__ void filter_slot(const Params& P, FiltShared& sh, int
   const int nch = draft ? P.nch_d : P.nch_t;
   Partial* pp = P.partials + ((int64_t)s * P.slots + r) * P.nch_max;
   if (wv == 0) {
+    __builtin_amdgcn_s_setprio(3);           // the block's other waves wait for this one
     // the packed layout (as the scan checks it) and this sequence's offset
     uint32_t tot = 0, bef = 0;
     int oor = 0;
@@ -2041,6 +2046,7 @@ __device__ __forceinline__ void filter_slot(const Params& P, FiltShared& sh, int
       sh.M = m;
       sh.zrow = z * kMassOne;
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   __syncthreads();
   if (!uni(sh.ok)) return;                   // the scan reports the layout
