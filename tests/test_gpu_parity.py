@@ -161,11 +161,19 @@ def test_sample_without_draft_logits(verifier, torch_mod):
     assert ((out["status"] == 16) == ((b.mode == MODE_SAMPLE) & (b.num_draft > 0))).all()
 
 
-@pytest.mark.parametrize("nd", [[2, 3], [-1, 5]])
-def test_bad_layout(verifier, torch_mod, nd):
+@pytest.mark.parametrize("nd,filtered", [([2, 3], False), ([-1, 5], False), ([2, 3], True), ([-1, 5], True),
+                                         ([8, 8], True)])
+def test_bad_layout(verifier, torch_mod, nd, filtered):
+    """num_draft that does not add up to total_draft: every output cleared,
+    status SV_ST_BAD_LAYOUT.  With filters, the filter's row list that row
+    statistics writes is clamped to the n_t + n_d rows the call has (K = 8
+    and 8 against total_draft 4 asks for 34 rows of 10)."""
     b = make_random_batch(33, B=2, V=50, kmax=2, k_min=2, dtype="f32")
     assert b.total_draft == 4
     b.num_draft = np.array(nd, np.int32)
+    if filtered:
+        b.top_k = np.array([5, 0], np.int32)
+        b.top_p = np.array([0.9, 0.8], np.float32)
     out = gu.run_gpu(verifier, b, torch_mod, total_draft=4)
     ref = gu.oracle_for(b, MAX_K, total_draft=4)
     assert not ref.layout_ok
