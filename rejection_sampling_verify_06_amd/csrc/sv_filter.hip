@@ -11,8 +11,10 @@
 // after top-k, keeps a token iff the mass of the strictly larger tokens is
 // below p (the largest logit always kept).
 //
-// One 512-thread block per used slot of a filtered sequence, after the row
-// statistics (four blocks per CU).  The row maximum M comes from the row's
+// One 512-thread block per used row of a filtered sequence, after the row
+// statistics (four blocks per CU), in the order of the list that row
+// statistics' first block writes (the sequences by temperature, the flattest
+// rows, whose filter costs most, first).  The row maximum M comes from the row's
 // chunk partials (for top-p alone, also the row's mass).  Then:
 //   A. the bounded selection (two reads of the row, no per-element atomics):
 //      every thread's two largest logits over a sample of the row (top-k)

@@ -7,7 +7,9 @@
 //             reduced in float32 to (max of the raw logits, sum of
 //             exp2(x*c - round(max*c)), lowest-index argmax for greedy rows):
 //             block max first, then one sum against it.  No inter-block
-//             communication.
+//             communication.  In a filtered call one more block (the first)
+//             orders the sequences by temperature and writes the list of the
+//             rows the filter kernel takes, in that order.
 // final       grid (nsplit, B) of 1024-thread blocks.  Wave 0 runs the
 //             acceptance scan of its sequence: validates it, merges each
 //             row's chunk partials in chunk order (lane r: row r), computes
@@ -1205,7 +1207,7 @@ __global__ void __launch_bounds__(kThreads) k_row_stats(Params P) {
     for (int i = threadIdx.x; i < P.B; i += kThreads) P.fincnt[i] = 0u;
   }
   int b = (int)lin;
-  if (P.order_block) {            // a filtered call: block 0 orders the filter's rows
+  if (P.order_block) {            // a filtered call: block 0 lists the filter's rows
     if (b == 0) {
       filter_order(P);
       return;
