@@ -216,6 +216,7 @@ struct FiltShared {
   float M;
   double zrow;                 // the row's mass against M, 2^-40 units, from the chunk partials
   int nk, ne, ni;
+  uint32_t nsegc;              // bounded selection: segments whose maximum reaches the bound (listed in hc)
   int vt_over;                 // value table: more distinct values than it takes
   uint32_t vt_n;               // value table: distinct values inserted
   uint32_t vt_tau;             // value table: the threshold key (0: none)
@@ -531,6 +532,13 @@ __device__ __forceinline__ float vec_elem(const uint4& w, int j) {
   return __uint_as_float((j & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
 }
 constexpr uint32_t kNanFill = 0x7FC07FC0u;     // NaN as one fp32 word and as two bf16 halves
+// a row-statistics segment (the 16-lane group that wrote its maximum): 8 runs
+// of 16 vectors, kThreads vectors apart, in a chunk of 2048 16-byte vectors
+constexpr int kChunkVecs = kChunkBytes / 16;
+constexpr int kSegRun = kThreads / kSegPerChunk;
+constexpr int kSegVecs = kChunkVecs / kSegPerChunk;
+constexpr int kSegRound = kFThreads * kVecPer / kSegVecs;   // segments a round of the bounded selection's read 2
+static_assert(kSegRun == 16 && kSegVecs == 128 && kSegRound == 16, "the row statistics' segment layout");
 
 // rounds of 16-byte vectors [vb, ve) (vb a multiple of kFThreads * kVecPer):
 // f(w, v0) per round, vectors at or past ve filled with NaN
@@ -848,13 +856,17 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
                           : sp.nvec;
 
   // ---- read 1: every thread's maximum over the sample ----
-  // (the first round stays in registers for read 2)
+  // (the first round stays in registers for read 2; with segment maxima it
+  // is loaded only if read 2 reads the whole row)
   uint4 w0[kVecPer];
+  auto first_round = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int u = 0; u < kVecPer; ++u) {
-    const int vi = u * kFThreads + t;
-    w0[u] = vi < sp.nvec ? vp[vi] : make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
-  }
+    for (int u = 0; u < kVecPer; ++u) {
+      const int vi = u * kFThreads + t;
+      w0[u] = vi < sp.nvec ? vp[vi] : make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
+    }
+  };
+  if (!segp) first_round();
   // two maxima per thread, over its even and its odd vectors of each round
   float mxa = -INFINITY, mxb = -INFINITY;
   auto take_max = [&](const uint4(&w)[kVecPer], int) __attribute__((always_inline)) {
@@ -940,7 +952,70 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
       }
     }
   };
-  if (sp.nvec > 0) for_rounds_pipe(vp, w0, 0, sp.nvec, collect);
+  // With segment maxima only the segments whose maximum reaches the bound
+  // can hold such tokens: those are read (segment g of chunk k: the vectors
+  // u * 256 + 16 g + i of the chunk, u < 8, i < 16, as row statistics loads
+  // them), 16 segments a round, when there are at most kBins of them.
+  bool seg_read = false;
+  if (segp) {
+    if (t == 0) sh.nsegc = 0;
+    __syncthreads();
+    for (int i0 = 0; i0 < nseg; i0 += kFThreads) {   // whole waves: claim_slot
+      const int i = i0 + t;
+      const bool want = i < nseg && segp[i] >= tf;
+      const uint32_t pos = claim_slot(&sh.nsegc, want);
+      if (want && pos < (uint32_t)kBins) sh.hc[pos] = (uint32_t)i;
+    }
+    __syncthreads();
+    const int nc = uni((int)sh.nsegc);
+    seg_read = nc <= kBins;
+    if (seg_read) {
+      auto collect_seg = [&](const uint4(&w)[kVecPer], int x0, int x1, int x2, int x3) __attribute__((always_inline)) {
+        uint64_t hit = 0;
+#pragma unroll
+        for (int u = 0; u < kVecPer; ++u)
+#pragma unroll
+          for (int j = 0; j < epv; ++j) hit |= (uint64_t)(vec_elem<BF>(w[u], j) >= tf) << (u * epv + j);
+        if (__any(hit != 0)) {
+          uint32_t pos = hit ? atomicAdd(&sh.ncand, (uint32_t)__popcll(hit)) : 0u;
+          while (hit) {
+            const int b = __builtin_ctzll(hit);
+            hit &= hit - 1;
+            const int u = b / epv;
+            const int vi = u == 0 ? x0 : u == 1 ? x1 : u == 2 ? x2 : x3;
+            if (pos < (uint32_t)kCap) {
+              sh.ck[pos] = fkey(round_elem<BF>(w, b));
+              sh.bb.ci[pos] = sp.head + vi * epv + b % epv;
+            }
+            ++pos;
+          }
+        }
+      };
+      for (int r0 = 0; r0 < nc; r0 += kSegRound) {
+        uint4 w[kVecPer];
+        int x[kVecPer];
+#pragma unroll
+        for (int u = 0; u < kVecPer; ++u) {
+          const int f = u * kFThreads + t;     // 16 segments of 128 vectors
+          const int ci = r0 + f / kSegVecs, vs = f % kSegVecs;
+          int vi = -1;
+          if (ci < nc) {
+            const int seg = (int)sh.hc[ci];
+            vi = (seg / kSegPerChunk) * kChunkVecs + (vs / kSegRun) * kThreads + (seg % kSegPerChunk) * kSegRun +
+                 vs % kSegRun;
+            if (vi >= sp.nvec) vi = -1;        // past the row's whole vectors (its tail: read below)
+          }
+          x[u] = vi;
+          w[u] = vi >= 0 ? vp[vi] : make_uint4(kNanFill, kNanFill, kNanFill, kNanFill);
+        }
+        collect_seg(w, x[0], x[1], x[2], x[3]);
+      }
+    }
+  }
+  if (!seg_read && sp.nvec > 0) {
+    if (segp) first_round();
+    for_rounds_pipe(vp, w0, 0, sp.nvec, collect);
+  }
   for_singles<BF>(rowp, sp, collect);
   __syncthreads();
   const int n = uni((int)sh.ncand);

@@ -291,6 +291,52 @@ def test_topk_heavy_tokens_in_one_segment(verifier, torch_mod, dtype):
     gu.check_batch(verifier, b, torch_mod, label=f"top-k, heavy tokens in one segment {dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("where", ["tail", "last_vector", "many_segments"])
+def test_bounded_read_of_the_bound_segments(torch_mod, dtype, where):
+    """The bounded selection reads only the row-statistics segments whose
+    maximum reaches its bound.  The row's largest logits placed in its last
+    few elements (V not a multiple of a vector, rows on 16 bytes: read as
+    single elements), in
+    its last whole vector, or tied at the top across more segments than the
+    list holds (V = 2,097,152: 2048 segments a row, the tie on 600 of them,
+    so the whole row is read); top-k 50 and top-p 0.9 per sequence as in the
+    benchmark's filtered workload, every mode."""
+    import rejection_sampling_verify_06_amd as sv
+    rng = np.random.default_rng(660 + ["tail", "last_vector", "many_segments"].index(where) + (dtype == "f32"))
+    # (the segment maxima bound top-k when there are at least 2k of them: 16 a 32 KB chunk)
+    V = {"tail": 100_003, "last_vector": 163_840, "many_segments": 2_097_152}[where]
+    B = 3 if where == "many_segments" else 8
+    # rows on 16 bytes (the segment maxima exist only for such rows): V = 100,003 in rows 100,008 apart
+    b = make_random_batch(661, B=B, V=V, kmax=2, k_min=1, dtype=dtype, modes=ALL_MODES, scale=(0.5, 2.0),
+                          ld_pad=5 if where == "tail" else 0)
+    vec = 8 if dtype == "bf16" else 4
+    assert (b.target.shape[1] * (2 if dtype == "bf16" else 4)) % 16 == 0
+    for arr in (b.target, b.draft):
+        if arr is None:
+            continue
+        for r in range(arr.shape[0]):
+            row = bf16_widen(arr[r, :V]) if dtype == "bf16" else arr[r, :V].copy()
+            top = float(row.max())
+            if where == "tail":
+                cols = np.arange(V - (V % vec), V)              # the elements after the last whole vector
+                vals = top + np.linspace(3.0, 2.0, cols.size)
+            elif where == "last_vector":
+                cols = np.arange(V - vec, V)
+                vals = top + np.linspace(3.0, 2.0, cols.size)
+            else:
+                cols = rng.choice(V // 1024, size=600, replace=False) * 1024 + rng.integers(0, 1024, size=600)
+                vals = np.full(cols.size, top + 2.0)
+            arr[r, cols] = bf16_round(vals.astype(np.float32)) if dtype == "bf16" else vals.astype(np.float32)
+    b.top_k = np.full(b.batch, 50, np.int32)
+    b.top_p = np.full(b.batch, 0.9, np.float32)
+    v = sv.Verifier(max_batch=16, max_k=4, max_vocab=V, device=0)
+    try:
+        gu.check_batch(v, b, torch_mod, label=f"bounded read of the bound's segments: {where} {dtype} V={V}")
+    finally:
+        v.close()
+
+
 @pytest.mark.parametrize("dtype,V,ks", [("bf16", 152064, (1025, 2000, 5000)), ("f32", 40000, (1100, 3000, 30000)),
                                         ("bf16", 20000, (1500, 19999))])
 def test_large_top_k_count_bracket(verifier, torch_mod, dtype, V, ks):
