@@ -56,7 +56,8 @@
  * the strictly larger tokens is below p (the largest logit always kept).
  * The output then follows the filtered target distribution.  A filtered
  * call runs one more kernel (one block per used row of a filtered sequence)
- * that reads those rows again.
+ * that reads those rows again: whole, or only the parts whose maximum can
+ * reach the row's threshold.
  *
  * Final draw: inverse CDF over the unnormalised weights w (residual, one-hot
  * residual or p_K): t = u * sum(w), emit the first token k whose inclusive
