@@ -80,3 +80,43 @@ def test_max_vocab_filtered(torch_mod, dtype):
         gu.check_batch(v, b, torch_mod, label=f"V {V} {dtype} filtered")
     finally:
         v.close()
+
+
+def _random_filters(seed, B, V):
+    import numpy as np
+    rng = np.random.default_rng(np.random.PCG64([79, seed]))
+    top_k = rng.choice(np.array([0, 1, 3, 10, 40, V], np.int32), size=B).astype(np.int32)
+    top_p = rng.choice(np.array([1.0, 0.3, 0.9, 0.99], np.float32), size=B).astype(np.float32)
+    return top_k, top_p
+
+
+def test_max_k_128_filtered(torch_mod):
+    """Filtered rows at K up to 128: a SAMPLE sequence lists 257 rows (target
+    rows 0..K, then its draft rows) for the filter kernel."""
+    import rejection_sampling_verify_06_amd as sv
+    v = sv.Verifier(max_batch=16, max_k=128, max_vocab=5000, device=0)
+    try:
+        for seed, dtype, k_min in ((3, "bf16", 128), (4, "f32", 0)):
+            b = make_random_batch(740 + seed, B=8, V=300, kmax=128, k_min=k_min, dtype=dtype, modes=ALL_MODES,
+                                  p_hit=0.97, temp=(0.2, 0.4), noise=(0.0, 0.3))
+            b.top_k, b.top_p = _random_filters(seed, b.batch, b.vocab)
+            _, out, _ = gu.check_batch(v, b, torch_mod, label=f"max_k 128 {dtype} filtered")
+            gu.log(f"      K {b.num_draft.tolist()} accepted {out['accepted_len'].tolist()}")
+    finally:
+        v.close()
+
+
+def test_batch_4096_filtered(torch_mod):
+    """Filtered rows of 4096 sequences: the list of the filter's rows is
+    built over the whole batch (16 sequences a thread of the order block)."""
+    import rejection_sampling_verify_06_amd as sv
+    v = sv.Verifier(max_batch=4096, max_k=4, max_vocab=1000, device=0)
+    try:
+        b = make_random_batch(750, B=4096, V=64, kmax=3, dtype="bf16", modes=ALL_MODES)
+        b.top_k, b.top_p = _random_filters(5, b.batch, b.vocab)
+        gu.check_batch(v, b, torch_mod, label="B 4096 filtered")
+        b = make_random_batch(751, B=4093, V=200, kmax=4, dtype="f32", modes=ALL_MODES, ld_pad=3)
+        b.top_k, b.top_p = _random_filters(6, b.batch, b.vocab)
+        gu.check_batch(v, b, torch_mod, label="B 4093 filtered, unaligned rows")
+    finally:
+        v.close()
