@@ -16,13 +16,16 @@
 // statistics' first block writes (the sequences by temperature, the flattest
 // rows, whose filter costs most, first).  The row maximum M comes from the row's
 // chunk partials (for top-p alone, also the row's mass).  Then:
-//   A. the bounded selection (two reads of the row, no per-element atomics):
-//      every thread's two largest logits over a sample of the row (top-k)
-//      or the whole row (top-p alone); a 2-pass radix select over those
-//      1024 maxima gives a bound that every kept token is at or above; the
-//      second read collects the tokens at or above it into LDS; exact
-//      thresholds among them (ranks, or a sort when there are many); the
-//      filtered chunk sums are the kept tokens' masses;
+//   A. the bounded selection (no per-element atomics): a bound that every
+//      kept token is at or above, from the row's segment maxima that the
+//      row statistics wrote (16 per 32 KB; top-k of at most half their
+//      number, and top-p alone), else from every thread's two largest
+//      logits over a sample of the row (top-k) or the whole row (top-p
+//      alone), by ranks or a 2-pass radix select over those maxima; one
+//      read collects the tokens at or above it into LDS (with segment
+//      maxima only the segments whose maximum reaches the bound, when at
+//      most 256 do); exact thresholds among them (ranks, or a sort when
+//      there are many); the filtered chunk sums are the kept tokens' masses;
 //   B. when the bound cannot hold (top-k above 1024, maxima short of the
 //      top-p mass, more tokens than the LDS buffer) and one filter acts
 //      alone: on 16-byte aligned bf16 rows the value table (a sample picks a
@@ -2152,8 +2155,8 @@ __device__ __forceinline__ void filter_slot(const Params& P, FiltShared& sh, int
     filter_row<false>(P, sh, pp, rowp, nch, ce, c, mc, M, use_k, topk, use_p, topp, xs, segp, tau_out);
 }
 
-// One block per row of the list row_stats wrote (the filter's rows, costliest
-// first; blocks past its count return at once); four blocks per CU (8 waves
+// One block per row of the list row_stats wrote (the filter's rows, the
+// flattest first; blocks past its count return at once); four blocks per CU (8 waves
 // per SIMD: at most 64 VGPRs).
 __global__ void __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) k_filter(Params P) {
   __shared__ FiltShared sh;
