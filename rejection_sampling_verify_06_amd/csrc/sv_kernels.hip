@@ -7,9 +7,11 @@
 //             reduced in float32 to (max of the raw logits, sum of
 //             exp2(x*c - round(max*c)), lowest-index argmax for greedy rows):
 //             block max first, then one sum against it.  No inter-block
-//             communication.  In a filtered call one more block (the first)
-//             orders the sequences by temperature and writes the list of the
-//             rows the filter kernel takes, in that order.
+//             communication.  In a filtered call every block also writes
+//             its chunk's 16 segment maxima (one per 16-lane group: the bound
+//             of the filter's bounded selection), and one more block (the
+//             first) orders the sequences by temperature and writes the list
+//             of the rows the filter kernel takes, in that order.
 // final       grid (nsplit, B) of 1024-thread blocks.  Wave 0 runs the
 //             acceptance scan of its sequence: validates it, merges each
 //             row's chunk partials in chunk order (lane r: row r), computes
