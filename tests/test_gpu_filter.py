@@ -117,6 +117,24 @@ def test_c3_with_filters_bench_context(torch_mod):
         v.close()
 
 
+@pytest.mark.parametrize("config", [2, 4])
+def test_c2_c4_with_filters_full_size(torch_mod, config):
+    """The same filters on the other benchmark shapes: float32 rows of
+    128,256 tokens (C2: the bracket searches, the split final draw over
+    eight blocks a sequence) and one-hot and greedy bf16 rows (C4: greedy
+    ignores the filter, one-hot draws from the filtered p)."""
+    import rejection_sampling_verify_06_amd as sv
+    v = sv.Verifier(max_batch=128, max_k=8, max_vocab=128256, device=0)
+    try:
+        for step, (k, p) in enumerate([(50, 0.9), (0, 0.95), (2000, 1.0)]):
+            b = make_config_batch(config, step)
+            b.top_k = np.full(b.batch, k, np.int32)
+            b.top_p = np.full(b.batch, p, np.float32)
+            gu.check_batch(v, b, torch_mod, label=f"C{config} step {step} top_k={k} top_p={p}")
+    finally:
+        v.close()
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_bounded_selection_edges(verifier, torch_mod, dtype):
     """Top-k at the edges of the bounded selection (1, 1023, 1024; 1025 takes
