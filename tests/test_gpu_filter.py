@@ -135,6 +135,22 @@ def test_c2_c4_with_filters_full_size(torch_mod, config):
         v.close()
 
 
+def test_c3_strict_with_filters_full_size(torch_mod):
+    """C3 in strict sample-match mode with the three filters: the filtered
+    target rows' mass below the proposal (the strict draw's split) at the
+    benchmark shape."""
+    import rejection_sampling_verify_06_amd as sv
+    v = sv.Verifier(max_batch=256, max_k=8, max_vocab=152064, device=0)
+    try:
+        for step, (k, p) in enumerate([(50, 0.9), (0, 0.95), (2000, 1.0)]):
+            b = make_config_batch(3, step, strict=True)
+            b.top_k = np.full(b.batch, k, np.int32)
+            b.top_p = np.full(b.batch, p, np.float32)
+            gu.check_batch(v, b, torch_mod, label=f"C3 strict step {step} top_k={k} top_p={p}")
+    finally:
+        v.close()
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_bounded_selection_edges(verifier, torch_mod, dtype):
     """Top-k at the edges of the bounded selection (1, 1023, 1024; 1025 takes
