@@ -148,8 +148,8 @@ typedef struct spec_verify_args {
 /* Create a context on HIP device `device` for batches of at most max_batch
  * sequences, K_s <= max_k (1..128) and vocab <= max_vocab.  Allocates the
  * context's device scratch (per-chunk partial row statistics and, for the
- * filters, 16 segment maxima per chunk; per-sequence final-draw records
- * and tile sums; defaults for NULL optional inputs): about 80 bytes per 8192
+ * filters, 32 segment maxima per chunk; per-sequence final-draw records
+ * and tile sums; defaults for NULL optional inputs): about 144 bytes per 8192
  * vocabulary entries per row slot, max_batch * (2 * max_k + 1) slots, plus
  * small per-slot and per-sequence arrays (among them the filter's list of
  * rows).  The caller owns every input and output
@@ -177,7 +177,7 @@ int spec_verify_run(spec_verify_ctx* ctx, const spec_verify_args* args, void* hi
  * SV_NOALLOC_SCRATCH_BYTES bytes in the library's device data, which every
  * GPU the library runs on holds until the process ends; it is laid out per
  * call for exactly the call's sizes (about 16 bytes per 32 KB chunk of each
- * of batch * (2 * max_k + 1) row slots, four times that more with top_k /
+ * of batch * (2 * max_k + 1) row slots, eight times that more with top_k /
  * top_p, plus small per-sequence arrays).  max_k (1..128) plays the part of
  * the context's max_k (K_s > max_k: status SV_ST_K_TOO_LARGE); batch <= 4096.
  * A call that would need more scratch returns SV_ERR_CAPACITY with the

@@ -18,7 +18,7 @@
 // chunk partials (for top-p alone, also the row's mass).  Then:
 //   A. the bounded selection (no per-element atomics): a bound that every
 //      kept token is at or above, from the row's segment maxima that the
-//      row statistics wrote (16 per 32 KB; top-k of at most half their
+//      row statistics wrote (32 per 32 KB; top-k of at most half their
 //      number, and top-p alone), else from every thread's two largest
 //      logits over a sample of the row (top-k) or the whole row (top-p
 //      alone), by ranks or a 2-pass radix select over those maxima; one
@@ -535,13 +535,17 @@ __device__ __forceinline__ float vec_elem(const uint4& w, int j) {
   return __uint_as_float((j & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
 }
 constexpr uint32_t kNanFill = 0x7FC07FC0u;     // NaN as one fp32 word and as two bf16 halves
-// a row-statistics segment (the 16-lane group that wrote its maximum): 8 runs
-// of 16 vectors, kThreads vectors apart, in a chunk of 2048 16-byte vectors
+// a row-statistics segment (the 8-lane group that wrote its maximum): 8 runs
+// of 8 vectors (128 bytes each), kThreads vectors apart, in a chunk of 2048
+// 16-byte vectors
 constexpr int kChunkVecs = kChunkBytes / 16;
 constexpr int kSegRun = kThreads / kSegPerChunk;
 constexpr int kSegVecs = kChunkVecs / kSegPerChunk;
 constexpr int kSegRound = kFThreads * kVecPer / kSegVecs;   // segments a round of the bounded selection's read 2
-static_assert(kSegRun == 16 && kSegVecs == 128 && kSegRound == 16, "the row statistics' segment layout");
+static_assert(kSegRun == 8 && kSegVecs == 64 && kSegRound == 32, "the row statistics' segment layout");
+// top-k from at most this many segment maxima: the k-th largest by ranks, all
+// pairs in LDS; from more, the radix select (cheaper at C3's 320 a row)
+constexpr int kRankSegs = 256;
 
 // rounds of 16-byte vectors [vb, ve) (vb a multiple of kFThreads * kVecPer):
 // f(w, v0) per round, vectors at or past ve filled with NaN
@@ -882,10 +886,10 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
       }
   };
   if (segp) {
-    // top-p alone, or more than kFThreads segments: every thread folds the
+    // top-p alone, or more than kRankSegs segments: every thread folds the
     // segments t, t + 1024, ... and t + 512, t + 1536, ... (maxima of
     // disjoint parts)
-    if (nseg > kFThreads || !use_k) {
+    if (nseg > kRankSegs || !use_k) {
       for (int i = t; i < nseg; i += 2 * kFThreads) mxa = fmaxf(mxa, segp[i]);
       for (int i = t + kFThreads; i < nseg; i += 2 * kFThreads) mxb = fmaxf(mxb, segp[i]);
     }
@@ -903,7 +907,7 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
   }
   const uint32_t ka = fkey(mxa), kb = fkey(mxb);   // no elements: the key of -inf, mass 0
   uint32_t bound;
-  if (segp && use_k && nseg <= kFThreads) {
+  if (segp && use_k && nseg <= kRankSegs) {
     // few segment maxima: the topk-th largest by ranks (ties by position),
     // one per thread, against all of them in LDS
     const uint32_t my = t < nseg ? fkey(segp[t]) : 0u;
@@ -957,8 +961,8 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
   };
   // With segment maxima only the segments whose maximum reaches the bound
   // can hold such tokens: those are read (segment g of chunk k: the vectors
-  // u * 256 + 16 g + i of the chunk, u < 8, i < 16, as row statistics loads
-  // them), 16 segments a round, when there are at most kBins of them.
+  // u * 256 + 8 g + i of the chunk, u < 8, i < 8, as row statistics loads
+  // them), 32 segments a round, when there are at most kBins of them.
   bool seg_read = false;
   if (segp) {
     if (t == 0) sh.nsegc = 0;
@@ -999,7 +1003,7 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
         int x[kVecPer];
 #pragma unroll
         for (int u = 0; u < kVecPer; ++u) {
-          const int f = u * kFThreads + t;     // 16 segments of 128 vectors
+          const int f = u * kFThreads + t;     // 32 segments of 64 vectors
           const int ci = r0 + f / kSegVecs, vs = f % kSegVecs;
           int vi = -1;
           if (ci < nc) {

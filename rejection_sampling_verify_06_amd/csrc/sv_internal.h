@@ -13,7 +13,7 @@ namespace sv {
 
 constexpr int kThreads = 256;           // row-statistics blocks: 4 waves of 64
 constexpr int kChunkBytes = 32768;      // bytes of one logit row streamed by one row-stats block
-constexpr int kSegPerChunk = 16;        // 16-lane groups of a row-stats block: the segments whose maxima it writes
+constexpr int kSegPerChunk = 32;        // 8-lane groups of a row-stats block: the segments whose maxima it writes
 constexpr int kTileElems = 8192;        // elements of a tile of the final draw
 constexpr int kMaxK = 128;
 constexpr int kMaxTiles = 256;          // => vocab <= 2,097,152
@@ -91,7 +91,7 @@ struct Params {
   // s*slots + max_k + 1 + i
   Partial* partials;  // chunk k of slot r at r*nch_max + k
   float* segmax;      // or null: segment j of chunk k of slot r at (r*nch_max + k)*kSegPerChunk + j, the
-                      // largest logit of a 16-lane group's elements (written by the vector path only)
+                      // largest logit of an 8-lane group's elements (written by the vector path only)
   float* xval;        // per slot: the row's logit at its proposed token
   int32_t* ptok;      // [B * max_k]: the proposed tokens, copied by row statistics
   SeqFinal* fin;      // [B]

@@ -8,7 +8,7 @@
 //             exp2(x*c - round(max*c)), lowest-index argmax for greedy rows):
 //             block max first, then one sum against it.  No inter-block
 //             communication.  In a filtered call every block also writes
-//             its chunk's 16 segment maxima (one per 16-lane group: the bound
+//             its chunk's 32 segment maxima (one per 8-lane group: the bound
 //             of the filter's bounded selection), and one more block (the
 //             first) orders the sequences by temperature and writes the list
 //             of the rows the filter kernel takes, in that order.
@@ -53,7 +53,7 @@ namespace sv {
 namespace {
 
 using namespace wave;   // kWave and the DPP reductions and scans (sv_wave.h)
-static_assert(kSegPerChunk * 16 == kThreads, "one segment maximum per 16-lane group of a row-stats block");
+static_assert(kSegPerChunk * 8 == kThreads, "one segment maximum per 8-lane group of a row-stats block");
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = kThreads / kWave;
@@ -977,7 +977,7 @@ __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp,
   float tmx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < N; ++k) tmx = fmaxf(tmx, f[k]);
-  const float rmx = row16_max(tmx);        // the maximum of this thread's 16-lane group
+  const float rmx = row8_max(tmx);         // the maximum of this thread's 8-lane group
   const float mx = wave_max(rmx);
   if (lane == 0) sh.m[wv] = mx;
   __syncthreads();
@@ -988,8 +988,8 @@ __device__ __forceinline__ void row_stats_vec(const Params& P, const char* rowp,
   if (own.s < 0) return;                   // the whole block: inconsistent layout
   if (P.segmax) {                          // filtered calls: the groups' maxima bound the filter
     const int sbs = __builtin_amdgcn_readfirstlane(sh.sb);
-    if (sbs >= 0 && (lane & 15) == 0)
-      P.segmax[((int64_t)sbs * P.nch_max + chunk) * kSegPerChunk + wv * (kWave / 16) + (lane >> 4)] = rmx;
+    if (sbs >= 0 && (lane & 7) == 0)
+      P.segmax[((int64_t)sbs * P.nch_max + chunk) * kSegPerChunk + wv * (kWave / 8) + (lane >> 3)] = rmx;
   }
   const float M = fmaxf(fmaxf(sh.m[0], sh.m[1]), fmaxf(sh.m[2], sh.m[3]));
   const float c = row_scale(own.md, own.T);

@@ -52,13 +52,13 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// the maximum over each row of 16 lanes, in every lane of the row
-__device__ __forceinline__ float row16_max(float v) {
+// the maximum over each group of 8 lanes (half a DPP row), in every lane of
+// the group: the quads first, then each quad against the mirrored other one
+__device__ __forceinline__ float row8_max(float v) {
   const float n = -INFINITY;
   v = fmaxf(v, dpp_f<kDppQuadXor1>(n, v));
   v = fmaxf(v, dpp_f<kDppQuadXor2>(n, v));
   v = fmaxf(v, dpp_f<kDppRowHalfMirror>(n, v));
-  v = fmaxf(v, dpp_f<kDppRowMirror>(n, v));
   return v;
 }
 

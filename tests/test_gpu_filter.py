@@ -286,22 +286,22 @@ def test_topp_bracket_search_flat_rows(verifier, torch_mod, dtype, grid):
 
 def _segment_elements(dtype: str, V: int, chunk: int, group: int) -> np.ndarray:
     """Element indices of one row-statistics segment: the elements that the
-    16 lanes of `group` (of 16) load from 32 KB chunk `chunk`, 16-byte
+    8 lanes of `group` (of 32) load from 32 KB chunk `chunk`, 16-byte
     vectors handed out to 256 threads in turn."""
     vec = 8 if dtype == "bf16" else 4
     ce = 32768 // (2 if dtype == "bf16" else 4)
     e = np.arange(chunk * ce, min(V, (chunk + 1) * ce))
     thread = ((e - chunk * ce) // vec) % 256
-    return e[thread // 16 == group]
+    return e[thread // 8 == group]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_topk_heavy_tokens_in_one_segment(verifier, torch_mod, dtype):
     """Top-k whose largest logits all sit in one segment of the row statistics:
     the k-th largest segment maximum then lies far below the k-th largest
-    logit, so the bound from the segment maxima admits many tokens: about 130
-    for top-k 50, and on every other row, where 1500 tokens tie just below the
-    heavy ones, more than the candidate buffer holds (the histogram path then
+    logit, so the bound from the segment maxima admits many more tokens than
+    k, and on every other row, where 1500 tokens tie just below the heavy
+    ones, more than the candidate buffer holds (the histogram path then
     decides)."""
     rng = np.random.default_rng(640 + (dtype == "bf16"))
     V, B, K = 100_000, 6, 2
@@ -317,7 +317,7 @@ def test_topk_heavy_tokens_in_one_segment(verifier, torch_mod, dtype):
                 arr[r, rng.choice(np.arange(3 * 32768 // 4, V), size=tied.size, replace=False)] = (
                     bf16_round(tied) if dtype == "bf16" else tied)
             heavy = (top + np.linspace(2.0, 1.0, 64)).astype(np.float32)   # the row's 64 largest
-            seg = _segment_elements(dtype, V, int(rng.integers(0, 3)), int(rng.integers(0, 16)))
+            seg = _segment_elements(dtype, V, int(rng.integers(0, 3)), int(rng.integers(0, 32)))
             cols = rng.choice(seg, size=heavy.size, replace=False)
             arr[r, cols] = bf16_round(heavy) if dtype == "bf16" else heavy
     b.top_k = rng.choice(np.array([10, 50, 64], np.int32), size=B)
@@ -333,12 +333,12 @@ def test_bounded_read_of_the_bound_segments(torch_mod, dtype, where):
     few elements (V not a multiple of a vector, rows on 16 bytes: read as
     single elements), in
     its last whole vector, or tied at the top across more segments than the
-    list holds (V = 2,097,152: 2048 segments a row, the tie on 600 of them,
-    so the whole row is read); top-k 50 and top-p 0.9 per sequence as in the
+    list holds (V = 2,097,152: 4096 segments a bf16 row, 8192 a float32 one,
+    the tie on about 600 of them, so the whole row is read); top-k 50 and top-p 0.9 per sequence as in the
     benchmark's filtered workload, every mode."""
     import rejection_sampling_verify_06_amd as sv
     rng = np.random.default_rng(660 + ["tail", "last_vector", "many_segments"].index(where) + (dtype == "f32"))
-    # (the segment maxima bound top-k when there are at least 2k of them: 16 a 32 KB chunk)
+    # (the segment maxima bound top-k when there are at least 2k of them: 32 a 32 KB chunk)
     V = {"tail": 100_003, "last_vector": 163_840, "many_segments": 2_097_152}[where]
     B = 3 if where == "many_segments" else 8
     # rows on 16 bytes (the segment maxima exist only for such rows): V = 100,003 in rows 100,008 apart
