@@ -705,13 +705,19 @@ __device__ __forceinline__ void mass_prefix(FiltShared& sh, const uint32_t* keys
   }
 }
 
+constexpr uint32_t kKeyNegInf = 0x007FFFFFu;   // fkey(-inf)
+
 // A lower bound of the key at a crossing among two keys per thread: the
 // need-th largest (by count) or the key where the mass from the top first
 // reaches `target` (by mass), taken 8 bits a pass for `passes` passes; the
 // bits below are returned as zeros (so the result is at most the exact key,
 // which it equals after 4 passes).  Leaves sh.bin < 0 when the first pass
 // never reaches the target (mass only; the key returned is then
-// meaningless).  Every thread of the block calls it.
+// meaningless).  Keys of -inf (threads without elements) are left out: by
+// mass they weigh 0, and by count they could only be the answer when fewer
+// than `need` finite keys exist, where the result 0 leads the caller to the
+// same bound, the key of -inf; left in, they all hit one histogram bin, and
+// such LDS atomics serialise.  Every thread of the block calls it.
 template <bool BY_MASS>
 __device__ __forceinline__ uint32_t radix_select_regs(FiltShared& sh, uint32_t ka, unsigned long long ma,
                                                       uint32_t kb, unsigned long long mb, uint32_t need,
@@ -725,12 +731,12 @@ __device__ __forceinline__ uint32_t radix_select_regs(FiltShared& sh, uint32_t k
       sh.rm[t] = 0;
     }
     __syncthreads();
-    if ((ka & pmask) == prefix) {
+    if ((ka & pmask) == prefix && ka != kKeyNegInf) {
       const int by = (ka >> shift) & 0xFF;
       atomicAdd(&sh.rc[by], 1u);
       if (BY_MASS) atomicAdd(&sh.rm[by], ma);
     }
-    if ((kb & pmask) == prefix) {
+    if ((kb & pmask) == prefix && kb != kKeyNegInf) {
       const int by = (kb >> shift) & 0xFF;
       atomicAdd(&sh.rc[by], 1u);
       if (BY_MASS) atomicAdd(&sh.rm[by], mb);
@@ -754,7 +760,6 @@ constexpr int kTargetCand = 160;               // top-k: tokens expected at or a
 // 16 key bits (sign, exponent, 7 mantissa bits) of the bound: within 2^-7
 // of the exact maximum, for 8 barriers instead of 16
 constexpr int kBoundPasses = 2;
-constexpr uint32_t kKeyNegInf = 0x007FFFFFu;   // fkey(-inf)
 
 // Exact thresholds among the n candidates in sh.ck after sorting them
 // (largest first): the top-k key (the k-th), the kept set's end, then the
