@@ -21,7 +21,8 @@
 //      row statistics wrote (32 per 32 KB; top-k of at most half their
 //      number, and top-p alone), else from every thread's two largest
 //      logits over a sample of the row (top-k) or the whole row (top-p
-//      alone), by ranks or a 2-pass radix select over those maxima; one
+//      alone): the k-th largest of at most 512 segment maxima by ballots in
+//      one wave, else a 2-pass radix select over the maxima; one
 //      read collects the tokens at or above it into LDS (with segment
 //      maxima only the segments whose maximum reaches the bound, when at
 //      most 256 do); exact thresholds among them (ranks, or a sort when
@@ -543,9 +544,9 @@ constexpr int kSegRun = kThreads / kSegPerChunk;
 constexpr int kSegVecs = kChunkVecs / kSegPerChunk;
 constexpr int kSegRound = kFThreads * kVecPer / kSegVecs;   // segments a round of the bounded selection's read 2
 static_assert(kSegRun == 8 && kSegVecs == 64 && kSegRound == 32, "the row statistics' segment layout");
-// top-k from at most this many segment maxima: the k-th largest by ranks, all
-// pairs in LDS; from more, the radix select (cheaper at C3's 320 a row)
-constexpr int kRankSegs = 256;
+// top-k from at most this many segment maxima: wave 0 holds them all (8 a
+// lane) and finds the k-th largest bit by bit; from more, the radix select
+constexpr int kBallotSegs = 8 * kWave;
 
 // rounds of 16-byte vectors [vb, ve) (vb a multiple of kFThreads * kVecPer):
 // f(w, v0) per round, vectors at or past ve filled with NaN
@@ -891,10 +892,10 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
       }
   };
   if (segp) {
-    // top-p alone, or more than kRankSegs segments: every thread folds the
+    // top-p alone, or more than kBallotSegs segments: every thread folds the
     // segments t, t + 1024, ... and t + 512, t + 1536, ... (maxima of
     // disjoint parts)
-    if (nseg > kRankSegs || !use_k) {
+    if (nseg > kBallotSegs || !use_k) {
       for (int i = t; i < nseg; i += 2 * kFThreads) mxa = fmaxf(mxa, segp[i]);
       for (int i = t + kFThreads; i < nseg; i += 2 * kFThreads) mxb = fmaxf(mxb, segp[i]);
     }
@@ -912,23 +913,33 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
   }
   const uint32_t ka = fkey(mxa), kb = fkey(mxb);   // no elements: the key of -inf, mass 0
   uint32_t bound;
-  if (segp && use_k && nseg <= kRankSegs) {
-    // few segment maxima: the topk-th largest by ranks (ties by position),
-    // one per thread, against all of them in LDS
-    const uint32_t my = t < nseg ? fkey(segp[t]) : 0u;
-    if (t < nseg) sh.ck[t] = my;
-    __syncthreads();
-    if (t < nseg) {
-      uint32_t above = 0;
-      for (int j = 0; j < nseg; ++j) {
-        const uint32_t kj = sh.ck[j];
-        above += (kj > my || (kj == my && j < t)) ? 1u : 0u;
+  if (segp && use_k && nseg <= kBallotSegs) {
+    // the topk-th largest segment maximum: wave 0 holds their keys (key 0,
+    // below every maximum's, where there is none) and builds, bit by bit
+    // from the top, the largest key that at least topk of them reach -- a
+    // ballot and a bit count per key slot and bit, no LDS atomics and no
+    // barrier until the result
+    if (t < kWave) {
+      __builtin_amdgcn_s_setprio(3);           // the block's other waves wait for this one
+      uint32_t k[kBallotSegs / kWave];
+#pragma unroll
+      for (int j = 0; j < kBallotSegs / kWave; ++j) {
+        const int i = t + j * kWave;
+        k[j] = i < nseg ? fkey(segp[i]) : 0u;
       }
-      if (above == (uint32_t)topk - 1) sh.segb = my;   // one thread: ranks are distinct
+      uint32_t res = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = res | (1u << bit);
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < kBallotSegs / kWave; ++j) cnt += (uint32_t)__popcll(__ballot(k[j] >= cand));
+        if (cnt >= (uint32_t)topk) res = cand;
+      }
+      if (t == 0) sh.segb = res;
+      __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();
     bound = sh.segb;
-    __syncthreads();                           // sh.ck is the candidates' buffer from here on
   } else if (use_k) {
     bound = radix_select_regs<false>(sh, ka, 0ull, kb, 0ull, (uint32_t)topk, 0.0, kBoundPasses);
   } else {
