@@ -547,6 +547,7 @@ static_assert(kSegRun == 8 && kSegVecs == 64 && kSegRound == 32, "the row statis
 // top-k from at most this many segment maxima: wave 0 holds them all (8 a
 // lane) and finds the k-th largest bit by bit; from more, the radix select
 constexpr int kBallotSegs = 8 * kWave;
+static_assert(kBallotSegs <= kCap, "the ballot search reads the segment maxima from their copy in sh.ck");
 
 // rounds of 16-byte vectors [vb, ve) (vb a multiple of kFThreads * kVecPer):
 // f(w, v0) per round, vectors at or past ve filled with NaN
@@ -853,6 +854,7 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
   const RowSplit sp = split_row<BF>(rowp, V);
   const uint4* vp = (const uint4*)(rowp + (size_t)sp.head * (BF ? 2 : 4));
   constexpr int kRound = kFThreads * kVecPer;  // vectors per round
+  const bool seg_lds = segp && nseg <= kCap;   // the segment maxima are in sh.ck (copied at the row's start)
   // Top-k reads only a sample here, the first nva whole vectors: the k-th
   // largest of any subset is at most the row's k-th largest, and a fraction
   // k/kTargetCand of the row leaves about kTargetCand tokens at or above the
@@ -896,8 +898,9 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
     // segments t, t + 1024, ... and t + 512, t + 1536, ... (maxima of
     // disjoint parts)
     if (nseg > kBallotSegs || !use_k) {
-      for (int i = t; i < nseg; i += 2 * kFThreads) mxa = fmaxf(mxa, segp[i]);
-      for (int i = t + kFThreads; i < nseg; i += 2 * kFThreads) mxb = fmaxf(mxb, segp[i]);
+      for (int i = t; i < nseg; i += 2 * kFThreads) mxa = fmaxf(mxa, seg_lds ? __uint_as_float(sh.ck[i]) : segp[i]);
+      for (int i = t + kFThreads; i < nseg; i += 2 * kFThreads)
+        mxb = fmaxf(mxb, seg_lds ? __uint_as_float(sh.ck[i]) : segp[i]);
     }
   } else {
     take_max(w0, 0);
@@ -925,7 +928,7 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
 #pragma unroll
       for (int j = 0; j < kBallotSegs / kWave; ++j) {
         const int i = t + j * kWave;
-        k[j] = i < nseg ? fkey(segp[i]) : 0u;
+        k[j] = i < nseg ? fkey(__uint_as_float(sh.ck[i])) : 0u;
       }
       uint32_t res = 0;
       for (int bit = 31; bit >= 0; --bit) {
@@ -985,7 +988,7 @@ __device__ __forceinline__ bool bounded_filter(FiltShared& sh, const char* rowp,
     __syncthreads();
     for (int i0 = 0; i0 < nseg; i0 += kFThreads) {   // whole waves: claim_slot
       const int i = i0 + t;
-      const bool want = i < nseg && segp[i] >= tf;
+      const bool want = i < nseg && (seg_lds ? __uint_as_float(sh.ck[i]) : segp[i]) >= tf;
       const uint32_t pos = claim_slot(&sh.nsegc, want);
       if (want && pos < (uint32_t)kBins) sh.hc[pos] = (uint32_t)i;
     }
@@ -2108,6 +2111,18 @@ __device__ __forceinline__ void filter_slot(const Params& P, FiltShared& sh, int
 
   const int nch = draft ? P.nch_d : P.nch_t;
   Partial* pp = P.partials + ((int64_t)s * P.slots + r) * P.nch_max;
+  // the row's segment maxima: written by the row statistics' vector path
+  // (rows of this matrix 16-byte aligned, V of a vector or more); used for
+  // top-k of at most half their number, where they bound it closely, and
+  // for top-p alone
+  const int bf = draft ? P.d_bf16 : P.t_bf16;
+  const bool vec_rows = (draft ? P.d_vec : P.t_vec) && P.V >= (bf ? 8 : 4);
+  const float* segp = (P.segmax && vec_rows && (use_k ? 2 * topk <= nch * kSegPerChunk : use_p))
+                          ? P.segmax + (pp - P.partials) * kSegPerChunk : nullptr;
+  // wave 1 copies them to LDS (sh.ck is not used before the bound) while
+  // wave 0 runs the setup below
+  if (wv == 1 && segp && nch * kSegPerChunk <= kCap)
+    for (int i = lane; i < nch * kSegPerChunk; i += kWave) sh.ck[i] = __float_as_uint(segp[i]);
   if (wv == 0) {
     __builtin_amdgcn_s_setprio(3);           // the block's other waves wait for this one
     // the packed layout (as the scan checks it) and this sequence's offset
@@ -2156,19 +2171,11 @@ __device__ __forceinline__ void filter_slot(const Params& P, FiltShared& sh, int
 
   const int offd = uni(sh.offd);
   const int64_t row = draft ? (int64_t)offd + (r - mk - 1) : (int64_t)offd + s + r;
-  const int bf = draft ? P.d_bf16 : P.t_bf16;
   const char* rowp = (const char*)(draft ? P.dft : P.tgt) + row * (draft ? P.ld_d : P.ld_t) * (bf ? 2 : 4);
   const float mc = M * c;
   const int ce = draft ? P.ce_d : P.ce_t;
   const int xs = (md == kModeStrict && !draft && r < K) ? P.ptok[(int64_t)s * mk + r] : -1;
   float* tau_out = P.tau + (int64_t)s * P.slots + r;
-  // the row's segment maxima: written by the row statistics' vector path
-  // (rows of this matrix 16-byte aligned, V of a vector or more); used for
-  // top-k of at most half their number, where they bound it closely, and
-  // for top-p alone
-  const bool vec_rows = (draft ? P.d_vec : P.t_vec) && P.V >= (bf ? 8 : 4);
-  const float* segp = (P.segmax && vec_rows && (use_k ? 2 * topk <= nch * kSegPerChunk : use_p))
-                          ? P.segmax + (pp - P.partials) * kSegPerChunk : nullptr;
   if (bf)
     filter_row<true>(P, sh, pp, rowp, nch, ce, c, mc, M, use_k, topk, use_p, topp, xs, segp, tau_out);
   else
